@@ -1,0 +1,73 @@
+"""Group-wise asymmetric min-max quantizer (oracle, test infrastructure only).
+
+Sources:
+* "LLM quantization principles: GPTQ, AWQ, GGUF", §2.1: q = round(x / scale)
+  + zero_point; the linear min-max mapping scale = (max - min) / (qmax - qmin).
+* "Quantized deployment, 1.5 TB to 250 GB", §2.1: dequantization
+  r = (q - zero_point) * scale.
+* "Calibration algorithms guide", §2.2: each group of weights gets its own
+  min/max, hence its own scale and zero-point.
+
+Conventions the pages leave open (parity unpinned by the pages; fixed here and
+followed by the device path):
+* the range is widened to include 0: [min(0, min v), max(0, max v)], so the
+  zero-point lies in [0, maxq] and 0 is exactly representable;
+* an all-zero group uses the range [-1, 1];
+* zero = round((-xmin * maxq) / (xmax - xmin)) rather than round(-xmin / scale),
+  a form that is stable at exact ties for bf16 inputs;
+* codes are unsigned in [0, 2^bits - 1], clamped after adding the zero-point;
+* rounding is round-half-to-even (IEEE rint) and every division is a true
+  division, never a multiplication by a reciprocal;
+* the decision precision is fp32 (see the package docstring).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f32(x) -> np.ndarray:
+    """Round fp64 values to the nearest fp32 value, returned as fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def group_params(v: np.ndarray, bits: int, sym: bool = False):
+    """Scale and zero-point of each row of ``v`` ([rows, group_len] current values).
+
+    Returns (scale, zero), both fp64 arrays holding fp32 values; zero is integral.
+    Asymmetric: min-max range with 0 included.  Symmetric: zero-point fixed at
+    the middle of the code range, scale = 2*max|v| / maxq (the symmetric variant
+    of "LLM quantization principles" §2.3, expressed on unsigned codes).
+    """
+    maxq = float(2 ** bits - 1)
+    v32 = f32(v)
+    if sym:
+        amax = np.abs(v32).max(axis=1)
+        amax = np.where(amax == 0.0, 1.0, amax)
+        scale = f32(f32(2.0 * amax) / maxq)
+        zero = np.full_like(scale, np.floor((maxq + 1.0) / 2.0))
+        return scale, zero
+    xmin = np.minimum(v32.min(axis=1), 0.0)
+    xmax = np.maximum(v32.max(axis=1), 0.0)
+    degenerate = xmin == xmax
+    xmin = np.where(degenerate, -1.0, xmin)
+    xmax = np.where(degenerate, 1.0, xmax)
+    span = f32(xmax - xmin)
+    scale = f32(span / maxq)
+    zero = np.rint(f32(f32(-xmin * maxq) / span))
+    return scale, zero
+
+
+def pre_round_value(w: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """w / scale in fp32 (the value whose rounding gives the code before the offset)."""
+    return f32(f32(w) / scale)
+
+
+def quantize_codes(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int) -> np.ndarray:
+    """q = clamp(round(w / scale) + zero, 0, maxq), ties to even; fp64 integral values."""
+    maxq = float(2 ** bits - 1)
+    return np.clip(np.rint(pre_round_value(w, scale)) + zero, 0.0, maxq)
+
+
+def dequantize(q: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """r = (q - zero) * scale, in fp64 (exact for fp32 scale and small integers)."""
+    return (np.asarray(q, dtype=np.float64) - zero) * scale

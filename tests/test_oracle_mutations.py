@@ -1,0 +1,91 @@
+"""Mutation tests: plant a plausible mistake in the oracle's source, show a pin catches it.
+
+Each mutant is the oracle module's source with one textual change (a dropped
+term, a flipped sign, a transposed operand, a wrong reduction), executed as a
+fresh module inside the ``oracle`` package and swapped in for the duration of
+one pin.  CPU only.
+"""
+import inspect
+import sys
+import types
+
+import pytest
+
+import oracle
+
+# the package re-exports functions named like their modules (oracle.prepare is the
+# function), so take the modules themselves from sys.modules
+GPTQ_MOD = sys.modules["oracle.gptq"]
+HESS_MOD = sys.modules["oracle.hessian"]
+PREP_MOD = sys.modules["oracle.prepare"]
+QUANT_MOD = sys.modules["oracle.quantizer"]
+
+import test_oracle_gptq as tg
+import test_oracle_hessian_prepare as th
+import test_oracle_quantizer as tq
+
+
+def _mutant(mod, old, new):
+    src = inspect.getsource(mod)
+    assert src.count(old) >= 1, old
+    src = src.replace(old, new)
+    m = types.ModuleType(mod.__name__ + "_mutant")
+    m.__package__ = "oracle"
+    sys.modules[m.__name__] = m  # dataclasses resolve their module through sys.modules
+    try:
+        exec(compile(src, m.__name__, "exec"), m.__dict__)
+    finally:
+        del sys.modules[m.__name__]
+    return m
+
+
+MUTANTS = [
+    # (module, old text, new text, names to swap into ``oracle``, pin to run)
+    (GPTQ_MOD, "W1[:, j + 1:] -= np.outer(e, U[c, c + 1:i1])",
+     "W1[:, j + 1:] += np.outer(e, U[c, c + 1:i1])", ["gptq_quantize"],
+     lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
+    (GPTQ_MOD, "Wp[:, i1:] -= E @ U[i:i1, i1:]",
+     "Wp[:, i1:] -= 0.0 * (E @ U[i:i1, i1:])", ["gptq_quantize"],
+     lambda gd: tg.test_block_size_invariance()),
+    (GPTQ_MOD, "W1[:, j + 1:] -= np.outer(e, U[c, c + 1:i1])",
+     "W1[:, j + 1:] -= np.outer(e, U[c + 1:i1, c])", ["gptq_quantize"],
+     lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
+    (GPTQ_MOD, "e = (w - dequantize(q, scale, zero)) / U[c, c]",
+     "e = (w - dequantize(q, scale, zero)) * U[c, c]", ["gptq_quantize"],
+     lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
+    (GPTQ_MOD, "scale, zero = group_params(W1[:, j:j + glen], bits, sym)",
+     "scale, zero = group_params(W[:, perm][:, c:c + glen], bits, sym)", ["gptq_quantize"],
+     lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
+    (QUANT_MOD, "zero = np.rint(f32(f32(-xmin * maxq) / span))",
+     "zero = np.rint(f32(f32(xmin * maxq) / span))", ["group_params"],
+     lambda gd: tq.test_codes_and_zero_in_range(4)),
+    (QUANT_MOD, "scale = f32(span / maxq)", "scale = f32(span / (maxq + 1.0))",
+     ["group_params"], lambda gd: tq.test_worked_example_minmax_int8(gd)),
+    (PREP_MOD, "lam = float(perc_damp) * float(np.mean(np.diag(H)))",
+     "lam = float(perc_damp) * float(np.sum(np.diag(H)))", ["prepare"],
+     lambda gd: th.test_damping_closed_form_on_diagonal_S()),
+    (PREP_MOD, "U = sla.cholesky(Hinv, lower=False)",
+     "U = sla.cholesky(Hinv, lower=True)", ["prepare"],
+     lambda gd: th.test_prepare_factor_properties()),
+    (HESS_MOD, "S += X64.T @ X64", "S += X64.T @ X64 - np.diag(np.diag(X64.T @ X64)) * 0.5",
+     ["hessian_S"], lambda gd: th.test_hessian_term_by_term()),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MUTANTS)))
+def test_pins_catch_planted_mistake(idx, monkeypatch, golden_dir):
+    mod, old, new, names, pin = MUTANTS[idx]
+    m = _mutant(mod, old, new)
+    for nm in names:
+        monkeypatch.setattr(oracle, nm, getattr(m, nm))
+    # quantizer mutants must also reach the loop, which imported the name directly
+    if mod is QUANT_MOD:
+        for nm in names:
+            monkeypatch.setattr(GPTQ_MOD, nm, getattr(m, nm))
+    with pytest.raises(AssertionError):
+        pin(golden_dir)
+
+
+def test_unmutated_pins_pass(golden_dir):
+    for _, _, _, _, pin in MUTANTS:
+        pin(golden_dir)
