@@ -1,0 +1,175 @@
+/*
+ * gptq_mi355x.h -- C ABI of the MI355X (gfx950) GPTQ layer quantizer.
+ *
+ * The method: GPTQ layer-wise weight quantization as set out on the page
+ * "GPTQ deep dive" (hncyxsy.com news 243429), section 3.1, four steps per
+ * linear layer: (1) H = 2 X X^T + lambda I from the layer's calibration
+ * inputs, (2) a Cholesky factorization standing in for repeated inversion,
+ * (3) quantization of W column by column in blocks of 128 with error
+ * compensation, (4) storing the integer weights with scale and zero-point.
+ * The layer objective is min ||WX - W_qX||^2 ("LLM quantization principles:
+ * GPTQ, AWQ, GGUF", 0539edu.com news 6111416, section 3.1).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer (HBM) owned by the caller.  The
+ *    library never allocates device memory: scratch space comes from a
+ *    caller-provided workspace whose size the *_workspace_size queries give.
+ *  - Matrices are row-major with an explicit leading dimension (in elements).
+ *  - All work is enqueued on `stream` (NULL = the default stream); calls return
+ *    without synchronizing.  Argument errors are detected on the host and
+ *    returned synchronously before anything is enqueued.  Data-dependent
+ *    errors (a non-positive pivot, a non-finite value) are written to a device
+ *    int32 `info` (0 = ok), which the caller reads after synchronizing.
+ *  - Calls on one stream are ordered; calls that share output or workspace
+ *    buffers must not run concurrently on different streams.
+ *  - Results are deterministic: the same inputs give bitwise-identical outputs.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPTQ_ABI_VERSION 0x00010000u /* major 1, minor 0 */
+
+typedef enum gptq_status {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1, /* bad shape, pointer, stride or configuration     */
+  GPTQ_ERR_NOT_PD = 2,      /* reported through `info` only (see gptq_prepare) */
+  GPTQ_ERR_NONFINITE = 3,   /* reported through `info` only                    */
+  GPTQ_ERR_EMPTY = 4,       /* no calibration tokens were accumulated          */
+  GPTQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query     */
+  GPTQ_ERR_HIP = 6,         /* a HIP runtime call failed (launch error)        */
+  GPTQ_ERR_UNSUPPORTED = 7  /* valid for the method, not built in this library */
+} gptq_status;
+
+typedef enum gptq_dtype { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
+
+/* Quantization settings.  The user-facing knobs of the pages: bits,
+ * group_size, desc_act and damp_percent ("LLM quantization principles",
+ * section 3.1; "GPTQ deep dive", section 3.3), and block_size, which must be a
+ * multiple of group_size ("AWQ, MinMax, GPTQ calibration in Model Optimizer",
+ * gtnt.cn news 115337, section 4). */
+typedef struct gptq_config {
+  int32_t bits;       /* 2..8                                                  */
+  int32_t group_size; /* 8, 16, 32, 64 or 128 dividing block_size; -1 = one
+                         group per row spanning all columns                   */
+  int32_t block_size; /* 128 (the only block width built)                      */
+  float perc_damp;    /* damping fraction (default 0.01); used by gptq_prepare  */
+  int32_t desc_act;   /* 0/1: columns in descending Hessian-diagonal order      */
+  int32_t sym;        /* 0 = asymmetric min-max; 1 = symmetric (zero = 2^(b-1)) */
+} gptq_config;
+
+/* Version of this ABI (GPTQ_ABI_VERSION of the built library). */
+uint32_t gptq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* gptq_status_str(int32_t status);
+
+/* ------------------------------------------------------------------------
+ * Hessian accumulation -- "GPTQ deep dive", section 3.1, step 1.
+ *
+ * S[n, n] += X^T X for the calibration activations X[tokens, n] (row stride
+ * ldx >= n elements, token-major as a layer sees them).  fp32 accumulation of
+ * exact bf16 x bf16 (or fp32 x fp32) products.  Only the lower triangle
+ * (i >= j) of S is read and written; the strict upper triangle is untouched.
+ * S is the raw sum: H = 2S is formed by gptq_prepare.  Accumulation is
+ * additive, so a caller may feed the calibration set in any number of calls
+ * (S is the caller's resumable state).  tokens == 0 is a no-op.
+ * Workspace: gptq_hessian_workspace_size(n, tokens) bytes (0 allowed -> ws may
+ * be NULL).
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_hessian_workspace_size(int64_t n, int64_t tokens, size_t* bytes);
+gptq_status gptq_hessian_accumulate(float* S, int64_t n, int64_t lds, const void* X,
+                                    gptq_dtype xdt, int64_t tokens, int64_t ldx, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Prepare -- "GPTQ deep dive", sections 3.1 (step 2) and 3.3, and 2.4 (the
+ * Cholesky factorization replacing repeated inversion).
+ *
+ * From S (lower triangle, as accumulated above) over `tokens` calibration
+ * tokens:  H = 2S; dead columns (H_ii == 0) get H_ii := 1 and dead[i] = 1;
+ * with desc_act the processing order perm is the stable descending order of
+ * diag(H) (else the identity); lambda = perc_damp * mean(diag H);
+ * H_d = H + lambda I (permuted); and U[n, n] (row stride ldu) receives the
+ * upper Cholesky factor of H_d^-1 in processing order (H_d^-1 = U^T U), with
+ * zeros below the diagonal.  Computed in fp64 on the device, rounded to fp32.
+ * U may alias S (same buffer, ldu == lds).
+ * perm[n] (int32; processing position -> original column), dead[n] (uint8)
+ * and lambda_out (one fp32) may each be NULL.  info: 0 ok, k > 0 = the
+ * 1-based processing position of the first non-positive pivot (raise
+ * perc_damp, as "GPTQ deep dive" section 3.3 advises), -1 = a non-finite
+ * value in S.  Returns GPTQ_ERR_EMPTY synchronously when tokens == 0.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_prepare_workspace_size(int64_t n, size_t* bytes);
+gptq_status gptq_prepare(const float* S, int64_t n, int64_t lds, int64_t tokens,
+                         float perc_damp, int32_t desc_act, float* U, int64_t ldu,
+                         int32_t* perm, uint8_t* dead, float* lambda_out, int32_t* info,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Quantize one layer -- "GPTQ deep dive", section 3.1, step 3 (blocks of 128
+ * columns; in each block, per column: group scale, rounding, error
+ * accumulation; then one batched update of the later columns), section 2.2
+ * (compensation through the inverse Hessian) and section 2.4 (fixed order,
+ * lazy batched updates).
+ *
+ * W[m, n] (row stride ldw, fp32 or bf16) is read only.  U and perm come from
+ * gptq_prepare (perm may be NULL = identity, dead may be NULL = none).
+ * Outputs, all in ORIGINAL column order except where stated:
+ *   codes[m, n]  uint8 in [0, 2^bits - 1], row stride n;
+ *   scales[m, ngroups], zeros[m, ngroups] fp32 (zeros hold integers), groups
+ *                numbered in processing order; ngroups = ceil(n / group_size)
+ *                (1 when group_size == -1);
+ *   g_idx[n]     int32 group of each original column (may be NULL);
+ *   row_err[m]   fp32 sum over columns of e_c^2 = delta^T H_d delta for the
+ *                row's error delta = W - dequant(Q) (may be NULL).
+ * info (may be NULL): set to -1 if W holds a non-finite value.
+ * Group parameters: range [min(0, min v), max(0, max v)] of the group's
+ * current (compensated) values, scale = range / maxq,
+ * zero = rne(-min * maxq / range), q = clamp(rne(w / scale) + zero, 0, maxq),
+ * all in fp32 with IEEE division.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_quantize_workspace_size(int64_t m, int64_t n, const gptq_config* cfg,
+                                         size_t* bytes);
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_t n,
+                                int64_t ldw, const float* U, int64_t ldu, const int32_t* perm,
+                                const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
+                                float* scales, float* zeros, int32_t* g_idx, float* row_err,
+                                int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Bit packing.  The pages fix the storage cost (b bits per weight plus the
+ * per-group scale and zero-point, "LLM quantization principles", section 4.2)
+ * but not a layout; this library's layout: row r of codes[m, n] becomes one
+ * little-endian bitstream of uint32 words, column c in bits [c*b, c*b + b)
+ * (3-bit codes straddle words), zero-padded, packed[m, ceil(n*b/32)].
+ * Codes must be < 2^bits (higher bits are masked off).
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int32_t bits,
+                      uint32_t* packed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Round-to-nearest baseline -- "GPTQ deep dive", section 1.2 (RTN rounds each
+ * weight on its own, no compensation) with group-wise min-max parameters
+ * ("Calibration algorithms guide", bhfrc.com news 5741, section 2.2): the
+ * quantizer of gptq_quantize_layer applied to the original W, groups of
+ * group_size consecutive original columns (-1 = whole row).
+ * codes[m, n] (row stride n), scales/zeros[m, ceil(n / group_size)].
+ * ---------------------------------------------------------------------- */
+gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                       int32_t bits, int32_t group_size, int32_t sym, uint8_t* codes,
+                       float* scales, float* zeros, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

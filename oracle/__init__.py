@@ -41,7 +41,7 @@ from .quantizer import (  # noqa: F401
     pre_round_value,
 )
 from .hessian import hessian_S, hessian  # noqa: F401
-from .prepare import prepare, Prepared  # noqa: F401
+from .prepare import prepare, Prepared, check_descending_order  # noqa: F401
 from .gptq import (  # noqa: F401
     GPTQResult,
     gptq_quantize,

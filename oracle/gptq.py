@@ -185,7 +185,7 @@ def recon_error_from_H(W: np.ndarray, Wq: np.ndarray, H: np.ndarray) -> float:
     one column order.
     """
     D = np.asarray(W, np.float64) - np.asarray(Wq, np.float64)
-    return 0.5 * float(np.einsum("rc,cd,rd->", D, H, D))
+    return 0.5 * float(np.sum((D @ np.asarray(H, np.float64)) * D))
 
 
 def recon_error_direct(W: np.ndarray, Wq: np.ndarray, X_tokens: np.ndarray) -> float:

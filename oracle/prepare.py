@@ -39,14 +39,24 @@ class NotPositiveDefinite(ValueError):
     pass
 
 
-def prepare(S: np.ndarray, perc_damp: float = 0.01, desc_act: bool = False) -> Prepared:
+def prepare(S: np.ndarray, perc_damp: float = 0.01, desc_act: bool = False,
+            order: np.ndarray | None = None) -> Prepared:
+    """``order``: with desc_act, an externally chosen processing order to use instead
+    of the argsort.  Keys that differ by less than the accumulation error of S may be
+    ordered either way (both orders are correct); a caller that has checked an order
+    with ``check_descending_order`` passes it here so the rest of the computation
+    follows that choice."""
     S = np.asarray(S, dtype=np.float64)
     n = S.shape[0]
     H = 2.0 * S
     d = np.diag(H).copy()
     dead = d == 0.0
     H[dead, dead] = 1.0
-    if desc_act:
+    if desc_act and order is not None:
+        perm = np.asarray(order, dtype=np.int64)
+        if not np.array_equal(np.sort(perm), np.arange(n)):
+            raise ValueError("order is not a permutation")
+    elif desc_act:
         perm = np.argsort(-np.diag(H), kind="stable")
     else:
         perm = np.arange(n)
@@ -60,3 +70,26 @@ def prepare(S: np.ndarray, perc_damp: float = 0.01, desc_act: bool = False) -> P
     Hinv = sla.cho_solve(cf, np.eye(n))
     U = sla.cholesky(Hinv, lower=False)
     return Prepared(U=U, perm=perm, dead=dead, lam=lam, H=H, Hd=Hd)
+
+
+def check_descending_order(order: np.ndarray, diag: np.ndarray, rel_tol: float) -> int:
+    """Validate ``order`` as a descending order of ``diag`` up to ``rel_tol``.
+
+    Every key must be at most rel_tol * max|diag| above the smallest key placed
+    before it.  Returns the number of positions at which ``order`` differs from the
+    exact stable order; raises ValueError if ``order`` is not a permutation or
+    places a key above an earlier one by more than the tolerance.
+    """
+    order = np.asarray(order, dtype=np.int64)
+    n = diag.shape[0]
+    if not np.array_equal(np.sort(order), np.arange(n)):
+        raise ValueError("not a permutation")
+    d = np.asarray(diag, dtype=np.float64)[order]
+    tol = rel_tol * float(np.max(np.abs(diag))) if n else 0.0
+    if n > 1:
+        rise = d[1:] - np.minimum.accumulate(d[:-1])  # must be <= 0 for a descending order
+        if np.any(rise > tol):
+            k = int(np.argmax(rise)) + 1
+            raise ValueError(f"order raises key at position {k} by {rise[k - 1]:.3e} > {tol:.3e}")
+    exact = np.argsort(-np.asarray(diag, dtype=np.float64), kind="stable")
+    return int(np.sum(order != exact))

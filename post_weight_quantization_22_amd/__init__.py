@@ -1,0 +1,28 @@
+"""GPTQ layer-wise weight quantization for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libgptq_mi355x.so`` (hand-written HIP kernels
+behind a C ABI, declared in ``include/gptq_mi355x.h``).  This package is its
+Python binding: ``_lib`` mirrors the C entry points one to one and
+``pipeline`` chains them for one layer.  Importing the package loads the
+library and raises ImportError when it has not been built; there is no
+fallback implementation.
+"""
+from . import _lib
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    GPTQConfig,
+    GPTQError,
+    gptq_abi_version,
+    gptq_hessian_accumulate,
+    gptq_hessian_workspace_size,
+    gptq_pack,
+    gptq_prepare,
+    gptq_prepare_workspace_size,
+    gptq_quantize_layer,
+    gptq_quantize_workspace_size,
+    gptq_status_str,
+    make_config,
+    rtn_minmax,
+)
+
+_lib.load()

@@ -1,0 +1,236 @@
+"""ctypes binding of libgptq_mi355x.so (argument marshalling only).
+
+Every computation happens in the library's HIP kernels; this module converts
+torch tensors into device pointers, passes the current HIP stream and maps a
+non-zero status to an exception.  It never computes a result itself, and it
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
+
+GPTQ_OK = 0
+GPTQ_ERR_INVALID_ARG = 1
+GPTQ_ERR_NOT_PD = 2
+GPTQ_ERR_NONFINITE = 3
+GPTQ_ERR_EMPTY = 4
+GPTQ_ERR_WORKSPACE = 5
+GPTQ_ERR_HIP = 6
+GPTQ_ERR_UNSUPPORTED = 7
+
+GPTQ_F32 = 0
+GPTQ_BF16 = 1
+
+# every symbol the C header declares
+EXPORTED = (
+    "gptq_abi_version",
+    "gptq_status_str",
+    "gptq_hessian_workspace_size",
+    "gptq_hessian_accumulate",
+    "gptq_prepare_workspace_size",
+    "gptq_prepare",
+    "gptq_quantize_workspace_size",
+    "gptq_quantize_layer",
+    "gptq_pack",
+    "rtn_minmax",
+)
+
+
+class GPTQConfig(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("perc_damp", ctypes.c_float),
+        ("desc_act", ctypes.c_int32),
+        ("sym", ctypes.c_int32),
+    ]
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m post_weight_quantization_22_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gptq_abi_version.restype = ctypes.c_uint32
+    lib.gptq_abi_version.argtypes = []
+    lib.gptq_status_str.restype = ctypes.c_char_p
+    lib.gptq_status_str.argtypes = [_i32]
+    lib.gptq_hessian_workspace_size.restype = _i32
+    lib.gptq_hessian_workspace_size.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.gptq_hessian_accumulate.restype = _i32
+    lib.gptq_hessian_accumulate.argtypes = [_vp, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _sz, _vp]
+    lib.gptq_prepare_workspace_size.restype = _i32
+    lib.gptq_prepare_workspace_size.argtypes = [_i64, ctypes.POINTER(_sz)]
+    lib.gptq_prepare.restype = _i32
+    lib.gptq_prepare.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_float, _i32, _vp, _i64, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp]
+    lib.gptq_quantize_workspace_size.restype = _i32
+    lib.gptq_quantize_workspace_size.argtypes = [_i64, _i64, ctypes.POINTER(GPTQConfig),
+                                                 ctypes.POINTER(_sz)]
+    lib.gptq_quantize_layer.restype = _i32
+    lib.gptq_quantize_layer.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
+                                        ctypes.POINTER(GPTQConfig), _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]
+    lib.gptq_pack.restype = _i32
+    lib.gptq_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+    lib.rtn_minmax.restype = _i32
+    lib.rtn_minmax.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().gptq_status_str(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != GPTQ_OK:
+        raise GPTQError(status, where, status_str(status))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return GPTQ_BF16
+    if t.dtype == torch.float32:
+        return GPTQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _workspace(nbytes: int, device):
+    import torch
+
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def gptq_abi_version() -> int:
+    return int(load().gptq_abi_version())
+
+
+def gptq_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def gptq_hessian_workspace_size(n: int, tokens: int) -> int:
+    out = _sz(0)
+    _check(load().gptq_hessian_workspace_size(n, tokens, ctypes.byref(out)),
+           "gptq_hessian_workspace_size")
+    return out.value
+
+
+def gptq_hessian_accumulate(S, X, ws=None, stream=None) -> None:
+    """S[n, n] (fp32, lower triangle) += X^T X for X[tokens, n] (bf16 or fp32)."""
+    n = S.shape[0]
+    tokens = X.shape[0]
+    need = gptq_hessian_workspace_size(n, tokens) if _dtype_code(X) == GPTQ_BF16 else 0
+    if ws is None:
+        ws = _workspace(need, S.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().gptq_hessian_accumulate(_ptr(S), n, _ld(S), _ptr(X), _dtype_code(X), tokens,
+                                          _ld(X), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_hessian_accumulate")
+
+
+def gptq_prepare_workspace_size(n: int) -> int:
+    out = _sz(0)
+    _check(load().gptq_prepare_workspace_size(n, ctypes.byref(out)), "gptq_prepare_workspace_size")
+    return out.value
+
+
+def gptq_prepare(S, tokens: int, perc_damp: float, desc_act: bool, U, perm=None, dead=None,
+                 lambda_out=None, info=None, ws=None, stream=None) -> None:
+    n = S.shape[0]
+    if ws is None:
+        ws = _workspace(gptq_prepare_workspace_size(n), S.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().gptq_prepare(_ptr(S), n, _ld(S), int(tokens), float(perc_damp), int(desc_act),
+                               _ptr(U), _ld(U), _ptr(perm), _ptr(dead), _ptr(lambda_out),
+                               _ptr(info), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_prepare")
+
+
+def make_config(bits: int, group_size: int, block_size: int = 128, perc_damp: float = 0.01,
+                desc_act: bool = False, sym: bool = False) -> GPTQConfig:
+    return GPTQConfig(bits, group_size, block_size, perc_damp, int(desc_act), int(sym))
+
+
+def gptq_quantize_workspace_size(m: int, n: int, cfg: GPTQConfig) -> int:
+    out = _sz(0)
+    _check(load().gptq_quantize_workspace_size(m, n, ctypes.byref(cfg), ctypes.byref(out)),
+           "gptq_quantize_workspace_size")
+    return out.value
+
+
+def gptq_quantize_layer(W, U, cfg: GPTQConfig, codes, scales, zeros, perm=None, dead=None,
+                        g_idx=None, row_err=None, info=None, ws=None, stream=None) -> None:
+    m, n = W.shape
+    if ws is None:
+        ws = _workspace(gptq_quantize_workspace_size(m, n, cfg), W.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(U), _ld(U),
+                                      _ptr(perm), _ptr(dead), ctypes.byref(cfg), _ptr(codes),
+                                      _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_err),
+                                      _ptr(info), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_quantize_layer")
+
+
+def gptq_pack(codes, bits: int, packed, stream=None) -> None:
+    m, n = codes.shape
+    _check(load().gptq_pack(_ptr(codes), m, n, int(bits), _ptr(packed), _stream(stream)),
+           "gptq_pack")
+
+
+def rtn_minmax(W, bits: int, group_size: int, codes, scales, zeros, sym: bool = False,
+               stream=None) -> None:
+    m, n = W.shape
+    _check(load().rtn_minmax(_ptr(W), _dtype_code(W), m, n, _ld(W), int(bits), int(group_size),
+                             int(sym), _ptr(codes), _ptr(scales), _ptr(zeros), _stream(stream)),
+           "rtn_minmax")

@@ -1,0 +1,156 @@
+// extern "C" entry points: argument validation, workspace sizing, launches.
+// Every check here runs on the host before anything is enqueued.
+#include <cmath>
+
+#include "kernels.hpp"
+
+using namespace gptq;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // sanity bound on m, n
+
+inline bool bad_dim(int64_t v) { return v < 0 || v > kMaxDim; }
+
+inline gptq_status hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP; }
+
+inline bool valid_dtype(int dt) { return dt == GPTQ_F32 || dt == GPTQ_BF16; }
+
+inline bool quant_group_ok(int32_t g) {
+  return g == -1 || g == 8 || g == 16 || g == 32 || g == 64 || g == 128;
+}
+
+gptq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return GPTQ_OK;
+  if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t gptq_abi_version(void) { return GPTQ_ABI_VERSION; }
+
+const char* gptq_status_str(int32_t status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+    case GPTQ_ERR_NOT_PD: return "damped Hessian is not positive definite (raise perc_damp)";
+    case GPTQ_ERR_NONFINITE: return "non-finite value in the input";
+    case GPTQ_ERR_EMPTY: return "no calibration tokens";
+    case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case GPTQ_ERR_HIP: return "HIP runtime error";
+    case GPTQ_ERR_UNSUPPORTED: return "configuration not supported by this library";
+    default: return "unknown status";
+  }
+}
+
+gptq_status gptq_hessian_workspace_size(int64_t n, int64_t tokens, size_t* bytes) {
+  if (!bytes || n <= 0 || bad_dim(n) || tokens < 0) return GPTQ_ERR_INVALID_ARG;
+  *bytes = hessian_ws_bytes(n, tokens, GPTQ_BF16);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_hessian_accumulate(float* S, int64_t n, int64_t lds, const void* X,
+                                    gptq_dtype xdt, int64_t tokens, int64_t ldx, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!S || n <= 0 || bad_dim(n) || lds < n || tokens < 0 || !valid_dtype(xdt))
+    return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (!X || ldx < n) return GPTQ_ERR_INVALID_ARG;
+  const gptq_status w = check_ws(ws, ws_bytes, hessian_ws_bytes(n, tokens, xdt));
+  if (w != GPTQ_OK) return w;
+  return hip_status(launch_hessian(S, n, lds, X, xdt, tokens, ldx, ws, ws_bytes, stream));
+}
+
+gptq_status gptq_prepare_workspace_size(int64_t n, size_t* bytes) {
+  if (!bytes || n <= 0 || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  *bytes = prepare_ws_bytes(n);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_prepare(const float* S, int64_t n, int64_t lds, int64_t tokens, float perc_damp,
+                         int32_t desc_act, float* U, int64_t ldu, int32_t* perm, uint8_t* dead,
+                         float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!S || !U || !info || n <= 0 || bad_dim(n) || lds < n || ldu < n || tokens < 0 ||
+      !(perc_damp >= 0.0f) || !std::isfinite(perc_damp) || (desc_act != 0 && desc_act != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (U == S && ldu != lds) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_ERR_EMPTY;
+  const gptq_status w = check_ws(ws, ws_bytes, prepare_ws_bytes(n));
+  if (w != GPTQ_OK) return w;
+  return hip_status(launch_prepare(S, n, lds, perc_damp, desc_act, U, ldu, perm, dead, lambda_out,
+                                   info, ws, stream));
+}
+
+gptq_status gptq_quantize_workspace_size(int64_t m, int64_t n, const gptq_config* cfg,
+                                         size_t* bytes) {
+  if (!bytes || !cfg || bad_dim(m) || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  *bytes = quantize_ws_bytes(m, n, cfg->desc_act);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                                const float* U, int64_t ldu, const int32_t* perm,
+                                const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
+                                float* scales, float* zeros, int32_t* g_idx, float* row_err,
+                                int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!cfg || bad_dim(m) || bad_dim(n) || !valid_dtype(wdt)) return GPTQ_ERR_INVALID_ARG;
+  if (cfg->bits < 2 || cfg->bits > 8 || cfg->block_size <= 0 || cfg->group_size == 0 ||
+      (cfg->group_size > 0 && cfg->block_size % cfg->group_size != 0) ||
+      (cfg->desc_act != 0 && cfg->desc_act != 1) || (cfg->sym != 0 && cfg->sym != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (cfg->block_size != 128 || !quant_group_ok(cfg->group_size)) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros || ldw < n || ldu < n) return GPTQ_ERR_INVALID_ARG;
+  if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
+  const gptq_status w = check_ws(ws, ws_bytes, quantize_ws_bytes(m, n, cfg->desc_act));
+  if (w != GPTQ_OK) return w;
+  QuantArgs a;
+  a.W = W;
+  a.wdt = wdt;
+  a.m = m;
+  a.n = n;
+  a.ldw = ldw;
+  a.U = U;
+  a.ldu = ldu;
+  a.perm = perm;
+  a.dead = dead;
+  a.bits = cfg->bits;
+  a.group_size = cfg->group_size;
+  a.block_size = cfg->block_size;
+  a.desc_act = cfg->desc_act;
+  a.sym = cfg->sym;
+  a.codes = codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.g_idx = g_idx;
+  a.row_err = row_err;
+  a.info = info;
+  a.ws = ws;
+  return hip_status(launch_quantize(a, stream));
+}
+
+gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int32_t bits, uint32_t* packed,
+                      hipStream_t stream) {
+  if (bad_dim(m) || bad_dim(n) || bits < 1 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (!codes || !packed) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_pack(codes, m, n, bits, packed, stream));
+}
+
+gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                       int32_t bits, int32_t group_size, int32_t sym, uint8_t* codes,
+                       float* scales, float* zeros, hipStream_t stream) {
+  if (bad_dim(m) || bad_dim(n) || !valid_dtype(wdt) || bits < 2 || bits > 8 ||
+      group_size == 0 || group_size < -1 || (sym != 0 && sym != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (!W || !codes || !scales || !zeros || ldw < n) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_rtn(W, wdt, m, n, ldw, bits, group_size, sym, codes, scales, zeros,
+                               stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Shared device helpers for the gfx950 GPTQ kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gptq_mi355x.h"
+
+namespace gptq {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Load one weight as fp32 from an fp32 or bf16 matrix.
+__device__ __forceinline__ float load_elem(const void* p, int dt, int64_t idx) {
+  if (dt == GPTQ_BF16) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[idx]);
+  }
+  return reinterpret_cast<const float*>(p)[idx];
+}
+
+// Group parameters of the asymmetric min-max quantizer (range widened to
+// include 0; an all-zero group uses [-1, 1]).  IEEE fp32 arithmetic, true
+// division, round-half-even; the same sequence of fp32 operations as the
+// method's definition, so that integer outcomes are reproducible.
+__device__ __forceinline__ void minmax_params(float vmin, float vmax, float maxq, float& scale,
+                                              float& zero) {
+  float xmin = fminf(vmin, 0.0f);
+  float xmax = fmaxf(vmax, 0.0f);
+  if (xmin == xmax) {
+    xmin = -1.0f;
+    xmax = 1.0f;
+  }
+  const float span = xmax - xmin;
+  scale = __fdiv_rn(span, maxq);
+  zero = rintf(__fdiv_rn(__fmul_rn(-xmin, maxq), span));
+}
+
+// Symmetric variant: zero-point fixed at 2^(bits-1), scale = 2*max|v| / maxq.
+__device__ __forceinline__ void sym_params(float amax, float maxq, float& scale, float& zero) {
+  if (amax == 0.0f) amax = 1.0f;
+  scale = __fdiv_rn(__fmul_rn(2.0f, amax), maxq);
+  zero = floorf(__fmul_rn(maxq + 1.0f, 0.5f));
+}
+
+// q = clamp(rne(w / scale) + zero, 0, maxq)
+__device__ __forceinline__ float quant_code(float w, float scale, float zero, float maxq) {
+  float q = rintf(__fdiv_rn(w, scale)) + zero;
+  return fminf(fmaxf(q, 0.0f), maxq);
+}
+
+__device__ __forceinline__ bool is_finite(float x) { return isfinite(x); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
+inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace gptq

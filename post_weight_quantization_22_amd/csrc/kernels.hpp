@@ -1,0 +1,49 @@
+// Internal launchers of the gfx950 kernels (C++ linkage, not part of the ABI).
+#pragma once
+
+#include "common.hpp"
+
+namespace gptq {
+
+// ---- rtn.hip --------------------------------------------------------------
+hipError_t launch_rtn(const void* W, int dt, int64_t m, int64_t n, int64_t ldw, int bits,
+                      int64_t G, int sym, uint8_t* codes, float* scales, float* zeros,
+                      hipStream_t stream);
+
+// ---- pack.hip -------------------------------------------------------------
+hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uint32_t* packed,
+                       hipStream_t stream);
+
+// ---- hessian.hip ----------------------------------------------------------
+size_t hessian_ws_bytes(int64_t n, int64_t tokens, int dt);
+hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int dt, int64_t tokens,
+                          int64_t ldx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// ---- prepare.hip ----------------------------------------------------------
+size_t prepare_ws_bytes(int64_t n);
+hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_damp, int desc_act,
+                          float* U, int64_t ldu, int32_t* perm, uint8_t* dead, float* lambda_out,
+                          int32_t* info, void* ws, hipStream_t stream);
+
+// ---- quantize.hip ---------------------------------------------------------
+struct QuantArgs {
+  const void* W;
+  int wdt;
+  int64_t m, n, ldw;
+  const float* U;
+  int64_t ldu;
+  const int32_t* perm;  // used only when desc_act
+  const uint8_t* dead;  // may be null
+  int bits, group_size, block_size, desc_act, sym;
+  uint8_t* codes;
+  float* scales;
+  float* zeros;
+  int32_t* g_idx;
+  float* row_err;
+  int32_t* info;
+  void* ws;
+};
+size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+}  // namespace gptq

@@ -1,0 +1,178 @@
+"""GPU parity: gptq_hessian_accumulate and gptq_prepare against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.quantizer import f32
+
+from gpu_util import dev, host, need_gpu, say, torch
+
+pytestmark = pytest.mark.gpu
+
+HESS_CASES = [
+    # n, tokens, chunk, dtype
+    (200, 300, 300, "bf16"),      # ragged tiles, one split
+    (384, 8192, 2048, "bf16"),    # 3x3 tiles -> split over tokens (partials + reduce)
+    (256, 1024, 1024, "f32"),     # fp32 activations (SIMT path)
+    (130, 77, 77, "f32"),
+    (1024, 4096, 2048, "bf16"),
+]
+
+
+def _x(n, tokens, chunk, dt, seed=0):
+    wl = synth.custom_workload("hx", 8, n, tokens, chunk, x_dtype=dt, outlier_frac=0.02,
+                               outlier_mult=30.0, workload_id=200 + seed)
+    return synth.x_all(wl, "x")
+
+
+@pytest.mark.parametrize("n,tokens,chunk,dt", HESS_CASES)
+def test_hessian_lower_triangle(n, tokens, chunk, dt):
+    q = need_gpu()
+    X = _x(n, tokens, chunk, dt)
+    S_ref = oracle.hessian_S([X])
+    A_ref = oracle.hessian_S([np.abs(X)])  # sum |x_i x_j|, for the rounding bound
+    S_l = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    S_l += torch.triu(torch.full((n, n), 7.0, device="cuda"), 1)  # sentinel above the diagonal
+    say("hessian", n, tokens, dt)
+    q.gptq_hessian_accumulate(S_l, dev(X, torch.bfloat16 if dt == "bf16" else torch.float32))
+    torch.cuda.synchronize()
+    got = host(S_l).astype(np.float64)
+    low = np.tril(np.ones((n, n), dtype=bool))
+    # strict upper triangle untouched
+    assert np.all(got[~low] == 7.0)
+    err = np.abs(got - S_ref)[low]
+    # fp32 accumulation (worst case): |err| <= (tokens + 8) * 2^-24 * sum_t |x_ti x_tj|
+    bound = (tokens + 8) * 2.0 ** -24 * A_ref[low] + 1e-30
+    assert np.all(err <= bound)
+    assert err.max() <= 1e-5 * np.abs(S_ref).max()
+
+
+def test_hessian_is_additive_over_calls():
+    q = need_gpu()
+    X = _x(256, 6144, 2048, "bf16", seed=3)
+    Xd = dev(X, torch.bfloat16)
+    S1 = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    S2 = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    say("hessian additive")
+    q.gptq_hessian_accumulate(S1, Xd)
+    for c in range(3):
+        q.gptq_hessian_accumulate(S2, Xd[c * 2048:(c + 1) * 2048])
+    torch.cuda.synchronize()
+    S_ref = oracle.hessian_S([X])
+    low = np.tril(np.ones((256, 256), dtype=bool))
+    for S in (S1, S2):
+        assert np.abs(host(S) - S_ref)[low].max() <= 1e-5 * np.abs(S_ref).max()
+
+
+def test_hessian_deterministic():
+    q = need_gpu()
+    X = dev(_x(384, 8192, 2048, "bf16", seed=4), torch.bfloat16)
+    outs = []
+    say("hessian determinism")
+    for _ in range(3):
+        S = torch.zeros((384, 384), dtype=torch.float32, device="cuda")
+        q.gptq_hessian_accumulate(S, X)
+        outs.append(host(S))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+PREP_CASES = [
+    # n, tokens, desc_act, perc_damp
+    (256, 1024, False, 0.01),
+    (200, 900, True, 0.01),      # ragged panels, desc_act
+    (520, 4096, True, 0.01),     # several panels + ragged tail
+    (64, 256, False, 0.1),
+    (1, 10, False, 0.01),
+    (130, 2048, False, 0.0),
+]
+
+
+def _S_case(n, tokens, seed=0):
+    X = _x(n, tokens, tokens, "bf16", seed=seed)
+    return f32(oracle.hessian_S([X]))  # the fp32 S both sides start from
+
+
+@pytest.mark.parametrize("n,tokens,desc,damp", PREP_CASES)
+def test_prepare_matches_oracle(n, tokens, desc, damp):
+    q = need_gpu()
+    S = _S_case(n, tokens, seed=n)
+    # perc_damp crosses the ABI as fp32: the oracle gets that same value
+    P = oracle.prepare(S, float(np.float32(damp)), desc)
+    Sd = dev(S.astype(np.float32), torch.float32)
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    dead = torch.empty(n, dtype=torch.uint8, device="cuda")
+    lam = torch.empty(1, dtype=torch.float32, device="cuda")
+    info = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+    say("prepare", n, tokens, desc, damp)
+    q.gptq_prepare(Sd, tokens, damp, desc, U, perm=perm, dead=dead, lambda_out=lam, info=info)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0
+    assert np.array_equal(host(perm), P.perm)
+    assert np.array_equal(host(dead).astype(bool), P.dead)
+    assert abs(float(host(lam)[0]) - P.lam) <= 2.0 ** -23 * abs(P.lam) + 1e-30
+    Ug = host(U).astype(np.float64)
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    # fp64 on both sides, rounded to fp32 on the device: within 2 ulp of fp32
+    tol = 2.0 ** -22 * np.abs(P.U) + 1e-12 * np.abs(P.U).max()
+    assert np.all(np.abs(Ug - P.U) <= tol)
+
+
+def test_prepare_in_place_and_dead_columns():
+    q = need_gpu()
+    n = 192
+    X = _x(n, 512, 512, "bf16", seed=11)
+    X[:, [5, 77, 150]] = 0.0
+    S = f32(oracle.hessian_S([X]))
+    P = oracle.prepare(S, float(np.float32(0.01)), True)
+    Sd = dev(S.astype(np.float32), torch.float32)
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    dead = torch.empty(n, dtype=torch.uint8, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("prepare in place")
+    q.gptq_prepare(Sd, 512, 0.01, True, Sd, perm=perm, dead=dead, info=info)  # U aliases S
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0
+    assert np.flatnonzero(host(dead)).tolist() == [5, 77, 150]
+    assert np.array_equal(host(perm), P.perm)
+    Ug = host(Sd).astype(np.float64)
+    assert np.all(np.abs(Ug - P.U) <= 2.0 ** -22 * np.abs(P.U) + 1e-12 * np.abs(P.U).max())
+
+
+def test_prepare_reports_not_positive_definite():
+    q = need_gpu()
+    n = 96
+    rng = np.random.default_rng(1)
+    B = rng.standard_normal((n, n))
+    S = f32(B + B.T)  # indefinite
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    say("prepare not-PD")
+    q.gptq_prepare(dev(S.astype(np.float32), torch.float32), 10, 0.0, False, U, info=info)
+    torch.cuda.synchronize()
+    v = int(host(info)[0])
+    assert 1 <= v <= n
+
+
+def test_prepare_reports_non_finite():
+    q = need_gpu()
+    n = 64
+    S = _S_case(n, 256, seed=2)
+    S[10, 3] = np.nan
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    say("prepare non-finite")
+    q.gptq_prepare(dev(S.astype(np.float32), torch.float32), 256, 0.01, False, U, info=info)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == -1
+
+
+def test_prepare_empty_calibration_is_refused():
+    q = need_gpu()
+    S = torch.zeros((8, 8), dtype=torch.float32, device="cuda")
+    U = torch.empty((8, 8), dtype=torch.float32, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(q.GPTQError) as ei:
+        q.gptq_prepare(S, 0, 0.01, False, U, info=info)
+    assert ei.value.status == 4

@@ -89,3 +89,17 @@ def test_not_positive_definite_without_damping():
     S = np.array([[1.0, 2.0], [2.0, 1.0]])  # indefinite
     with pytest.raises(NotPositiveDefinite):
         oracle.prepare(S, 0.0, False)
+
+
+def test_accepted_order_near_ties():
+    d = np.array([5.0, 3.0, 3.0 + 1e-9, 1.0])
+    # exact order puts index 2 before 1; swapping them is within tolerance
+    assert oracle.check_descending_order(np.array([0, 1, 2, 3]), d, 1e-6) == 2
+    assert oracle.check_descending_order(np.array([0, 2, 1, 3]), d, 1e-6) == 0
+    with pytest.raises(ValueError):
+        oracle.check_descending_order(np.array([1, 0, 2, 3]), d, 1e-6)
+    with pytest.raises(ValueError):
+        oracle.check_descending_order(np.array([0, 0, 2, 3]), d, 1e-6)
+    P = oracle.prepare(np.diag(d), 0.01, True, order=np.array([0, 1, 2, 3]))
+    assert P.perm.tolist() == [0, 1, 2, 3]
+    assert np.allclose(np.diag(P.H), 2 * d)
