@@ -79,9 +79,15 @@ def test_llama7b_attn_full_size():
     assert rate >= 0.999
     assert rep.hard == 0 and rep.zero_hard == 0
     assert rep.scale_max_rel <= 1e-4
-    sc_rel = np.abs(scales - ref.scales) / ref.scales
-    print(f"free-running scales within 1e-4: {np.mean(sc_rel <= 1e-4):.6f}", flush=True)
-    assert np.mean(sc_rel <= 1e-4) >= 0.999
+    # free running, rows whose codes all agree must agree on every group's scale and
+    # zero; rows downstream of a tie follow another (equally valid) trajectory, which
+    # the replay above has checked
+    clean = np.all(codes == ref.codes, axis=1)
+    sc_rel = np.abs(scales[clean] - ref.scales[clean]) / ref.scales[clean]
+    print(f"rows without divergence: {int(clean.sum())} of {m}; their max scale rel "
+          f"{sc_rel.max():.2e}", flush=True)
+    assert sc_rel.max() <= 1e-4
+    assert np.array_equal(zeros[clean], ref.zeros[clean])
     H = 2.0 * S_ref
     Wq = oracle.dequant_layer(codes.astype(np.float64), scales.astype(np.float64),
                               zeros.astype(np.float64), host(buf.g_idx))
