@@ -31,9 +31,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int HT = 128;    // output tile edge
-constexpr int HK = 32;     // tokens per stage
-constexpr int HKP = HK + 8;  // LDS row length in bf16 (padding vs bank conflicts)
+constexpr int HT = 256;        // output tile edge (channels)
+constexpr int HK = 64;         // tokens per stage
+constexpr int HROW = HK + 8;   // LDS row length in bf16: 144 B = 9 x 16 B (odd, conflict-free)
+constexpr int HWT = HT / 2;    // per-wave tile edge (2 x 2 waves)
+constexpr int HSUB = HWT / 32; // 32x32 MFMA sub-tiles per wave edge
 
 __device__ __forceinline__ void tile_coords(int64_t L, int64_t& ti, int64_t& tj) {
   // lower-triangle tile L -> (ti >= tj), row-major over the triangle
@@ -44,131 +46,158 @@ __device__ __forceinline__ void tile_coords(int64_t L, int64_t& ti, int64_t& tj)
   tj = L - t * (t + 1) / 2;
 }
 
-struct Rows2 {
-  uint4 a, b;  // two token rows x 8 channels (bf16)
+// One lane's share of a stage for one operand: 8 tokens x 8 channels.
+struct Block8 {
+  uint4 r[8];  // r[e]: token 8o + e, channels c .. c + 7
 };
 
-__device__ __forceinline__ Rows2 load_rows2(const uint16_t* __restrict__ X, int64_t ldx,
-                                            int64_t tokens, int64_t n, int64_t t, int64_t c,
-                                            bool vec_ok) {
-  Rows2 r;
-  const bool full_c = c + 8 <= n;
-  if (vec_ok && full_c) {
-    r.a = t < tokens ? *reinterpret_cast<const uint4*>(X + t * ldx + c) : make_uint4(0, 0, 0, 0);
-    r.b = t + 1 < tokens ? *reinterpret_cast<const uint4*>(X + (t + 1) * ldx + c)
-                         : make_uint4(0, 0, 0, 0);
-    return r;
-  }
-  uint32_t wa[4], wb[4];
+__device__ __forceinline__ void load_block8(const uint16_t* __restrict__ X, int64_t ldx,
+                                            int64_t t_end, int64_t n, int64_t t, int64_t c,
+                                            bool vec_ok, Block8& b) {
+  const bool full = vec_ok && c + 8 <= n && t + 8 <= t_end;
+  if (full) {
+    const uint16_t* p = X + t * ldx + c;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t lo = 0, hi = 0, lo2 = 0, hi2 = 0;
-    if (t < tokens) {
-      if (c + 2 * k < n) lo = X[t * ldx + c + 2 * k];
-      if (c + 2 * k + 1 < n) hi = X[t * ldx + c + 2 * k + 1];
-    }
-    if (t + 1 < tokens) {
-      if (c + 2 * k < n) lo2 = X[(t + 1) * ldx + c + 2 * k];
-      if (c + 2 * k + 1 < n) hi2 = X[(t + 1) * ldx + c + 2 * k + 1];
-    }
-    wa[k] = lo | (hi << 16);
-    wb[k] = lo2 | (hi2 << 16);
+    for (int e = 0; e < 8; ++e) b.r[e] = *reinterpret_cast<const uint4*>(p + e * ldx);
+    return;
   }
-  r.a = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-  r.b = make_uint4(wb[0], wb[1], wb[2], wb[3]);
-  return r;
-}
-
-// Write the 8 channels x 2 tokens held in r into T[channel][token pair].
-__device__ __forceinline__ void store_transposed(uint32_t* __restrict__ T, int ch0, int tp,
-                                                 const Rows2& r) {
-  const uint32_t a[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-  const uint32_t b[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // channel 2k: low halves of token t and t+1; channel 2k+1: high halves
-    T[(ch0 + 2 * k) * (HKP / 2) + tp] = (a[k] & 0xFFFFu) | (b[k] << 16);
-    T[(ch0 + 2 * k + 1) * (HKP / 2) + tp] = (a[k] >> 16) | (b[k] & 0xFFFF0000u);
+  for (int e = 0; e < 8; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t lo = 0, hi = 0;
+      if (t + e < t_end) {
+        if (c + 2 * q < n) lo = X[(t + e) * ldx + c + 2 * q];
+        if (c + 2 * q + 1 < n) hi = X[(t + e) * ldx + c + 2 * q + 1];
+      }
+      w[q] = lo | (hi << 16);
+    }
+    b.r[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+// Transpose the 8 x 8 bf16 block in registers (v_perm_b32) and store channel
+// rows: T[(c0 + ch) * HROW + 8 * o .. + 8] = tokens 8o .. 8o + 7 of channel c0 + ch.
+__device__ __forceinline__ void store_block8(uint16_t* __restrict__ T, int c0, int o,
+                                             const Block8& b) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t even = word_of(b.r[2 * p], w);      // token 2p: channels 2w, 2w+1
+      const uint32_t odd = word_of(b.r[2 * p + 1], w);   // token 2p+1
+      lo[p] = __builtin_amdgcn_perm(odd, even, 0x05040100u);  // channel 2w, tokens 2p, 2p+1
+      hi[p] = __builtin_amdgcn_perm(odd, even, 0x07060302u);  // channel 2w+1
+    }
+    *reinterpret_cast<uint4*>(T + (c0 + 2 * w) * HROW + 8 * o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(T + (c0 + 2 * w + 1) * HROW + 8 * o) =
+        make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+}
+
+// grid.x = ntiles * P; block L = blockIdx.x / P, split p = blockIdx.x % P (with P a
+// multiple of 8 the workgroups of one token split share an XCD and its L2).
 __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restrict__ X,
                                                         int64_t ldx, int64_t tokens, int64_t n,
-                                                        int64_t tok_per_split,
+                                                        int64_t tok_per_split, int64_t P,
                                                         float* __restrict__ S, int64_t lds,
                                                         float* __restrict__ part,
                                                         int64_t ntiles) {
-  __shared__ uint32_t At[HT * HKP / 2];
-  __shared__ uint32_t Bt[HT * HKP / 2];
+  __shared__ __align__(16) uint16_t smem[4 * HT * HROW];
+  // buffer b: operand A at smem + 2b * HT * HROW, operand B right after it
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int wr = wv >> 1, wc = wv & 1;
-  const int64_t L = blockIdx.x;
-  const int64_t p = blockIdx.y;
+  const int64_t L = blockIdx.x / P;
+  const int64_t p = blockIdx.x % P;
   int64_t ti, tj;
   tile_coords(L, ti, tj);
   const int64_t i0 = ti * HT, j0 = tj * HT;
   const bool diag = ti == tj;
+  const bool skip_wave = diag && wr < wc;  // strictly upper quarter of a diagonal tile
   const int64_t t_begin = p * tok_per_split;
   const int64_t t_end = min(tokens, t_begin + tok_per_split);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && (ldx % 8 == 0);
 
-  // loader mapping: token pair tp (0..15), channel chunk cc (0..15)
-  const int tp = tid >> 4, cc = tid & 15;
+  // loader mapping: token octet o (0..7), channel block cb (0..31)
+  const int o = tid & 7, cb = tid >> 3;
 
-  f32x16 acc[2][2];
+  f32x16 acc[HSUB][HSUB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < HSUB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < HSUB; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
 
-  Rows2 ra, rb;
+  // The next stage is fetched one operand at a time (32 registers in flight),
+  // each behind half of the current stage's MFMAs, then transposed into the
+  // other LDS buffer; one barrier per stage.
+  Block8 rg;
+  int buf = 0;
   if (t_begin < t_end) {
-    ra = load_rows2(X, ldx, t_end, n, t_begin + 2 * tp, i0 + 8 * cc, vec_ok);
-    if (!diag) rb = load_rows2(X, ldx, t_end, n, t_begin + 2 * tp, j0 + 8 * cc, vec_ok);
-  }
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += HK) {
-    __syncthreads();
-    store_transposed(At, 8 * cc, tp, ra);
-    if (!diag) store_transposed(Bt, 8 * cc, tp, rb);
-    __syncthreads();
-    if (t0 + HK < t_end) {  // prefetch the next stage into registers
-      ra = load_rows2(X, ldx, t_end, n, t0 + HK + 2 * tp, i0 + 8 * cc, vec_ok);
-      if (!diag) rb = load_rows2(X, ldx, t_end, n, t0 + HK + 2 * tp, j0 + 8 * cc, vec_ok);
+    load_block8(X, ldx, t_end, n, t_begin + 8 * o, i0 + 8 * cb, vec_ok, rg);
+    store_block8(smem, 8 * cb, o, rg);
+    if (!diag) {
+      load_block8(X, ldx, t_end, n, t_begin + 8 * o, j0 + 8 * cb, vec_ok, rg);
+      store_block8(smem + HT * HROW, 8 * cb, o, rg);
     }
-    const uint32_t* Bsrc = diag ? At : Bt;
+  }
+  __syncthreads();
+  auto mfma_half = [&](const uint16_t* At, const uint16_t* Bt, int kk0) {
 #pragma unroll
-    for (int kk = 0; kk < HK / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+    for (int kk = kk0; kk < kk0 + HK / 32; ++kk) {
+      bf16x8 af[HSUB], bfr[HSUB];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = 64 * wr + 32 * a + (lane & 31);
-        af[a] = *reinterpret_cast<const bf16x8*>(&At[row * (HKP / 2) + 8 * kk + 4 * (lane >> 5)]);
+      for (int a = 0; a < HSUB; ++a) {
+        const int row = HWT * wr + 32 * a + (lane & 31);
+        af[a] = *reinterpret_cast<const bf16x8*>(At + row * HROW + 16 * kk + 8 * (lane >> 5));
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int col = 64 * wc + 32 * b + (lane & 31);
-        bfr[b] = *reinterpret_cast<const bf16x8*>(&Bsrc[col * (HKP / 2) + 8 * kk + 4 * (lane >> 5)]);
+      for (int b = 0; b < HSUB; ++b) {
+        const int col = HWT * wc + 32 * b + (lane & 31);
+        bfr[b] = *reinterpret_cast<const bf16x8*>(Bt + col * HROW + 16 * kk + 8 * (lane >> 5));
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < HSUB; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < HSUB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
+  };
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += HK) {
+    const bool more = t0 + HK < t_end;
+    const uint16_t* At = smem + 2 * buf * HT * HROW;
+    const uint16_t* Bt = diag ? At : At + HT * HROW;
+    uint16_t* nxt = smem + 2 * (buf ^ 1) * HT * HROW;
+    if (more) load_block8(X, ldx, t_end, n, t0 + HK + 8 * o, i0 + 8 * cb, vec_ok, rg);
+    if (!skip_wave) mfma_half(At, Bt, 0);
+    if (more) {
+      store_block8(nxt, 8 * cb, o, rg);
+      if (!diag) load_block8(X, ldx, t_end, n, t0 + HK + 8 * o, j0 + 8 * cb, vec_ok, rg);
+    }
+    if (!skip_wave) mfma_half(At, Bt, HK / 32);
+    if (more && !diag) store_block8(nxt + HT * HROW, 8 * cb, o, rg);
+    __syncthreads();
+    buf ^= 1;
   }
+  if (skip_wave) return;
 
   // D layout of the 32x32 MFMA: lane l, register q -> row 8*(q/4) + 4*(l/32) + q%4, col l%32
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < HSUB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < HSUB; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int ii = 64 * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int jj = 64 * wc + 32 * b + (lane & 31);
+        const int ii = HWT * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int jj = HWT * wc + 32 * b + (lane & 31);
         if (part) {
           part[((p * ntiles + L) * HT + ii) * HT + jj] = acc[a][b][q];
         } else {
@@ -183,15 +212,17 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
                                                               int64_t P, int64_t ntiles,
                                                               int64_t n, float* __restrict__ S,
                                                               int64_t lds) {
-  const int64_t L = blockIdx.x;
+  const int64_t L = blockIdx.x / (HT * HT / 1024);
+  const int64_t chunk = blockIdx.x % (HT * HT / 1024);
   int64_t ti, tj;
   tile_coords(L, ti, tj);
-  for (int e = threadIdx.x; e < HT * HT; e += blockDim.x) {
+  for (int r = 0; r < 4; ++r) {
+    const int e = (int)chunk * 1024 + r * 256 + threadIdx.x;
     const int ii = e / HT, jj = e % HT;
     const int64_t gi = ti * HT + ii, gj = tj * HT + jj;
     if (gi >= n || gj > gi) continue;
     float s = 0.0f;
-    for (int64_t p = 0; p < P; ++p) s += part[(p * ntiles + L) * HT * HT + e];
+    for (int64_t q = 0; q < P; ++q) s += part[(q * ntiles + L) * HT * HT + e];
     S[gi * lds + gj] += s;
   }
 }
@@ -249,11 +280,11 @@ HessPlan plan_bf16(int64_t n, int64_t tokens) {
   HessPlan pl;
   const int64_t T = ceil_div(n, HT);
   pl.ntiles = T * (T + 1) / 2;
-  // aim for >= ~2048 workgroups; each split keeps at least 2048 tokens
-  int64_t P = ceil_div(2048, pl.ntiles);
-  P = hmax(1, hmin(P, tokens / 2048));
+  // Few tiles: split the tokens 8 ways, one split per XCD, partials reduced after.
+  int64_t P = (pl.ntiles < 256 && tokens >= 8 * 512) ? 8 : 1;
   pl.tok_per_split = ceil_div(ceil_div(tokens, P), HK) * HK;
   P = hmax(1, ceil_div(tokens, pl.tok_per_split));
+  if (P > 1 && P < 8) P = 8;  // keep p -> XCD; trailing splits may be empty
   pl.P = P;
   pl.ws = P > 1 ? (size_t)P * pl.ntiles * HT * HT * sizeof(float) : 0;
   return pl;
@@ -278,12 +309,12 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
   const HessPlan pl = plan_bf16(n, tokens);
   if (ws_bytes < pl.ws) return hipErrorInvalidValue;
   float* part = pl.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)pl.ntiles, (unsigned)pl.P), dim3(256), 0,
-                     stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens, n,
-                     pl.tok_per_split, S, lds, part, pl.ntiles);
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(X), ldx, tokens, n, pl.tok_per_split, pl.P,
+                     S, lds, part, pl.ntiles);
   if (pl.P > 1) {
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)pl.ntiles), dim3(256), 0, stream,
-                       part, pl.P, pl.ntiles, n, S, lds);
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)(pl.ntiles * (HT * HT / 1024))),
+                       dim3(256), 0, stream, part, pl.P, pl.ntiles, n, S, lds);
   }
   return hipGetLastError();
 }

@@ -10,46 +10,64 @@
 //
 // The column loop needs U, the upper Cholesky factor of H_d^-1
 // (H_d^-1 = U^T U).  With H_d = R R^T, R upper (a Cholesky factorization taken
-// from the last index backwards), U = R^-1, which costs one factorization and
-// one triangular inverse (2n^3/3 flops).  Reversing the index order turns it
-// into the textbook form: with J the reversal, A = J H_d J = L L^T (L lower),
-// R = J L J and U = J L^-1 J.  So the kernels build A (permuted, damped,
-// reversed) in fp64, run a blocked right-looking lower Cholesky and a blocked
-// lower triangular inverse in place, and write U[k][l] = L^-1[n-1-k][n-1-l]
+// from the last index backwards), U = R^-1: one factorization and one
+// triangular inverse, 2n^3/3 flops.  Reversing the index order gives the
+// textbook form: with J the reversal, A = J H_d J = L L^T (L lower), R = J L J
+// and U = J L^-1 J.  So the kernels build A (permuted, damped, reversed) in
+// fp64 and compute X = L^-1 directly, then write U[k][l] = X[n-1-k][n-1-l]
 // rounded to fp32.
 //
-// Blocked with NB = 64: per panel a one-workgroup factorization of the 64x64
-// diagonal block (which also inverts it), a triangular solve of the panel
-// below it and a lower-triangle SYRK of the trailing matrix; then per block
-// column (last to first) one kernel forms L^-1 below the diagonal.
+// X = L^-1 by recursive halving.  For A = [[A11, .], [A21, A22]]:
+//   X11 = chol_inv(A11)                  (recursion; nodes of <= 128 in one kernel)
+//   T   = A21 X11^T          (= L21)     GEMM, X11 lower
+//   A22 = A22 - T T^T                    SYRK, lower tiles
+//   M   = T X11              (= L21 X11) GEMM, stored over A21
+//   X22 = chol_inv(A22)                  (recursion)
+//   X21 = -X22 M                         GEMM, X22 lower
+// which follows from A21 = L21 L11^T, A22 = L21 L21^T + L22 L22^T and
+// L^-1 = [[X11, 0], [-X22 L21 X11, X22]].  The leaves run in order; everything
+// between them is a large GEMM on v_mfma_f64_16x16x4_f64, so no kernel carries
+// a long serial reduction.
 #include "kernels.hpp"
 
 namespace gptq {
 
 namespace {
 
-constexpr int NB = 64;
-constexpr int NBP = NB + 1;
+constexpr int NB = 64;     // register-blocked factor/inverse size
+constexpr int NODE = 128;  // subproblems up to this size run in one workgroup
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 struct PrepWs {
-  double* A;     // [n, n]
-  double* Dinv;  // [nblk, NB, NB]
-  double* P;     // [n, NB]
+  double* A;     // [n, n] lower: damped, permuted, reversed Hessian (overwritten)
+  double* X;     // [n, n] lower: L^-1
+  double* T;     // [s2, s1] of the top split
   double* diag;  // [n]
   double* lam;   // [1]
   int32_t* perm; // [n]
 };
 
+int64_t split_first(int64_t s) {
+  const int64_t blocks = ceil_div(s, NODE);
+  return ((blocks + 1) / 2) * NODE;
+}
+
+size_t t_elems(int64_t n) {
+  if (n <= NODE) return 0;
+  const int64_t s1 = split_first(n);
+  return (size_t)(n - s1) * (size_t)s1;
+}
+
 PrepWs carve(void* ws, int64_t n) {
-  const int64_t nblk = ceil_div(n, NB);
   char* p = reinterpret_cast<char*>(ws);
   PrepWs w;
   w.A = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * n * sizeof(double), 256);
-  w.Dinv = reinterpret_cast<double*>(p);
-  p += align_up((size_t)nblk * NB * NB * sizeof(double), 256);
-  w.P = reinterpret_cast<double*>(p);
-  p += align_up((size_t)n * NB * sizeof(double), 256);
+  w.X = reinterpret_cast<double*>(p);
+  p += align_up((size_t)n * n * sizeof(double), 256);
+  w.T = reinterpret_cast<double*>(p);
+  p += align_up(t_elems(n) * sizeof(double), 256);
   w.diag = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * sizeof(double), 256);
   w.lam = reinterpret_cast<double*>(p);
@@ -147,210 +165,392 @@ __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ 
   }
 }
 
-// Factor the diagonal block at kb (lower Cholesky) and invert it.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int64_t n,
-                                                         int64_t kb, double* __restrict__ Dinv,
-                                                         int32_t* __restrict__ info) {
-  __shared__ double Ls[NB][NBP];
-  __shared__ double Li[NB][NBP];
-  const int tid = threadIdx.x;
-  const int nb = (int)min<int64_t>(NB, n - kb);
-  for (int e = tid; e < NB * NB; e += blockDim.x) {
-    const int i = e / NB, j = e % NB;
-    Ls[i][j] = (i < nb && j <= i) ? A[(kb + i) * n + kb + j] : (i == j ? 1.0 : 0.0);
-    Li[i][j] = i == j ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  for (int k = 0; k < nb; ++k) {
-    if (tid == 0) {
-      double d = Ls[k][k];
-      if (!(d > 0.0) || !isfinite(d)) {
-        if (*info == 0) *info = (int32_t)(n - (kb + k));  // processing position + 1
+// ---------------------------------------------------------------------------
+// Register-blocked 64x64 factor + inverse, shared by the node kernel.
+// 16 x 16 threads, each owning the 4 x 4 entries (ty + 16u, tx + 16v).  One
+// sweep over the columns k does both: the right-looking Cholesky step (column
+// k of L from the updated column of A, rank-1 update of the trailing part) and
+// the forward elimination of X = L^-1 (row k of X becomes final as x_kj / l_kk,
+// then x_ij -= l_ik x_kj below it), which needs exactly column k of L and the
+// reciprocal pivot of the same step.  Column k of A and row k of X travel
+// through LDS, double buffered: one barrier per column.  L itself is never
+// stored.  Entries of `a` above the diagonal are scratch; rows/cols >= s hold
+// the identity.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void chol_inv_regs(double (&a)[4][4], double (&x)[4][4], int s,
+                                              int64_t n, int64_t off, int32_t* info,
+                                              double (*colb)[NB], double (*rowb)[NB]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[u][v] = (ty + 16 * u == tx + 16 * v) ? 1.0 : 0.0;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    for (int kk = 0; kk < 16; ++kk) {
+      const int k = 16 * kb + kk;
+      if (k >= s) break;
+      double* cb = colb[k & 1];
+      double* xb = rowb[k & 1];
+      if (tx == kk) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cb[ty + 16 * u] = a[u][kb];
+      }
+      if (ty == kk) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xb[tx + 16 * v] = x[kb][v];
+      }
+      __syncthreads();
+      double d = cb[k];
+      const bool bad = !(d > 0.0) || !isfinite(d);
+      if (bad) {
+        if (threadIdx.x == 0 && *info == 0) *info = (int32_t)(n - (off + k));  // position + 1
         d = 1.0;
       }
-      Ls[k][k] = sqrt(d);
-    }
-    __syncthreads();
-    for (int i = k + 1 + tid; i < nb; i += blockDim.x) Ls[i][k] /= Ls[k][k];
-    __syncthreads();
-    const int rem = nb - k - 1;
-    for (int e = tid; e < rem * rem; e += blockDim.x) {
-      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
-      if (j <= i) Ls[i][j] -= Ls[i][k] * Ls[j][k];
-    }
-    __syncthreads();
-  }
-  // Li = Ls^-1 by forward elimination applied to the identity
-  for (int k = 0; k < nb; ++k) {
-    for (int c = tid; c <= k; c += blockDim.x) Li[k][c] /= Ls[k][k];
-    __syncthreads();
-    const int rem = nb - k - 1;
-    for (int e = tid; e < rem * (k + 1); e += blockDim.x) {
-      const int i = k + 1 + e / (k + 1), c = e % (k + 1);
-      Li[i][c] -= Ls[i][k] * Li[k][c];
-    }
-    __syncthreads();
-  }
-  const int64_t blk = kb / NB;
-  for (int e = tid; e < NB * NB; e += blockDim.x) {
-    const int i = e / NB, j = e % NB;
-    if (i < nb && j <= i) A[(kb + i) * n + kb + j] = Ls[i][j];
-    Dinv[(blk * NB + i) * NB + j] = (i < nb && j < nb && j <= i) ? Li[i][j] : 0.0;
-  }
-}
-
-// 64x64 fp64 tile product, 256 threads x 4x4 outputs.  acc[u][v] accumulates
-// sum_k Aop(ty + 16u, k) * Bop(k, tx + 16v) for k in [0, K).
-// Aop(i, k) = Ablk[i * lda + k]; Bop(k, j) = Bblk[k * ldb + j] if b_kmajor
-// else Bblk[j * ldb + k].  Rows/cols past (mi, nj) read as 0.
-__device__ void tile_gemm64(const double* __restrict__ Ablk, int64_t lda, int mi,
-                            const double* __restrict__ Bblk, int64_t ldb, int nj, bool b_kmajor,
-                            int K, double (*As)[NBP], double (*Bs)[NBP], double acc[4][4]) {
-  constexpr int KC = 16;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  for (int k0 = 0; k0 < K; k0 += KC) {
-    __syncthreads();
-    for (int e = tid; e < KC * NB; e += blockDim.x) {
-      const int kk = e % KC, ii = e / KC;
-      const bool kin = k0 + kk < K;
-      As[kk][ii] = (kin && ii < mi) ? Ablk[ii * lda + k0 + kk] : 0.0;
-      if (!b_kmajor) Bs[kk][ii] = (kin && ii < nj) ? Bblk[ii * ldb + k0 + kk] : 0.0;
-    }
-    if (b_kmajor) {
-      for (int e = tid; e < KC * NB; e += blockDim.x) {
-        const int kk = e / NB, jj = e % NB;
-        Bs[kk][jj] = (k0 + kk < K && jj < nj) ? Bblk[(k0 + kk) * ldb + jj] : 0.0;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      double a[4], b[4];
+      const double rp = 1.0 / sqrt(d);  // 1 / l_kk
+      double ci[4], cj[4], xk[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a[u] = As[kk][ty + 16 * u];
-        b[u] = Bs[kk][tx + 16 * u];
+        const int i = ty + 16 * u;
+        ci[u] = (i > k && i < s) ? cb[i] * rp : 0.0;  // l_ik
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = tx + 16 * v;
+        cj[v] = (j > k && j < s) ? cb[j] * rp : 0.0;  // l_jk
+        xk[v] = j <= k ? xb[j] * rp : 0.0;            // final x_kj
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+        for (int v = 0; v < 4; ++v) {
+          a[u][v] = fma(-ci[u], cj[v], a[u][v]);
+          x[u][v] = fma(-ci[u], xk[v], x[u][v]);
+        }
+      if (ty == kk) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[kb][v] = xk[v];
+      }
     }
   }
-}
-
-// Panel below the diagonal block: A[i, kb:kb+nb] <- A[i, kb:kb+nb] * Dinv_kb^T.
-__global__ __launch_bounds__(256) void trsm_panel_kernel(double* __restrict__ A, int64_t n,
-                                                         int64_t kb,
-                                                         const double* __restrict__ Dinv) {
-  __shared__ double As[16][NBP], Bs[16][NBP];
-  __shared__ double Out[NB][NBP];
-  const int nb = (int)min<int64_t>(NB, n - kb);
-  const int64_t r0 = kb + nb + (int64_t)blockIdx.x * NB;
-  const int mi = (int)min<int64_t>(NB, n - r0);
-  double acc[4][4] = {};
-  tile_gemm64(A + r0 * n + kb, n, mi, Dinv + (kb / NB) * NB * NB, NB, nb, false, nb, As, Bs, acc);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) Out[ty + 16 * u][tx + 16 * v] = acc[u][v];
-  __syncthreads();  // every read of this row block precedes the write-back
-  for (int e = threadIdx.x; e < NB * NB; e += blockDim.x) {
-    const int i = e / NB, j = e % NB;
-    if (i < mi && j < nb) A[(r0 + i) * n + kb + j] = Out[i][j];
-  }
-}
-
-// Trailing update: A[i][j] -= sum_k L[i][kb+k] L[j][kb+k], lower tiles past the panel.
-__device__ __forceinline__ void lower_tile(int64_t L, int64_t& ti, int64_t& tj) {
-  int64_t t = (int64_t)((sqrt(8.0 * (double)L + 1.0) - 1.0) * 0.5);
-  while (t * (t + 1) / 2 > L) --t;
-  while ((t + 1) * (t + 2) / 2 <= L) ++t;
-  ti = t;
-  tj = L - t * (t + 1) / 2;
-}
-
-__global__ __launch_bounds__(256) void syrk_update_kernel(double* __restrict__ A, int64_t n,
-                                                          int64_t kb) {
-  __shared__ double As[16][NBP], Bs[16][NBP];
-  const int nb = (int)min<int64_t>(NB, n - kb);
-  const int64_t base = kb + nb;
-  int64_t ti, tj;
-  lower_tile(blockIdx.x, ti, tj);
-  const int64_t i0 = base + ti * NB, j0 = base + tj * NB;
-  const int mi = (int)min<int64_t>(NB, n - i0), nj = (int)min<int64_t>(NB, n - j0);
-  double acc[4][4] = {};
-  tile_gemm64(A + i0 * n + kb, n, mi, A + j0 * n + kb, n, nj, false, nb, As, Bs, acc);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t gi = i0 + ty + 16 * u, gj = j0 + tx + 16 * v;
-      if (gi < n && gj < n && gj <= gi) A[gi * n + gj] -= acc[u][v];
-    }
-}
-
-// Copy the L column block jb below its diagonal block into P[k - (jb+1)NB][0:NB].
-__global__ __launch_bounds__(256) void copy_panel_kernel(const double* __restrict__ A, int64_t n,
-                                                         int64_t jb, double* __restrict__ P) {
-  const int64_t k = (jb + 1) * NB + blockIdx.x;
-  if (k >= n) return;
-  for (int c = threadIdx.x; c < NB; c += blockDim.x) P[(k - (jb + 1) * NB) * NB + c] = A[k * n + jb * NB + c];
-}
-
-// L^-1 block column jb: for row block i > jb,
-//   X[i, jb] = -(sum_{kb=jb+1}^{i} X[i, kb] L[kb, jb]) X[jb, jb],
-// X[i, kb] for kb > jb already in A (kb < i) or Dinv (kb == i); L[kb, jb] in P.
-__global__ __launch_bounds__(256) void trtri_step_kernel(double* __restrict__ A, int64_t n,
-                                                         int64_t jb,
-                                                         const double* __restrict__ Dinv,
-                                                         const double* __restrict__ P) {
-  __shared__ double As[16][NBP], Bs[16][NBP];
-  __shared__ double T[NB][NBP];
-  const int64_t ib = jb + 1 + blockIdx.x;
-  const int64_t i0 = ib * NB;
-  const int mi = (int)min<int64_t>(NB, n - i0);
-  double acc[4][4] = {};
-  // off-diagonal part: X[i, (jb+1)NB : i0] * P[0 : i0 - (jb+1)NB]
-  const int64_t koff = (jb + 1) * NB;
-  const int64_t K1 = i0 - koff;
-  for (int64_t k0 = 0; k0 < K1; k0 += NB)
-    tile_gemm64(A + i0 * n + koff + k0, n, mi, P + k0 * NB, NB, NB, true, NB, As, Bs, acc);
-  // diagonal part: Dinv_ib * P[i0 - koff : i0 - koff + mi]
-  tile_gemm64(Dinv + ib * NB * NB, NB, mi, P + K1 * NB, NB, NB, true, mi, As, Bs, acc);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   __syncthreads();
+}
+
+// acc[u][v] (+)= sum_k P(ty + 16u, k) * Q(k, tx + 16v), k < 64, operands in LDS.
+// P is read as Ps[i][k]; Q as Qs[k][j] (QT == false) or Qs[j][k] (QT == true).
+template <bool QT>
+__device__ __forceinline__ void mm64(const double (*Ps)[NB + 1], const double (*Qs)[NB + 1],
+                                     double (&acc)[4][4]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll 4
+  for (int k = 0; k < NB; ++k) {
+    double p[4], q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = Ps[ty + 16 * u][k];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) q[v] = QT ? Qs[tx + 16 * v][k] : Qs[k][tx + 16 * v];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[u][v] = fma(p[u], q[v], acc[u][v]);
+  }
+}
+
+__device__ __forceinline__ void to_lds(double (*S)[NB + 1], const double (&r)[4][4]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) T[ty + 16 * u][tx + 16 * v] = acc[u][v];
-  // out = -T * Dinv_jb   (Dinv_jb k-major: Dinv[jb][k][c])
-  double acc2[4][4] = {};
-  tile_gemm64(&T[0][0], NBP, mi, Dinv + jb * NB * NB, NB, NB, true, NB, As, Bs, acc2);
+    for (int v = 0; v < 4; ++v) S[ty + 16 * u][tx + 16 * v] = r[u][v];
+}
+
+// A node of size s <= 128 in one workgroup: X[off:off+s, off:off+s] = inverse of
+// the Cholesky factor of A[off:off+s, off:off+s], by the same split as chol_inv
+// (64 + rest) with every product done from LDS.
+__global__ __launch_bounds__(256) void node_kernel(const double* __restrict__ A,
+                                                   double* __restrict__ X, int64_t n,
+                                                   int64_t off, int s,
+                                                   int32_t* __restrict__ info) {
+  __shared__ double Ls[NB][NB + 1];
+  __shared__ double Rs[NB][NB + 1];
+  __shared__ double colb[2][NB];
+  __shared__ double rowb[2][NB];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int s1 = s < NB ? s : NB;
+  const int s2 = s - s1;
+  double a[4][4], x11[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int i = ty + 16 * u, c = tx + 16 * v;
-      if (i < mi) A[(i0 + i) * n + jb * NB + c] = -acc2[u][v];
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      a[u][v] = (i < s1 && j <= i) ? A[(off + i) * n + off + j] : (i == j ? 1.0 : 0.0);
+    }
+  chol_inv_regs(a, x11, s1, n, off, info, colb, rowb);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      if (i < s1 && j < s1) X[(off + i) * n + off + j] = x11[u][v];
+    }
+  if (s2 <= 0) return;
+  const int64_t o2 = off + NB;
+  // T = A21 X11^T
+  double t[4][4] = {};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      Ls[i][j] = i < s2 ? A[(o2 + i) * n + off + j] : 0.0;
+    }
+  to_lds(Rs, x11);  // Rs[j][k] = X11(j, k)
+  __syncthreads();
+  mm64<true>(Ls, Rs, t);
+  __syncthreads();
+  // A22 -= T T^T (lower), M = T X11
+  to_lds(Ls, t);  // Ls[i][k] = T(i, k)
+  double a22[4][4], m[4][4] = {};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      a22[u][v] = (i < s2 && j <= i) ? A[(o2 + i) * n + o2 + j] : (i == j ? 1.0 : 0.0);
+    }
+  __syncthreads();
+  double tt[4][4] = {};
+  mm64<true>(Ls, Ls, tt);  // sum_k T(i,k) T(j,k)
+  mm64<false>(Ls, Rs, m);  // sum_k T(i,k) X11(k,j), Rs[k][j] = X11(k, j)
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      if (i < s2 && j <= i) a22[u][v] -= tt[u][v];
+    }
+  double x22[4][4];
+  chol_inv_regs(a22, x22, s2, n, o2, info, colb, rowb);
+  // X21 = -X22 M
+  to_lds(Ls, x22);
+  to_lds(Rs, m);
+  __syncthreads();
+  double x21[4][4] = {};
+  mm64<false>(Ls, Rs, x21);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ty + 16 * u, j = tx + 16 * v;
+      if (i < s2) {
+        X[(o2 + i) * n + off + j] = -x21[u][v];
+        if (j < s2) X[(o2 + i) * n + o2 + j] = x22[u][v];
+      }
     }
 }
 
-// U[k][l] = L^-1[n-1-k][n-1-l] for l >= k (fp32), 0 below the diagonal.
-__global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__ A,
-                                                      const double* __restrict__ Dinv, int64_t n,
+// C = alpha * opA * opB + beta * C with v_mfma_f64_16x16x4_f64 on TILE x TILE
+// output tiles (4 waves, each (TILE/2)^2), K staged through LDS in chunks of 32
+// with the next chunk prefetched into registers.
+// opA(i, k) = TA ? A[k * lda + i] : A[i * lda + k];
+// opB(k, j) = TB ? B[j * ldb + k] : B[k * ldb + j].
+// K range per tile for triangular operands: KLO_J: k >= j0; KHI_J: k < j0 + TILE;
+// KHI_I: k < i0 + TILE (the skipped part is all zero; entries of a triangular
+// operand inside the range but outside its triangle are stored zeros).
+// LOWER: only tiles and entries with i >= j (M == N).  beta == 0 never reads C.
+enum { KLO_J = 1, KHI_J = 2, KHI_I = 4 };
+
+struct GemmArgs {
+  const double* A;
+  int64_t lda;
+  const double* B;
+  int64_t ldb;
+  double* C;
+  int64_t ldc;
+  int64_t M, N, K;
+  double alpha, beta;
+  int kmode;
+  int lower;
+  int64_t tiles_n;
+};
+
+constexpr int GK = 32;
+
+template <int TILE, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs g) {
+  constexpr int HALF = TILE / 2;          // per-wave edge
+  constexpr int SUB = HALF / 16;          // MFMA sub-tiles per wave edge
+  constexpr int PER = GK * TILE / 256;    // staged elements per thread per operand
+  __shared__ double As[GK][TILE + 1];
+  __shared__ double Bs[GK][TILE + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wr = wv >> 1, wc = wv & 1;
+  int64_t ti, tj;
+  if (g.lower) {
+    const int64_t L = blockIdx.x;
+    int64_t t = (int64_t)((sqrt(8.0 * (double)L + 1.0) - 1.0) * 0.5);
+    while (t * (t + 1) / 2 > L) --t;
+    while ((t + 1) * (t + 2) / 2 <= L) ++t;
+    ti = t;
+    tj = L - t * (t + 1) / 2;
+  } else {
+    ti = blockIdx.x / g.tiles_n;
+    tj = blockIdx.x % g.tiles_n;
+  }
+  const int64_t i0 = ti * TILE, j0 = tj * TILE;
+  int64_t kb = 0, ke = g.K;
+  if (g.kmode & KLO_J) kb = j0;
+  if (g.kmode & KHI_J) ke = min(ke, j0 + TILE);
+  if (g.kmode & KHI_I) ke = min(ke, i0 + TILE);
+
+  f64x4 acc[SUB][SUB];
+#pragma unroll
+  for (int a = 0; a < SUB; ++a)
+#pragma unroll
+    for (int b = 0; b < SUB; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  double ra[PER], rb[PER];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e = tid + 256 * r;
+      int ii, kk;
+      if (TA) { ii = e % TILE; kk = e / TILE; } else { kk = e % GK; ii = e / GK; }
+      const int64_t gi = i0 + ii, gk = k0 + kk;
+      ra[r] = (gi < g.M && gk < ke) ? (TA ? g.A[gk * g.lda + gi] : g.A[gi * g.lda + gk]) : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e = tid + 256 * r;
+      int jj, kk;
+      if (TB) { kk = e % GK; jj = e / GK; } else { jj = e % TILE; kk = e / TILE; }
+      const int64_t gj = j0 + jj, gk = k0 + kk;
+      rb[r] = (gj < g.N && gk < ke) ? (TB ? g.B[gj * g.ldb + gk] : g.B[gk * g.ldb + gj]) : 0.0;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e = tid + 256 * r;
+      if (TA) As[e / TILE][e % TILE] = ra[r]; else As[e % GK][e / GK] = ra[r];
+      if (TB) Bs[e % GK][e / GK] = rb[r]; else Bs[e / TILE][e % TILE] = rb[r];
+    }
+  };
+
+  if (kb < ke) fetch(kb);
+  for (int64_t k0 = kb; k0 < ke; k0 += GK) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (k0 + GK < ke) fetch(k0 + GK);
+#pragma unroll
+    for (int ks = 0; ks < GK; ks += 4) {
+      double af[SUB], bf[SUB];
+#pragma unroll
+      for (int a = 0; a < SUB; ++a) af[a] = As[ks + (lane >> 4)][HALF * wr + 16 * a + (lane & 15)];
+#pragma unroll
+      for (int b = 0; b < SUB; ++b) bf[b] = Bs[ks + (lane >> 4)][HALF * wc + 16 * b + (lane & 15)];
+#pragma unroll
+      for (int a = 0; a < SUB; ++a)
+#pragma unroll
+        for (int b = 0; b < SUB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+  }
+  // D layout of the f64 16x16x4 MFMA (measured): lane l, element q -> row l/16 + 4q,
+  // column l%16 of the 16x16 tile (rows interleaved, unlike the f32 variant)
+#pragma unroll
+  for (int a = 0; a < SUB; ++a)
+#pragma unroll
+    for (int b = 0; b < SUB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t gi = i0 + HALF * wr + 16 * a + (lane >> 4) + 4 * q;
+        const int64_t gj = j0 + HALF * wc + 16 * b + (lane & 15);
+        if (gi >= g.M || gj >= g.N) continue;
+        if (g.lower && gj > gi) continue;
+        double* c = g.C + gi * g.ldc + gj;
+        const double v = g.alpha * acc[a][b][q];
+        *c = g.beta == 0.0 ? v : fma(g.beta, *c, v);
+      }
+}
+
+template <int TILE>
+void launch_gemm_tile(const GemmArgs& g0, bool ta, bool tb, hipStream_t stream) {
+  GemmArgs g = g0;
+  const int64_t tm = ceil_div(g.M, TILE), tn = ceil_div(g.N, TILE);
+  g.tiles_n = tn;
+  const int64_t tiles = g.lower ? tm * (tm + 1) / 2 : tm * tn;
+  if (tiles == 0) return;
+  const dim3 grid((unsigned)tiles);
+  if (!ta && !tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, false, false>), grid, dim3(256), 0, stream, g);
+  else if (!ta && tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, false, true>), grid, dim3(256), 0, stream, g);
+  else if (ta && !tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, true, false>), grid, dim3(256), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_f64_kernel<TILE, true, true>), grid, dim3(256), 0, stream, g);
+}
+
+hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t ldb, bool tb,
+                double* C, int64_t ldc, int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                int kmode, bool lower, hipStream_t stream) {
+  GemmArgs g;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K; g.alpha = alpha; g.beta = beta; g.kmode = kmode;
+  g.lower = lower ? 1 : 0;
+  g.tiles_n = 0;
+  // large problems: 128-wide tiles (better operand reuse) while they still fill the chip
+  const bool big = ceil_div(M, 128) * ceil_div(N, 128) >= 192;
+  if (big) launch_gemm_tile<128>(g, ta, tb, stream);
+  else launch_gemm_tile<64>(g, ta, tb, stream);
+  return hipGetLastError();
+}
+
+__global__ void fill_f64_kernel(double* __restrict__ p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = i; k < count; k += stride) p[k] = 0.0;
+}
+
+// X[off:off+s, off:off+s] = inverse of the Cholesky factor of A[off:off+s, off:off+s].
+hipError_t chol_inv(const PrepWs& w, int64_t n, int64_t off, int64_t s, int32_t* info,
+                    hipStream_t stream) {
+  if (s <= NODE) {
+    hipLaunchKernelGGL(node_kernel, dim3(1), dim3(256), 0, stream, w.A, w.X, n, off, (int)s,
+                       info);
+    return hipGetLastError();
+  }
+  const int64_t s1 = split_first(s), s2 = s - s1;
+  double* A21 = w.A + (off + s1) * n + off;
+  double* A22 = w.A + (off + s1) * n + off + s1;
+  const double* X11 = w.X + off * n + off;
+  double* X21 = w.X + (off + s1) * n + off;
+  const double* X22 = w.X + (off + s1) * n + off + s1;
+  hipError_t e = chol_inv(w, n, off, s1, info, stream);
+  if (e != hipSuccess) return e;
+  // T = A21 X11^T   (X11(j, k) = 0 for k > j)
+  e = gemm(A21, n, false, X11, n, true, w.T, s1, s2, s1, s1, 1.0, 0.0, KHI_J, false, stream);
+  if (e != hipSuccess) return e;
+  // A22 -= T T^T    (lower tiles)
+  e = gemm(w.T, s1, false, w.T, s1, true, A22, n, s2, s2, s1, -1.0, 1.0, 0, true, stream);
+  if (e != hipSuccess) return e;
+  // A21 := T X11    (X11(k, j) = 0 for k < j)
+  e = gemm(w.T, s1, false, X11, n, false, A21, n, s2, s1, s1, 1.0, 0.0, KLO_J, false, stream);
+  if (e != hipSuccess) return e;
+  e = chol_inv(w, n, off + s1, s2, info, stream);
+  if (e != hipSuccess) return e;
+  // X21 = -X22 A21  (X22(i, k) = 0 for k > i)
+  return gemm(X22, n, false, A21, n, false, X21, n, s2, s1, s2, -1.0, 0.0, KHI_I, false, stream);
+}
+
+// U[k][l] = X[n-1-k][n-1-l] for l >= k (fp32), 0 below the diagonal.
+__global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__ X, int64_t n,
                                                       float* __restrict__ U, int64_t ldu) {
   const int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (l >= n) return;
   for (int64_t k = blockIdx.y; k < n; k += gridDim.y) {
     float v = 0.0f;
-    if (l >= k) {
-      const int64_t a = n - 1 - k, b = n - 1 - l;
-      const int64_t ba = a / NB, bb = b / NB;
-      v = (float)(ba == bb ? Dinv[(ba * NB + a % NB) * NB + b % NB] : A[a * n + b]);
-    }
+    if (l >= k) v = (float)X[(n - 1 - k) * n + (n - 1 - l)];
     U[k * ldu + l] = v;
   }
 }
@@ -358,10 +558,8 @@ __global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t n) {
-  const int64_t nblk = ceil_div(n, NB);
-  size_t b = align_up((size_t)n * n * sizeof(double), 256);
-  b += align_up((size_t)nblk * NB * NB * sizeof(double), 256);
-  b += align_up((size_t)n * NB * sizeof(double), 256);
+  size_t b = 2 * align_up((size_t)n * n * sizeof(double), 256);
+  b += align_up(t_elems(n) * sizeof(double), 256);
   b += align_up((size_t)n * sizeof(double), 256);
   b += 256;
   b += align_up((size_t)n * sizeof(int32_t), 256);
@@ -373,7 +571,6 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
                           int32_t* info, void* ws, hipStream_t stream) {
   PrepWs w = carve(ws, n);
   int32_t* pm = perm ? perm : w.perm;
-  const int64_t nblk = ceil_div(n, NB);
   hipLaunchKernelGGL(diag_damp_kernel, dim3(1), dim3(1024), 0, stream, S, n, lds, perc_damp,
                      w.diag, dead, w.lam, lambda_out, info);
   if (desc_act) {
@@ -387,27 +584,13 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
     hipLaunchKernelGGL(build_a_kernel, grid, dim3(256), 0, stream, S, n, lds, pm, w.diag, w.lam,
                        w.A, info);
   }
-  for (int64_t kb = 0; kb < n; kb += NB) {
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, n, kb, w.Dinv, info);
-    const int64_t rest = n - kb - NB;
-    if (rest > 0) {
-      const int64_t rb = ceil_div(rest, NB);
-      hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)rb), dim3(256), 0, stream, w.A, n, kb,
-                         w.Dinv);
-      hipLaunchKernelGGL(syrk_update_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0,
-                         stream, w.A, n, kb);
-    }
-  }
-  for (int64_t jb = nblk - 2; jb >= 0; --jb) {
-    const int64_t rows = n - (jb + 1) * NB;
-    hipLaunchKernelGGL(copy_panel_kernel, dim3((unsigned)rows), dim3(64), 0, stream, w.A, n, jb,
-                       w.P);
-    hipLaunchKernelGGL(trtri_step_kernel, dim3((unsigned)(nblk - 1 - jb)), dim3(256), 0, stream,
-                       w.A, n, jb, w.Dinv, w.P);
-  }
+  // X's strict upper triangle must read as zero for the 128-wide GEMM tiles
+  hipLaunchKernelGGL(fill_f64_kernel, dim3(2048), dim3(256), 0, stream, w.X, n * n);
+  hipError_t e = chol_inv(w, n, 0, n, info, stream);
+  if (e != hipSuccess) return e;
   {
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(n, 2048));
-    hipLaunchKernelGGL(write_u_kernel, grid, dim3(256), 0, stream, w.A, w.Dinv, n, U, ldu);
+    hipLaunchKernelGGL(write_u_kernel, grid, dim3(256), 0, stream, w.X, n, U, ldu);
   }
   return hipGetLastError();
 }
