@@ -207,6 +207,105 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
       }
 }
 
+// Interior variant: every tile full (n % 256 == 0), every split a whole number of
+// 64-token stages, rows 16-byte aligned.  No bounds checks and no branches in the
+// stage loop, so the next stage's 16 global loads, this stage's 64 MFMAs with
+// their LDS reads, and the transposed LDS writes can be interleaved freely.
+// Diagonal tiles load both operands (the same data) to keep the loop uniform.
+__global__ __launch_bounds__(256) void syrk_bf16_full_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t ldx, int64_t tok_per_split,
+                                                             int64_t P, float* __restrict__ S,
+                                                             int64_t lds,
+                                                             float* __restrict__ part,
+                                                             int64_t ntiles) {
+  __shared__ __align__(16) uint16_t smem[4 * HT * HROW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wr = wv >> 1, wc = wv & 1;
+  const int64_t L = blockIdx.x / P;
+  const int64_t p = blockIdx.x % P;
+  int64_t ti, tj;
+  tile_coords(L, ti, tj);
+  const int64_t i0 = ti * HT, j0 = tj * HT;
+  const int o = tid & 7, cb = tid >> 3;
+  const int64_t t_begin = p * tok_per_split;
+  const int nstage = (int)(tok_per_split / HK);
+  const uint16_t* pa = X + (t_begin + 8 * o) * ldx + i0 + 8 * cb;
+  const uint16_t* pb = X + (t_begin + 8 * o) * ldx + j0 + 8 * cb;
+  const int64_t step = HK * ldx;
+
+  f32x16 acc[HSUB][HSUB];
+#pragma unroll
+  for (int a = 0; a < HSUB; ++a)
+#pragma unroll
+    for (int b = 0; b < HSUB; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+
+  Block8 ra, rb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ra.r[e] = *reinterpret_cast<const uint4*>(pa + e * ldx);
+    rb.r[e] = *reinterpret_cast<const uint4*>(pb + e * ldx);
+  }
+  store_block8(smem, 8 * cb, o, ra);
+  store_block8(smem + HT * HROW, 8 * cb, o, rb);
+  __syncthreads();
+  int buf = 0;
+  for (int s = 0; s < nstage; ++s) {
+    // next stage (the last iteration re-reads the current one; it is not used)
+    const int64_t adv = (s + 1 < nstage) ? step : 0;
+    pa += adv;
+    pb += adv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ra.r[e] = *reinterpret_cast<const uint4*>(pa + e * ldx);
+      rb.r[e] = *reinterpret_cast<const uint4*>(pb + e * ldx);
+    }
+    const uint16_t* At = smem + 2 * buf * HT * HROW;
+    const uint16_t* Bt = At + HT * HROW;
+#pragma unroll 2
+    for (int kk = 0; kk < HK / 16; ++kk) {
+      bf16x8 af[HSUB], bfr[HSUB];
+#pragma unroll
+      for (int a = 0; a < HSUB; ++a) {
+        const int row = HWT * wr + 32 * a + (lane & 31);
+        af[a] = *reinterpret_cast<const bf16x8*>(At + row * HROW + 16 * kk + 8 * (lane >> 5));
+      }
+#pragma unroll
+      for (int b = 0; b < HSUB; ++b) {
+        const int col = HWT * wc + 32 * b + (lane & 31);
+        bfr[b] = *reinterpret_cast<const bf16x8*>(Bt + col * HROW + 16 * kk + 8 * (lane >> 5));
+      }
+#pragma unroll
+      for (int a = 0; a < HSUB; ++a)
+#pragma unroll
+        for (int b = 0; b < HSUB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+    uint16_t* nxt = smem + 2 * (buf ^ 1) * HT * HROW;
+    store_block8(nxt, 8 * cb, o, ra);
+    store_block8(nxt + HT * HROW, 8 * cb, o, rb);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+#pragma unroll
+  for (int a = 0; a < HSUB; ++a)
+#pragma unroll
+    for (int b = 0; b < HSUB; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int ii = HWT * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int jj = HWT * wc + 32 * b + (lane & 31);
+        if (part) {
+          part[((p * ntiles + L) * HT + ii) * HT + jj] = acc[a][b][q];
+        } else if (jj + j0 <= ii + i0) {
+          S[(i0 + ii) * lds + j0 + jj] += acc[a][b][q];
+        }
+      }
+}
+
 // S[lower] += sum over splits of the partial tiles, splits in order.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part,
                                                               int64_t P, int64_t ntiles,
@@ -309,9 +408,18 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
   const HessPlan pl = plan_bf16(n, tokens);
   if (ws_bytes < pl.ws) return hipErrorInvalidValue;
   float* part = pl.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(X), ldx, tokens, n, pl.tok_per_split, pl.P,
-                     S, lds, part, pl.ntiles);
+  const bool interior = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ldx % 8 == 0 &&
+                        n % HT == 0 && tokens % (pl.P * HK) == 0 &&
+                        pl.tok_per_split * pl.P == tokens;
+  if (interior) {
+    hipLaunchKernelGGL(syrk_bf16_full_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0,
+                       stream, reinterpret_cast<const uint16_t*>(X), ldx, pl.tok_per_split, pl.P,
+                       S, lds, part, pl.ntiles);
+  } else {
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(X), ldx, tokens, n, pl.tok_per_split,
+                       pl.P, S, lds, part, pl.ntiles);
+  }
   if (pl.P > 1) {
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)(pl.ntiles * (HT * HT / 1024))),
                        dim3(256), 0, stream, part, pl.P, pl.ntiles, n, S, lds);
