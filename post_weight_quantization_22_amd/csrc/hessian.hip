@@ -208,11 +208,16 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 }
 
 // Interior variant: every tile full (n % 256 == 0), every split a whole number of
-// 64-token stages, rows 16-byte aligned.  No bounds checks and no branches in the
-// stage loop, so the next stage's 16 global loads, this stage's 64 MFMAs with
-// their LDS reads, and the transposed LDS writes can be interleaved freely.
+// 64-token stages, rows 16-byte aligned.  No bounds checks, no branches in the
+// stage loop.  256 x 256 lower tiles; 512 threads = 8 waves (2 per SIMD), each
+// a 128 x 64 block (4 x 2 MFMA accumulators), so one wave's memory and LDS
+// waits are covered by its SIMD partner's MFMAs.  Each thread owns one 8 x 8
+// block of one operand per stage, fetched one stage ahead and transposed into
+// the idle LDS buffer after the current stage's MFMAs; one barrier per stage.
 // Diagonal tiles load both operands (the same data) to keep the loop uniform.
-__global__ __launch_bounds__(256) void syrk_bf16_full_kernel(const uint16_t* __restrict__ X,
+constexpr int FT_I = 256, FT_J = 256;   // tile
+constexpr int FW_I = 128, FW_J = 64;    // per wave
+__global__ __launch_bounds__(512) void syrk_bf16_full_kernel(const uint16_t* __restrict__ X,
                                                              int64_t ldx, int64_t tok_per_split,
                                                              int64_t P, float* __restrict__ S,
                                                              int64_t lds,
@@ -221,89 +226,98 @@ __global__ __launch_bounds__(256) void syrk_bf16_full_kernel(const uint16_t* __r
   __shared__ __align__(16) uint16_t smem[4 * HT * HROW];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wr = wv >> 1, wc = wv & 1;
+  const int wr = wv >> 2, wc = wv & 3;
   const int64_t L = blockIdx.x / P;
   const int64_t p = blockIdx.x % P;
   int64_t ti, tj;
   tile_coords(L, ti, tj);
   const int64_t i0 = ti * HT, j0 = tj * HT;
-  const int o = tid & 7, cb = tid >> 3;
-  const int64_t t_begin = p * tok_per_split;
+  const int opnd = tid >> 8, o = tid & 7, cb = (tid & 255) >> 3;
   const int nstage = (int)(tok_per_split / HK);
-  const uint16_t* pa = X + (t_begin + 8 * o) * ldx + i0 + 8 * cb;
-  const uint16_t* pb = X + (t_begin + 8 * o) * ldx + j0 + 8 * cb;
+  const uint16_t* src = X + (p * tok_per_split + 8 * o) * ldx + (opnd ? j0 : i0) + 8 * cb;
   const int64_t step = HK * ldx;
+  const int slot = opnd * HT * HROW;
 
-  f32x16 acc[HSUB][HSUB];
+  f32x16 acc[FW_I / 32][FW_J / 32];
 #pragma unroll
-  for (int a = 0; a < HSUB; ++a)
+  for (int a = 0; a < FW_I / 32; ++a)
 #pragma unroll
-    for (int b = 0; b < HSUB; ++b)
+    for (int b = 0; b < FW_J / 32; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
 
-  Block8 ra, rb;
+  Block8 rg;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    ra.r[e] = *reinterpret_cast<const uint4*>(pa + e * ldx);
-    rb.r[e] = *reinterpret_cast<const uint4*>(pb + e * ldx);
-  }
-  store_block8(smem, 8 * cb, o, ra);
-  store_block8(smem + HT * HROW, 8 * cb, o, rb);
+  for (int e = 0; e < 8; ++e) rg.r[e] = *reinterpret_cast<const uint4*>(src + e * ldx);
+  store_block8(smem + slot, 8 * cb, o, rg);
   __syncthreads();
   int buf = 0;
   for (int s = 0; s < nstage; ++s) {
-    // next stage (the last iteration re-reads the current one; it is not used)
     const int64_t adv = (s + 1 < nstage) ? step : 0;
-    pa += adv;
-    pb += adv;
+    src += adv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ra.r[e] = *reinterpret_cast<const uint4*>(pa + e * ldx);
-      rb.r[e] = *reinterpret_cast<const uint4*>(pb + e * ldx);
-    }
+    for (int e = 0; e < 8; ++e) rg.r[e] = *reinterpret_cast<const uint4*>(src + e * ldx);
     const uint16_t* At = smem + 2 * buf * HT * HROW;
     const uint16_t* Bt = At + HT * HROW;
 #pragma unroll 2
     for (int kk = 0; kk < HK / 16; ++kk) {
-      bf16x8 af[HSUB], bfr[HSUB];
+      bf16x8 af[FW_I / 32], bfr[FW_J / 32];
 #pragma unroll
-      for (int a = 0; a < HSUB; ++a) {
-        const int row = HWT * wr + 32 * a + (lane & 31);
+      for (int a = 0; a < FW_I / 32; ++a) {
+        const int row = FW_I * wr + 32 * a + (lane & 31);
         af[a] = *reinterpret_cast<const bf16x8*>(At + row * HROW + 16 * kk + 8 * (lane >> 5));
       }
 #pragma unroll
-      for (int b = 0; b < HSUB; ++b) {
-        const int col = HWT * wc + 32 * b + (lane & 31);
+      for (int b = 0; b < FW_J / 32; ++b) {
+        const int col = FW_J * wc + 32 * b + (lane & 31);
         bfr[b] = *reinterpret_cast<const bf16x8*>(Bt + col * HROW + 16 * kk + 8 * (lane >> 5));
       }
 #pragma unroll
-      for (int a = 0; a < HSUB; ++a)
+      for (int a = 0; a < FW_I / 32; ++a)
 #pragma unroll
-        for (int b = 0; b < HSUB; ++b)
+        for (int b = 0; b < FW_J / 32; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
-    uint16_t* nxt = smem + 2 * (buf ^ 1) * HT * HROW;
-    store_block8(nxt, 8 * cb, o, ra);
-    store_block8(nxt + HT * HROW, 8 * cb, o, rb);
+    store_block8(smem + 2 * (buf ^ 1) * HT * HROW + slot, 8 * cb, o, rg);
     __syncthreads();
     buf ^= 1;
   }
 
 #pragma unroll
-  for (int a = 0; a < HSUB; ++a)
+  for (int a = 0; a < FW_I / 32; ++a)
 #pragma unroll
-    for (int b = 0; b < HSUB; ++b)
+    for (int b = 0; b < FW_J / 32; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int ii = HWT * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int jj = HWT * wc + 32 * b + (lane & 31);
+        const int ii = FW_I * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int jj = FW_J * wc + 32 * b + (lane & 31);
         if (part) {
-          part[((p * ntiles + L) * HT + ii) * HT + jj] = acc[a][b][q];
+          part[((p * ntiles + L) * FT_I + ii) * FT_J + jj] = acc[a][b][q];
         } else if (jj + j0 <= ii + i0) {
           S[(i0 + ii) * lds + j0 + jj] += acc[a][b][q];
         }
       }
+}
+
+// S[lower] += sum over splits of the 256 x 256 partial tiles, splits in order.
+__global__ __launch_bounds__(256) void reduce_full_partials_kernel(const float* __restrict__ part,
+                                                                   int64_t P, int64_t ntiles,
+                                                                   float* __restrict__ S,
+                                                                   int64_t lds) {
+  constexpr int CH = FT_I * FT_J / 1024;
+  const int64_t L = blockIdx.x / CH;
+  const int64_t chunk = blockIdx.x % CH;
+  int64_t ti, tj;
+  tile_coords(L, ti, tj);
+  for (int r = 0; r < 4; ++r) {
+    const int e = (int)chunk * 1024 + r * 256 + threadIdx.x;
+    const int ii = e / FT_J, jj = e % FT_J;
+    const int64_t gi = ti * FT_I + ii, gj = tj * FT_J + jj;
+    if (gj > gi) continue;
+    float s = 0.0f;
+    for (int64_t q = 0; q < P; ++q) s += part[(q * ntiles + L) * FT_I * FT_J + e];
+    S[gi * lds + gj] += s;
+  }
 }
 
 // S[lower] += sum over splits of the partial tiles, splits in order.
@@ -389,11 +403,37 @@ HessPlan plan_bf16(int64_t n, int64_t tokens) {
   return pl;
 }
 
+// Interior tiling (256 x 256 tiles of the lower triangle).  P = 0: not usable
+// for these sizes (n not a multiple of 256, or not whole 64-token stages).
+struct FullPlan {
+  int64_t ntiles, P;
+  size_t ws;
+};
+
+FullPlan plan_full(int64_t n, int64_t tokens) {
+  FullPlan fp{0, 0, 0};
+  if (n % FT_I != 0) return fp;
+  const int64_t T = n / FT_I;
+  fp.ntiles = T * (T + 1) / 2;
+  // Token split, one split per XCD: with one workgroup per CU, a grid of
+  // ntiles workgroups runs in ceil(ntiles / 256) rounds, so few tiles leave a
+  // large idle tail; 8 splits make the rounds many (the partial tiles cost one
+  // extra pass over 8 ntiles * 256 KB).
+  int64_t P = 1;
+  if (fp.ntiles <= 2048 && tokens % (8 * HK) == 0 && tokens >= 8 * 512) P = 8;
+  if (tokens % (P * HK) != 0) return fp;
+  fp.P = P;
+  fp.ws = P > 1 ? (size_t)P * fp.ntiles * FT_I * FT_J * sizeof(float) : 0;
+  return fp;
+}
+
 }  // namespace
 
 size_t hessian_ws_bytes(int64_t n, int64_t tokens, int dt) {
   if (dt != GPTQ_BF16 || tokens <= 0 || n <= 0) return 0;
-  return plan_bf16(n, tokens).ws;
+  const FullPlan fp = plan_full(n, tokens);
+  const size_t g = plan_bf16(n, tokens).ws;
+  return fp.P > 0 && fp.ws > g ? fp.ws : g;
 }
 
 hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int dt, int64_t tokens,
@@ -405,21 +445,27 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
                        reinterpret_cast<const float*>(X), ldx, tokens, n, S, lds);
     return hipGetLastError();
   }
+  const FullPlan fp = plan_full(n, tokens);
+  const bool interior = fp.P > 0 && (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ldx % 8 == 0;
+  if (interior) {
+    if (ws_bytes < fp.ws) return hipErrorInvalidValue;
+    float* part = fp.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+    hipLaunchKernelGGL(syrk_bf16_full_kernel, dim3((unsigned)(fp.ntiles * fp.P)), dim3(512), 0,
+                       stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens / fp.P, fp.P, S,
+                       lds, part, fp.ntiles);
+    if (fp.P > 1) {
+      hipLaunchKernelGGL(reduce_full_partials_kernel,
+                         dim3((unsigned)(fp.ntiles * (FT_I * FT_J / 1024))), dim3(256), 0, stream,
+                         part, fp.P, fp.ntiles, S, lds);
+    }
+    return hipGetLastError();
+  }
   const HessPlan pl = plan_bf16(n, tokens);
   if (ws_bytes < pl.ws) return hipErrorInvalidValue;
   float* part = pl.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  const bool interior = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ldx % 8 == 0 &&
-                        n % HT == 0 && tokens % (pl.P * HK) == 0 &&
-                        pl.tok_per_split * pl.P == tokens;
-  if (interior) {
-    hipLaunchKernelGGL(syrk_bf16_full_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0,
-                       stream, reinterpret_cast<const uint16_t*>(X), ldx, pl.tok_per_split, pl.P,
-                       S, lds, part, pl.ntiles);
-  } else {
-    hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(X), ldx, tokens, n, pl.tok_per_split,
-                       pl.P, S, lds, part, pl.ntiles);
-  }
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(pl.ntiles * pl.P)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(X), ldx, tokens, n, pl.tok_per_split,
+                     pl.P, S, lds, part, pl.ntiles);
   if (pl.P > 1) {
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)(pl.ntiles * (HT * HT / 1024))),
                        dim3(256), 0, stream, part, pl.P, pl.ntiles, n, S, lds);
