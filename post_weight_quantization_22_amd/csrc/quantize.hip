@@ -18,8 +18,14 @@
 //     min/max is a butterfly over the G/8 lanes holding the group, taken from
 //     the current (already compensated) values when the group's first column
 //     is reached.
-//   trailing_update_kernel: W'[:, i0+128:] -= E * U[i0:i0+128, i0+128:], an
-//     fp32 GEMM with K = 128 on v_mfma_f32_16x16x4_f32.
+//   The deferred update of the later columns is blocked twice: blocks of 128
+//   columns form super-blocks of SB columns.  After each block, only the rest
+//   of its super-block is updated (K = 128); after each super-block, every
+//   column past it at once (K = SB), from the errors of the whole super-block.
+//   Both are W'[:, c0:c1] -= E[:, k0:k1] U[k0:k1, c0:c1] on
+//   v_mfma_f32_16x16x4_f32 (update_gemm_kernel); the second carries most of
+//   the flops, with K long enough to keep the matrix cores busy instead of
+//   re-streaming W' every 128 columns.
 #include <utility>
 
 #include "kernels.hpp"
@@ -110,25 +116,62 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* __restrict
   }
 }
 
+// q = clamp(rne(w / scale) + zero, 0, maxq) with the IEEE quotient w / scale,
+// computed as w * (1 / scale): that product is within 1.5 * 2^-23 |w / scale|
+// of the quotient, so the two round to different integers only if a
+// half-integer lies that close; then (rarely) the division itself decides.
+__device__ __forceinline__ float quant_code_fast(float w, float scale, float rscale, float zero,
+                                                 float maxq) {
+  const float t = w * rscale;
+  float q = rintf(t);
+  const float tol = fmaxf(fabsf(t), 1.0f) * 3.6e-7f;
+  if (fabsf(fabsf(t - floorf(t)) - 0.5f) <= tol) q = rintf(__fdiv_rn(w, scale));
+  return fminf(fmaxf(q + zero, 0.0f), maxq);
+}
+
 // One 128-column block.  G > 0: group size (8..128, divides 128); G < 0: one
 // group per row with parameters already in scales/zeros (ngroups == 1).
+// Errors go to E[r, e0 + c] (row stride lde), c < 128.
 template <int G>
 __global__ __launch_bounds__(256) void block_quant_kernel(
     float* __restrict__ Wp, int64_t m, int64_t n, const float* __restrict__ U, int64_t ldu,
     int64_t i0, float maxq, int sym, uint8_t* __restrict__ codes, float* __restrict__ scales,
-    float* __restrict__ zeros, int64_t ngroups, float* __restrict__ E,
+    float* __restrict__ zeros, int64_t ngroups, float* __restrict__ E, int64_t lde, int64_t e0,
     float* __restrict__ row_err, int first_block) {
-  __shared__ float Us[BLK][BLK + UPAD];
+  __shared__ __align__(16) float Us[BLK][BLK + UPAD];
   __shared__ float uinv[BLK];
   const int tid = threadIdx.x;
   const int bw = (int)min((int64_t)BLK, n - i0);
 
-  // Stage the diagonal block of U: upper triangle of the block's columns.
-  for (int idx = tid; idx < BLK * BLK; idx += blockDim.x) {
-    const int j = idx / BLK, k = idx % BLK;
-    float v = 0.0f;
-    if (k >= j && k < bw) v = U[(i0 + j) * ldu + i0 + k];
-    Us[j][k] = v;
+  // Stage the diagonal block of U (upper triangle of the block's columns):
+  // 16 float4 per thread, all in flight before the first LDS store.
+  {
+    const bool vec = (ldu % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
+    float4 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;
+      const int j = idx >> 5, k = 4 * (idx & 31);
+      const int64_t row = i0 + (j < bw ? j : 0);
+      const float* src = U + row * ldu + i0 + k;
+      if (vec && k + 4 <= bw) {
+        v[q] = *reinterpret_cast<const float4*>(src);
+      } else {
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = k + e < bw ? src[e] : 0.0f;
+        v[q] = make_float4(t[0], t[1], t[2], t[3]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;
+      const int j = idx >> 5, k = 4 * (idx & 31);
+      float t[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (j < bw && k + e >= j && k + e < bw) ? t[e] : 0.0f;
+      *reinterpret_cast<float4*>(&Us[j][k]) = make_float4(t[0], t[1], t[2], t[3]);
+    }
   }
   __syncthreads();
   if (tid < BLK) uinv[tid] = tid < bw ? 1.0f / Us[tid][tid] : 0.0f;
@@ -155,12 +198,13 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
     for (int s = 0; s < CPL; ++s) w[s] = (rv && cbase + s < n) ? Wp[r * n + cbase + s] : 0.0f;
   }
 
-  float scale = 1.0f, zero = 0.0f;
+  float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
   if constexpr (G < 0) {
     if (rv) {
       scale = scales[r];
       zero = zeros[r];
     }
+    rscale = 1.0f / scale;
   }
   float e_own[CPL], q_own[CPL];
 #pragma unroll
@@ -169,10 +213,18 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
     q_own[s] = 0.0f;
   }
 
+  // row j of the U block for this lane's columns, one column ahead
+  float4 uc0 = *reinterpret_cast<const float4*>(&Us[0][CPL * l16]);
+  float4 uc1 = *reinterpret_cast<const float4*>(&Us[0][CPL * l16 + 4]);
   static_for<BLK>([&](auto J) {
     constexpr int j = decltype(J)::value;
     constexpr int s = j % CPL;
     constexpr int owner = j / CPL;
+    float4 un0 = uc0, un1 = uc1;
+    if constexpr (j + 1 < BLK) {
+      un0 = *reinterpret_cast<const float4*>(&Us[j + 1][CPL * l16]);
+      un1 = *reinterpret_cast<const float4*>(&Us[j + 1][CPL * l16 + 4]);
+    }
     if constexpr (G > 0) {
       if constexpr (j % G == 0) {
         // parameters of the group starting at column j, for the lanes holding it
@@ -189,6 +241,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
         }
         if (sym) sym_params(fmaxf(fabsf(vmin), fabsf(vmax)), maxq, scale, zero);
         else minmax_params(vmin, vmax, maxq, scale, zero);
+        rscale = 1.0f / scale;
         if (l16 == owner && rv && i0 + j < n) {
           const int64_t g = (i0 + j) / G;
           scales[r * ngroups + g] = scale;
@@ -197,7 +250,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
       }
     }
     const float wj = w[s];
-    const float q = quant_code(wj, scale, zero, maxq);
+    const float q = quant_code_fast(wj, scale, rscale, zero, maxq);
     const float dq = scale * (q - zero);
     float e = (wj - dq) * uinv[j];
     e = row_bcast<owner>(e);
@@ -205,16 +258,16 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
       e_own[s] = e;
       q_own[s] = q;
     }
-    const float4 u0 = *reinterpret_cast<const float4*>(&Us[j][CPL * l16]);
-    const float4 u1 = *reinterpret_cast<const float4*>(&Us[j][CPL * l16 + 4]);
-    w[0] = fmaf(-e, u0.x, w[0]);
-    w[1] = fmaf(-e, u0.y, w[1]);
-    w[2] = fmaf(-e, u0.z, w[2]);
-    w[3] = fmaf(-e, u0.w, w[3]);
-    w[4] = fmaf(-e, u1.x, w[4]);
-    w[5] = fmaf(-e, u1.y, w[5]);
-    w[6] = fmaf(-e, u1.z, w[6]);
-    w[7] = fmaf(-e, u1.w, w[7]);
+    w[0] = fmaf(-e, uc0.x, w[0]);
+    w[1] = fmaf(-e, uc0.y, w[1]);
+    w[2] = fmaf(-e, uc0.z, w[2]);
+    w[3] = fmaf(-e, uc0.w, w[3]);
+    w[4] = fmaf(-e, uc1.x, w[4]);
+    w[5] = fmaf(-e, uc1.y, w[5]);
+    w[6] = fmaf(-e, uc1.z, w[6]);
+    w[7] = fmaf(-e, uc1.w, w[7]);
+    uc0 = un0;
+    uc1 = un1;
   });
 
   // errors of columns past the end of the layer are zero (uinv = 0 there)
@@ -225,7 +278,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
   for (int off = 1; off < LPR; off <<= 1) err += __shfl_xor(err, off, LPR);
 
   if (!rv) return;
-  float* erow = E + r * BLK + CPL * l16;
+  float* erow = E + r * lde + e0 + CPL * l16;
   *reinterpret_cast<float4*>(erow) = make_float4(e_own[0], e_own[1], e_own[2], e_own[3]);
   *reinterpret_cast<float4*>(erow + 4) = make_float4(e_own[4], e_own[5], e_own[6], e_own[7]);
   uint8_t* crow = codes + r * n + cbase;
@@ -245,26 +298,37 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
   if (row_err && l16 == 0) row_err[r] = (first_block ? 0.0f : row_err[r]) + err;
 }
 
-// W'[:, c0:] -= E[:, 0:128] * U[i0:i0+128, c0:], c0 = i0 + 128.
-// 128x128 output tile per workgroup, 4 waves of 64x64, K staged by 32.
+// W'[:, c0 + j] -= sum_{k < kc} E[i, k0 + k] U[u0 + k, c0 + j], j < nc.
+// 128 x 128 output tile per workgroup (4 waves of 64 x 64, 4 x 4 MFMA tiles
+// each), K in chunks of 32: the next chunk is loaded into registers while the
+// current one is multiplied out of LDS (double-buffered, one barrier per
+// chunk).  Tiles are numbered so that each XCD (every 8th workgroup) takes a
+// contiguous range of them, sharing its L2 for the operands.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int TT = 128;  // tile edge
 constexpr int TK = 32;   // K chunk
 
-__global__ __launch_bounds__(256) void trailing_update_kernel(float* __restrict__ Wp, int64_t m,
-                                                              int64_t n,
-                                                              const float* __restrict__ E,
-                                                              const float* __restrict__ U,
-                                                              int64_t ldu, int64_t i0,
-                                                              int64_t tiles_n) {
-  __shared__ float As[TT][TK + 1];
-  __shared__ float Bs[TK][TT + 4];
+struct UpdArgs {
+  float* Wp;
+  int64_t m, n;
+  const float* E;
+  int64_t lde, k0, kc;
+  const float* U;
+  int64_t ldu, u0, c0, nc;
+  int64_t tiles_n, tiles;
+  int vec_u;
+};
+
+__global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
+  __shared__ float As[2][TT][TK + 1];
+  __shared__ __align__(16) float Bs[2][TK][TT + 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int wr = wv >> 1, wc = wv & 1;
-  const int64_t c0 = i0 + BLK;
-  const int64_t tr = blockIdx.x / tiles_n, tc = blockIdx.x % tiles_n;
-  const int64_t row0 = tr * TT, col0 = c0 + tc * TT;
+  const int64_t T8 = (g.tiles / 8) * 8;
+  const int64_t bid = blockIdx.x;
+  const int64_t t = bid < T8 ? (bid % 8) * (T8 / 8) + bid / 8 : bid;
+  const int64_t row0 = (t / g.tiles_n) * TT, col0 = (t % g.tiles_n) * TT;  // col0 relative to c0
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -275,35 +339,83 @@ __global__ __launch_bounds__(256) void trailing_update_kernel(float* __restrict_
       for (int q = 0; q < 4; ++q) {
         const int64_t row = row0 + 64 * wr + 16 * a + 4 * (lane >> 4) + q;
         const int64_t col = col0 + 64 * wc + 16 * b + (lane & 15);
-        acc[a][b][q] = (row < m && col < n) ? Wp[row * n + col] : 0.0f;
+        acc[a][b][q] = (row < g.m && col < g.nc) ? g.Wp[row * g.n + g.c0 + col] : 0.0f;
       }
 
-  for (int kc = 0; kc < BLK; kc += TK) {
-    __syncthreads();
-    for (int idx = tid; idx < TT * TK; idx += 256) {
-      const int rr = idx / TK, kk = idx % TK;
+  // staging: A chunk 128 x 32 (thread: rows tid/8 + 32q, k 4 (tid%8) .. +3),
+  //          B chunk 32 x 128 (thread: k tid/32 + 8q, cols 4 (tid%32) .. +3)
+  float4 ra[4], rb[4];
+  auto fetch = [&](int64_t kk0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
       const int64_t row = row0 + rr;
-      As[rr][kk] = row < m ? -E[row * BLK + kc + kk] : 0.0f;
+      const int64_t k = kk0 + kk;
+      if (row < g.m && k + 4 <= g.kc) {
+        ra[q] = *reinterpret_cast<const float4*>(g.E + row * g.lde + g.k0 + k);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (row < g.m && k + e < g.kc) ? g.E[row * g.lde + g.k0 + k + e] : 0.0f;
+        ra[q] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
-    for (int idx = tid; idx < TK * TT; idx += 256) {
-      const int kk = idx / TT, cc = idx % TT;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = (tid >> 5) + 8 * q, cc = 4 * (tid & 31);
+      const int64_t k = kk0 + kk;
       const int64_t col = col0 + cc;
-      Bs[kk][cc] = col < n ? U[(i0 + kc + kk) * ldu + col] : 0.0f;
+      const float* src = g.U + (g.u0 + (k < g.kc ? k : 0)) * g.ldu + g.c0 + col;
+      if (g.vec_u && k < g.kc && col + 4 <= g.nc) {
+        rb[q] = *reinterpret_cast<const float4*>(src);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (k < g.kc && col + e < g.nc) ? src[e] : 0.0f;
+        rb[q] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
+      As[buf][rr][kk] = -ra[q].x;
+      As[buf][rr][kk + 1] = -ra[q].y;
+      As[buf][rr][kk + 2] = -ra[q].z;
+      As[buf][rr][kk + 3] = -ra[q].w;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = (tid >> 5) + 8 * q, cc = 4 * (tid & 31);
+      *reinterpret_cast<float4*>(&Bs[buf][kk][cc]) = rb[q];
+    }
+  };
+
+  const int nchunks = (int)((g.kc + TK - 1) / TK);
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) fetch((int64_t)(c + 1) * TK);
 #pragma unroll
     for (int ks = 0; ks < TK; ks += 4) {
       float af[4], bf[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = As[64 * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
+      for (int a = 0; a < 4; ++a) af[a] = As[buf][64 * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = Bs[ks + (lane >> 4)][64 * wc + 16 * b + (lane & 15)];
+      for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][64 * wc + 16 * b + (lane & 15)];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -314,8 +426,21 @@ __global__ __launch_bounds__(256) void trailing_update_kernel(float* __restrict_
       for (int q = 0; q < 4; ++q) {
         const int64_t row = row0 + 64 * wr + 16 * a + 4 * (lane >> 4) + q;
         const int64_t col = col0 + 64 * wc + 16 * b + (lane & 15);
-        if (row < m && col < n) Wp[row * n + col] = acc[a][b][q];
+        if (row < g.m && col < g.nc) g.Wp[row * g.n + g.c0 + col] = acc[a][b][q];
       }
+}
+
+void launch_update(float* Wp, int64_t m, int64_t n, const float* E, int64_t lde, int64_t k0,
+                   int64_t kc, const float* U, int64_t ldu, int64_t u0, int64_t c0, int64_t nc,
+                   hipStream_t stream) {
+  if (nc <= 0 || kc <= 0 || m <= 0) return;
+  UpdArgs g;
+  g.Wp = Wp; g.m = m; g.n = n; g.E = E; g.lde = lde; g.k0 = k0; g.kc = kc;
+  g.U = U; g.ldu = ldu; g.u0 = u0; g.c0 = c0; g.nc = nc;
+  g.tiles_n = ceil_div(nc, TT);
+  g.tiles = g.tiles_n * ceil_div(m, TT);
+  g.vec_u = (ldu % 4 == 0) && (c0 % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
+  hipLaunchKernelGGL(update_gemm_kernel, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
 }
 
 __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
@@ -343,9 +468,12 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
 
 }  // namespace
 
+// Super-block width: the K of the update past each super-block.
+int64_t super_block(int64_t n) { return hmin(ceil_div(n, BLK) * BLK, 1024); }
+
 size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act) {
-  size_t b = align_up((size_t)m * n * sizeof(float), 256);   // W'
-  b += align_up((size_t)m * BLK * sizeof(float), 256);       // E
+  size_t b = align_up((size_t)m * n * sizeof(float), 256);              // W'
+  b += align_up((size_t)m * super_block(n) * sizeof(float), 256);       // E
   if (desc_act) {
     b += align_up((size_t)m * n, 256);                       // codes, processing order
     b += align_up((size_t)n * sizeof(int32_t), 256);         // inverse permutation
@@ -358,8 +486,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   char* ws = reinterpret_cast<char*>(a.ws);
   float* Wp = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)m * n * sizeof(float), 256);
+  const int64_t SB = super_block(n);
   float* E = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)m * BLK * sizeof(float), 256);
+  ws += align_up((size_t)m * SB * sizeof(float), 256);
   uint8_t* cproc = a.codes;
   int32_t* inv = nullptr;
   if (a.desc_act) {
@@ -382,26 +511,29 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
                        stream, Wp, m, n, maxq, a.sym, a.scales, a.zeros);
   }
   const dim3 qgrid((unsigned)ceil_div(m, QROWS));
-  for (int64_t i0 = 0; i0 < n; i0 += BLK) {
-    const int first = i0 == 0;
+  for (int64_t s0 = 0; s0 < n; s0 += SB) {
+    const int64_t s1 = hmin(n, s0 + SB);
+    for (int64_t i0 = s0; i0 < s1; i0 += BLK) {
+      const int first = i0 == 0;
 #define GPTQ_BQ(GV)                                                                              \
   hipLaunchKernelGGL(block_quant_kernel<GV>, qgrid, dim3(256), 0, stream, Wp, m, n, a.U, a.ldu,  \
-                     i0, maxq, a.sym, cproc, a.scales, a.zeros, ngroups, E, a.row_err, first)
-    switch (G) {
-      case 8: GPTQ_BQ(8); break;
-      case 16: GPTQ_BQ(16); break;
-      case 32: GPTQ_BQ(32); break;
-      case 64: GPTQ_BQ(64); break;
-      case 128: GPTQ_BQ(128); break;
-      default: GPTQ_BQ(-1); break;
-    }
+                     i0, maxq, a.sym, cproc, a.scales, a.zeros, ngroups, E, SB, i0 - s0,        \
+                     a.row_err, first)
+      switch (G) {
+        case 8: GPTQ_BQ(8); break;
+        case 16: GPTQ_BQ(16); break;
+        case 32: GPTQ_BQ(32); break;
+        case 64: GPTQ_BQ(64); break;
+        case 128: GPTQ_BQ(128); break;
+        default: GPTQ_BQ(-1); break;
+      }
 #undef GPTQ_BQ
-    if (i0 + BLK < n) {
-      const int64_t tiles_n = ceil_div(n - i0 - BLK, TT);
-      const int64_t tiles = tiles_n * ceil_div(m, TT);
-      hipLaunchKernelGGL(trailing_update_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, Wp,
-                         m, n, E, a.U, a.ldu, i0, tiles_n);
+      // the rest of this super-block, from this block's errors
+      const int64_t i1 = i0 + BLK;
+      if (i1 < s1) launch_update(Wp, m, n, E, SB, i0 - s0, BLK, a.U, a.ldu, i0, i1, s1 - i1, stream);
     }
+    // every column past the super-block, from all of its errors
+    if (s1 < n) launch_update(Wp, m, n, E, SB, 0, s1 - s0, a.U, a.ldu, s0, s1, n - s1, stream);
   }
   if (a.desc_act) {
     hipLaunchKernelGGL(invert_perm_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
