@@ -6,16 +6,18 @@
 // token-major, X[tokens, n], so X X^T = sum over tokens of x_t x_t^T: a SYRK
 // whose reduction axis is the token axis.
 //
-// bf16 path (the dense contraction, on MFMA): lower-triangle 128x128 output
-// tiles, 4 waves each holding a 64x64 sub-tile as 2x2
-// v_mfma_f32_32x32x16_bf16 accumulators.  A stage covers 32 tokens.  Both
-// operands need the token axis in the per-lane k slots, while X is contiguous
-// along channels, so the stage is transposed on its way into LDS: a lane loads
-// two token rows x 8 channels (2 x 16 B, coalesced along channels), pairs the
-// two tokens of each channel into one 32-bit word and stores it at
-// [channel][token pair]; an MFMA operand is then one 16-byte LDS read.
-// bf16 x bf16 products are exact in fp32; accumulation is fp32.
-//
+// bf16 path (the dense contraction, on MFMA v_mfma_f32_32x32x16_bf16):
+// lower-triangle 256 x 256 output tiles, 64-token stages, bf16 x bf16
+// products exact in fp32, fp32 accumulation.  The MFMA operands need the
+// token axis in the per-lane k slots while X is contiguous along channels:
+//  - interior kernel (n a multiple of 256, whole stages, aligned rows): the
+//    stage goes global -> LDS by DMA in X's own layout (XOR-swizzled 16-byte
+//    chunks) and the operands are read back with the transposing LDS read
+//    ds_read_b64_tr_b16; 8 waves of 128 x 64.
+//  - general kernel (any shape): each lane loads an 8-token x 8-channel
+//    block into registers (bounds-checked), transposes it with v_perm and
+//    stores channel rows of 144 bytes (9 x 16 B: conflict-free) to LDS;
+//    4 waves of 128 x 128.
 // Tiles are few when n is small, so the token axis is split P ways; each
 // split writes its partial tile to the workspace and a reduction kernel adds
 // the P partials to S in a fixed order (deterministic, no atomics).  With
@@ -207,90 +209,141 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
       }
 }
 
-// Interior variant: every tile full (n % 256 == 0), every split a whole number of
-// 64-token stages, rows 16-byte aligned.  No bounds checks, no branches in the
-// stage loop.  256 x 256 lower tiles; 512 threads = 8 waves (2 per SIMD), each
-// a 128 x 64 block (4 x 2 MFMA accumulators), so one wave's memory and LDS
-// waits are covered by its SIMD partner's MFMAs.  Each thread owns one 8 x 8
-// block of one operand per stage, fetched one stage ahead and transposed into
-// the idle LDS buffer after the current stage's MFMAs; one barrier per stage.
-// Diagonal tiles load both operands (the same data) to keep the loop uniform.
+// Interior kernel: every tile full (n % 256 == 0), every split a whole number
+// of 64-token stages, rows 16-byte aligned; no bounds checks.  256 x 256 lower
+// tiles, 512 threads = 8 waves (2 per SIMD), each a 128 x 64 block (4 x 2
+// MFMA accumulators), so one wave's waits are covered by its SIMD partner's
+// MFMAs.  Each 64-token stage of the two 256-channel operands
+// goes from global memory straight into LDS with global_load_lds_dwordx4 (16
+// bytes per lane, lane l landing at base + 16 l), in X's own token-major
+// layout: token row t takes 512 bytes and 16-byte chunk k of the row sits at
+// position k ^ 4 (t % 4).  MFMA operands come back with ds_read_b64_tr_b16,
+// which hands each 16-lane group a 4-token x 16-channel block transposed
+// (lane i: channel i, 4 consecutive tokens), i.e. the bf16 operand layout, so
+// there is no register staging and no permute.  With the swizzle the 16 lanes
+// x 4 tokens of a half-wave read 16 distinct chunk positions: all 64 banks.
+// The DMA of stage s + 1 runs under the MFMAs of stage s; one barrier each.
 constexpr int FT_I = 256, FT_J = 256;   // tile
-constexpr int FW_I = 128, FW_J = 64;    // per wave
-__global__ __launch_bounds__(512) void syrk_bf16_full_kernel(const uint16_t* __restrict__ X,
-                                                             int64_t ldx, int64_t tok_per_split,
-                                                             int64_t P, float* __restrict__ S,
-                                                             int64_t lds,
-                                                             float* __restrict__ part,
-                                                             int64_t ntiles) {
-  __shared__ __align__(16) uint16_t smem[4 * HT * HROW];
+constexpr int WI = 128, WJ = 64;        // per wave
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr int DROW = FT_I * 2;    // bytes per token row of one operand stage
+constexpr int DSTAGE = HK * DROW;  // 32 KB per operand per stage
+
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
+  // two transposing reads: tokens +0..3 and +4..7 of this lane's channel
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p0 + 4 * DROW));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
+                                                            int64_t ldx, int64_t tok_per_split,
+                                                            int64_t P, float* __restrict__ S,
+                                                            int64_t lds,
+                                                            float* __restrict__ part,
+                                                            int64_t ntiles) {
+  __shared__ __align__(16) uint8_t smem[4 * DSTAGE];  // [buffer][operand]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
+  constexpr int RPW = HK / 8;  // token rows loaded per wave per operand
   const int wr = wv >> 2, wc = wv & 3;
   const int64_t L = blockIdx.x / P;
   const int64_t p = blockIdx.x % P;
   int64_t ti, tj;
   tile_coords(L, ti, tj);
-  const int64_t i0 = ti * HT, j0 = tj * HT;
-  const int opnd = tid >> 8, o = tid & 7, cb = (tid & 255) >> 3;
+  const int64_t i0 = ti * FT_I, j0 = tj * FT_J;
+  const bool diag = ti == tj;
   const int nstage = (int)(tok_per_split / HK);
-  const uint16_t* src = X + (p * tok_per_split + 8 * o) * ldx + (opnd ? j0 : i0) + 8 * cb;
-  const int64_t step = HK * ldx;
-  const int slot = opnd * HT * HROW;
 
-  f32x16 acc[FW_I / 32][FW_J / 32];
+  // DMA: instruction q of wave wv fills token rows RPW wv + 2 q and + 1; the
+  // swizzle depends on the row only through (2 q + lane / 32) % 4, so two
+  // per-lane source pointers (q even / odd) serve all q, 4 rows apart.
+  const uint16_t* srcA[2];
 #pragma unroll
-  for (int a = 0; a < FW_I / 32; ++a)
+  for (int q = 0; q < 2; ++q) {
+    const int t = RPW * wv + 2 * q + (lane >> 5);
+    const int k = (lane & 31) ^ (4 * (t & 3));
+    srcA[q] = X + (p * tok_per_split + t) * ldx + 8 * k + i0;
+  }
+  const int64_t jmi = j0 - i0;
+  const int64_t step = HK * ldx;
+  auto issue = [&](int s, int buf) {
+    uint8_t* dA = smem + (2 * buf) * DSTAGE + RPW * wv * DROW;
+    uint8_t* dB = dA + DSTAGE;
+    const int64_t adv = (int64_t)s * step;
 #pragma unroll
-    for (int b = 0; b < FW_J / 32; ++b)
+    for (int q = 0; q < RPW / 2; ++q)
+      __builtin_amdgcn_global_load_lds(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx,
+                                       (__attribute__((address_space(3))) void*)(dA + 1024 * q),
+                                       16, 0, 0);
+    if (!diag) {
+#pragma unroll
+      for (int q = 0; q < RPW / 2; ++q)
+        __builtin_amdgcn_global_load_lds(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx + jmi,
+                                         (__attribute__((address_space(3))) void*)(dB + 1024 * q),
+                                         16, 0, 0);
+    }
+  };
+
+  // transposing reads: lane (g = lane / 16, i = lane % 16) points at token
+  // 8 (g / 2) + i / 4 (+ 16 kk, + 4 for the second read), channel quad
+  // 16 (g % 2) + 4 (i % 4) of a 32-channel block
+  const int g = lane >> 4, i = lane & 15, qq = i >> 2, pch = i & 3;
+  const int lane_off = (8 * (g >> 1) + qq) * DROW + 8 * (pch & 1);
+  const int lane_chk = 2 * (g & 1) + (pch >> 1);
+  int offA[WI / 32], offB[WJ / 32];
+#pragma unroll
+  for (int a = 0; a < WI / 32; ++a)
+    offA[a] = lane_off + 16 * ((((WI * wr + 32 * a) >> 3) ^ (4 * qq)) + lane_chk);
+#pragma unroll
+  for (int b = 0; b < WJ / 32; ++b)
+    offB[b] = lane_off + 16 * ((((WJ * wc + 32 * b) >> 3) ^ (4 * qq)) + lane_chk);
+
+  f32x16 acc[WI / 32][WJ / 32];
+#pragma unroll
+  for (int a = 0; a < WI / 32; ++a)
+#pragma unroll
+    for (int b = 0; b < WJ / 32; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
 
-  Block8 rg;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) rg.r[e] = *reinterpret_cast<const uint4*>(src + e * ldx);
-  store_block8(smem + slot, 8 * cb, o, rg);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
-  int buf = 0;
   for (int s = 0; s < nstage; ++s) {
-    const int64_t adv = (s + 1 < nstage) ? step : 0;
-    src += adv;
+    const int buf = s & 1;
+    if (s + 1 < nstage) issue(s + 1, buf ^ 1);
+    const uint8_t* At = smem + (2 * buf) * DSTAGE;
+    const uint8_t* Bt = diag ? At : At + DSTAGE;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rg.r[e] = *reinterpret_cast<const uint4*>(src + e * ldx);
-    const uint16_t* At = smem + 2 * buf * HT * HROW;
-    const uint16_t* Bt = At + HT * HROW;
-#pragma unroll 2
     for (int kk = 0; kk < HK / 16; ++kk) {
-      bf16x8 af[FW_I / 32], bfr[FW_J / 32];
+      bf16x8 af[WI / 32], bfr[WJ / 32];
 #pragma unroll
-      for (int a = 0; a < FW_I / 32; ++a) {
-        const int row = FW_I * wr + 32 * a + (lane & 31);
-        af[a] = *reinterpret_cast<const bf16x8*>(At + row * HROW + 16 * kk + 8 * (lane >> 5));
-      }
+      for (int a = 0; a < WI / 32; ++a) af[a] = tr_operand(At + offA[a] + 16 * kk * DROW);
 #pragma unroll
-      for (int b = 0; b < FW_J / 32; ++b) {
-        const int col = FW_J * wc + 32 * b + (lane & 31);
-        bfr[b] = *reinterpret_cast<const bf16x8*>(Bt + col * HROW + 16 * kk + 8 * (lane >> 5));
-      }
+      for (int b = 0; b < WJ / 32; ++b) bfr[b] = tr_operand(Bt + offB[b] + 16 * kk * DROW);
 #pragma unroll
-      for (int a = 0; a < FW_I / 32; ++a)
+      for (int a = 0; a < WI / 32; ++a)
 #pragma unroll
-        for (int b = 0; b < FW_J / 32; ++b)
+        for (int b = 0; b < WJ / 32; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
-    store_block8(smem + 2 * (buf ^ 1) * HT * HROW + slot, 8 * cb, o, rg);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    buf ^= 1;
   }
 
 #pragma unroll
-  for (int a = 0; a < FW_I / 32; ++a)
+  for (int a = 0; a < WI / 32; ++a)
 #pragma unroll
-    for (int b = 0; b < FW_J / 32; ++b)
+    for (int b = 0; b < WJ / 32; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int ii = FW_I * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int jj = FW_J * wc + 32 * b + (lane & 31);
+        const int ii = WI * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int jj = WJ * wc + 32 * b + (lane & 31);
         if (part) {
           part[((p * ntiles + L) * FT_I + ii) * FT_J + jj] = acc[a][b][q];
         } else if (jj + j0 <= ii + i0) {
@@ -450,7 +503,7 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
   if (interior) {
     if (ws_bytes < fp.ws) return hipErrorInvalidValue;
     float* part = fp.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-    hipLaunchKernelGGL(syrk_bf16_full_kernel, dim3((unsigned)(fp.ntiles * fp.P)), dim3(512), 0,
+    hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)(fp.ntiles * fp.P)), dim3(512), 0,
                        stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens / fp.P, fp.P, S,
                        lds, part, fp.ntiles);
     if (fp.P > 1) {
