@@ -48,6 +48,45 @@ __device__ __forceinline__ void tile_coords(int64_t L, int64_t& ti, int64_t& tj)
   tj = L - t * (t + 1) / 2;
 }
 
+// Work order of the interior kernel.  Workgroup b runs on XCD b % 8; the
+// units (split p, tile) are dealt so that XCD x takes a contiguous range of
+// them: whole token splits when P is a multiple of 8, and within a split the
+// lower-triangle tiles by 4 x 4 super-tiles (rows of super-tiles, then rows
+// of tiles), so the ~32 workgroups in flight on one XCD read the same token
+// rows of a few channel blocks and share them through that XCD's L2.
+// Super-tile order needs T % 4 == 0; otherwise tiles go row by row.
+__device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64_t& p,
+                                          int64_t& ti, int64_t& tj) {
+  const int64_t ntiles = T * (T + 1) / 2;
+  const int64_t U = ntiles * P;
+  const int64_t U8 = (U / 8) * 8;
+  const int64_t u = b < U8 ? (b % 8) * (U8 / 8) + b / 8 : b;
+  p = u / ntiles;
+  const int64_t Lb = u % ntiles;
+  if (T % 4 != 0) {
+    tile_coords(Lb, ti, tj);
+    return;
+  }
+  // super-row bi holds 16 bi + 10 tiles; 8 bi^2 + 2 bi tiles precede it
+  int64_t bi = (int64_t)((sqrt(4.0 + 32.0 * (double)Lb) - 2.0) / 16.0);
+  while (8 * bi * bi + 2 * bi > Lb) --bi;
+  while (8 * (bi + 1) * (bi + 1) + 2 * (bi + 1) <= Lb) ++bi;
+  const int64_t r = Lb - (8 * bi * bi + 2 * bi);
+  int64_t bj, li, lj;
+  if (r < 16 * bi) {
+    bj = r / 16;
+    li = (r % 16) / 4;
+    lj = r % 4;
+  } else {
+    const int64_t d = r - 16 * bi;  // lower triangle of the diagonal super-tile
+    bj = bi;
+    li = d >= 6 ? 3 : d >= 3 ? 2 : d >= 1 ? 1 : 0;
+    lj = d - li * (li + 1) / 2;
+  }
+  ti = 4 * bi + li;
+  tj = 4 * bj + lj;
+}
+
 // One lane's share of a stage for one operand: 8 tokens x 8 channels.
 struct Block8 {
   uint4 r[8];  // r[e]: token 8o + e, channels c .. c + 7
@@ -240,21 +279,39 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS DMA of 16 bytes per lane (lane l lands at lds + 16 l), issued from asm:
+// the compiler cannot tell this write from the LDS reads of the other buffer
+// and would otherwise wait for it before every one of them; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the stage.  The
+// instruction writes no VGPR (its data goes to LDS), and its address VGPRs
+// are consumed at issue.  M0 (the LDS base of the transfer, read at issue)
+// is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
 __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
                                                             int64_t ldx, int64_t tok_per_split,
                                                             int64_t P, float* __restrict__ S,
                                                             int64_t lds,
                                                             float* __restrict__ part,
-                                                            int64_t ntiles) {
+                                                            int64_t ntiles, int64_t ntiles_edge) {
   __shared__ __align__(16) uint8_t smem[4 * DSTAGE];  // [buffer][operand]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   constexpr int RPW = HK / 8;  // token rows loaded per wave per operand
   const int wr = wv >> 2, wc = wv & 3;
-  const int64_t L = blockIdx.x / P;
-  const int64_t p = blockIdx.x % P;
-  int64_t ti, tj;
-  tile_coords(L, ti, tj);
+  int64_t p, ti, tj;
+  hess_unit(blockIdx.x, P, ntiles_edge, p, ti, tj);
+  const int64_t L = ti * (ti + 1) / 2 + tj;  // row-major index of the partial tile
   const int64_t i0 = ti * FT_I, j0 = tj * FT_J;
   const bool diag = ti == tj;
   const int nstage = (int)(tok_per_split / HK);
@@ -275,17 +332,17 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
     uint8_t* dA = smem + (2 * buf) * DSTAGE + RPW * wv * DROW;
     uint8_t* dB = dA + DSTAGE;
     const int64_t adv = (int64_t)s * step;
+    const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dA);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dB);
 #pragma unroll
     for (int q = 0; q < RPW / 2; ++q)
-      __builtin_amdgcn_global_load_lds(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx,
-                                       (__attribute__((address_space(3))) void*)(dA + 1024 * q),
-                                       16, 0, 0);
+      dma16(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx, la + 1024 * q);
     if (!diag) {
 #pragma unroll
       for (int q = 0; q < RPW / 2; ++q)
-        __builtin_amdgcn_global_load_lds(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx + jmi,
-                                         (__attribute__((address_space(3))) void*)(dB + 1024 * q),
-                                         16, 0, 0);
+        dma16(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx + jmi, lb + 1024 * q);
     }
   };
 
@@ -468,12 +525,24 @@ FullPlan plan_full(int64_t n, int64_t tokens) {
   if (n % FT_I != 0) return fp;
   const int64_t T = n / FT_I;
   fp.ntiles = T * (T + 1) / 2;
-  // Token split, one split per XCD: with one workgroup per CU, a grid of
-  // ntiles workgroups runs in ceil(ntiles / 256) rounds, so few tiles leave a
-  // large idle tail; 8 splits make the rounds many (the partial tiles cost one
-  // extra pass over 8 ntiles * 256 KB).
+  // Token split, one split per XCD (P a multiple of 8).  With one workgroup
+  // per CU the grid runs in ceil(ntiles P / 256) rounds of tokens / P tokens
+  // each; more splits fill the last round better but write and re-read more
+  // partial tiles (256 KB each).  Time model fitted to n = 4096 with 8 to 32
+  // splits: ~33 ns per token per round, ~0.35 us per partial tile.
   int64_t P = 1;
-  if (fp.ntiles <= 2048 && tokens % (8 * HK) == 0 && tokens >= 8 * 512) P = 8;
+  if (fp.ntiles <= 2048 && tokens % (8 * HK) == 0 && tokens >= 8 * 512) {
+    double best = 0.0;
+    for (int64_t c = 8; c <= 32; c *= 2) {
+      if (tokens % (c * HK) != 0) break;
+      const double t = (double)ceil_div(fp.ntiles * c, 256) * (double)(tokens / c) * 33e-9 +
+                       (double)(c * fp.ntiles) * 0.35e-6;
+      if (P == 1 || t < best) {
+        P = c;
+        best = t;
+      }
+    }
+  }
   if (tokens % (P * HK) != 0) return fp;
   fp.P = P;
   fp.ws = P > 1 ? (size_t)P * fp.ntiles * FT_I * FT_J * sizeof(float) : 0;
@@ -505,7 +574,7 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
     float* part = fp.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
     hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)(fp.ntiles * fp.P)), dim3(512), 0,
                        stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens / fp.P, fp.P, S,
-                       lds, part, fp.ntiles);
+                       lds, part, fp.ntiles, n / FT_I);
     if (fp.P > 1) {
       hipLaunchKernelGGL(reduce_full_partials_kernel,
                          dim3((unsigned)(fp.ntiles * (FT_I * FT_J / 1024))), dim3(256), 0, stream,
