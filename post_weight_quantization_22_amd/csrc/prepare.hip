@@ -28,6 +28,8 @@
 // L^-1 = [[X11, 0], [-X22 L21 X11, X22]].  The leaves run in order; everything
 // between them is a large GEMM on v_mfma_f64_16x16x4_f64, so no kernel carries
 // a long serial reduction.
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace gptq {
@@ -39,13 +41,15 @@ constexpr int NODE = 128;  // subproblems up to this size run in one workgroup
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+constexpr int MAXDEPTH = 24;
+
 struct PrepWs {
-  double* A;     // [n, n] lower: damped, permuted, reversed Hessian (overwritten)
-  double* X;     // [n, n] lower: L^-1
-  double* T;     // [s2, s1] of the top split
-  double* diag;  // [n]
-  double* lam;   // [1]
-  int32_t* perm; // [n]
+  double* A;               // [n, n] lower: damped, permuted, reversed Hessian (overwritten)
+  double* X;               // [n, n] lower: L^-1
+  double* T[MAXDEPTH];     // per recursion depth: [s2, s1] of that depth's split
+  double* diag;            // [n]
+  double* lam;             // [1]
+  int32_t* perm;           // [n]
 };
 
 int64_t split_first(int64_t s) {
@@ -53,10 +57,21 @@ int64_t split_first(int64_t s) {
   return ((blocks + 1) / 2) * NODE;
 }
 
-size_t t_elems(int64_t n) {
-  if (n <= NODE) return 0;
-  const int64_t s1 = split_first(n);
-  return (size_t)(n - s1) * (size_t)s1;
+// Largest T of each depth: t[d] = max over the depth-d splits of s2 * s1.
+void t_sizes(int64_t s, int d, size_t (&t)[MAXDEPTH]) {
+  if (s <= NODE || d >= MAXDEPTH) return;
+  const int64_t s1 = split_first(s), s2 = s - s1;
+  t[d] = hmax((int64_t)t[d], s1 * s2);
+  t_sizes(s1, d + 1, t);
+  t_sizes(s2, d + 1, t);
+}
+
+size_t t_bytes(int64_t n) {
+  size_t t[MAXDEPTH] = {};
+  t_sizes(n, 0, t);
+  size_t b = 0;
+  for (int d = 0; d < MAXDEPTH; ++d) b += align_up(t[d] * sizeof(double), 256);
+  return b;
 }
 
 PrepWs carve(void* ws, int64_t n) {
@@ -66,14 +81,50 @@ PrepWs carve(void* ws, int64_t n) {
   p += align_up((size_t)n * n * sizeof(double), 256);
   w.X = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * n * sizeof(double), 256);
-  w.T = reinterpret_cast<double*>(p);
-  p += align_up(t_elems(n) * sizeof(double), 256);
+  size_t t[MAXDEPTH] = {};
+  t_sizes(n, 0, t);
+  for (int d = 0; d < MAXDEPTH; ++d) {
+    w.T[d] = reinterpret_cast<double*>(p);
+    p += align_up(t[d] * sizeof(double), 256);
+  }
   w.diag = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * sizeof(double), 256);
   w.lam = reinterpret_cast<double*>(p);
   p += 256;
   w.perm = reinterpret_cast<int32_t*>(p);
   return w;
+}
+
+// Second stream (default priority) for work off the critical path, with one
+// pair of events per recursion depth; created once per device.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t t_done[MAXDEPTH];
+  hipEvent_t m_done[MAXDEPTH];
+};
+
+hipError_t side_stream(SideStream*& out) {
+  static std::mutex mu;
+  static SideStream sides[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream& sd = sides[dev];
+  if (!sd.s) {
+    hipStream_t st;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    for (int d = 0; d < MAXDEPTH; ++d) {
+      e = hipEventCreateWithFlags(&sd.t_done[d], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.m_done[d], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    sd.s = st;
+  }
+  out = &sd;
+  return hipSuccess;
 }
 
 // diag(H) with the dead-column fix, lambda = perc_damp * mean(diag H), info reset.
@@ -860,33 +911,44 @@ __global__ void fill_f64_kernel(double* __restrict__ p, int64_t count) {
 }
 
 // X[off:off+s, off:off+s] = inverse of the Cholesky factor of A[off:off+s, off:off+s].
-hipError_t chol_inv(const PrepWs& w, int64_t n, int64_t off, int64_t s, int32_t* info,
-                    hipStream_t stream) {
+// M = T X11 is needed only by the last product, so it runs on the side stream
+// while the main stream goes on with A22 -= T T^T and the whole recursion on
+// A22 (mostly single-CU nodes and small products, which leave the chip idle).
+// T has one buffer per depth: a depth's splits follow each other, and each
+// joins its side work before returning.
+hipError_t chol_inv(const PrepWs& w, int64_t n, int64_t off, int64_t s, int d, int32_t* info,
+                    hipStream_t stream, SideStream* side) {
   if (s <= NODE) {
     hipLaunchKernelGGL(node_kernel, dim3(1), dim3(256), 0, stream, w.A, w.X, n, off, (int)s,
                        info);
     return hipGetLastError();
   }
+  if (d >= MAXDEPTH) return hipErrorInvalidValue;
   const int64_t s1 = split_first(s), s2 = s - s1;
   double* A21 = w.A + (off + s1) * n + off;
   double* A22 = w.A + (off + s1) * n + off + s1;
   const double* X11 = w.X + off * n + off;
   double* X21 = w.X + (off + s1) * n + off;
   const double* X22 = w.X + (off + s1) * n + off + s1;
-  hipError_t e = chol_inv(w, n, off, s1, info, stream);
+  double* T = w.T[d];
+  hipError_t e = chol_inv(w, n, off, s1, d + 1, info, stream, side);
   if (e != hipSuccess) return e;
   // T = A21 X11^T   (X11(j, k) = 0 for k > j)
-  e = gemm(A21, n, false, X11, n, true, w.T, s1, s2, s1, s1, 1.0, 0.0, KHI_J, false, stream);
+  e = gemm(A21, n, false, X11, n, true, T, s1, s2, s1, s1, 1.0, 0.0, KHI_J, false, stream);
   if (e != hipSuccess) return e;
+  // A21 := T X11    (X11(k, j) = 0 for k < j), on the side stream
+  if ((e = hipEventRecord(side->t_done[d], stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side->s, side->t_done[d], 0)) != hipSuccess) return e;
+  e = gemm(T, s1, false, X11, n, false, A21, n, s2, s1, s1, 1.0, 0.0, KLO_J, false, side->s);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(side->m_done[d], side->s)) != hipSuccess) return e;
   // A22 -= T T^T    (lower tiles)
-  e = gemm(w.T, s1, false, w.T, s1, true, A22, n, s2, s2, s1, -1.0, 1.0, 0, true, stream);
+  e = gemm(T, s1, false, T, s1, true, A22, n, s2, s2, s1, -1.0, 1.0, 0, true, stream);
   if (e != hipSuccess) return e;
-  // A21 := T X11    (X11(k, j) = 0 for k < j)
-  e = gemm(w.T, s1, false, X11, n, false, A21, n, s2, s1, s1, 1.0, 0.0, KLO_J, false, stream);
-  if (e != hipSuccess) return e;
-  e = chol_inv(w, n, off + s1, s2, info, stream);
+  e = chol_inv(w, n, off + s1, s2, d + 1, info, stream, side);
   if (e != hipSuccess) return e;
   // X21 = -X22 A21  (X22(i, k) = 0 for k > i)
+  if ((e = hipStreamWaitEvent(stream, side->m_done[d], 0)) != hipSuccess) return e;
   return gemm(X22, n, false, A21, n, false, X21, n, s2, s1, s2, -1.0, 0.0, KHI_I, false, stream);
 }
 
@@ -906,7 +968,7 @@ __global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__
 
 size_t prepare_ws_bytes(int64_t n) {
   size_t b = 2 * align_up((size_t)n * n * sizeof(double), 256);
-  b += align_up(t_elems(n) * sizeof(double), 256);
+  b += t_bytes(n);
   b += align_up((size_t)n * sizeof(double), 256);
   b += 256;
   b += align_up((size_t)n * sizeof(int32_t), 256);
@@ -933,7 +995,10 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   }
   // X's strict upper triangle must read as zero for the 128-wide GEMM tiles
   hipLaunchKernelGGL(fill_f64_kernel, dim3(2048), dim3(256), 0, stream, w.X, n * n);
-  hipError_t e = chol_inv(w, n, 0, n, info, stream);
+  SideStream* side = nullptr;
+  hipError_t e = side_stream(side);
+  if (e != hipSuccess) return e;
+  e = chol_inv(w, n, 0, n, 0, info, stream, side);
   if (e != hipSuccess) return e;
   {
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(n, 2048));
