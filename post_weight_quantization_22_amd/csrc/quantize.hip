@@ -305,8 +305,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
 // chunk).  Tiles are numbered so that each XCD (every 8th workgroup) takes a
 // contiguous range of them, sharing its L2 for the operands.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int TT = 128;  // tile edge
-constexpr int TK = 32;   // K chunk
+constexpr int TK = 32;  // K chunk
 
 struct UpdArgs {
   float* Wp;
@@ -319,7 +318,14 @@ struct UpdArgs {
   int vec_u;
 };
 
+// TT x TT output tile per workgroup (4 waves of TT/2 x TT/2, (TT/32)^2 MFMA
+// tiles each); TT = 64 for the narrow updates inside a super-block, where
+// 128-wide tiles would leave most CUs idle.
+template <int TT>
 __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
+  constexpr int HW = TT / 2;        // per-wave edge
+  constexpr int SUBT = HW / 16;     // MFMA tiles per wave edge
+  constexpr int AQ = TT * TK / 1024;  // float4 per thread per operand chunk
   __shared__ float As[2][TT][TK + 1];
   __shared__ __align__(16) float Bs[2][TK][TT + 4];
   const int tid = threadIdx.x;
@@ -330,24 +336,24 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
   const int64_t t = bid < T8 ? (bid % 8) * (T8 / 8) + bid / 8 : bid;
   const int64_t row0 = (t / g.tiles_n) * TT, col0 = (t % g.tiles_n) * TT;  // col0 relative to c0
 
-  f32x4 acc[4][4];
+  f32x4 acc[SUBT][SUBT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SUBT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < SUBT; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = row0 + 64 * wr + 16 * a + 4 * (lane >> 4) + q;
-        const int64_t col = col0 + 64 * wc + 16 * b + (lane & 15);
+        const int64_t row = row0 + HW * wr + 16 * a + 4 * (lane >> 4) + q;
+        const int64_t col = col0 + HW * wc + 16 * b + (lane & 15);
         acc[a][b][q] = (row < g.m && col < g.nc) ? g.Wp[row * g.n + g.c0 + col] : 0.0f;
       }
 
-  // staging: A chunk 128 x 32 (thread: rows tid/8 + 32q, k 4 (tid%8) .. +3),
-  //          B chunk 32 x 128 (thread: k tid/32 + 8q, cols 4 (tid%32) .. +3)
-  float4 ra[4], rb[4];
+  // staging: A chunk TT x 32 (thread: rows tid/8 + 32q, k 4 (tid%8) .. +3),
+  //          B chunk 32 x TT (thread: k (tid / (TT/4)) + (1024/TT) q, cols 4 (tid % (TT/4)) .. +3)
+  float4 ra[AQ], rb[AQ];
   auto fetch = [&](int64_t kk0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < AQ; ++q) {
       const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
       const int64_t row = row0 + rr;
       const int64_t k = kk0 + kk;
@@ -362,8 +368,8 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kk = (tid >> 5) + 8 * q, cc = 4 * (tid & 31);
+    for (int q = 0; q < AQ; ++q) {
+      const int kk = (tid / (TT / 4)) + (1024 / TT) * q, cc = 4 * (tid % (TT / 4));
       const int64_t k = kk0 + kk;
       const int64_t col = col0 + cc;
       const float* src = g.U + (g.u0 + (k < g.kc ? k : 0)) * g.ldu + g.c0 + col;
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < AQ; ++q) {
       const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
       As[buf][rr][kk] = -ra[q].x;
       As[buf][rr][kk + 1] = -ra[q].y;
@@ -387,8 +393,8 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
       As[buf][rr][kk + 3] = -ra[q].w;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kk = (tid >> 5) + 8 * q, cc = 4 * (tid & 31);
+    for (int q = 0; q < AQ; ++q) {
+      const int kk = (tid / (TT / 4)) + (1024 / TT) * q, cc = 4 * (tid % (TT / 4));
       *reinterpret_cast<float4*>(&Bs[buf][kk][cc]) = rb[q];
     }
   };
@@ -403,15 +409,15 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
     if (more) fetch((int64_t)(c + 1) * TK);
 #pragma unroll
     for (int ks = 0; ks < TK; ks += 4) {
-      float af[4], bf[4];
+      float af[SUBT], bf[SUBT];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = As[buf][64 * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
+      for (int a = 0; a < SUBT; ++a) af[a] = As[buf][HW * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][64 * wc + 16 * b + (lane & 15)];
+      for (int b = 0; b < SUBT; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][HW * wc + 16 * b + (lane & 15)];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < SUBT; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < SUBT; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
     if (more) stash(buf ^ 1);
@@ -419,13 +425,13 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
   }
 
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SUBT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < SUBT; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = row0 + 64 * wr + 16 * a + 4 * (lane >> 4) + q;
-        const int64_t col = col0 + 64 * wc + 16 * b + (lane & 15);
+        const int64_t row = row0 + HW * wr + 16 * a + 4 * (lane >> 4) + q;
+        const int64_t col = col0 + HW * wc + 16 * b + (lane & 15);
         if (row < g.m && col < g.nc) g.Wp[row * g.n + g.c0 + col] = acc[a][b][q];
       }
 }
@@ -437,10 +443,17 @@ void launch_update(float* Wp, int64_t m, int64_t n, const float* E, int64_t lde,
   UpdArgs g;
   g.Wp = Wp; g.m = m; g.n = n; g.E = E; g.lde = lde; g.k0 = k0; g.kc = kc;
   g.U = U; g.ldu = ldu; g.u0 = u0; g.c0 = c0; g.nc = nc;
-  g.tiles_n = ceil_div(nc, TT);
-  g.tiles = g.tiles_n * ceil_div(m, TT);
   g.vec_u = (ldu % 4 == 0) && (c0 % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
-  hipLaunchKernelGGL(update_gemm_kernel, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
+  // 128-wide tiles when they fill the chip, else 64-wide ones
+  if (ceil_div(nc, 128) * ceil_div(m, 128) >= 256) {
+    g.tiles_n = ceil_div(nc, 128);
+    g.tiles = g.tiles_n * ceil_div(m, 128);
+    hipLaunchKernelGGL(update_gemm_kernel<128>, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
+  } else {
+    g.tiles_n = ceil_div(nc, 64);
+    g.tiles = g.tiles_n * ceil_div(m, 64);
+    hipLaunchKernelGGL(update_gemm_kernel<64>, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
+  }
 }
 
 __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
