@@ -139,9 +139,31 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
     float* __restrict__ zeros, int64_t ngroups, float* __restrict__ E, int64_t lde, int64_t e0,
     float* __restrict__ row_err, int first_block) {
   __shared__ __align__(16) float Us[BLK][BLK + UPAD];
-  __shared__ float uinv[BLK];
+  __shared__ __align__(16) float uinv[BLK];
   const int tid = threadIdx.x;
   const int bw = (int)min((int64_t)BLK, n - i0);
+
+  // this lane's 8 values of its row, in flight while U is staged
+  const int l16 = tid & (LPR - 1);
+  const int64_t r = (int64_t)blockIdx.x * QROWS + (tid >> 4);
+  const bool rv = r < m;
+  const int64_t cbase = i0 + CPL * l16;  // first column of this lane
+
+  float w[CPL];
+  if (rv && cbase + CPL <= n) {
+    const float4* p = reinterpret_cast<const float4*>(Wp + r * n + cbase);
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      const float4 a = p[0], b = p[1];
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) w[s] = Wp[r * n + cbase + s];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) w[s] = (rv && cbase + s < n) ? Wp[r * n + cbase + s] : 0.0f;
+  }
 
   // Stage the diagonal block of U (upper triangle of the block's columns):
   // 16 float4 per thread, all in flight before the first LDS store.
@@ -176,26 +198,13 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
   __syncthreads();
   if (tid < BLK) uinv[tid] = tid < bw ? 1.0f / Us[tid][tid] : 0.0f;
   __syncthreads();
-
-  const int l16 = tid & (LPR - 1);
-  const int64_t r = (int64_t)blockIdx.x * QROWS + (tid >> 4);
-  const bool rv = r < m;
-  const int64_t cbase = i0 + CPL * l16;  // first column of this lane
-
-  float w[CPL];
-  if (rv && cbase + CPL <= n) {
-    const float4* p = reinterpret_cast<const float4*>(Wp + r * n + cbase);
-    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-      const float4 a = p[0], b = p[1];
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
-#pragma unroll
-      for (int s = 0; s < CPL; ++s) w[s] = Wp[r * n + cbase + s];
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < CPL; ++s) w[s] = (rv && cbase + s < n) ? Wp[r * n + cbase + s] : 0.0f;
+  // 1 / U_jj of this lane's own columns (only the owner's error is broadcast)
+  float uown[CPL];
+  {
+    const float4 a0 = *reinterpret_cast<const float4*>(&uinv[CPL * l16]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&uinv[CPL * l16 + 4]);
+    uown[0] = a0.x; uown[1] = a0.y; uown[2] = a0.z; uown[3] = a0.w;
+    uown[4] = a1.x; uown[5] = a1.y; uown[6] = a1.z; uown[7] = a1.w;
   }
 
   float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
     const float wj = w[s];
     const float q = quant_code_fast(wj, scale, rscale, zero, maxq);
     const float dq = scale * (q - zero);
-    float e = (wj - dq) * uinv[j];
+    float e = (wj - dq) * uown[s];
     e = row_bcast<owner>(e);
     if (l16 == owner) {
       e_own[s] = e;
