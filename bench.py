@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=128)
     ap.add_argument("--cpu-sample-chunks", type=int, default=2)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one Hessian accumulate of the workload and one 2 GiB device copy, "
+                         "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter files of two --traffic-probe runs into "
+                         "profiles/traffic_hessian_llama7b_attn.json, then exit")
     return ap.parse_args()
 
 
@@ -65,6 +71,51 @@ def measured_traffic():
     if rec.get("kernel_source_sha256") != source_hash(HESSIAN_SRC):
         return None  # the kernel changed since the counters were taken
     return rec.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 31  # the calibration copy of --traffic-probe
+HESS_KERNELS = ("syrk_bf16_dma_kernel", "reduce_full_partials_kernel")
+
+
+def traffic_record(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes of one Hessian launch from two counter runs of --traffic-probe.
+
+    Each counter (KiB per dispatch, summed over the L2 channels) is scaled by
+    the ratio of the known bytes of the 2 GiB device copy to what the same
+    counter reads for that copy; the launch is the last pair of Hessian
+    dispatches (interior SYRK + split reduction) in each file.
+    """
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(path, counter):
+        val = defaultdict(float)
+        name = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            val[d] += float(r["Counter_Value"])
+            name[d] = r["Kernel_Name"]
+        return val, name
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        val, name = per_dispatch(path, counter)
+        copies = [d for d in val if "copyBuffer" in name[d]]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch")
+        copy_kib = val[max(copies)]
+        hess = 0.0
+        for k in HESS_KERNELS:
+            ds = [d for d in val if k in name[d]]
+            if not ds:
+                raise SystemExit(f"{path}: no {k} dispatch")
+            hess += val[max(ds)]
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[counter] = {"hessian_kib": hess, "copy_kib": copy_kib, "scale": factor,
+                        "bytes": hess * 1024.0 * factor}
+    return out
 
 
 def cpu_baseline(wl, rows: int, chunks: int):
@@ -114,6 +165,33 @@ def cpu_baseline(wl, rows: int, chunks: int):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        t = traffic_record(*args.traffic_record)
+        rec = {
+            "kernel": "gptq_hessian_accumulate: " + " + ".join(HESS_KERNELS),
+            "workload": WORKLOAD,
+            "bytes_per_launch": round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]),
+            "fetch": t["FETCH_SIZE"],
+            "write": t["WRITE_SIZE"],
+            "calibration": f"device copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write "
+                           f"{COPY_BYTES})",
+            "commands": [
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format "
+                "csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py "
+                "--traffic-probe",
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format "
+                "csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py "
+                "--traffic-probe",
+                "python3 bench.py --traffic-record gpurun_out/pmc_fetch/run_counter_collection.csv "
+                "gpurun_out/pmc_write/run_counter_collection.csv",
+            ],
+            "kernel_source_sha256": source_hash(HESSIAN_SRC),
+        }
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU split of the path is described, not built)", file=sys.stderr)
@@ -153,6 +231,20 @@ def main():
 
     cfg = gq.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
     buf = pipeline.allocate(m, n, cfg, N)
+    if args.traffic_probe:
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            buf.S.zero_()
+            gq.gptq_hessian_accumulate(buf.S, X, ws=buf.ws_hess, stream=stream)
+        torch.cuda.synchronize()
+        del X
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("traffic probe: 2 Hessian accumulates and one device copy of "
+              f"{COPY_BYTES} bytes done", flush=True)
+        return
     ng = pipeline.ngroups(n, q.group_size)
     rtn_codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
     rtn_scales = torch.empty((m, ng), dtype=torch.float32, device=dev)
@@ -208,7 +300,7 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "hessian (syrk_bf16_kernel + split reduction; one gptq_hessian_accumulate)",
+        "kernel": "hessian: gptq_hessian_accumulate (syrk_bf16_dma_kernel + reduce_full_partials_kernel)",
         "achieved": round(hess_tf, 2),
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
