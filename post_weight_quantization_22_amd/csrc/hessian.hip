@@ -13,7 +13,8 @@
 //  - interior kernel (n a multiple of 256, whole stages, aligned rows): the
 //    stage goes global -> LDS by DMA in X's own layout (XOR-swizzled 16-byte
 //    chunks) and the operands are read back with the transposing LDS read
-//    ds_read_b64_tr_b16; 8 waves of 128 x 64.
+//    ds_read_b64_tr_b16; 8 waves of 128 x 64, LDS double buffer with the
+//    next stage's first operands read across the barrier.
 //  - general kernel (any shape): each lane loads an 8-token x 8-channel
 //    block into registers (bounds-checked), transposes it with v_perm and
 //    stores channel rows of 144 bytes (9 x 16 B: conflict-free) to LDS;
@@ -261,7 +262,12 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 // (lane i: channel i, 4 consecutive tokens), i.e. the bf16 operand layout, so
 // there is no register staging and no permute.  With the swizzle the 16 lanes
 // x 4 tokens of a half-wave read 16 distinct chunk positions: all 64 banks.
-// The DMA of stage s + 1 runs under the MFMAs of stage s; one barrier each.
+// Two LDS buffers: the DMA of stage s + 2 is issued as soon as stage s is in
+// registers.  The one barrier per stage (publishing stage s + 1) sits before
+// the MFMAs of the last 16 tokens of stage s, so the first operands of stage
+// s + 1 are read while those MFMAs run.  On diagonal tiles the B operand is
+// the A operand (no second DMA) and the two waves whose block lies wholly
+// above the diagonal skip their MFMAs.
 constexpr int FT_I = 256, FT_J = 256;   // tile
 constexpr int WI = 128, WJ = 64;        // per wave
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -279,22 +285,23 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS DMA of 16 bytes per lane (lane l lands at lds + 16 l), issued from asm:
-// the compiler cannot tell this write from the LDS reads of the other buffer
-// and would otherwise wait for it before every one of them; completion is
-// awaited explicitly (vmcnt) before the barrier that publishes the stage.  The
-// instruction writes no VGPR (its data goes to LDS), and its address VGPRs
-// are consumed at issue.  M0 (the LDS base of the transfer, read at issue)
-// is saved and restored around it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+// LDS DMA of 16 bytes per lane (lane l lands at lds + 16 l) from
+// sbase + voff (wave-uniform 64-bit base in SGPRs, per-lane 32-bit byte
+// offset), issued from asm: the compiler cannot tell this write from the LDS
+// reads of the other buffer and would otherwise wait for it before every one
+// of them; completion is awaited explicitly (vmcnt) before the barrier that
+// publishes the stage.  The instruction writes no VGPR (its data goes to
+// LDS), and its address registers are consumed at issue.  M0 (the LDS base
+// of the transfer, read at issue) is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   __asm__ volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 
@@ -314,35 +321,36 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
   const int64_t L = ti * (ti + 1) / 2 + tj;  // row-major index of the partial tile
   const int64_t i0 = ti * FT_I, j0 = tj * FT_J;
   const bool diag = ti == tj;
+  const bool idle = diag && WJ * wc >= WI * (wr + 1);  // block wholly above the diagonal
   const int nstage = (int)(tok_per_split / HK);
 
-  // DMA: instruction q of wave wv fills token rows RPW wv + 2 q and + 1; the
-  // swizzle depends on the row only through (2 q + lane / 32) % 4, so two
-  // per-lane source pointers (q even / odd) serve all q, 4 rows apart.
-  const uint16_t* srcA[2];
+  // DMA: instruction q of wave wv fills token rows RPW wv + 2 q and + 1 (lane
+  // / 32); the swizzle depends on the row only through (2 q + lane / 32) % 4,
+  // so two per-lane offsets (q even / odd) serve all q, with the rest of the
+  // address wave-uniform.
+  uint32_t voff[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int t = RPW * wv + 2 * q + (lane >> 5);
+    const int t = 2 * q + (lane >> 5);
     const int k = (lane & 31) ^ (4 * (t & 3));
-    srcA[q] = X + (p * tok_per_split + t) * ldx + 8 * k + i0;
+    voff[q] = (uint32_t)(2 * (t * ldx + 8 * k));
   }
-  const int64_t jmi = j0 - i0;
-  const int64_t step = HK * ldx;
-  auto issue = [&](int s, int buf) {
-    uint8_t* dA = smem + (2 * buf) * DSTAGE + RPW * wv * DROW;
-    uint8_t* dB = dA + DSTAGE;
-    const int64_t adv = (int64_t)s * step;
-    const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dA);
-    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dB);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const char* xa = reinterpret_cast<const char*>(X + (p * tok_per_split + RPW * wvu) * ldx + i0);
+  const int64_t jmi2 = 2 * (j0 - i0);
+  const int64_t step2 = 2 * HK * ldx;
+  const uint32_t lbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) void*)(smem + RPW * wv * DROW));
+  auto issue = [&](int s) {
+    const uint32_t la = lbase + (uint32_t)((s & 1) * 2 * DSTAGE);
+    const char* base = xa + (int64_t)s * step2;
 #pragma unroll
     for (int q = 0; q < RPW / 2; ++q)
-      dma16(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx, la + 1024 * q);
+      dma16(base + (int64_t)(4 * (q & ~1)) * ldx, voff[q & 1], la + 1024 * q);
     if (!diag) {
 #pragma unroll
       for (int q = 0; q < RPW / 2; ++q)
-        dma16(srcA[q & 1] + adv + (int64_t)(2 * (q & ~1)) * ldx + jmi, lb + 1024 * q);
+        dma16(base + (int64_t)(4 * (q & ~1)) * ldx + jmi2, voff[q & 1], la + DSTAGE + 1024 * q);
     }
   };
 
@@ -367,31 +375,60 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
     for (int b = 0; b < WJ / 32; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
-
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
-  __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nstage) issue(s + 1, buf ^ 1);
-    const uint8_t* At = smem + (2 * buf) * DSTAGE;
+  struct Ops {
+    bf16x8 a[WI / 32], b[WJ / 32];
+  };
+  auto read_ops = [&](int s, int kk, Ops& o) {
+    if (idle) return;
+    const uint8_t* At = smem + (s & 1) * 2 * DSTAGE;
     const uint8_t* Bt = diag ? At : At + DSTAGE;
 #pragma unroll
-    for (int kk = 0; kk < HK / 16; ++kk) {
-      bf16x8 af[WI / 32], bfr[WJ / 32];
+    for (int a = 0; a < WI / 32; ++a) o.a[a] = tr_operand(At + offA[a] + 16 * kk * DROW);
 #pragma unroll
-      for (int a = 0; a < WI / 32; ++a) af[a] = tr_operand(At + offA[a] + 16 * kk * DROW);
+    for (int b = 0; b < WJ / 32; ++b) o.b[b] = tr_operand(Bt + offB[b] + 16 * kk * DROW);
+  };
+  auto mfma = [&](const Ops& o) {
+    if (idle) return;
 #pragma unroll
-      for (int b = 0; b < WJ / 32; ++b) bfr[b] = tr_operand(Bt + offB[b] + 16 * kk * DROW);
+    for (int a = 0; a < WI / 32; ++a)
 #pragma unroll
-      for (int a = 0; a < WI / 32; ++a)
-#pragma unroll
-        for (int b = 0; b < WJ / 32; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
-    }
+      for (int b = 0; b < WJ / 32; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[a], o.b[b], acc[a][b], 0, 0, 0);
+  };
+
+  // stages 0 and 1 in flight; wait for stage 0 (vmcnt counts this wave's
+  // outstanding DMA instructions: RPW per stage, RPW / 2 on diagonal tiles)
+  issue(0);
+  if (nstage > 1) issue(1);
+  if (nstage > 1 && diag) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (RPW / 2));
+  } else if (nstage > 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | RPW);
+  } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
   }
+  __syncthreads();
+  static_assert(HK == 64, "the k-step schedule below covers 4 x 16 tokens");
+  Ops r0, r1;
+  read_ops(0, 0, r0);
+  for (int s = 0; s < nstage; ++s) {
+    read_ops(s, 1, r1);
+    mfma(r0);
+    read_ops(s, 2, r0);
+    mfma(r1);
+    read_ops(s, 3, r1);
+    mfma(r0);
+    // stage s is in registers once r1 has landed (the barrier waits for this
+    // wave's LDS reads); stage s + 1 is published once every wave's DMA has
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 2 < nstage) issue(s + 2);
+    if (s + 1 < nstage) read_ops(s + 1, 0, r0);
+    mfma(r1);
+  }
+  if (idle) return;
 
 #pragma unroll
   for (int a = 0; a < WI / 32; ++a)
