@@ -17,17 +17,31 @@
 // fp64 and compute X = L^-1 directly, then write U[k][l] = X[n-1-k][n-1-l]
 // rounded to fp32.
 //
-// X = L^-1 by recursive halving.  For A = [[A11, .], [A21, A22]]:
-//   X11 = chol_inv(A11)                  (recursion; nodes of <= 128 in one kernel)
-//   T   = A21 X11^T          (= L21)     GEMM, X11 lower
-//   A22 = A22 - T T^T                    SYRK, lower tiles
-//   M   = T X11              (= L21 X11) GEMM, stored over A21
-//   X22 = chol_inv(A22)                  (recursion)
-//   X21 = -X22 M                         GEMM, X22 lower
-// which follows from A21 = L21 L11^T, A22 = L21 L21^T + L22 L22^T and
-// L^-1 = [[X11, 0], [-X22 L21 X11, X22]].  The leaves run in order; everything
-// between them is a large GEMM on v_mfma_f64_16x16x4_f64, so no kernel carries
-// a long serial reduction.
+// X = L^-1 in two phases, with 128-wide blocks (block k = rows 128k ..).
+//
+// 1. Blocked right-looking Cholesky.  Step k: the diagonal node kernel turns
+//    the (fully updated) block A_kk into X_kk = L_kk^-1 in one workgroup; the
+//    panel L_ik = A_ik X_kk^T (i > k) is a GEMM, stored in X's block (i, k);
+//    the rank-128 update A_ij -= L_ik L_jk^T (k < j <= i) follows from
+//    A = L L^T.  The update is split so that the next node can start early:
+//    block column k + 1 on the main stream, the rest of the trailing matrix
+//    (columns >= k + 2) on a side stream, where it overlaps node k + 1 and
+//    panel k + 1.  Before the main stream updates column k + 2 it waits for
+//    that side update (both write it).
+// 2. X = L^-1 by groups of GRP blocks (rows c .. c + 512), from L X = I:
+//    X[g, 0:c] = -X_gg L[g, 0:c] X[0:c, 0:c].  Per group, on a third stream:
+//      X_gg, the inverse of the group's own diagonal block, joins the nodes'
+//      X_ii pairwise: for a split [[L11, 0], [L21, L22]] the inverse is
+//      [[X11, 0], [-X22 L21 X11, X22]] (M = L21 X11, X21 = -X22 M);
+//      M_g = L[g, 0:c] X[0:c, 0:c] needs only the panels of L in the
+//      group's rows (all written before the group's first node) and the
+//      groups above, so it runs while the group's nodes are factored;
+//      X[g, 0:c] = -X_gg M_g once X_gg exists.
+//    So all that follows the last node is the last group's joins and one
+//    product.  L's blocks sit in X's lower blocks and are overwritten by X's.
+//
+// The products run on v_mfma_f64_16x16x4_f64, so no kernel carries a long
+// serial reduction; the serial part is the chain of 128-wide nodes.
 #include <mutex>
 
 #include "kernels.hpp"
@@ -41,38 +55,19 @@ constexpr int NODE = 128;  // subproblems up to this size run in one workgroup
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-constexpr int MAXDEPTH = 24;
-
 struct PrepWs {
   double* A;               // [n, n] lower: damped, permuted, reversed Hessian (overwritten)
-  double* X;               // [n, n] lower: L^-1
-  double* T[MAXDEPTH];     // per recursion depth: [s2, s1] of that depth's split
+  double* X;               // [n, n] lower: L^-1 (holds the panels of L while phase 1 runs)
+  double* M;               // phase-2 products: M_g, then the joins' M
   double* diag;            // [n]
   double* lam;             // [1]
   int32_t* perm;           // [n]
 };
 
-int64_t split_first(int64_t s) {
-  const int64_t blocks = ceil_div(s, NODE);
-  return ((blocks + 1) / 2) * NODE;
-}
+constexpr int GRP = 4;  // blocks per group of the inverse
 
-// Largest T of each depth: t[d] = max over the depth-d splits of s2 * s1.
-void t_sizes(int64_t s, int d, size_t (&t)[MAXDEPTH]) {
-  if (s <= NODE || d >= MAXDEPTH) return;
-  const int64_t s1 = split_first(s), s2 = s - s1;
-  t[d] = hmax((int64_t)t[d], s1 * s2);
-  t_sizes(s1, d + 1, t);
-  t_sizes(s2, d + 1, t);
-}
-
-size_t t_bytes(int64_t n) {
-  size_t t[MAXDEPTH] = {};
-  t_sizes(n, 0, t);
-  size_t b = 0;
-  for (int d = 0; d < MAXDEPTH; ++d) b += align_up(t[d] * sizeof(double), 256);
-  return b;
-}
+// Phase-2 product buffers: M_g ([GRP NODE, n]) and the joins' M ([2 NODE, 2 NODE]).
+int64_t m_elems(int64_t n) { return n > NODE ? GRP * NODE * n + 4 * NODE * NODE : 0; }
 
 PrepWs carve(void* ws, int64_t n) {
   char* p = reinterpret_cast<char*>(ws);
@@ -81,12 +76,8 @@ PrepWs carve(void* ws, int64_t n) {
   p += align_up((size_t)n * n * sizeof(double), 256);
   w.X = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * n * sizeof(double), 256);
-  size_t t[MAXDEPTH] = {};
-  t_sizes(n, 0, t);
-  for (int d = 0; d < MAXDEPTH; ++d) {
-    w.T[d] = reinterpret_cast<double*>(p);
-    p += align_up(t[d] * sizeof(double), 256);
-  }
+  w.M = reinterpret_cast<double*>(p);
+  p += align_up((size_t)m_elems(n) * sizeof(double), 256);
   w.diag = reinterpret_cast<double*>(p);
   p += align_up((size_t)n * sizeof(double), 256);
   w.lam = reinterpret_cast<double*>(p);
@@ -95,12 +86,16 @@ PrepWs carve(void* ws, int64_t n) {
   return w;
 }
 
-// Second stream (default priority) for work off the critical path, with one
-// pair of events per recursion depth; created once per device.
+// Two more streams (default priority), one for the trailing updates and one
+// for the block rows of the inverse, and the events that order them against
+// the main stream; created once per device.
 struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t t_done[MAXDEPTH];
-  hipEvent_t m_done[MAXDEPTH];
+  hipStream_t s = nullptr;    // trailing updates
+  hipStream_t inv = nullptr;  // block rows of X
+  hipEvent_t step_done;       // main -> s, inv: panel k and column k + 1 are done
+  hipEvent_t trailing_done;   // s -> main: trailing update k is applied
+  hipEvent_t last_node;       // main -> inv: the last node is done
+  hipEvent_t inv_done;        // inv -> main: the last group of X is written
 };
 
 hipError_t side_stream(SideStream*& out) {
@@ -113,14 +108,16 @@ hipError_t side_stream(SideStream*& out) {
   std::lock_guard<std::mutex> lock(mu);
   SideStream& sd = sides[dev];
   if (!sd.s) {
-    hipStream_t st;
+    hipStream_t st, si;
     e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
     if (e != hipSuccess) return e;
-    for (int d = 0; d < MAXDEPTH; ++d) {
-      e = hipEventCreateWithFlags(&sd.t_done[d], hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.m_done[d], hipEventDisableTiming);
+    e = hipStreamCreateWithFlags(&si, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    for (hipEvent_t* ev : {&sd.step_done, &sd.trailing_done, &sd.last_node, &sd.inv_done}) {
+      e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
       if (e != hipSuccess) return e;
     }
+    sd.inv = si;
     sd.s = st;
   }
   out = &sd;
@@ -625,6 +622,7 @@ struct GemmArgs {
   int kmode;
   int lower;
   int64_t tiles_m, tiles_n;
+  int64_t tiles;  // workgroup b takes tiles b, b + gridDim.x, ...
 };
 
 constexpr int GK = 32;
@@ -665,8 +663,9 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int wr = wv >> 1, wc = wv & 1;
+  for (int64_t bid = blockIdx.x; bid < g.tiles; bid += gridDim.x) {
   int64_t ti, tj;
-  gemm_tile_of(g, blockIdx.x, ti, tj);
+  gemm_tile_of(g, bid, ti, tj);
   const int64_t i0 = ti * TILE, j0 = tj * TILE;
   int64_t kb = 0, ke = g.K;
   if (g.kmode & KLO_J) kb = j0;
@@ -743,17 +742,19 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs g) {
         const double v = g.alpha * acc[a][b][q];
         *c = g.beta == 0.0 ? v : fma(g.beta, *c, v);
       }
+  }
 }
 
 template <int TILE>
-void launch_gemm_tile(const GemmArgs& g0, bool ta, bool tb, hipStream_t stream) {
+void launch_gemm_tile(const GemmArgs& g0, bool ta, bool tb, int64_t max_wg, hipStream_t stream) {
   GemmArgs g = g0;
   const int64_t tm = ceil_div(g.M, TILE), tn = ceil_div(g.N, TILE);
   g.tiles_m = tm;
   g.tiles_n = tn;
   const int64_t tiles = g.lower ? tm * (tm + 1) / 2 : tm * tn;
   if (tiles == 0) return;
-  const dim3 grid((unsigned)tiles);
+  g.tiles = tiles;
+  const dim3 grid((unsigned)(max_wg > 0 ? hmin(tiles, max_wg) : tiles));
   if (!ta && !tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, false, false>), grid, dim3(256), 0, stream, g);
   else if (!ta && tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, false, true>), grid, dim3(256), 0, stream, g);
   else if (ta && !tb) hipLaunchKernelGGL((gemm_f64_kernel<TILE, true, false>), grid, dim3(256), 0, stream, g);
@@ -772,8 +773,9 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs g) {
   __shared__ double red[3 * TILE * TILE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, kq = lane >> 4;
+  for (int64_t bid = blockIdx.x; bid < g.tiles; bid += gridDim.x) {
   int64_t ti, tj;
-  gemm_tile_of(g, blockIdx.x, ti, tj);
+  gemm_tile_of(g, bid, ti, tj);
   const int64_t i0 = ti * TILE, j0 = tj * TILE;
   int64_t kb = 0, ke = g.K;
   if (g.kmode & KLO_J) kb = j0;
@@ -854,7 +856,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs g) {
           red[(((wv - 1) * SUB * SUB + a * SUB + b) * 4 + q) * 64 + lane] = acc[a][b][q];
   }
   __syncthreads();
-  if (wv != 0) return;
+  if (wv == 0) {
 #pragma unroll
   for (int a = 0; a < SUB; ++a)
 #pragma unroll
@@ -873,34 +875,42 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs g) {
         const double o = g.alpha * v;
         *c = g.beta == 0.0 ? o : fma(g.beta, *c, o);
       }
+  }
+  __syncthreads();  // red is refilled by the next tile
+  }
 }
 
 template <int TILE>
-void launch_splitk(const GemmArgs& g0, bool tb, hipStream_t stream) {
+void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stream) {
   GemmArgs g = g0;
   const int64_t tm = ceil_div(g.M, TILE), tn = ceil_div(g.N, TILE);
   g.tiles_m = tm;
   g.tiles_n = tn;
   const int64_t tiles = g.lower ? tm * (tm + 1) / 2 : tm * tn;
   if (tiles == 0) return;
-  if (tb) hipLaunchKernelGGL((gemm_splitk_kernel<TILE, true>), dim3((unsigned)tiles), dim3(256), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_splitk_kernel<TILE, false>), dim3((unsigned)tiles), dim3(256), 0, stream, g);
+  g.tiles = tiles;
+  const dim3 grid((unsigned)(max_wg > 0 ? hmin(tiles, max_wg) : tiles));
+  if (tb) hipLaunchKernelGGL((gemm_splitk_kernel<TILE, true>), grid, dim3(256), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_splitk_kernel<TILE, false>), grid, dim3(256), 0, stream, g);
 }
 
 hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t ldb, bool tb,
                 double* C, int64_t ldc, int64_t M, int64_t N, int64_t K, double alpha, double beta,
-                int kmode, bool lower, hipStream_t stream) {
+                int kmode, bool lower, hipStream_t stream, int64_t max_wg = 0) {
+  if (M <= 0 || N <= 0) return hipSuccess;
   GemmArgs g;
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K; g.alpha = alpha; g.beta = beta; g.kmode = kmode;
   g.lower = lower ? 1 : 0;
-  g.tiles_m = g.tiles_n = 0;
-  // Up to 256 tiles of 32 x 32 (the lower levels of the recursion, bound by
-  // latency) the split-K kernel; above, 64-wide tiles staged through LDS,
-  // dispatched longest K range first.  (Measured on the levels n/2 .. 128 of a
-  // 4096 factorization; 128-wide tiles lost at every size.)
-  if (!ta && ceil_div(M, 32) * ceil_div(N, 32) <= 256) launch_splitk<32>(g, tb, stream);
-  else launch_gemm_tile<64>(g, ta, tb, stream);
+  g.tiles_m = g.tiles_n = g.tiles = 0;
+  // Fewer than 256 tiles of 64 x 64 (too few to fill the chip, or a long K
+  // over a narrow output) the split-K kernel on 32 x 32 tiles; otherwise
+  // 64-wide tiles staged through LDS, dispatched longest K range first.
+  // (Measured on products of 128 to 2048; 128-wide tiles lost at every size.)
+  const int64_t t64 = lower ? ceil_div(M, 64) * (ceil_div(M, 64) + 1) / 2
+                            : ceil_div(M, 64) * ceil_div(N, 64);
+  if (!ta && t64 < 256) launch_splitk<32>(g, tb, max_wg, stream);
+  else launch_gemm_tile<64>(g, ta, tb, max_wg, stream);
   return hipGetLastError();
 }
 
@@ -910,46 +920,111 @@ __global__ void fill_f64_kernel(double* __restrict__ p, int64_t count) {
   for (int64_t k = i; k < count; k += stride) p[k] = 0.0;
 }
 
-// X[off:off+s, off:off+s] = inverse of the Cholesky factor of A[off:off+s, off:off+s].
-// M = T X11 is needed only by the last product, so it runs on the side stream
-// while the main stream goes on with A22 -= T T^T and the whole recursion on
-// A22 (mostly single-CU nodes and small products, which leave the chip idle).
-// T has one buffer per depth: a depth's splits follow each other, and each
-// joins its side work before returning.
-hipError_t chol_inv(const PrepWs& w, int64_t n, int64_t off, int64_t s, int d, int32_t* info,
-                    hipStream_t stream, SideStream* side) {
-  if (s <= NODE) {
-    hipLaunchKernelGGL(node_kernel, dim3(1), dim3(256), 0, stream, w.A, w.X, n, off, (int)s,
-                       info);
-    return hipGetLastError();
+// X's blocks below the diagonal inside rows o .. o + s1 + s2: join the
+// inverted neighbours [o, o + s1) and [o + s1, o + s1 + s2) through the
+// panel L21 that sits where X21 goes.
+hipError_t join(const PrepWs& w, int64_t n, int64_t o, int64_t s1, int64_t s2, double* Mj,
+                hipStream_t st) {
+  const int64_t o2 = o + s1;
+  // M = L21 X11   (X11(c, j) = 0 for c < j)
+  hipError_t e = gemm(w.X + o2 * n + o, n, false, w.X + o * n + o, n, false, Mj, s1, s2, s1, s1,
+                      1.0, 0.0, KLO_J, false, st);
+  // X21 = -X22 M  (X22(i, c) = 0 for c > i)
+  if (e == hipSuccess)
+    e = gemm(w.X + o2 * n + o2, n, false, Mj, s1, false, w.X + o2 * n + o, n, s2, s1, s2, -1.0,
+             0.0, KHI_I, false, st);
+  return e;
+}
+
+// X_gg for the group of blocks [b0, b0 + cnt): pairs of blocks, then the two pairs.
+hipError_t invert_group_diag(const PrepWs& w, int64_t n, int64_t b0, int64_t cnt, double* Mj,
+                             hipStream_t st) {
+  hipError_t e = hipSuccess;
+  for (int64_t wd = 1; wd < cnt && e == hipSuccess; wd *= 2) {
+    for (int64_t a = 0; a + wd < cnt && e == hipSuccess; a += 2 * wd) {
+      const int64_t o = NODE * (b0 + a), s1 = NODE * wd;
+      const int64_t s2 = hmin(n, NODE * (b0 + hmin(a + 2 * wd, cnt))) - (o + s1);
+      e = join(w, n, o, s1, s2, Mj, st);
+    }
   }
-  if (d >= MAXDEPTH) return hipErrorInvalidValue;
-  const int64_t s1 = split_first(s), s2 = s - s1;
-  double* A21 = w.A + (off + s1) * n + off;
-  double* A22 = w.A + (off + s1) * n + off + s1;
-  const double* X11 = w.X + off * n + off;
-  double* X21 = w.X + (off + s1) * n + off;
-  const double* X22 = w.X + (off + s1) * n + off + s1;
-  double* T = w.T[d];
-  hipError_t e = chol_inv(w, n, off, s1, d + 1, info, stream, side);
-  if (e != hipSuccess) return e;
-  // T = A21 X11^T   (X11(j, k) = 0 for k > j)
-  e = gemm(A21, n, false, X11, n, true, T, s1, s2, s1, s1, 1.0, 0.0, KHI_J, false, stream);
-  if (e != hipSuccess) return e;
-  // A21 := T X11    (X11(k, j) = 0 for k < j), on the side stream
-  if ((e = hipEventRecord(side->t_done[d], stream)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(side->s, side->t_done[d], 0)) != hipSuccess) return e;
-  e = gemm(T, s1, false, X11, n, false, A21, n, s2, s1, s1, 1.0, 0.0, KLO_J, false, side->s);
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(side->m_done[d], side->s)) != hipSuccess) return e;
-  // A22 -= T T^T    (lower tiles)
-  e = gemm(T, s1, false, T, s1, true, A22, n, s2, s2, s1, -1.0, 1.0, 0, true, stream);
-  if (e != hipSuccess) return e;
-  e = chol_inv(w, n, off + s1, s2, d + 1, info, stream, side);
-  if (e != hipSuccess) return e;
-  // X21 = -X22 A21  (X22(i, k) = 0 for k > i)
-  if ((e = hipStreamWaitEvent(stream, side->m_done[d], 0)) != hipSuccess) return e;
-  return gemm(X22, n, false, A21, n, false, X21, n, s2, s1, s2, -1.0, 0.0, KHI_I, false, stream);
+  return e;
+}
+
+// Both phases: X's diagonal blocks from the nodes, L's panels into X's lower
+// blocks, then X group by group over them.  The node kernel needs a CU of its
+// own (most of the LDS), so the large products of the other two streams are
+// released only when the main stream reaches the node (after the column
+// update of step k): launched earlier they would fill every CU first.
+hipError_t factor_invert(const PrepWs& w, int64_t n, int32_t* info, hipStream_t stream,
+                         SideStream* side) {
+  const int64_t nb = ceil_div(n, NODE);
+  double* Mg = w.M;
+  double* Mj = w.M + GRP * NODE * n;
+  auto node = [&](int64_t k) {
+    const int64_t o = NODE * k;
+    hipLaunchKernelGGL(node_kernel, dim3(1), dim3(256), 0, stream, w.A, w.X, n, o,
+                       (int)hmin(n - o, (int64_t)NODE), info);
+    return hipGetLastError();
+  };
+  // the inverse stream's work for group g once its last node is done
+  auto group_tail = [&](int64_t g) {
+    const int64_t b0 = GRP * g, cnt = hmin((int64_t)GRP, nb - b0);
+    const int64_t c = NODE * b0, sg = hmin(n, c + GRP * NODE) - c;
+    hipError_t e = invert_group_diag(w, n, b0, cnt, Mj, side->inv);
+    // X[g, 0:c] = -X_gg M_g   (X_gg(i, j) = 0 for j > i)
+    if (e == hipSuccess && g > 0)
+      e = gemm(w.X + c * n + c, n, false, Mg, c, false, w.X + c * n, n, sg, c, sg, -1.0, 0.0,
+               KHI_I, false, side->inv);
+    return e;
+  };
+  // M_g = L[g, 0:c] X[0:c, 0:c] (X(r, j) = 0 for r < j): needs the groups above
+  // and the panels of L in the group's rows, the last of them by step c / 128 - 1
+  auto group_head = [&](int64_t g) {
+    const int64_t c = NODE * GRP * g, sg = hmin(n, c + GRP * NODE) - c;
+    return gemm(w.X + c * n, n, false, w.X, n, false, Mg, c, sg, c, c, 1.0, 0.0, KLO_J, false,
+                side->inv);
+  };
+  hipError_t e = node(0);
+  bool pending = false;  // a trailing update is queued on the side stream
+  for (int64_t k = 0; k + 1 < nb && e == hipSuccess; ++k) {
+    const int64_t bk = NODE * k, r1 = bk + NODE, rows = n - r1;
+    const int64_t s1 = hmin(rows, (int64_t)NODE);  // width of block k + 1
+    double* Lk = w.X + r1 * n + bk;                 // panel k: rows r1.., 128 columns
+    // L_ik = A_ik X_kk^T  (X_kk(j, c) = 0 for c > j)
+    e = gemm(w.A + r1 * n + bk, n, false, w.X + bk * n + bk, n, true, Lk, n, rows, NODE, NODE,
+             1.0, 0.0, KHI_J, false, stream);
+    // column k + 1 is also written by the trailing update of step k - 1
+    if (e == hipSuccess && pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
+    // A[:, k+1] -= L_k L_{k+1,k}^T  (rows r1..; the diagonal block's upper part is not read)
+    if (e == hipSuccess)
+      e = gemm(Lk, n, false, Lk, n, true, w.A + r1 * n + r1, n, rows, s1, NODE, -1.0, 1.0, 0,
+               false, stream);
+    if (e == hipSuccess) e = hipEventRecord(side->step_done, stream);
+    if (e == hipSuccess) e = node(k + 1);
+    const int64_t r2 = r1 + NODE;
+    if (e == hipSuccess && r2 < n) {
+      // A[r2.., r2..] -= L_k L_k^T (lower tiles), off the critical path
+      e = hipStreamWaitEvent(side->s, side->step_done, 0);
+      if (e == hipSuccess)
+        e = gemm(w.X + r2 * n + bk, n, false, w.X + r2 * n + bk, n, true, w.A + r2 * n + r2, n,
+                 n - r2, n - r2, NODE, -1.0, 1.0, 0, true, side->s);
+      if (e == hipSuccess) e = hipEventRecord(side->trailing_done, side->s);
+      pending = true;
+    }
+    if (e == hipSuccess && k % GRP == GRP - 1) {  // node k closed group k / GRP
+      e = hipStreamWaitEvent(side->inv, side->step_done, 0);
+      if (e == hipSuccess) e = group_tail(k / GRP);
+      if (e == hipSuccess) e = group_head(k / GRP + 1);
+    }
+  }
+  if (e == hipSuccess && pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
+  // the last group, closed by node nb - 1
+  if (e == hipSuccess) e = hipEventRecord(side->last_node, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->inv, side->last_node, 0);
+  if (e == hipSuccess) e = group_tail((nb - 1) / GRP);
+  if (e == hipSuccess) e = hipEventRecord(side->inv_done, side->inv);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->inv_done, 0);
+  return e;
 }
 
 // U[k][l] = X[n-1-k][n-1-l] for l >= k (fp32), 0 below the diagonal.
@@ -968,7 +1043,7 @@ __global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__
 
 size_t prepare_ws_bytes(int64_t n) {
   size_t b = 2 * align_up((size_t)n * n * sizeof(double), 256);
-  b += t_bytes(n);
+  b += align_up((size_t)m_elems(n) * sizeof(double), 256);
   b += align_up((size_t)n * sizeof(double), 256);
   b += 256;
   b += align_up((size_t)n * sizeof(int32_t), 256);
@@ -998,7 +1073,7 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   SideStream* side = nullptr;
   hipError_t e = side_stream(side);
   if (e != hipSuccess) return e;
-  e = chol_inv(w, n, 0, n, 0, info, stream, side);
+  e = factor_invert(w, n, info, stream, side);
   if (e != hipSuccess) return e;
   {
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(n, 2048));
