@@ -447,23 +447,51 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
 }
 
 // S[lower] += sum over splits of the 256 x 256 partial tiles, splits in order.
+// Each thread sums 4 consecutive entries of a tile row (16-byte loads, the
+// loads of 8 splits in flight before their in-order adds).
 __global__ __launch_bounds__(256) void reduce_full_partials_kernel(const float* __restrict__ part,
                                                                    int64_t P, int64_t ntiles,
                                                                    float* __restrict__ S,
-                                                                   int64_t lds) {
+                                                                   int64_t lds, int vec_s) {
   constexpr int CH = FT_I * FT_J / 1024;
   const int64_t L = blockIdx.x / CH;
   const int64_t chunk = blockIdx.x % CH;
   int64_t ti, tj;
   tile_coords(L, ti, tj);
-  for (int r = 0; r < 4; ++r) {
-    const int e = (int)chunk * 1024 + r * 256 + threadIdx.x;
-    const int ii = e / FT_J, jj = e % FT_J;
-    const int64_t gi = ti * FT_I + ii, gj = tj * FT_J + jj;
-    if (gj > gi) continue;
-    float s = 0.0f;
-    for (int64_t q = 0; q < P; ++q) s += part[(q * ntiles + L) * FT_I * FT_J + e];
-    S[gi * lds + gj] += s;
+  const int e = (int)chunk * 1024 + 4 * threadIdx.x;
+  const int ii = e / FT_J, jj = e % FT_J;
+  const int64_t gi = ti * FT_I + ii, gj = tj * FT_J + jj;
+  if (gj > gi) return;  // the whole quad lies above the diagonal
+  const float4* src = reinterpret_cast<const float4*>(part + L * FT_I * FT_J + e);
+  const int64_t stride = ntiles * (FT_I * FT_J / 4);  // float4s from one split to the next
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int64_t q0 = 0; q0 < P; q0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < P) v[u] = src[(q0 + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < P) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
+      }
+  }
+  float* d = S + gi * lds + gj;
+  if (vec_s && gj + 3 <= gi) {
+    float4 o = *reinterpret_cast<float4*>(d);
+    o.x += s.x;
+    o.y += s.y;
+    o.z += s.z;
+    o.w += s.w;
+    *reinterpret_cast<float4*>(d) = o;
+  } else {
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (gj + u <= gi) d[u] += sv[u];
   }
 }
 
@@ -613,9 +641,10 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
                        stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens / fp.P, fp.P, S,
                        lds, part, fp.ntiles, n / FT_I);
     if (fp.P > 1) {
+      const int vec_s = (reinterpret_cast<uintptr_t>(S) % 16 == 0) && lds % 4 == 0;
       hipLaunchKernelGGL(reduce_full_partials_kernel,
                          dim3((unsigned)(fp.ntiles * (FT_I * FT_J / 1024))), dim3(256), 0, stream,
-                         part, fp.P, fp.ntiles, S, lds);
+                         part, fp.P, fp.ntiles, S, lds, vec_s);
     }
     return hipGetLastError();
   }

@@ -189,6 +189,9 @@ __global__ void iota_kernel(int32_t* __restrict__ perm, int64_t n) {
 }
 
 // A[a][b] (a >= b) = H_d[perm[n-1-a]][perm[n-1-b]], H = 2S (lower of S authoritative).
+// 32 x 32 tiles of A through LDS: without reordering, entry (a, b) comes from
+// S[n-1-b][n-1-a], so the tile is read along rows of S (lanes along a) and
+// written along rows of A (lanes along b).
 __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ S, int64_t n,
                                                       int64_t lds,
                                                       const int32_t* __restrict__ perm,
@@ -196,20 +199,30 @@ __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ 
                                                       const double* __restrict__ lam,
                                                       double* __restrict__ A,
                                                       int32_t* __restrict__ info) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ double tile[32][33];  // [b - b0][a - a0]
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t a0 = (int64_t)blockIdx.y * 32, b0 = (int64_t)blockIdx.x * 32;
+  if (b0 > a0) return;  // the whole tile lies above the diagonal
   const double l = *lam;
-  for (int64_t a = blockIdx.y; a < n; a += gridDim.y) {
-    if (b > a) continue;
-    const int64_t p = perm[n - 1 - a], q = perm[n - 1 - b];
-    double v;
-    if (a == b) {
-      v = diag[p] + l;
-    } else {
-      const float s = p > q ? S[p * lds + q] : S[q * lds + p];
-      if (!isfinite(s)) *info = -1;
-      v = 2.0 * (double)s;
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t a = a0 + tx, b = b0 + r;
+    double v = 0.0;
+    if (a < n && b <= a) {
+      const int64_t p = perm[n - 1 - a], q = perm[n - 1 - b];
+      if (a == b) {
+        v = diag[p] + l;
+      } else {
+        const float sv = p > q ? S[p * lds + q] : S[q * lds + p];
+        if (!isfinite(sv)) *info = -1;
+        v = 2.0 * (double)sv;
+      }
     }
-    A[a * n + b] = v;
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t a = a0 + r, b = b0 + tx;
+    if (a < n && b <= a) A[a * n + b] = tile[tx][r];
   }
 }
 
@@ -558,9 +571,12 @@ __global__ __launch_bounds__(256) void node_kernel(const double* __restrict__ A,
     const int sh = half ? s2 : s1;
     const int64_t oh = half ? o2 : off;
     node64(half ? &B3[0][0] : &B0[0][0], &B1[0][0], sh, cbuf, xbuf, n, oh, info);  // X11 / X22 -> B1
+    // the diagonal block of X, its upper part as zeros: the products read
+    // triangular operands by whole tiles of 32 or 64 inside these blocks
     for (int e = tid; e < NB * NB; e += 256) {
       const int i = e / NB, j = e % NB;
-      if (i < sh && j <= i) X[(oh + i) * n + oh + j] = B1[i][j];
+      if (i < sh && j < sh) X[(oh + i) * n + oh + j] = j <= i ? B1[i][j] : 0.0;
+      if (half == 0 && i < s1 && j < s2) X[(off + i) * n + o2 + j] = 0.0;
     }
     if (s2 <= 0) return;
     f64x4 acc[2][2];
@@ -914,12 +930,6 @@ hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t 
   return hipGetLastError();
 }
 
-__global__ void fill_f64_kernel(double* __restrict__ p, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t k = i; k < count; k += stride) p[k] = 0.0;
-}
-
 // X's blocks below the diagonal inside rows o .. o + s1 + s2: join the
 // inverted neighbours [o, o + s1) and [o + s1, o + s1 + s2) through the
 // panel L21 that sits where X21 goes.
@@ -1064,12 +1074,10 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, pm, n);
   }
   {
-    const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(n, 2048));
+    const dim3 grid((unsigned)ceil_div(n, 32), (unsigned)ceil_div(n, 32));
     hipLaunchKernelGGL(build_a_kernel, grid, dim3(256), 0, stream, S, n, lds, pm, w.diag, w.lam,
                        w.A, info);
   }
-  // X's strict upper triangle must read as zero for the 128-wide GEMM tiles
-  hipLaunchKernelGGL(fill_f64_kernel, dim3(2048), dim3(256), 0, stream, w.X, n * n);
   SideStream* side = nullptr;
   hipError_t e = side_stream(side);
   if (e != hipSuccess) return e;

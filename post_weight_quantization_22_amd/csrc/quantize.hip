@@ -77,6 +77,41 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(const void* __restric
   }
 }
 
+// The same for bf16 W in column order (no desc_act) with 16-byte aligned rows
+// and n % 8 == 0: 8 columns per thread, 16-byte loads and stores.
+__global__ __launch_bounds__(256) void prep_weights_bf16_kernel(const uint16_t* __restrict__ W,
+                                                                int64_t m, int64_t n,
+                                                                int64_t ldw,
+                                                                const uint8_t* __restrict__ dead,
+                                                                float* __restrict__ Wp,
+                                                                int32_t* __restrict__ info) {
+  const int64_t c = 8 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (c >= n) return;
+  bool dz[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) dz[t] = dead && dead[c + t];
+  bool bad = false;
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + r * ldw + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f[2 * t] = __uint_as_float(w[t] << 16);
+      f[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bad |= !isfinite(f[t]);
+      if (dz[t]) f[t] = 0.0f;
+    }
+    float4* o = reinterpret_cast<float4*>(Wp + r * n + c);
+    o[0] = make_float4(f[0], f[1], f[2], f[3]);
+    o[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  if (bad && info) *info = -1;
+}
+
 // One group per row: parameters from the whole row.
 __global__ __launch_bounds__(256) void row_params_kernel(const float* __restrict__ Wp, int64_t m,
                                                          int64_t n, float maxq, int sym,
@@ -523,7 +558,12 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   const int64_t ngroups = G > 0 ? ceil_div(n, G) : 1;
 
   if (a.info) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(1), 0, stream, a.info, 0);
-  {
+  if (a.wdt == GPTQ_BF16 && !a.desc_act && n % 8 == 0 && a.ldw % 8 == 0 &&
+      reinterpret_cast<uintptr_t>(a.W) % 16 == 0) {
+    const dim3 grid((unsigned)ceil_div(n, 8 * 256), (unsigned)hmin(m, 1024));
+    hipLaunchKernelGGL(prep_weights_bf16_kernel, grid, dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(a.W), m, n, a.ldw, a.dead, Wp, a.info);
+  } else {
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(m, 1024));
     hipLaunchKernelGGL(prep_weights_kernel, grid, dim3(256), 0, stream, a.W, a.wdt, m, n, a.ldw,
                        a.desc_act ? a.perm : nullptr, a.dead, Wp, a.info);
