@@ -49,21 +49,10 @@ __device__ __forceinline__ void tile_coords(int64_t L, int64_t& ti, int64_t& tj)
   tj = L - t * (t + 1) / 2;
 }
 
-// Work order of the interior kernel.  Workgroup b runs on XCD b % 8; the
-// units (split p, tile) are dealt so that XCD x takes a contiguous range of
-// them: whole token splits when P is a multiple of 8, and within a split the
-// lower-triangle tiles by 4 x 4 super-tiles (rows of super-tiles, then rows
-// of tiles), so the ~32 workgroups in flight on one XCD read the same token
-// rows of a few channel blocks and share them through that XCD's L2.
-// Super-tile order needs T % 4 == 0; otherwise tiles go row by row.
-__device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64_t& p,
-                                          int64_t& ti, int64_t& tj) {
-  const int64_t ntiles = T * (T + 1) / 2;
-  const int64_t U = ntiles * P;
-  const int64_t U8 = (U / 8) * 8;
-  const int64_t u = b < U8 ? (b % 8) * (U8 / 8) + b / 8 : b;
-  p = u / ntiles;
-  const int64_t Lb = u % ntiles;
+// Order of the lower-triangle tiles for the interior kernel: by 4 x 4
+// super-tiles (rows of super-tiles, then rows of tiles), so that consecutive
+// tiles share few channel blocks; needs T % 4 == 0, else tiles go row by row.
+__device__ __forceinline__ void tile_of_order(int64_t Lb, int64_t T, int64_t& ti, int64_t& tj) {
   if (T % 4 != 0) {
     tile_coords(Lb, ti, tj);
     return;
@@ -86,6 +75,42 @@ __device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64
   }
   ti = 4 * bi + li;
   tj = 4 * bj + lj;
+}
+
+// Position of tile (ti, tj) in that order.
+__device__ __forceinline__ int64_t order_of_tile(int64_t ti, int64_t tj, int64_t T) {
+  if (T % 4 != 0) return ti * (ti + 1) / 2 + tj;
+  const int64_t bi = ti / 4, bj = tj / 4, li = ti % 4, lj = tj % 4;
+  const int64_t base = 8 * bi * bi + 2 * bi;
+  return bj < bi ? base + 16 * bj + 4 * li + lj : base + 16 * bi + li * (li + 1) / 2 + lj;
+}
+
+// Work units of the interior kernel.  The first ntiles - T2 tiles (in the
+// order above) are split P ways over the tokens, the last T2 tiles 2P ways
+// into half-length units, which run last: T2 is chosen so that the full
+// units fill whole rounds of 256 workgroups and the half units the rest, so
+// no CU idles through a last, partly filled round of full units.  Workgroup
+// b runs on XCD b % 8; each kind of unit is dealt so that XCD x takes a
+// contiguous range of it: whole token splits per XCD when the split count is
+// a multiple of 8, and so the ~32 workgroups in flight on one XCD read the
+// same token rows of a few channel blocks and share them through its L2.
+// half: the unit is a half-length one; slot: its partial tile.
+__device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64_t T2,
+                                          int64_t& p, int64_t& ti, int64_t& tj, bool& half,
+                                          int64_t& slot) {
+  const int64_t ntiles = T * (T + 1) / 2;
+  const int64_t n1 = ntiles - T2;
+  const int64_t U1 = n1 * P;
+  half = b >= U1;
+  const int64_t bb = half ? b - U1 : b;
+  const int64_t U = half ? T2 * 2 * P : U1;
+  const int64_t U8 = (U / 8) * 8;
+  const int64_t u = bb < U8 ? (bb % 8) * (U8 / 8) + bb / 8 : bb;
+  const int64_t nt = half ? T2 : n1;
+  p = u / nt;
+  const int64_t Lb = (half ? n1 : 0) + u % nt;
+  tile_of_order(Lb, T, ti, tj);
+  slot = half ? P * ntiles + p * T2 + (Lb - n1) : p * ntiles + ti * (ti + 1) / 2 + tj;
 }
 
 // One lane's share of a stage for one operand: 8 tokens x 8 channels.
@@ -306,19 +331,20 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 
 __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
-                                                            int64_t ldx, int64_t tok_per_split,
-                                                            int64_t P, float* __restrict__ S,
-                                                            int64_t lds,
+                                                            int64_t ldx, int64_t tokens,
+                                                            int64_t P, int64_t T2,
+                                                            float* __restrict__ S, int64_t lds,
                                                             float* __restrict__ part,
-                                                            int64_t ntiles, int64_t ntiles_edge) {
+                                                            int64_t ntiles_edge) {
   __shared__ __align__(16) uint8_t smem[4 * DSTAGE];  // [buffer][operand]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   constexpr int RPW = HK / 8;  // token rows loaded per wave per operand
   const int wr = wv >> 2, wc = wv & 3;
-  int64_t p, ti, tj;
-  hess_unit(blockIdx.x, P, ntiles_edge, p, ti, tj);
-  const int64_t L = ti * (ti + 1) / 2 + tj;  // row-major index of the partial tile
+  int64_t p, ti, tj, slot;
+  bool half;
+  hess_unit(blockIdx.x, P, ntiles_edge, T2, p, ti, tj, half, slot);
+  const int64_t tok_per_split = half ? tokens / (2 * P) : tokens / P;
   const int64_t i0 = ti * FT_I, j0 = tj * FT_J;
   const bool diag = ti == tj;
   const bool idle = diag && WJ * wc >= WI * (wr + 1);  // block wholly above the diagonal
@@ -439,7 +465,7 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
         const int ii = WI * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         const int jj = WJ * wc + 32 * b + (lane & 31);
         if (part) {
-          part[((p * ntiles + L) * FT_I + ii) * FT_J + jj] = acc[a][b][q];
+          part[(slot * FT_I + ii) * FT_J + jj] = acc[a][b][q];
         } else if (jj + j0 <= ii + i0) {
           S[(i0 + ii) * lds + j0 + jj] += acc[a][b][q];
         }
@@ -450,10 +476,12 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
 // Each thread sums 4 consecutive entries of a tile row (16-byte loads, the
 // loads of 8 splits in flight before their in-order adds).
 __global__ __launch_bounds__(256) void reduce_full_partials_kernel(const float* __restrict__ part,
-                                                                   int64_t P, int64_t ntiles,
+                                                                   int64_t P, int64_t T2,
+                                                                   int64_t T,
                                                                    float* __restrict__ S,
                                                                    int64_t lds, int vec_s) {
   constexpr int CH = FT_I * FT_J / 1024;
+  const int64_t ntiles = T * (T + 1) / 2;
   const int64_t L = blockIdx.x / CH;
   const int64_t chunk = blockIdx.x % CH;
   int64_t ti, tj;
@@ -462,17 +490,23 @@ __global__ __launch_bounds__(256) void reduce_full_partials_kernel(const float* 
   const int ii = e / FT_J, jj = e % FT_J;
   const int64_t gi = ti * FT_I + ii, gj = tj * FT_J + jj;
   if (gj > gi) return;  // the whole quad lies above the diagonal
-  const float4* src = reinterpret_cast<const float4*>(part + L * FT_I * FT_J + e);
-  const int64_t stride = ntiles * (FT_I * FT_J / 4);  // float4s from one split to the next
+  // this tile's partials: P full splits, or 2P half splits for the last T2 tiles
+  const int64_t Lb = order_of_tile(ti, tj, T), n1 = ntiles - T2;
+  const bool halves = Lb >= n1;
+  const int64_t first = halves ? P * ntiles + (Lb - n1) : L;
+  const int64_t nq = halves ? 2 * P : P;
+  const float4* src = reinterpret_cast<const float4*>(part + first * FT_I * FT_J + e);
+  // float4s from one split to the next
+  const int64_t stride = (halves ? T2 : ntiles) * (FT_I * FT_J / 4);
   float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int64_t q0 = 0; q0 < P; q0 += 8) {
+  for (int64_t q0 = 0; q0 < nq; q0 += 8) {
     float4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (q0 + u < P) v[u] = src[(q0 + u) * stride];
+      if (q0 + u < nq) v[u] = src[(q0 + u) * stride];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (q0 + u < P) {
+      if (q0 + u < nq) {
         s.x += v[u].x;
         s.y += v[u].y;
         s.z += v[u].z;
@@ -581,36 +615,49 @@ HessPlan plan_bf16(int64_t n, int64_t tokens) {
 // Interior tiling (256 x 256 tiles of the lower triangle).  P = 0: not usable
 // for these sizes (n not a multiple of 256, or not whole 64-token stages).
 struct FullPlan {
-  int64_t ntiles, P;
+  int64_t ntiles, P, T2;
   size_t ws;
 };
 
 FullPlan plan_full(int64_t n, int64_t tokens) {
-  FullPlan fp{0, 0, 0};
+  FullPlan fp{0, 0, 0, 0};
   if (n % FT_I != 0) return fp;
   const int64_t T = n / FT_I;
   fp.ntiles = T * (T + 1) / 2;
   // Token split, one split per XCD (P a multiple of 8).  With one workgroup
-  // per CU the grid runs in ceil(ntiles P / 256) rounds of tokens / P tokens
-  // each; more splits fill the last round better but write and re-read more
-  // partial tiles (256 KB each).  Time model fitted to n = 4096 with 8 to 32
-  // splits: ~33 ns per token per round, ~0.35 us per partial tile.
-  int64_t P = 1;
+  // per CU the grid runs in rounds of 256 units of tokens / P tokens each;
+  // more splits fill the rounds better but write and re-read more partial
+  // tiles (256 KB each).  T2 tiles split 2P ways make the last round one of
+  // half-length units.  Time model fitted to n = 4096 with 8 to 32 splits:
+  // ~30 ns per token per round, ~0.055 us per partial tile (its reduction).
+  int64_t P = 1, T2 = 0;
   if (fp.ntiles <= 2048 && tokens % (8 * HK) == 0 && tokens >= 8 * 512) {
     double best = 0.0;
     for (int64_t c = 8; c <= 32; c *= 2) {
       if (tokens % (c * HK) != 0) break;
-      const double t = (double)ceil_div(fp.ntiles * c, 256) * (double)(tokens / c) * 33e-9 +
-                       (double)(c * fp.ntiles) * 0.35e-6;
-      if (P == 1 || t < best) {
-        P = c;
-        best = t;
+      const double per_round = (double)(tokens / c) * 30e-9;
+      for (int h = 0; h < 2; ++h) {
+        int64_t t2 = 0;
+        if (h == 1) {
+          if (tokens % (2 * c * HK) != 0) continue;
+          t2 = fp.ntiles % (256 / c);
+          if (t2 == 0) continue;
+        }
+        const double rounds = (double)ceil_div((fp.ntiles - t2) * c, 256) +
+                              0.5 * (double)ceil_div(t2 * 2 * c, 256);
+        const double t = rounds * per_round + (double)(c * fp.ntiles + c * t2) * 0.055e-6;
+        if (P == 1 || t < best) {
+          P = c;
+          T2 = t2;
+          best = t;
+        }
       }
     }
   }
   if (tokens % (P * HK) != 0) return fp;
   fp.P = P;
-  fp.ws = P > 1 ? (size_t)P * fp.ntiles * FT_I * FT_J * sizeof(float) : 0;
+  fp.T2 = T2;
+  fp.ws = P > 1 ? (size_t)(P * fp.ntiles + 2 * P * T2) * FT_I * FT_J * sizeof(float) : 0;
   return fp;
 }
 
@@ -637,14 +684,15 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
   if (interior) {
     if (ws_bytes < fp.ws) return hipErrorInvalidValue;
     float* part = fp.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-    hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)(fp.ntiles * fp.P)), dim3(512), 0,
-                       stream, reinterpret_cast<const uint16_t*>(X), ldx, tokens / fp.P, fp.P, S,
-                       lds, part, fp.ntiles, n / FT_I);
+    const int64_t units = (fp.ntiles - fp.T2) * fp.P + fp.T2 * 2 * fp.P;
+    hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)units), dim3(512), 0, stream,
+                       reinterpret_cast<const uint16_t*>(X), ldx, tokens, fp.P, fp.T2, S, lds,
+                       part, n / FT_I);
     if (fp.P > 1) {
       const int vec_s = (reinterpret_cast<uintptr_t>(S) % 16 == 0) && lds % 4 == 0;
       hipLaunchKernelGGL(reduce_full_partials_kernel,
                          dim3((unsigned)(fp.ntiles * (FT_I * FT_J / 1024))), dim3(256), 0, stream,
-                         part, fp.P, fp.ntiles, S, lds, vec_s);
+                         part, fp.P, fp.T2, n / FT_I, S, lds, vec_s);
     }
     return hipGetLastError();
   }

@@ -17,6 +17,8 @@ HESS_CASES = [
     (256, 1024, 1024, "f32"),     # fp32 activations (SIMT path)
     (130, 77, 77, "f32"),
     (1024, 4096, 2048, "bf16"),
+    (1280, 8192, 2048, "bf16"),   # 5x5 tiles (row-major tile order), some tiles in half-length splits
+    (2048, 16384, 2048, "bf16"),  # 8x8 tiles (super-tile order), some tiles in half-length splits
 ]
 
 
