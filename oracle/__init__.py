@@ -19,7 +19,8 @@ It is a plain, slow, obviously-correct restatement of the method on these pages:
 * "Calibration algorithms guide" (bhfrc.com news 5741): §2.2 (group-wise
   min-max), §2.3 (GPTQ order by descending Hessian diagonal, block size).
 * "Quantized deployment, 1.5 TB to 250 GB" (lmnt.cn news 123823): §2.1
-  (dequantization r = (q - zero_point) * scale).
+  (dequantization r = (q - zero_point) * scale), used by the dequantized-weight
+  product of "LLM quantization principles" §5.2.
 * "AWQ, MinMax, GPTQ calibration in Model Optimizer" (gtnt.cn news 115337):
   §4 (block_size a multiple of group_size, perc_damp 0.01).
 
@@ -53,3 +54,4 @@ from .gptq import (  # noqa: F401
     replay_check,
 )
 from .pack import pack_ref, unpack_ref  # noqa: F401
+from .dequant import dequant_weights, dequant_matmul  # noqa: F401

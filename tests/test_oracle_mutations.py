@@ -19,10 +19,12 @@ GPTQ_MOD = sys.modules["oracle.gptq"]
 HESS_MOD = sys.modules["oracle.hessian"]
 PREP_MOD = sys.modules["oracle.prepare"]
 QUANT_MOD = sys.modules["oracle.quantizer"]
+DEQ_MOD = sys.modules["oracle.dequant"]
 
 import test_oracle_gptq as tg
 import test_oracle_hessian_prepare as th
 import test_oracle_quantizer as tq
+import test_oracle_dequant as td
 
 
 def _mutant(mod, old, new):
@@ -69,6 +71,14 @@ MUTANTS = [
      lambda gd: th.test_prepare_factor_properties()),
     (HESS_MOD, "S += X64.T @ X64", "S += X64.T @ X64 - np.diag(np.diag(X64.T @ X64)) * 0.5",
      ["hessian_S"], lambda gd: th.test_hessian_term_by_term()),
+    (DEQ_MOD, "return s * (q - z)", "return s * (q + z)", ["dequant_matmul"],
+     lambda gd: td.test_codes_at_zero_point_give_zero()),
+    (DEQ_MOD, "return np.asarray(X, dtype=np.float64) @ Wq.T",
+     "return np.asarray(X, dtype=np.float64) @ Wq[:, ::-1].T", ["dequant_matmul"],
+     lambda gd: td.test_dequant_matmul_brute_force(4)),
+    (DEQ_MOD, "s = np.asarray(scales, dtype=np.float64)[:, g]",
+     "s = np.asarray(scales, dtype=np.float64)[:, np.sort(g)]", ["dequant_matmul"],
+     lambda gd: td.test_dequant_matmul_brute_force(3)),
 ]
 
 
