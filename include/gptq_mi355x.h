@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00010000u /* major 1, minor 0 */
+#define GPTQ_ABI_VERSION 0x00010001u /* major 1, minor 1 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -155,6 +155,49 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_
  * ---------------------------------------------------------------------- */
 gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int32_t bits,
                       uint32_t* packed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Packing in processing order: the layout of gptq_pack applied to the row
+ * codes[r, perm[0]], codes[r, perm[1]], ..., so that stream position p holds
+ * the code of original column perm[p] (perm as gptq_prepare returns it; NULL =
+ * the identity, i.e. gptq_pack).  With desc_act the quantization groups are
+ * runs of group_size consecutive processing positions ("GPTQ deep dive",
+ * section 3.3), which is the form gptq_dequant_gemm reads.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_pack_ordered(const uint8_t* codes, int64_t m, int64_t n, int32_t bits,
+                              const int32_t* perm, uint32_t* packed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dequantized-weight product -- "Quantized deployment, 1.5 TB to 250 GB"
+ * (lmnt.cn news 123823), section 2.1 (a code q stands for (q - zero) * scale)
+ * and "LLM quantization principles", section 5.2 (low-bit weights are
+ * dequantized for the matrix product; fusing the two keeps the cost down):
+ *
+ *   Y[t, r] = sum_c X[t, c] * scale[r, g(c)] * (q[r, c] - zero[r, g(c)])
+ *
+ * X[tokens, n] bf16, row stride ldx >= n; without perm, ldx must be a
+ * multiple of 8 and X 16-byte aligned (it is read in 16-byte vectors).
+ * packed[m, ldp] uint32 (ldp >= ceil(n * bits / 32)): the codes packed in
+ * processing order by gptq_pack_ordered with this same perm.  scales, zeros
+ * [m, ngroups] fp32 as gptq_quantize_layer writes them: group k covers
+ * processing positions [k * group_size, (k + 1) * group_size); group_size is
+ * a multiple of 8, or -1 for one group per row.  perm[n] (may be NULL =
+ * identity): processing position -> original column.  Y[tokens, ldy] fp32 or
+ * bf16 (ydt); Y must not overlap the inputs.  bits 2..8; xdt must be BF16
+ * (GPTQ_ERR_UNSUPPORTED otherwise).
+ * Arithmetic: each weight is formed in fp32 as fma(q, scale, -(zero * scale)),
+ * rounded to bf16 (nearest even), multiplied exactly by the bf16 activation,
+ * and the products are summed in fp32 (in a fixed order: deterministic).
+ * Workspace: gptq_dequant_gemm_workspace_size(tokens, m, n, perm != NULL)
+ * bytes (may be 0).  tokens == 0 or m == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_dequant_gemm_workspace_size(int64_t tokens, int64_t m, int64_t n,
+                                             int32_t has_perm, size_t* bytes);
+gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                              int64_t ldx, const uint32_t* packed, int64_t ldp, int32_t bits,
+                              int32_t group_size, const float* scales, const float* zeros,
+                              const int32_t* perm, int64_t m, void* Y, gptq_dtype ydt,
+                              int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Round-to-nearest baseline -- "GPTQ deep dive", section 1.2 (RTN rounds each

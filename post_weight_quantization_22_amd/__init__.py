@@ -13,9 +13,12 @@ from ._lib import (  # noqa: F401
     GPTQConfig,
     GPTQError,
     gptq_abi_version,
+    gptq_dequant_gemm,
+    gptq_dequant_gemm_workspace_size,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_size,
     gptq_pack,
+    gptq_pack_ordered,
     gptq_prepare,
     gptq_prepare_workspace_size,
     gptq_quantize_layer,

@@ -36,6 +36,9 @@ EXPORTED = (
     "gptq_quantize_workspace_size",
     "gptq_quantize_layer",
     "gptq_pack",
+    "gptq_pack_ordered",
+    "gptq_dequant_gemm_workspace_size",
+    "gptq_dequant_gemm",
     "rtn_minmax",
 )
 
@@ -97,6 +100,13 @@ def load() -> ctypes.CDLL:
                                         _vp, _sz, _vp]
     lib.gptq_pack.restype = _i32
     lib.gptq_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+    lib.gptq_pack_ordered.restype = _i32
+    lib.gptq_pack_ordered.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _vp]
+    lib.gptq_dequant_gemm_workspace_size.restype = _i32
+    lib.gptq_dequant_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]
+    lib.gptq_dequant_gemm.restype = _i32
+    lib.gptq_dequant_gemm.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp,
+                                      _vp, _vp, _i64, _vp, _i32, _i64, _vp, _sz, _vp]
     lib.rtn_minmax.restype = _i32
     lib.rtn_minmax.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
     _lib = lib
@@ -226,6 +236,38 @@ def gptq_pack(codes, bits: int, packed, stream=None) -> None:
     m, n = codes.shape
     _check(load().gptq_pack(_ptr(codes), m, n, int(bits), _ptr(packed), _stream(stream)),
            "gptq_pack")
+
+
+def gptq_pack_ordered(codes, bits: int, perm, packed, stream=None) -> None:
+    """packed[r] = codes[r, perm[0]], codes[r, perm[1]], ... in the gptq_pack layout."""
+    m, n = codes.shape
+    _check(load().gptq_pack_ordered(_ptr(codes), m, n, int(bits), _ptr(perm), _ptr(packed),
+                                    _stream(stream)),
+           "gptq_pack_ordered")
+
+
+def gptq_dequant_gemm_workspace_size(tokens: int, m: int, n: int, has_perm: bool) -> int:
+    out = _sz(0)
+    _check(load().gptq_dequant_gemm_workspace_size(tokens, m, n, int(bool(has_perm)),
+                                                   ctypes.byref(out)),
+           "gptq_dequant_gemm_workspace_size")
+    return out.value
+
+
+def gptq_dequant_gemm(X, packed, bits: int, group_size: int, scales, zeros, Y, perm=None,
+                      ws=None, stream=None) -> None:
+    """Y[tokens, m] = X[tokens, n] W_q^T with W_q from processing-order packed codes."""
+    tokens, n = X.shape
+    m = packed.shape[0]
+    if ws is None:
+        ws = _workspace(gptq_dequant_gemm_workspace_size(tokens, m, n, perm is not None),
+                        X.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().gptq_dequant_gemm(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(packed),
+                                    _ld(packed), int(bits), int(group_size), _ptr(scales),
+                                    _ptr(zeros), _ptr(perm), m, _ptr(Y), _dtype_code(Y), _ld(Y),
+                                    _ptr(ws), nbytes, _stream(stream)),
+           "gptq_dequant_gemm")
 
 
 def rtn_minmax(W, bits: int, group_size: int, codes, scales, zeros, sym: bool = False,

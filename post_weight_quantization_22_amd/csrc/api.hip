@@ -138,7 +138,64 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int32_t bits, 
   if (bad_dim(m) || bad_dim(n) || bits < 1 || bits > 8) return GPTQ_ERR_INVALID_ARG;
   if (m == 0 || n == 0) return GPTQ_OK;
   if (!codes || !packed) return GPTQ_ERR_INVALID_ARG;
-  return hip_status(launch_pack(codes, m, n, bits, packed, stream));
+  return hip_status(launch_pack(codes, m, n, bits, nullptr, packed, stream));
+}
+
+gptq_status gptq_pack_ordered(const uint8_t* codes, int64_t m, int64_t n, int32_t bits,
+                              const int32_t* perm, uint32_t* packed, hipStream_t stream) {
+  if (bad_dim(m) || bad_dim(n) || bits < 1 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (!codes || !packed) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_pack(codes, m, n, bits, perm, packed, stream));
+}
+
+gptq_status gptq_dequant_gemm_workspace_size(int64_t tokens, int64_t m, int64_t n,
+                                             int32_t has_perm, size_t* bytes) {
+  if (!bytes || tokens < 0 || bad_dim(tokens) || bad_dim(m) || bad_dim(n) ||
+      (has_perm != 0 && has_perm != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  *bytes = (tokens == 0 || m == 0 || n == 0) ? 0 : dequant_gemm_ws_bytes(tokens, m, n, has_perm);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                              int64_t ldx, const uint32_t* packed, int64_t ldp, int32_t bits,
+                              int32_t group_size, const float* scales, const float* zeros,
+                              const int32_t* perm, int64_t m, void* Y, gptq_dtype ydt,
+                              int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (tokens < 0 || bad_dim(tokens) || bad_dim(m) || n <= 0 || bad_dim(n) || bits < 2 ||
+      bits > 8 || !valid_dtype(xdt) || !valid_dtype(ydt) ||
+      !(group_size == -1 || (group_size >= 8 && group_size % 8 == 0)))
+    return GPTQ_ERR_INVALID_ARG;
+  if (xdt != GPTQ_BF16) return GPTQ_ERR_UNSUPPORTED;
+  if (tokens == 0 || m == 0) return GPTQ_OK;
+  if (!X || !packed || !scales || !zeros || !Y || ldx < n || ldp < ceil_div(n * bits, 32) ||
+      ldy < m)
+    return GPTQ_ERR_INVALID_ARG;
+  // X is read with 16-byte loads unless the permutation gathers it first
+  if (!perm && (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0))
+    return GPTQ_ERR_INVALID_ARG;
+  const gptq_status w =
+      check_ws(ws, ws_bytes, dequant_gemm_ws_bytes(tokens, m, n, perm != nullptr ? 1 : 0));
+  if (w != GPTQ_OK) return w;
+  DequantArgs d;
+  d.X = X;
+  d.tokens = tokens;
+  d.n = n;
+  d.ldx = ldx;
+  d.packed = packed;
+  d.ldp = ldp;
+  d.bits = bits;
+  d.group_size = group_size;
+  d.scales = scales;
+  d.zeros = zeros;
+  d.perm = perm;
+  d.m = m;
+  d.Y = Y;
+  d.ydt = ydt;
+  d.ldy = ldy;
+  d.ws = ws;
+  return hip_status(launch_dequant_gemm(d, stream));
 }
 
 gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,

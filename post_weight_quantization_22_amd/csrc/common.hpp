@@ -54,6 +54,44 @@ __device__ __forceinline__ float quant_code(float w, float scale, float zero, fl
 
 __device__ __forceinline__ bool is_finite(float x) { return isfinite(x); }
 
+// LDS DMA of 16 (4) bytes per lane: lane l's bytes land at lds + 16 l (4 l),
+// read from sbase + voff (wave-uniform 64-bit base in SGPRs, per-lane 32-bit
+// byte offset).  Issued from asm: the compiler cannot tell this LDS write from
+// the LDS reads of other buffers and would otherwise wait for it before each
+// of them; completion is awaited explicitly (vmcnt) before the barrier that
+// publishes the data.  The instruction writes no VGPR (its data goes to LDS)
+// and its address registers are consumed at issue.  M0, the LDS base of the
+// transfer, is read at issue; it is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// LDS byte address of a __shared__ object (wave-uniform), for M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p));
+}
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
 inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }

@@ -1,0 +1,772 @@
+// Dequantized-weight matrix product Y = X W_q^T (16-bit activations, b-bit weights).
+//
+// "Quantized deployment, 1.5 TB to 250 GB" (lmnt.cn news 123823), section 2.1:
+// a stored code q becomes the real value (q - zero_point) * scale.  "LLM
+// quantization principles: GPTQ, AWQ, GGUF" (0539edu.com news 6111416), section
+// 5.2: low-bit weights are turned back into 16-bit values before the product,
+// and doing both in one operator is what keeps the dequantization from eating
+// the bandwidth the small weights save.  This is that fused operator:
+//
+//   Y[t, r] = sum_p Xp[t, p] * w[r, p],   w[r, p] = bf16(fma(q[r, p], s, -(z * s)))
+//
+// with p the processing position (the weights are packed in processing order,
+// so the groups of a row are runs of G consecutive positions), s = scale[r, p/G],
+// z = zero[r, p/G] and Xp[t, p] = X[t, perm[p]] (X itself when perm is null).
+//
+// Work split.  A workgroup owns a BM x BN tile of Y (BM tokens, BN weight rows)
+// and walks the 64-position chunks of its K range:
+//   - the X tile (BM x 64 bf16) is loaded with 16-byte vector loads;
+//   - the weight tile (BN x 64) arrives as packed words (2b words per row and
+//     chunk, so every chunk starts on a word) and each of 2 BN threads turns 32
+//     codes into bf16 in registers: the dequantization runs once per weight and
+//     workgroup and is shared by its BM tokens;
+//   - both tiles go to LDS (double-buffered, one barrier per chunk) in rows of
+//     128 B whose 16-byte segments are XOR-swizzled by the row, so the MFMA
+//     operand reads (8 consecutive positions of 32 rows) are free of bank
+//     conflicts;
+//   - waves of WM x WN run v_mfma_f32_32x32x16_bf16 on the tiles: exact bf16
+//     products, fp32 accumulation; the loads of chunk j + 1 are in flight while
+//     chunk j is multiplied.
+// Decode-sized batches (a handful of tokens) are bound by the packed weights'
+// HBM traffic; there the K range is split so the grid covers every CU, and the
+// splits' fp32 partial sums are added in split order by a second kernel
+// (deterministic).  Tiles are dealt to XCDs in contiguous runs, so the
+// workgroups of one XCD share a token block (prefill) in its L2.
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;         // positions per chunk
+constexpr int ROWB = BK * 2;   // bytes of one LDS tile row
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int seg_off(int r, int s) { return r * ROWB + ((s ^ (r & 7)) << 4); }
+
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Code i (0..31) of a 32-code run held in BITS words, as fp32.
+template <int BITS>
+__device__ __forceinline__ float code_f32(const uint32_t (&w)[BITS], int i) {
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  if constexpr (BITS == 1 || BITS == 2 || BITS == 4 || BITS == 8) {
+    // BITS divides 8: code i is field (i % PER) of byte (i / PER) of its word,
+    // so masking a whole word leaves one code per byte (v_cvt_f32_ubyteN)
+    constexpr int PER = 8 / BITS;
+    constexpr int CPW = 32 / BITS;
+    const uint32_t word = w[i / CPW];
+    const int k = i % CPW;
+    const uint32_t spread = (word >> ((k % PER) * BITS)) & (MASK * 0x01010101u);
+    return (float)((spread >> (8 * (k / PER))) & 0xFFu);
+  } else {
+    const int bit = i * BITS, wi = bit >> 5, off = bit & 31;
+    uint32_t q;
+    if (off + BITS <= 32) {
+      q = (w[wi] >> off) & MASK;
+    } else {
+      q = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off) & MASK;
+    }
+    return (float)q;
+  }
+}
+
+struct DqArgs {
+  const uint16_t* X;  // [tokens, ldx] bf16, 16-byte aligned, ldx % 8 == 0
+  int64_t ldx, tokens, n;
+  const uint32_t* P;  // [m, ldp] packed codes in processing order
+  int64_t ldp, nwr;   // nwr = ceil(n * bits / 32) words of a row
+  const float* scales;
+  const float* zeros;
+  int64_t ngroups, G;  // G <= 0: one group per row
+  int gshift;          // log2(G) when G is a power of two, else -1
+  int gs_run;          // 1 when every 32-position run lies in one group
+  int64_t m;
+  void* Y;  // [tokens, ldy] fp32 or bf16
+  int64_t ldy;
+  int ybf16;
+  float* part;  // [ks, tokens, m] fp32 partial sums when ks > 1
+  int64_t ntb, nrb, ks, chunks_per_split, nchunks, ntiles;
+};
+
+template <int BITS, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dequant_gemm_kernel(DqArgs a) {
+  constexpr int NWN = BN / WN;
+  constexpr int NT = (BM / WM) * NWN * 64;
+  constexpr int XSEG = BM * 8;               // 16-byte X segments per chunk
+  constexpr int XPT = (XSEG + NT - 1) / NT;  // per thread
+  constexpr int UNITS = 2 * BN;              // 32-code runs per chunk
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int FA = WM / 32, FB = WN / 32;
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+
+  // contiguous runs of tiles per XCD (workgroup b runs on XCD b % 8)
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, idx = b / kXcds;
+  const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return;
+  const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int64_t rb = L % a.nrb;
+  const int64_t kspl = (L / a.nrb) % a.ks;
+  const int64_t tb = L / (a.nrb * a.ks);
+  const int64_t tok0 = tb * BM, row0 = rb * BN;
+  const int64_t c_begin = kspl * a.chunks_per_split;
+  const int64_t c_end = min(a.nchunks, c_begin + a.chunks_per_split);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / NWN, wn = wv % NWN;
+
+  // ---- per-thread source rows (64-bit pointers formed once) ----
+  const uint16_t* xrow[XPT];
+  bool xlive[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int sid = tid + i * NT;
+    const int64_t t = tok0 + (sid >> 3);
+    xlive[i] = sid < XSEG && t < a.tokens;
+    xrow[i] = a.X + (xlive[i] ? t : 0) * a.ldx + 8 * (sid & 7);
+  }
+  const uint32_t* crow[UPT];
+  const float* srow[UPT];
+  const float* zrow[UPT];
+  bool clive[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int uid = tid + u * NT;
+    const int64_t r = row0 + (uid >> 1);
+    clive[u] = uid < UNITS && r < a.m;
+    const int64_t rr = clive[u] ? r : 0;
+    crow[u] = a.P + rr * a.ldp + (uid & 1) * BITS;
+    srow[u] = a.scales + rr * a.ngroups;
+    zrow[u] = a.zeros + rr * a.ngroups;
+  }
+  const int n32 = (int)a.n, nwr = (int)a.nwr, ng1 = (int)a.ngroups - 1, G = (int)a.G;
+
+  // ---- global -> registers ----
+  uint4 xr[XPT];
+  uint32_t cw[UPT][BITS];
+  float us[UPT][4], unz[UPT][4];
+
+  auto group_of = [&](int p) -> int {
+    if (G <= 0) return 0;
+    const int g = a.gshift >= 0 ? (p >> a.gshift) : p / G;
+    return min(g, ng1);
+  };
+
+  auto load_chunk = [&](int c) {
+    const int k0 = c * BK;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int sid = tid + i * NT;
+      const int col = k0 + 8 * (sid & 7);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (xlive[i] && col < n32) {
+        v = *reinterpret_cast<const uint4*>(xrow[i] + k0);
+        if (col + 8 > n32) {  // last, partial segment: zero the columns past n
+          uint32_t* e = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (col + 2 * q >= n32) e[q] = 0u;
+            else if (col + 2 * q + 1 >= n32) e[q] &= 0xFFFFu;
+          }
+        }
+      }
+      xr[i] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int uid = tid + u * NT;
+      const int h = uid & 1;
+      const int wbase = c * (2 * BITS) + h * BITS;
+      const uint32_t* src = crow[u] + c * (2 * BITS);
+      if (clive[u] && wbase + BITS <= nwr) {
+#pragma unroll
+        for (int q = 0; q < BITS; ++q) cw[u][q] = src[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < BITS; ++q) cw[u][q] = (clive[u] && wbase + q < nwr) ? src[q] : 0u;
+      }
+      const int p0 = k0 + 32 * h;
+      if (a.gs_run) {
+        const int g = group_of(p0);
+        const float sc = clive[u] ? srow[u][g] : 0.0f;
+        const float zz = clive[u] ? zrow[u][g] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          us[u][s] = sc;
+          unz[u][s] = zz;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int g = group_of(p0 + 8 * s);
+          us[u][s] = clive[u] ? srow[u][g] : 0.0f;
+          unz[u][s] = clive[u] ? zrow[u][g] : 0.0f;
+        }
+      }
+    }
+  };
+
+  // ---- registers -> LDS (dequantizing the weight runs) ----
+  auto store_chunk = [&](int c, int buf) {
+    uint8_t* xt = smem + buf * STAGE;
+    uint8_t* wt = xt + BM * ROWB;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int sid = tid + i * NT;
+      if (sid < XSEG) *reinterpret_cast<uint4*>(xt + seg_off(sid >> 3, sid & 7)) = xr[i];
+    }
+    const int k0 = c * BK;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int uid = tid + u * NT;
+      if (uid >= UNITS) continue;
+      const int rr = uid >> 1, h = uid & 1;
+      const int p0 = k0 + 32 * h;
+      const bool tail = p0 + 32 > n32;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float sc = us[u][s];
+        const float nzs = -(unz[u][s] * sc);
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = fmaf(code_f32<BITS>(cw[u], 8 * s + e), sc, nzs);
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (p0 + 8 * s + e >= n32) f[e] = 0.0f;
+        }
+        uint4 o;
+        o.x = bf16x2_bits(f[0], f[1]);
+        o.y = bf16x2_bits(f[2], f[3]);
+        o.z = bf16x2_bits(f[4], f[5]);
+        o.w = bf16x2_bits(f[6], f[7]);
+        *reinterpret_cast<uint4*>(wt + seg_off(rr, 4 * h + s)) = o;
+      }
+    }
+  };
+
+  f32x16 acc[FA][FB];
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // operand reads: lane -> row (lane & 31) of a 32-row block, logical segment
+  // 2 kk + (lane >> 5), i.e. positions 16 kk + 8 (lane >> 5) .. + 8
+  auto compute = [&](int buf) {
+    const uint8_t* xt = smem + buf * STAGE;
+    const uint8_t* wt = xt + BM * ROWB;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 av[FA], bv[FB];
+      const int sg = 2 * kk + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(WM * wm + 32 * i + (lane & 31), sg));
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(WN * wn + 32 * j + (lane & 31), sg));
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (c_begin < c_end) {
+    load_chunk((int)c_begin);
+    store_chunk((int)c_begin, 0);
+    __syncthreads();
+    for (int c = (int)c_begin; c < (int)c_end; ++c) {
+      const int buf = (c - (int)c_begin) & 1;
+      const bool more = c + 1 < c_end;
+      if (more) load_chunk(c + 1);
+      compute(buf);
+      if (more) store_chunk(c + 1, buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds weight row (lane & 31) of each 32-block and
+  // tokens 8 (q / 4) + 4 (lane / 32) + q % 4 ----
+  const int64_t tw = tok0 + WM * wm + 4 * (lane >> 5);
+  const int64_t rw = row0 + WN * wn + (lane & 31);
+  const bool full = tok0 + WM * (wm + 1) <= a.tokens && row0 + WN * (wn + 1) <= a.m;
+  float* outf;
+  int64_t ld;
+  if (a.ks > 1) {
+    outf = a.part + kspl * a.tokens * a.m;
+    ld = a.m;
+  } else {
+    outf = reinterpret_cast<float*>(a.Y);
+    ld = a.ldy;
+  }
+  __bf16* outh = reinterpret_cast<__bf16*>(a.Y);
+  const bool half = a.ks == 1 && a.ybf16;
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int j = 0; j < FB; ++j) {
+      const int64_t base = (tw + 32 * i) * ld + rw + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int dt = 8 * (q >> 2) + (q & 3);
+        if (!full && (tw + 32 * i + dt >= a.tokens || rw + 32 * j >= a.m)) continue;
+        const int64_t o = base + (int64_t)dt * ld;
+        if (half) {
+          outh[o] = (__bf16)acc[i][j][q];
+        } else {
+          outf[o] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large batches: 256 tokens x 128 weight rows per workgroup, 4 waves of 128 x 64.
+// Everything that comes from HBM arrives by LDS DMA (global_load_lds), so the
+// only loads the compiler schedules are LDS reads, and each stage's arrival is
+// awaited with one explicit vmcnt before the barrier that publishes it:
+//   X tile    3 stages, issued 2 chunks ahead (32 KB each);
+//   codes     4 stages, issued 3 chunks ahead (128 rows x 2b words);
+//   scale/zero 4 stages, with the codes (one group per row and chunk: G is a
+//             multiple of 64 or a whole row);
+//   W tile    2 buffers: chunk c + 1 is dequantized (codes -> bf16) by all
+//             threads while chunk c is multiplied.
+// Rows past the last token or weight row, and columns past n in the last chunk,
+// are read from clamped (valid) addresses; their products are discarded (rows)
+// or multiplied by weights forced to 0 (columns).
+constexpr int DM = 256, DN = 128;       // tile
+constexpr int DWM = 128, DWN = 64;      // per wave
+constexpr int DX_STAGES = 3, DC_STAGES = 4;
+constexpr int DX_BYTES = DM * ROWB;     // 32 KB
+constexpr int DW_BYTES = DN * ROWB;     // 16 KB
+
+template <int BITS>
+struct DmaLayout {
+  static constexpr int C_BYTES = DN * 2 * BITS * 4;  // codes of one chunk
+  static constexpr int Z_BYTES = DN * 2 * 4;         // scales then zeros
+  static constexpr int X_OFF = 0;
+  static constexpr int W_OFF = X_OFF + DX_STAGES * DX_BYTES;
+  static constexpr int C_OFF = W_OFF + 2 * DW_BYTES;
+  static constexpr int Z_OFF = C_OFF + DC_STAGES * C_BYTES;
+  static constexpr int TOTAL = Z_OFF + DC_STAGES * Z_BYTES;
+  // DMA instructions per wave and chunk: X 8 (1 KB each), codes BITS, scale/zero 1
+  static constexpr int X_PER_WAVE = DX_BYTES / 1024 / 4;
+  static constexpr int ISSUE = X_PER_WAVE + BITS + 1;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
+  using Lay = DmaLayout<BITS>;
+  static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
+  __shared__ __align__(16) uint8_t smem[Lay::TOTAL];
+
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, idx = b / kXcds;
+  const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return;
+  const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int64_t rb = L % a.nrb;
+  const int64_t kspl = (L / a.nrb) % a.ks;
+  const int64_t tb = L / (a.nrb * a.ks);
+  const int64_t tok0 = tb * DM, row0 = rb * DN;
+  const int c_begin = (int)(kspl * a.chunks_per_split);
+  const int c_end = (int)min(a.nchunks, (int64_t)c_begin + a.chunks_per_split);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int n32 = (int)a.n, nwr = (int)a.nwr;
+  const int tmax = (int)(a.tokens - 1 - tok0);  // last valid row of the tile
+  const int rmax = (int)(a.m - 1 - row0);
+
+  // ---- DMA sources (per-lane 32-bit offsets fixed for the tile) ----
+  uint32_t xoff[Lay::X_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < Lay::X_PER_WAVE; ++j) {
+    const int row = 8 * (wv * Lay::X_PER_WAVE + j) + (lane >> 3);
+    const int lseg = (lane & 7) ^ (lane >> 3);
+    xoff[j] = (uint32_t)(2 * ((int64_t)min(row, tmax) * a.ldx + 8 * lseg));
+  }
+  const char* xbase = reinterpret_cast<const char*>(a.X + tok0 * a.ldx);
+  uint32_t crow_off[BITS];
+  int cword[BITS];
+#pragma unroll
+  for (int q = 0; q < BITS; ++q) {
+    const int d = q * 256 + tid;
+    const int row = d / (2 * BITS);
+    cword[q] = d % (2 * BITS);
+    crow_off[q] = (uint32_t)(4 * ((int64_t)min(row, rmax) * a.ldp));
+  }
+  const char* cbase = reinterpret_cast<const char*>(a.P + row0 * a.ldp);
+  const int zrow = min(tid & 127, rmax);
+  const char* zbase = reinterpret_cast<const char*>((wv < 2 ? a.scales : a.zeros) +
+                                                    row0 * a.ngroups);
+  const uint32_t lds0 = lds_addr(smem);
+
+  auto issue_x = [&](int c) {
+    const int k0 = c * BK;
+    const uint32_t dst = lds0 + Lay::X_OFF + (c % DX_STAGES) * DX_BYTES +
+                         wv * Lay::X_PER_WAVE * 1024;
+    const char* src = xbase + 2 * (int64_t)k0;
+    if (k0 + BK <= n32) {
+#pragma unroll
+      for (int j = 0; j < Lay::X_PER_WAVE; ++j) lds_dma16(src, xoff[j], dst + 1024 * j);
+    } else {  // last chunk: segments past n re-read the last valid segment
+      const int lseg = (lane & 7) ^ (lane >> 3);
+      const int clamp = 2 * (min(8 * lseg, n32 - 8 - k0) - 8 * lseg);
+#pragma unroll
+      for (int j = 0; j < Lay::X_PER_WAVE; ++j)
+        lds_dma16(src, xoff[j] + (uint32_t)clamp, dst + 1024 * j);
+    }
+  };
+  auto issue_c = [&](int c) {
+    const int st = c % DC_STAGES;
+    const uint32_t dst = lds0 + Lay::C_OFF + st * Lay::C_BYTES + wv * 256;
+    const int w0 = c * 2 * BITS;
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) {
+      const int word = min(w0 + cword[q], nwr - 1);
+      lds_dma4(cbase, crow_off[q] + 4u * (uint32_t)word, dst + 1024 * q);
+    }
+    const int g = a.G > 0 ? min((c * BK) / (int)a.G, (int)a.ngroups - 1) : 0;
+    lds_dma4(zbase, (uint32_t)(4 * ((int64_t)zrow * a.ngroups + g)),
+             lds0 + Lay::Z_OFF + st * Lay::Z_BYTES + wv * 256);
+  };
+
+  // ---- dequantization of one chunk: thread -> weight row tid / 2, codes
+  // 32 (tid & 1) .. + 32 of the chunk, in 4 parts of 8 (one 16-byte LDS row
+  // segment each) that are interleaved with the MFMAs of the chunk before ----
+  const int drow = tid >> 1, dh = tid & 1;
+  struct Dq {
+    uint32_t w[BITS];
+    float sc, nzs;
+  };
+  auto dq_load = [&](int c, Dq& d) {
+    const int st = c % DC_STAGES;
+    const uint32_t* cs = reinterpret_cast<const uint32_t*>(smem + Lay::C_OFF + st * Lay::C_BYTES);
+    const float* zs = reinterpret_cast<const float*>(smem + Lay::Z_OFF + st * Lay::Z_BYTES);
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) d.w[q] = cs[drow * 2 * BITS + dh * BITS + q];
+    d.sc = zs[drow];
+    d.nzs = -(zs[DN + drow] * d.sc);
+  };
+  auto dq_part = [&](int c, const Dq& d, int s) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = fmaf(code_f32<BITS>(d.w, 8 * s + e), d.sc, d.nzs);
+    if ((c + 1) * BK > n32) {  // last chunk (uniform): positions past n weigh 0
+      const int p = c * BK + 32 * dh + 8 * s;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = p + e < n32 ? f[e] : 0.0f;
+    }
+    uint4 o;
+    o.x = bf16x2_bits(f[0], f[1]);
+    o.y = bf16x2_bits(f[2], f[3]);
+    o.z = bf16x2_bits(f[4], f[5]);
+    o.w = bf16x2_bits(f[6], f[7]);
+    uint8_t* wt = smem + Lay::W_OFF + (c & 1) * DW_BYTES;
+    *reinterpret_cast<uint4*>(wt + seg_off(drow, 4 * dh + s)) = o;
+  };
+
+  f32x16 acc[DWM / 32][DWN / 32];
+#pragma unroll
+  for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // multiply chunk c; with dq, dequantize chunk c + 1 alongside
+  auto compute = [&](int c, bool dq) {
+    const uint8_t* xt = smem + Lay::X_OFF + (c % DX_STAGES) * DX_BYTES;
+    const uint8_t* wt = smem + Lay::W_OFF + (c & 1) * DW_BYTES;
+    Dq d;
+    if (dq) dq_load(c + 1, d);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 av[DWM / 32], bv[DWN / 32];
+      const int sg = 2 * kk + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < DWM / 32; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(DWM * wm + 32 * i + (lane & 31), sg));
+#pragma unroll
+      for (int j = 0; j < DWN / 32; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(DWN * wn + 32 * j + (lane & 31), sg));
+#pragma unroll
+      for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < DWN / 32; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      if (dq) dq_part(c + 1, d, kk);
+    }
+  };
+
+  if (c_begin < c_end) {
+    // prologue: X of chunks 0, 1 and codes of chunks 0, 1, 2 in flight; chunk 0
+    // dequantized once its codes have landed
+    const int c0 = c_begin;
+    issue_c(c0);
+    issue_x(c0);
+    if (c0 + 1 < c_end) { issue_c(c0 + 1); issue_x(c0 + 1); }
+    if (c0 + 2 < c_end) issue_c(c0 + 2);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    {
+      Dq d;
+      dq_load(c0, d);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dq_part(c0, d, s);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    for (int c = c0; c < c_end; ++c) {
+      // X of c + 2 and codes of c + 3; the wait at the end covers everything
+      // issued one iteration ago (X of c + 1, codes of c + 2)
+      const bool full = c + 3 < c_end;
+      if (c + 2 < c_end) issue_x(c + 2);
+      if (c + 3 < c_end) issue_c(c + 3);
+      if (c + 1 < c_end) {
+        compute(c, true);
+      } else {
+        compute(c, false);
+      }
+      if (full) {
+        __builtin_amdgcn_s_waitcnt(0x0070 | (Lay::ISSUE & 15) | ((Lay::ISSUE >> 4) << 14));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  const int64_t tw = tok0 + DWM * wm + 4 * (lane >> 5);
+  const int64_t rw = row0 + DWN * wn + (lane & 31);
+  const bool fulltile = tok0 + DWM * (wm + 1) <= a.tokens && row0 + DWN * (wn + 1) <= a.m;
+  float* outf;
+  int64_t ld;
+  if (a.ks > 1) {
+    outf = a.part + kspl * a.tokens * a.m;
+    ld = a.m;
+  } else {
+    outf = reinterpret_cast<float*>(a.Y);
+    ld = a.ldy;
+  }
+  __bf16* outh = reinterpret_cast<__bf16*>(a.Y);
+  const bool half = a.ks == 1 && a.ybf16;
+#pragma unroll
+  for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j) {
+      const int64_t base = (tw + 32 * i) * ld + rw + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int dt = 8 * (q >> 2) + (q & 3);
+        if (!fulltile && (tw + 32 * i + dt >= a.tokens || rw + 32 * j >= a.m)) continue;
+        const int64_t o = base + (int64_t)dt * ld;
+        if (half) {
+          outh[o] = (__bf16)acc[i][j][q];
+        } else {
+          outf[o] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+// Y[t, r] = sum over splits s = 0, 1, ... of part[s, t, r], in that order.
+__global__ __launch_bounds__(256) void dequant_reduce_kernel(const float* __restrict__ part,
+                                                             int64_t ks, int64_t tokens,
+                                                             int64_t m, void* Y, int64_t ldy,
+                                                             int ybf16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= tokens * m) return;
+  const int64_t t = i / m, r = i - t * m;
+  float s = 0.0f;
+  for (int64_t k = 0; k < ks; ++k) s += part[k * tokens * m + i];
+  if (ybf16) {
+    reinterpret_cast<__bf16*>(Y)[t * ldy + r] = (__bf16)s;
+  } else {
+    reinterpret_cast<float*>(Y)[t * ldy + r] = s;
+  }
+}
+
+// Xp[t, p] = X[t, perm[p]] for p < n, 0 for n <= p < ldxp (ldxp = n rounded up
+// to 8); one thread per 8-column segment, one 16-byte store.
+__global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t ldx,
+                                                             const int32_t* __restrict__ perm,
+                                                             int64_t tokens, int64_t n,
+                                                             int64_t ldxp,
+                                                             uint16_t* __restrict__ Xp) {
+  const int64_t segs = ldxp / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= tokens * segs) return;
+  const int64_t t = i / segs, p0 = 8 * (i - t * segs);
+  const uint16_t* row = X + t * ldx;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t p = p0 + 2 * q;
+    const uint32_t lo = p < n ? row[perm[p]] : 0u;
+    const uint32_t hi = p + 1 < n ? row[perm[p + 1]] : 0u;
+    w[q] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(Xp + t * ldxp + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct Shape {
+  int bm, bn;
+  int64_t ks;
+};
+
+// Tile shape and K split for a problem.  Large batches take 256-token tiles
+// (the dequantization of a weight is shared by 256 tokens); small ones shrink
+// the token side and split K until the grid holds ~4 workgroups per CU.
+Shape choose_shape(int64_t tokens, int64_t m, int64_t n) {
+  Shape s;
+  if (tokens > 128) {
+    s.bm = 256;
+    s.bn = 128;
+  } else if (tokens > 32) {
+    s.bm = 128;
+    s.bn = 128;
+  } else {
+    s.bm = 32;
+    s.bn = 64;
+  }
+  const int64_t tiles = ceil_div(tokens, s.bm) * ceil_div(m, s.bn);
+  const int64_t nchunks = ceil_div(n, BK);
+  // split K until the grid holds ~4 workgroups per CU (small batches) or one
+  // per CU (256-token tiles, one resident per CU), keeping >= 4 (8) chunks per split
+  const int64_t want = tokens <= 128 ? 1024 : 256;
+  const int64_t min_chunks = tokens <= 128 ? 4 : 8;
+  s.ks = 1;
+  while (tiles * s.ks * 2 <= want && nchunks / (s.ks * 2) >= min_chunks) s.ks *= 2;
+  return s;
+}
+
+template <int BITS, int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const DqArgs& a, hipStream_t stream) {
+  const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  hipLaunchKernelGGL((dequant_gemm_kernel<BITS, BM, BN, WM, WN>), dim3((unsigned)grid),
+                     dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_dma(const DqArgs& a, hipStream_t stream) {
+  const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
+  hipLaunchKernelGGL((dequant_gemm_dma_kernel<BITS>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const DqArgs& a, int bm, hipStream_t stream) {
+  switch (bm) {
+    case 256: return launch_tile<BITS, 256, 128, 64, 64>(a, stream);
+    case 128: return launch_tile<BITS, 128, 128, 64, 64>(a, stream);
+    default: return launch_tile<BITS, 32, 64, 32, 32>(a, stream);
+  }
+}
+
+}  // namespace
+
+size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm) {
+  const Shape s = choose_shape(tokens, m, n);
+  size_t bytes = 0;
+  if (has_perm) bytes += align_up((size_t)tokens * (size_t)align_up((size_t)n, 8) * 2, 256);
+  if (s.ks > 1) bytes += (size_t)s.ks * (size_t)tokens * (size_t)m * 4;
+  return bytes;
+}
+
+hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
+  const Shape s = choose_shape(d.tokens, d.m, d.n);
+  DqArgs a;
+  uint8_t* ws = static_cast<uint8_t*>(d.ws);
+  a.X = static_cast<const uint16_t*>(d.X);
+  a.ldx = d.ldx;
+  if (d.perm) {
+    const int64_t ldxp = (int64_t)align_up((size_t)d.n, 8);
+    uint16_t* Xp = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up((size_t)d.tokens * (size_t)ldxp * 2, 256);
+    const int64_t total = d.tokens * (ldxp / 8);
+    hipLaunchKernelGGL(gather_columns_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                       stream, a.X, d.ldx, d.perm, d.tokens, d.n, ldxp, Xp);
+    a.X = Xp;
+    a.ldx = ldxp;
+  }
+  a.tokens = d.tokens;
+  a.n = d.n;
+  a.P = d.packed;
+  a.ldp = d.ldp;
+  a.nwr = ceil_div(d.n * d.bits, 32);
+  a.scales = d.scales;
+  a.zeros = d.zeros;
+  a.G = d.group_size > 0 ? d.group_size : 0;
+  a.ngroups = d.group_size > 0 ? ceil_div(d.n, d.group_size) : 1;
+  a.gs_run = (d.group_size <= 0 || d.group_size % 32 == 0) ? 1 : 0;
+  a.gshift = -1;
+  if (d.group_size > 0 && (d.group_size & (d.group_size - 1)) == 0) {
+    a.gshift = 0;
+    while ((1 << a.gshift) < d.group_size) ++a.gshift;
+  }
+  a.m = d.m;
+  a.Y = d.Y;
+  a.ldy = d.ldy;
+  a.ybf16 = d.ydt == GPTQ_BF16 ? 1 : 0;
+  a.part = s.ks > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ntb = ceil_div(d.tokens, s.bm);
+  a.nrb = ceil_div(d.m, s.bn);
+  a.ks = s.ks;
+  a.nchunks = ceil_div(d.n, BK);
+  a.chunks_per_split = ceil_div(a.nchunks, s.ks);
+  a.ntiles = a.ntb * a.nrb * a.ks;
+  // the DMA kernel: 256-token tiles, 16-byte X rows (n % 8 == 0, aligned), one
+  // group per row and chunk, codes of <= 6 bits (LDS budget), 32-bit offsets
+  const bool dma = s.bm == 256 && d.n % 8 == 0 && d.bits <= 6 &&
+                   (d.group_size <= 0 || d.group_size % 64 == 0) && a.ldx % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 && a.ldx < (int64_t(1) << 23) &&
+                   d.ldp < (int64_t(1) << 23);
+  hipError_t e;
+  if (dma) {
+    switch (d.bits) {
+      case 2: e = launch_dma<2>(a, stream); break;
+      case 3: e = launch_dma<3>(a, stream); break;
+      case 4: e = launch_dma<4>(a, stream); break;
+      case 5: e = launch_dma<5>(a, stream); break;
+      default: e = launch_dma<6>(a, stream); break;
+    }
+  } else {
+    switch (d.bits) {
+      case 2: e = launch_bits<2>(a, s.bm, stream); break;
+      case 3: e = launch_bits<3>(a, s.bm, stream); break;
+      case 4: e = launch_bits<4>(a, s.bm, stream); break;
+      case 5: e = launch_bits<5>(a, s.bm, stream); break;
+      case 6: e = launch_bits<6>(a, s.bm, stream); break;
+      case 7: e = launch_bits<7>(a, s.bm, stream); break;
+      default: e = launch_bits<8>(a, s.bm, stream); break;
+    }
+  }
+  if (e != hipSuccess || s.ks == 1) return e;
+  const int64_t total = d.tokens * d.m;
+  hipLaunchKernelGGL(dequant_reduce_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                     stream, a.part, s.ks, d.tokens, d.m, d.Y, d.ldy, a.ybf16);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -312,26 +312,6 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS DMA of 16 bytes per lane (lane l lands at lds + 16 l) from
-// sbase + voff (wave-uniform 64-bit base in SGPRs, per-lane 32-bit byte
-// offset), issued from asm: the compiler cannot tell this write from the LDS
-// reads of the other buffer and would otherwise wait for it before every one
-// of them; completion is awaited explicitly (vmcnt) before the barrier that
-// publishes the stage.  The instruction writes no VGPR (its data goes to
-// LDS), and its address registers are consumed at issue.  M0 (the LDS base
-// of the transfer, read at issue) is saved and restored around it.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
 __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
                                                             int64_t ldx, int64_t tokens,
                                                             int64_t P, int64_t T2,
@@ -372,10 +352,10 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
     const char* base = xa + (int64_t)s * step2;
 #pragma unroll
     for (int q = 0; q < RPW / 2; ++q)
-      dma16(base + (int64_t)(4 * (q & ~1)) * ldx, voff[q & 1], la + 1024 * q);
+      lds_dma16(base + (int64_t)(4 * (q & ~1)) * ldx, voff[q & 1], la + 1024 * q);
 #pragma unroll
     for (int q = 0; q < RPW / 2; ++q)
-      dma16(base + (int64_t)(4 * (q & ~1)) * ldx + jmi2, voff[q & 1], la + DSTAGE + 1024 * q);
+      lds_dma16(base + (int64_t)(4 * (q & ~1)) * ldx + jmi2, voff[q & 1], la + DSTAGE + 1024 * q);
   };
 
   // transposing reads: lane (g = lane / 16, i = lane % 16) points at token

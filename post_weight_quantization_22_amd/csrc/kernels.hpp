@@ -11,8 +11,9 @@ hipError_t launch_rtn(const void* W, int dt, int64_t m, int64_t n, int64_t ldw, 
                       hipStream_t stream);
 
 // ---- pack.hip -------------------------------------------------------------
-hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uint32_t* packed,
-                       hipStream_t stream);
+// perm (may be null): position p of a row's stream takes codes[r, perm[p]]
+hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits,
+                       const int32_t* perm, uint32_t* packed, hipStream_t stream);
 
 // ---- hessian.hip ----------------------------------------------------------
 size_t hessian_ws_bytes(int64_t n, int64_t tokens, int dt);
@@ -45,5 +46,24 @@ struct QuantArgs {
 };
 size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+// ---- dequant_gemm.hip -----------------------------------------------------
+struct DequantArgs {
+  const void* X;  // bf16 [tokens, ldx]
+  int64_t tokens, n, ldx;
+  const uint32_t* packed;  // [m, ldp], processing order
+  int64_t ldp;
+  int bits, group_size;
+  const float* scales;
+  const float* zeros;
+  const int32_t* perm;  // may be null
+  int64_t m;
+  void* Y;
+  int ydt;
+  int64_t ldy;
+  void* ws;
+};
+size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm);
+hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream);
 
 }  // namespace gptq

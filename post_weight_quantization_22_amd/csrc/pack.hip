@@ -9,7 +9,8 @@
 // output word, so stores are fully coalesced.  For b in {2, 4, 8} a word holds
 // a whole number of codes and the lane reads them with one aligned vector
 // load; other widths (3, 5, 6, 7 bits) gather the <= 11 + 1 codes that touch
-// the word.
+// the word.  Packing in processing order (a permutation of each row's columns)
+// takes the gathering kernel for every width.
 #include "kernels.hpp"
 
 namespace gptq {
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(256) void pack_pow2_kernel(const uint8_t* __restric
 
 __global__ __launch_bounds__(256) void pack_any_kernel(const uint8_t* __restrict__ codes,
                                                        int64_t m, int64_t n, int64_t nw, int bits,
+                                                       const int32_t* __restrict__ perm,
                                                        uint32_t* __restrict__ packed) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= m * nw) return;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void pack_any_kernel(const uint8_t* __restrict
   const uint8_t* row = codes + r * n;
   uint64_t acc = 0;
   for (int64_t c = cfirst; c <= clast; ++c) {
-    const uint64_t v = (uint64_t)(row[c] & mask);
+    const uint64_t v = (uint64_t)(row[perm ? perm[c] : c] & mask);
     const int64_t pos = c * bits - base;  // may be negative for a code entering from the left
     acc |= pos >= 0 ? (v << pos) : (v >> (-pos));
   }
@@ -69,12 +71,17 @@ __global__ __launch_bounds__(256) void pack_any_kernel(const uint8_t* __restrict
 
 }  // namespace
 
-hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uint32_t* packed,
-                       hipStream_t stream) {
+hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits,
+                       const int32_t* perm, uint32_t* packed, hipStream_t stream) {
   const int64_t nw = ceil_div(n * bits, 32);
   const int64_t total = m * nw;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)ceil_div(total, 256));
+  if (perm) {
+    hipLaunchKernelGGL(pack_any_kernel, grid, dim3(256), 0, stream, codes, m, n, nw, bits, perm,
+                       packed);
+    return hipGetLastError();
+  }
   switch (bits) {
     case 2:
       hipLaunchKernelGGL(pack_pow2_kernel<2>, grid, dim3(256), 0, stream, codes, m, n, nw, packed);
@@ -87,7 +94,7 @@ hipError_t launch_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uin
       break;
     default:
       hipLaunchKernelGGL(pack_any_kernel, grid, dim3(256), 0, stream, codes, m, n, nw, bits,
-                         packed);
+                         nullptr, packed);
   }
   return hipGetLastError();
 }

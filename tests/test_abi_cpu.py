@@ -136,3 +136,42 @@ def test_hessian_pack_rtn_argument_validation(lib):
     assert so.rtn_minmax(FAKE, 1, 4, 8, 4, 4, 8, 0, FAKE, FAKE, FAKE, None) == \
         lib.GPTQ_ERR_INVALID_ARG  # ldw < n
     assert so.rtn_minmax(FAKE, 1, 0, 8, 8, 4, 8, 0, FAKE, FAKE, FAKE, None) == lib.GPTQ_OK
+
+
+def test_dequant_gemm_argument_validation(lib):
+    so = lib.load()
+
+    def dq(X=FAKE, xdt=1, tokens=16, n=256, ldx=256, ldp=32, bits=4, G=128, m=64, ydt=0, ldy=64,
+           ws=1 << 40, perm=None):
+        return so.gptq_dequant_gemm(X, xdt, tokens, n, ldx, FAKE, ldp, bits, G, FAKE, FAKE, perm,
+                                    m, FAKE, ydt, ldy, FAKE, ws, None)
+
+    assert dq(bits=1) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(bits=9) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(G=12) == lib.GPTQ_ERR_INVALID_ARG          # not a multiple of 8
+    assert dq(G=0) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(xdt=0) == lib.GPTQ_ERR_UNSUPPORTED          # fp32 activations: not built
+    assert dq(xdt=5) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(ldx=260) == lib.GPTQ_ERR_INVALID_ARG       # row stride not a multiple of 8
+    assert dq(X=ctypes.c_void_p(0x100008)) == lib.GPTQ_ERR_INVALID_ARG  # not 16-byte aligned
+    assert dq(ldx=255) == lib.GPTQ_ERR_INVALID_ARG       # ldx < n
+    assert dq(ldp=31) == lib.GPTQ_ERR_INVALID_ARG        # < ceil(256 * 4 / 32)
+    assert dq(ldy=63) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(n=0) == lib.GPTQ_ERR_INVALID_ARG
+    assert dq(tokens=0) == lib.GPTQ_OK and dq(m=0) == lib.GPTQ_OK
+    # the column permutation needs the workspace
+    need = lib.gptq_dequant_gemm_workspace_size(16, 64, 256, True)
+    assert need >= 16 * 256 * 2
+    assert dq(perm=FAKE, ws=need - 1) == lib.GPTQ_ERR_WORKSPACE
+    assert so.gptq_pack_ordered(FAKE, 4, 4, 9, FAKE, FAKE, None) == lib.GPTQ_ERR_INVALID_ARG
+    assert so.gptq_pack_ordered(None, 4, 4, 4, FAKE, FAKE, None) == lib.GPTQ_ERR_INVALID_ARG
+    assert so.gptq_pack_ordered(FAKE, 0, 4, 4, FAKE, FAKE, None) == lib.GPTQ_OK
+
+
+def test_dequant_gemm_workspace_query(lib):
+    # large batches: no split, no permutation -> no workspace
+    assert lib.gptq_dequant_gemm_workspace_size(2048, 4096, 4096, False) == 0
+    assert lib.gptq_dequant_gemm_workspace_size(2048, 4096, 4096, True) == 2048 * 4096 * 2
+    # decode batches split K; the partial sums need room
+    assert lib.gptq_dequant_gemm_workspace_size(1, 4096, 4096, False) >= 2 * 4096 * 4
+    assert lib.gptq_dequant_gemm_workspace_size(0, 4096, 4096, True) == 0
