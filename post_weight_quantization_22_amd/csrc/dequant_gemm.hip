@@ -32,6 +32,8 @@
 // splits' fp32 partial sums are added in split order by a second kernel
 // (deterministic).  Tiles are dealt to XCDs in contiguous runs, so the
 // workgroups of one XCD share a token block (prefill) in its L2.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace gptq {
@@ -45,11 +47,37 @@ constexpr int BK = 64;         // positions per chunk
 constexpr int ROWB = BK * 2;   // bytes of one LDS tile row
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int seg_off(int r, int s) { return r * ROWB + ((s ^ (r & 7)) << 4); }
+// Segment s of row r lives at segment s ^ ((r >> 1) & 7).  A 16-byte read of 16
+// lanes covers 16 consecutive rows at one logical segment; the LDS serves 256
+// bytes (64 banks) per cycle, i.e. two 128-byte rows, so the 16 lanes must hit
+// 16 different (row parity, segment) pairs, which this swizzle gives.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int seg_off(int r, int s) { return r * ROWB + ((s ^ swz(r)) << 4); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// byte K of x as fp32 (v_cvt_f32_ubyteK; written out because the compiler folds
+// the byte extraction into a bit-field extract when it knows the masked bits)
+template <int K>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  float r;
+  if constexpr (K == 0) {
+    __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  } else if constexpr (K == 1) {
+    __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  } else if constexpr (K == 2) {
+    __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  } else {
+    __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  }
+  return r;
 }
 
 // Code i (0..31) of a 32-code run held in BITS words, as fp32.
@@ -74,6 +102,26 @@ __device__ __forceinline__ float code_f32(const uint32_t (&w)[BITS], int i) {
       q = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off) & MASK;
     }
     return (float)q;
+  }
+}
+
+// Codes 8 s .. 8 s + 7 of a 32-code run held in BITS words, as fp32.
+template <int BITS>
+__device__ __forceinline__ void decode8(const uint32_t (&w)[BITS], int s, float (&f)[8]) {
+  if constexpr (BITS == 4) {
+    const uint32_t lo = w[s] & 0x0F0F0F0Fu, hi = (w[s] >> 4) & 0x0F0F0F0Fu;
+    f[0] = ubyte_f32<0>(lo); f[1] = ubyte_f32<0>(hi);
+    f[2] = ubyte_f32<1>(lo); f[3] = ubyte_f32<1>(hi);
+    f[4] = ubyte_f32<2>(lo); f[5] = ubyte_f32<2>(hi);
+    f[6] = ubyte_f32<3>(lo); f[7] = ubyte_f32<3>(hi);
+  } else if constexpr (BITS == 8) {
+    f[0] = ubyte_f32<0>(w[2 * s]); f[1] = ubyte_f32<1>(w[2 * s]);
+    f[2] = ubyte_f32<2>(w[2 * s]); f[3] = ubyte_f32<3>(w[2 * s]);
+    f[4] = ubyte_f32<0>(w[2 * s + 1]); f[5] = ubyte_f32<1>(w[2 * s + 1]);
+    f[6] = ubyte_f32<2>(w[2 * s + 1]); f[7] = ubyte_f32<3>(w[2 * s + 1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = code_f32<BITS>(w, 8 * s + e);
   }
 }
 
@@ -334,11 +382,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dequant_gemm_kerne
 }
 
 // ---------------------------------------------------------------------------
-// Large batches: 256 tokens x 128 weight rows per workgroup, 4 waves of 128 x 64.
+// Tiles of TM tokens x 128 weight rows (TM = 256, 128 or 32), 4 waves.
 // Everything that comes from HBM arrives by LDS DMA (global_load_lds), so the
 // only loads the compiler schedules are LDS reads, and each stage's arrival is
 // awaited with one explicit vmcnt before the barrier that publishes it:
-//   X tile    3 stages, issued 2 chunks ahead (32 KB each);
+//   X tile    3 stages, issued 2 chunks ahead (TM x 128 bytes each);
 //   codes     4 stages, issued 3 chunks ahead (128 rows x 2b words);
 //   scale/zero 4 stages, with the codes (one group per row and chunk: G is a
 //             multiple of 64 or a whole row);
@@ -346,31 +394,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dequant_gemm_kerne
 //             threads while chunk c is multiplied.
 // Rows past the last token or weight row, and columns past n in the last chunk,
 // are read from clamped (valid) addresses; their products are discarded (rows)
-// or multiplied by weights forced to 0 (columns).
-constexpr int DM = 256, DN = 128;       // tile
-constexpr int DWM = 128, DWN = 64;      // per wave
+// or zeroed in LDS (columns).  Small batches (TM = 32) are bound by the codes'
+// HBM traffic; the deep DMA pipeline keeps several chunks of every workgroup
+// in flight.
+constexpr int DN = 128;  // weight rows per tile
 constexpr int DX_STAGES = 3, DC_STAGES = 4;
-constexpr int DX_BYTES = DM * ROWB;     // 32 KB
-constexpr int DW_BYTES = DN * ROWB;     // 16 KB
+constexpr int DW_BYTES = DN * ROWB;  // 16 KB
 
-template <int BITS>
+template <int BITS, int TM>
 struct DmaLayout {
+  static constexpr int X_BYTES = TM * ROWB;
   static constexpr int C_BYTES = DN * 2 * BITS * 4;  // codes of one chunk
   static constexpr int Z_BYTES = DN * 2 * 4;         // scales then zeros
   static constexpr int X_OFF = 0;
-  static constexpr int W_OFF = X_OFF + DX_STAGES * DX_BYTES;
+  static constexpr int W_OFF = X_OFF + DX_STAGES * X_BYTES;
   static constexpr int C_OFF = W_OFF + 2 * DW_BYTES;
   static constexpr int Z_OFF = C_OFF + DC_STAGES * C_BYTES;
   static constexpr int TOTAL = Z_OFF + DC_STAGES * Z_BYTES;
-  // DMA instructions per wave and chunk: X 8 (1 KB each), codes BITS, scale/zero 1
-  static constexpr int X_PER_WAVE = DX_BYTES / 1024 / 4;
-  static constexpr int ISSUE = X_PER_WAVE + BITS + 1;
+  // 4 waves: TM >= 128 -> 2 x 2 waves of (TM / 2) x 64; TM = 32 -> 1 x 4 of 32 x 32
+  static constexpr int NWM = TM >= 128 ? 2 : 1, NWN = 4 / NWM;
+  static constexpr int WM = TM / NWM, WN = DN / NWN;
+  static constexpr int X_PER_WAVE = X_BYTES / 1024 / 4;  // 1 KB X DMAs per wave and chunk
+  static constexpr int ISSUE = X_PER_WAVE + BITS + 1;    // DMAs per wave and chunk
 };
 
-template <int BITS>
+template <int BITS, int TM>
 __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
-  using Lay = DmaLayout<BITS>;
+  using Lay = DmaLayout<BITS, TM>;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
+  constexpr int DM = TM, DWM = Lay::WM, DWN = Lay::WN, NWN = Lay::NWN;
+  constexpr int X_PER_WAVE = Lay::X_PER_WAVE;
+  constexpr int DX_BYTES = Lay::X_BYTES;
   __shared__ __align__(16) uint8_t smem[Lay::TOTAL];
 
   const int64_t b = blockIdx.x;
@@ -387,18 +441,22 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / NWN, wn = wv % NWN;
   const int n32 = (int)a.n, nwr = (int)a.nwr;
   const int tmax = (int)(a.tokens - 1 - tok0);  // last valid row of the tile
   const int rmax = (int)(a.m - 1 - row0);
 
   // ---- DMA sources (per-lane 32-bit offsets fixed for the tile) ----
-  uint32_t xoff[Lay::X_PER_WAVE];
+  // X: instruction j of wave wv fills rows 8 (wv X_PER_WAVE + j) .. + 8; lane l
+  // lands on row + l / 8, physical segment l % 8, so it loads the logical
+  // segment (l % 8) ^ swz(row)
+  uint32_t xoff[X_PER_WAVE];
+  int xseg[X_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < Lay::X_PER_WAVE; ++j) {
-    const int row = 8 * (wv * Lay::X_PER_WAVE + j) + (lane >> 3);
-    const int lseg = (lane & 7) ^ (lane >> 3);
-    xoff[j] = (uint32_t)(2 * ((int64_t)min(row, tmax) * a.ldx + 8 * lseg));
+  for (int j = 0; j < X_PER_WAVE; ++j) {
+    const int row = 8 * (wv * X_PER_WAVE + j) + (lane >> 3);
+    xseg[j] = (lane & 7) ^ swz(row);
+    xoff[j] = (uint32_t)(2 * ((int64_t)min(row, tmax) * a.ldx + 8 * xseg[j]));
   }
   const char* xbase = reinterpret_cast<const char*>(a.X + tok0 * a.ldx);
   uint32_t crow_off[BITS];
@@ -411,7 +469,7 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
     crow_off[q] = (uint32_t)(4 * ((int64_t)min(row, rmax) * a.ldp));
   }
   const char* cbase = reinterpret_cast<const char*>(a.P + row0 * a.ldp);
-  const int zrow = min(tid & 127, rmax);
+  const int zrow = min(tid & 127, rmax);  // waves 0, 1: scales; 2, 3: zeros
   const char* zbase = reinterpret_cast<const char*>((wv < 2 ? a.scales : a.zeros) +
                                                     row0 * a.ngroups);
   const uint32_t lds0 = lds_addr(smem);
@@ -419,17 +477,17 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
   auto issue_x = [&](int c) {
     const int k0 = c * BK;
     const uint32_t dst = lds0 + Lay::X_OFF + (c % DX_STAGES) * DX_BYTES +
-                         wv * Lay::X_PER_WAVE * 1024;
+                         wv * X_PER_WAVE * 1024;
     const char* src = xbase + 2 * (int64_t)k0;
     if (k0 + BK <= n32) {
 #pragma unroll
-      for (int j = 0; j < Lay::X_PER_WAVE; ++j) lds_dma16(src, xoff[j], dst + 1024 * j);
-    } else {  // last chunk: segments past n re-read the last valid segment
-      const int lseg = (lane & 7) ^ (lane >> 3);
-      const int clamp = 2 * (min(8 * lseg, n32 - 8 - k0) - 8 * lseg);
+      for (int j = 0; j < X_PER_WAVE; ++j) lds_dma16(src, xoff[j], dst + 1024 * j);
+    } else {  // last chunk: segments past n re-read the last valid one (zeroed later)
 #pragma unroll
-      for (int j = 0; j < Lay::X_PER_WAVE; ++j)
+      for (int j = 0; j < X_PER_WAVE; ++j) {
+        const int clamp = 2 * (min(8 * xseg[j], n32 - 8 - k0) - 8 * xseg[j]);
         lds_dma16(src, xoff[j] + (uint32_t)clamp, dst + 1024 * j);
+      }
     }
   };
   auto issue_c = [&](int c) {
@@ -446,9 +504,9 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
              lds0 + Lay::Z_OFF + st * Lay::Z_BYTES + wv * 256);
   };
 
-  // ---- dequantization of one chunk: thread -> weight row tid / 2, codes
-  // 32 (tid & 1) .. + 32 of the chunk, in 4 parts of 8 (one 16-byte LDS row
-  // segment each) that are interleaved with the MFMAs of the chunk before ----
+  // ---- dequantization: thread -> weight row tid / 2, codes 32 (tid & 1) ..
+  // + 32 of the chunk, in 4 parts of 8 codes (one 16-byte LDS row segment each)
+  // interleaved with the MFMAs of the chunk before ----
   const int drow = tid >> 1, dh = tid & 1;
   struct Dq {
     uint32_t w[BITS];
@@ -465,13 +523,9 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
   };
   auto dq_part = [&](int c, const Dq& d, int s) {
     float f[8];
+    decode8<BITS>(d.w, s, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = fmaf(code_f32<BITS>(d.w, 8 * s + e), d.sc, d.nzs);
-    if ((c + 1) * BK > n32) {  // last chunk (uniform): positions past n weigh 0
-      const int p = c * BK + 32 * dh + 8 * s;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = p + e < n32 ? f[e] : 0.0f;
-    }
+    for (int e = 0; e < 8; ++e) f[e] = fmaf(f[e], d.sc, d.nzs);
     uint4 o;
     o.x = bf16x2_bits(f[0], f[1]);
     o.y = bf16x2_bits(f[2], f[3]);
@@ -489,30 +543,51 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // multiply chunk c; with dq, dequantize chunk c + 1 alongside
-  auto compute = [&](int c, bool dq) {
+  struct Ops {
+    bf16x8 a[DWM / 32], b[DWN / 32];
+  };
+  auto read_ops = [&](const uint8_t* xt, const uint8_t* wt, int kk, Ops& o) {
+    const int sg = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < DWM / 32; ++i)
+      o.a[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(DWM * wm + 32 * i + (lane & 31), sg));
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j)
+      o.b[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(DWN * wn + 32 * j + (lane & 31), sg));
+  };
+  // multiply chunk c (operands of step kk + 1 read while step kk multiplies);
+  // with DQ, dequantize chunk c + 1 alongside, one part per step
+  auto compute = [&](int c, auto dq_tag) {
+    constexpr bool DQ = decltype(dq_tag)::value;
     const uint8_t* xt = smem + Lay::X_OFF + (c % DX_STAGES) * DX_BYTES;
     const uint8_t* wt = smem + Lay::W_OFF + (c & 1) * DW_BYTES;
     Dq d;
-    if (dq) dq_load(c + 1, d);
+    if constexpr (DQ) dq_load(c + 1, d);
+    Ops o[2];
+    read_ops(xt, wt, 0, o[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 av[DWM / 32], bv[DWN / 32];
-      const int sg = 2 * kk + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < DWM / 32; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(DWM * wm + 32 * i + (lane & 31), sg));
-#pragma unroll
-      for (int j = 0; j < DWN / 32; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(DWN * wn + 32 * j + (lane & 31), sg));
+      if (kk + 1 < BK / 16) read_ops(xt, wt, kk + 1, o[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < DWM / 32; ++i)
 #pragma unroll
         for (int j = 0; j < DWN / 32; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-      if (dq) dq_part(c + 1, d, kk);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[kk & 1].a[i], o[kk & 1].b[j],
+                                                              acc[i][j], 0, 0, 0);
+      if constexpr (DQ) dq_part(c + 1, d, kk);
     }
   };
+  // columns past n of the last chunk (their X is a re-read of a valid segment)
+  // are set to 0 in LDS, so whatever the weights there, the products are 0
+  auto zero_x_tail = [&](int c) {
+    uint8_t* xt = smem + Lay::X_OFF + (c % DX_STAGES) * DX_BYTES;
+    const int k0 = c * BK;
+    for (int i = tid; i < DM * 8; i += 256) {
+      const int row = i >> 3, sg = i & 7;
+      if (k0 + 8 * sg >= n32) *reinterpret_cast<uint4*>(xt + seg_off(row, sg)) = make_uint4(0, 0, 0, 0);
+    }
+  };
+  const bool tail = c_end * BK > n32;  // this split ends with the partial last chunk
 
   if (c_begin < c_end) {
     // prologue: X of chunks 0, 1 and codes of chunks 0, 1, 2 in flight; chunk 0
@@ -532,24 +607,26 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    for (int c = c0; c < c_end; ++c) {
+    int c = c0;
+    for (; c + 1 < c_end; ++c) {
       // X of c + 2 and codes of c + 3; the wait at the end covers everything
       // issued one iteration ago (X of c + 1, codes of c + 2)
-      const bool full = c + 3 < c_end;
       if (c + 2 < c_end) issue_x(c + 2);
       if (c + 3 < c_end) issue_c(c + 3);
-      if (c + 1 < c_end) {
-        compute(c, true);
-      } else {
-        compute(c, false);
-      }
-      if (full) {
+      compute(c, std::true_type{});
+      if (c + 3 < c_end) {
         __builtin_amdgcn_s_waitcnt(0x0070 | (Lay::ISSUE & 15) | ((Lay::ISSUE >> 4) << 14));
       } else {
         __builtin_amdgcn_s_waitcnt(0x0070);
       }
       __syncthreads();
     }
+    if (tail) {
+      zero_x_tail(c);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
+    }
+    compute(c, std::false_type{});
   }
 
   // ---- epilogue ----
@@ -587,19 +664,50 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 }
 
 // Y[t, r] = sum over splits s = 0, 1, ... of part[s, t, r], in that order.
+// One thread per 4 consecutive outputs of a row; the loads of 8 splits are in
+// flight before their in-order adds.
 __global__ __launch_bounds__(256) void dequant_reduce_kernel(const float* __restrict__ part,
                                                              int64_t ks, int64_t tokens,
                                                              int64_t m, void* Y, int64_t ldy,
                                                              int ybf16) {
+  const int64_t per_row = (m + 3) / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= tokens * m) return;
-  const int64_t t = i / m, r = i - t * m;
-  float s = 0.0f;
-  for (int64_t k = 0; k < ks; ++k) s += part[k * tokens * m + i];
-  if (ybf16) {
-    reinterpret_cast<__bf16*>(Y)[t * ldy + r] = (__bf16)s;
+  if (i >= tokens * per_row) return;
+  const int64_t t = i / per_row, r0 = 4 * (i - t * per_row);
+  const int64_t plane = tokens * m;
+  const float* src = part + t * m + r0;
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (r0 + 4 <= m && (m & 3) == 0) {
+    int64_t k = 0;
+    for (; k + 8 <= ks; k += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (k + u) * plane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s[0] += v[u].x;
+        s[1] += v[u].y;
+        s[2] += v[u].z;
+        s[3] += v[u].w;
+      }
+    }
+    for (; k < ks; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(src + k * plane);
+      s[0] += v.x;
+      s[1] += v.y;
+      s[2] += v.z;
+      s[3] += v.w;
+    }
   } else {
-    reinterpret_cast<float*>(Y)[t * ldy + r] = s;
+    for (int64_t k = 0; k < ks; ++k)
+      for (int e = 0; e < 4 && r0 + e < m; ++e) s[e] += src[k * plane + e];
+  }
+  for (int e = 0; e < 4 && r0 + e < m; ++e) {
+    if (ybf16) {
+      reinterpret_cast<__bf16*>(Y)[t * ldy + r0 + e] = (__bf16)s[e];
+    } else {
+      reinterpret_cast<float*>(Y)[t * ldy + r0 + e] = s[e];
+    }
   }
 }
 
@@ -637,21 +745,14 @@ struct Shape {
 // the token side and split K until the grid holds ~4 workgroups per CU.
 Shape choose_shape(int64_t tokens, int64_t m, int64_t n) {
   Shape s;
-  if (tokens > 128) {
-    s.bm = 256;
-    s.bn = 128;
-  } else if (tokens > 32) {
-    s.bm = 128;
-    s.bn = 128;
-  } else {
-    s.bm = 32;
-    s.bn = 64;
-  }
+  s.bm = tokens > 128 ? 256 : (tokens > 32 ? 128 : 32);
+  s.bn = 128;
   const int64_t tiles = ceil_div(tokens, s.bm) * ceil_div(m, s.bn);
   const int64_t nchunks = ceil_div(n, BK);
-  // split K until the grid holds ~4 workgroups per CU (small batches) or one
-  // per CU (256-token tiles, one resident per CU), keeping >= 4 (8) chunks per split
-  const int64_t want = tokens <= 128 ? 1024 : 256;
+  // split K until the grid holds ~2 workgroups per CU for small batches (each
+  // keeps several chunks of codes in flight) or one per CU for 256-token tiles
+  // (one resident per CU), keeping >= 4 (8) chunks per split
+  const int64_t want = tokens <= 128 ? 512 : 256;
   const int64_t min_chunks = tokens <= 128 ? 4 : 8;
   s.ks = 1;
   while (tiles * s.ks * 2 <= want && nchunks / (s.ks * 2) >= min_chunks) s.ks *= 2;
@@ -668,10 +769,21 @@ hipError_t launch_tile(const DqArgs& a, hipStream_t stream) {
 }
 
 template <int BITS>
-hipError_t launch_dma(const DqArgs& a, hipStream_t stream) {
+hipError_t launch_dma(const DqArgs& a, int tm, hipStream_t stream) {
   const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
-  hipLaunchKernelGGL((dequant_gemm_dma_kernel<BITS>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     a);
+  switch (tm) {
+    case 256:
+      hipLaunchKernelGGL((dequant_gemm_dma_kernel<BITS, 256>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL((dequant_gemm_dma_kernel<BITS, 128>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((dequant_gemm_dma_kernel<BITS, 32>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -680,7 +792,7 @@ hipError_t launch_bits(const DqArgs& a, int bm, hipStream_t stream) {
   switch (bm) {
     case 256: return launch_tile<BITS, 256, 128, 64, 64>(a, stream);
     case 128: return launch_tile<BITS, 128, 128, 64, 64>(a, stream);
-    default: return launch_tile<BITS, 32, 64, 32, 32>(a, stream);
+    default: return launch_tile<BITS, 32, 128, 32, 32>(a, stream);
   }
 }
 
@@ -736,20 +848,20 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
   a.nchunks = ceil_div(d.n, BK);
   a.chunks_per_split = ceil_div(a.nchunks, s.ks);
   a.ntiles = a.ntb * a.nrb * a.ks;
-  // the DMA kernel: 256-token tiles, 16-byte X rows (n % 8 == 0, aligned), one
-  // group per row and chunk, codes of <= 6 bits (LDS budget), 32-bit offsets
-  const bool dma = s.bm == 256 && d.n % 8 == 0 && d.bits <= 6 &&
+  // the DMA kernel: 16-byte X rows (n % 8 == 0, aligned), one group per row and
+  // chunk, codes of <= 6 bits (LDS budget), 32-bit offsets
+  const bool dma = d.n % 8 == 0 && d.bits <= 6 &&
                    (d.group_size <= 0 || d.group_size % 64 == 0) && a.ldx % 8 == 0 &&
                    (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 && a.ldx < (int64_t(1) << 23) &&
                    d.ldp < (int64_t(1) << 23);
   hipError_t e;
   if (dma) {
     switch (d.bits) {
-      case 2: e = launch_dma<2>(a, stream); break;
-      case 3: e = launch_dma<3>(a, stream); break;
-      case 4: e = launch_dma<4>(a, stream); break;
-      case 5: e = launch_dma<5>(a, stream); break;
-      default: e = launch_dma<6>(a, stream); break;
+      case 2: e = launch_dma<2>(a, s.bm, stream); break;
+      case 3: e = launch_dma<3>(a, s.bm, stream); break;
+      case 4: e = launch_dma<4>(a, s.bm, stream); break;
+      case 5: e = launch_dma<5>(a, s.bm, stream); break;
+      default: e = launch_dma<6>(a, s.bm, stream); break;
     }
   } else {
     switch (d.bits) {
@@ -763,7 +875,7 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
     }
   }
   if (e != hipSuccess || s.ks == 1) return e;
-  const int64_t total = d.tokens * d.m;
+  const int64_t total = d.tokens * ceil_div(d.m, 4);
   hipLaunchKernelGGL(dequant_reduce_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
                      stream, a.part, s.ks, d.tokens, d.m, d.Y, d.ldy, a.ybf16);
   return hipGetLastError();
