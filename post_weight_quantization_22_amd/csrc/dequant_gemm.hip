@@ -663,6 +663,185 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode batches (<= 32 tokens), n a multiple of 128: bound by the codes' HBM
+// traffic and by how many cache lines the loads touch, so the codes never go
+// through LDS.  A workgroup of 4 waves owns 128 weight rows (32 per wave) and a
+// K range walked in 128-position steps.  Per step each lane loads the 64
+// codes of its row that its MFMA operands need (lane group g = lane / 32 takes
+// positions 64 g .. 64 g + 63: 2 adjacent 16-byte loads for 4-bit codes, one
+// cache line per row) and dequantizes them in registers straight into bf16 B
+// operands; the 32 x 128 X tile of the step is loaded once per workgroup
+// into LDS and read back as A operands with the same position order (step j,
+// lane group g: positions 64 g + 8 j .. + 8).  Loads run one step (two chunks)
+// ahead; K splits across workgroups are added by dequant_reduce_kernel.
+constexpr int GV_STEP = 128;          // positions per pipeline step
+constexpr int GV_ROWB = GV_STEP * 2;  // bytes of one X row of a step
+constexpr int GV_MAXG = 32;           // quantization groups per workgroup K range
+
+// X tile of a step: 32 rows of 16 segments; segment s of row r at s ^ (r & 15)
+__device__ __forceinline__ int gv_off(int r, int s) { return r * GV_ROWB + ((s ^ (r & 15)) << 4); }
+
+template <int BITS>
+__global__ __launch_bounds__(256) void dequant_gemv_kernel(DqArgs a) {
+  __shared__ __align__(16) uint8_t xs[2][32 * GV_ROWB];
+  __shared__ float zsc[GV_MAXG][128], zzp[GV_MAXG][128];  // scale, zero: [group][row]
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, idx = b / kXcds;
+  const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return;
+  const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int64_t rb = L % a.nrb;
+  const int64_t kspl = L / a.nrb;
+  const int64_t row0 = rb * 128;
+  // chunks_per_split counts 128-position steps here
+  const int s_begin = (int)(kspl * a.chunks_per_split);
+  const int s_end = (int)min(a.nchunks, (int64_t)s_begin + a.chunks_per_split);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t rw0 = row0 + 32 * wv;  // this wave's first weight row
+  const int64_t r = min(rw0 + l32, a.m - 1);
+  const uint32_t* crow = a.P + r * a.ldp + g * (2 * BITS);
+  // X staging: thread -> token tid / 8 (rows past the last token re-read row 0;
+  // their sums are never written), segments 2 (tid % 8), + 1
+  const int xt_row = tid >> 3, xt_seg = 2 * (tid & 7);
+  const uint16_t* xsrc = a.X + (xt_row < a.tokens ? xt_row : 0) * a.ldx + 8 * xt_seg;
+  // the group parameters of the workgroup's K range, staged once (after the
+  // first steps' code loads are in flight, so the two latencies overlap)
+  const int G = (int)a.G;
+  const int g_first = G > 0 ? (s_begin * GV_STEP) / G : 0;
+  const int g_cnt = G > 0 ? min((int)a.ngroups, (s_end * GV_STEP + G - 1) / G) - g_first : 1;
+  const int wrow = 32 * wv + l32;  // this lane's row within the workgroup
+
+  struct Ld {
+    uint32_t w[2 * BITS];  // codes 64 g .. 64 g + 63 of the step
+    uint4 x[2];            // this thread's share of the X tile
+    int st;                // the step
+  };
+  auto load = [&](int st, Ld& d) {
+    const uint32_t* src = crow + st * (4 * BITS);
+#pragma unroll
+    for (int q = 0; q < 2 * BITS; ++q) d.w[q] = src[q];
+    const int k0 = st * GV_STEP;
+    d.x[0] = *reinterpret_cast<const uint4*>(xsrc + k0);
+    d.x[1] = *reinterpret_cast<const uint4*>(xsrc + k0 + 8);
+    d.st = st;
+  };
+  auto stage_x = [&](const Ld& d, int buf) {
+    *reinterpret_cast<uint4*>(&xs[buf][gv_off(xt_row, xt_seg)]) = d.x[0];
+    *reinterpret_cast<uint4*>(&xs[buf][gv_off(xt_row, xt_seg + 1)]) = d.x[1];
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+  // lane group g's 64 codes are the half g of the step: half g's parameters
+  auto step = [&](const Ld& d, int buf) {
+    const int gi = G > 0 ? (d.st * GV_STEP + 64 * g) / G - g_first : 0;
+    const float sc = zsc[gi][wrow];
+    const float nzs = -(zzp[gi][wrow] * sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f[8];
+      uint32_t w4[BITS];
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) w4[q] = d.w[(j >> 2) * BITS + q];
+      decode8<BITS>(w4, j & 3, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fmaf(f[e], sc, nzs);
+      uint4 o;
+      o.x = bf16x2_bits(f[0], f[1]);
+      o.y = bf16x2_bits(f[2], f[3]);
+      o.z = bf16x2_bits(f[4], f[5]);
+      o.w = bf16x2_bits(f[6], f[7]);
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&xs[buf][gv_off(l32, 8 * g + j)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, o), acc, 0, 0,
+                                                    0);
+    }
+  };
+
+  // Pipeline: step i multiplies from X buffer i % 2; then step i + 2 is loaded
+  // into the registers step i has just consumed and the X of step i + 1 (loaded
+  // one step ago) is staged into the other buffer, so two steps of loads are in
+  // flight while a wave waits.  Loads are issued
+  // unconditionally inside the loop and the last steps are peeled, so every
+  // path issues a fixed sequence and the waits only cover the step in use.
+  auto stage_groups = [&]() {
+    for (int i = tid; i < g_cnt * 128; i += 256) {
+      const int j = i >> 7, rr = i & 127;
+      const int64_t rsrc = min(row0 + rr, a.m - 1);
+      zsc[j][rr] = a.scales[rsrc * a.ngroups + g_first + j];
+      zzp[j][rr] = a.zeros[rsrc * a.ngroups + g_first + j];
+    }
+  };
+  const int nst = s_end - s_begin;
+  Ld d0, d1;
+  // (scheduling barriers keep the compiler from hoisting the next step's
+  // work, and with it a wait on loads just issued, above the barrier)
+  auto half = [&](Ld& cur, Ld& nxt, int buf, bool stage_next, int load_step) {
+    step(cur, buf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (load_step >= 0) load(load_step, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (stage_next) stage_x(nxt, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (nst == 1) {
+    load(s_begin, d0);
+    stage_groups();
+    stage_x(d0, 0);
+    __syncthreads();
+    step(d0, 0);
+  } else if (nst > 1) {
+    load(s_begin, d0);
+    load(s_begin + 1, d1);
+    stage_groups();
+    stage_x(d0, 0);
+    __syncthreads();
+    int i = 0;
+    for (; i + 3 < nst; i += 2) {
+      half(d0, d1, 0, true, s_begin + i + 2);
+      half(d1, d0, 1, true, s_begin + i + 3);
+    }
+    if (nst - i == 3) {
+      half(d0, d1, 0, true, s_begin + i + 2);
+      half(d1, d0, 1, true, -1);
+      step(d0, 0);
+    } else {
+      half(d0, d1, 0, true, -1);
+      step(d1, 1);
+    }
+  }
+
+  // lane holds weight row rw0 + (lane & 31), tokens 8 (q / 4) + 4 (lane / 32) + q % 4
+  float* outf;
+  int64_t ld;
+  if (a.ks > 1) {
+    outf = a.part + kspl * a.tokens * a.m;
+    ld = a.m;
+  } else {
+    outf = reinterpret_cast<float*>(a.Y);
+    ld = a.ldy;
+  }
+  const int64_t rr = rw0 + l32;
+  if (rr < a.m) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tt = 8 * (q >> 2) + 4 * g + (q & 3);
+      if (tt >= a.tokens) continue;
+      const int64_t o = tt * ld + rr;
+      if (a.ks == 1 && a.ybf16) {
+        reinterpret_cast<__bf16*>(a.Y)[o] = (__bf16)acc[q];
+      } else {
+        outf[o] = acc[q];
+      }
+    }
+  }
+}
+
 // Y[t, r] = sum over splits s = 0, 1, ... of part[s, t, r], in that order.
 // One thread per 4 consecutive outputs of a row; the loads of 8 splits are in
 // flight before their in-order adds.
@@ -747,14 +926,24 @@ Shape choose_shape(int64_t tokens, int64_t m, int64_t n) {
   Shape s;
   s.bm = tokens > 128 ? 256 : (tokens > 32 ? 128 : 32);
   s.bn = 128;
-  const int64_t tiles = ceil_div(tokens, s.bm) * ceil_div(m, s.bn);
   const int64_t nchunks = ceil_div(n, BK);
-  // split K until the grid holds ~2 workgroups per CU for small batches (each
-  // keeps several chunks of codes in flight) or one per CU for 256-token tiles
-  // (one resident per CU), keeping >= 4 (8) chunks per split
+  s.ks = 1;
+  if (tokens <= 32) {
+    // decode batches: 128-row workgroups, K split until ~2 workgroups per CU,
+    // >= 2 steps of 128 positions per split (both steps' codes in flight at once)
+    const int64_t tiles = ceil_div(m, 128);
+    const int64_t steps = ceil_div(n, 128);
+    while (tiles * s.ks * 2 <= 512 && steps / (s.ks * 2) >= 2) s.ks *= 2;
+    // the group parameters of a split are staged in LDS: at most 16 steps
+    // (2048 positions, 32 groups of 64) per split
+    while (ceil_div(steps, s.ks) > 16) s.ks *= 2;
+    return s;
+  }
+  const int64_t tiles = ceil_div(tokens, s.bm) * ceil_div(m, s.bn);
+  // split K until the grid holds ~2 workgroups per CU (128-token tiles) or one
+  // per CU (256-token tiles, one resident per CU), keeping >= 4 (8) chunks per split
   const int64_t want = tokens <= 128 ? 512 : 256;
   const int64_t min_chunks = tokens <= 128 ? 4 : 8;
-  s.ks = 1;
   while (tiles * s.ks * 2 <= want && nchunks / (s.ks * 2) >= min_chunks) s.ks *= 2;
   return s;
 }
@@ -855,7 +1044,34 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
                    (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 && a.ldx < (int64_t(1) << 23) &&
                    d.ldp < (int64_t(1) << 23);
   hipError_t e;
-  if (dma) {
+  const int64_t gv_steps = d.n / GV_STEP;
+  const int64_t gv_per_split = ceil_div(gv_steps, s.ks);
+  const bool gv = dma && s.bm == 32 && d.n % GV_STEP == 0 &&
+                  (d.group_size <= 0 || ceil_div(gv_per_split * GV_STEP, d.group_size) + 1 <= GV_MAXG);
+  if (gv) {
+    a.nrb = ceil_div(d.m, 128);
+    a.nchunks = gv_steps;
+    a.chunks_per_split = gv_per_split;
+    a.ntiles = a.nrb * a.ks;
+    const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
+    switch (d.bits) {
+      case 2:
+        hipLaunchKernelGGL(dequant_gemv_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        break;
+      case 3:
+        hipLaunchKernelGGL(dequant_gemv_kernel<3>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        break;
+      case 4:
+        hipLaunchKernelGGL(dequant_gemv_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        break;
+      case 5:
+        hipLaunchKernelGGL(dequant_gemv_kernel<5>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        break;
+      default:
+        hipLaunchKernelGGL(dequant_gemv_kernel<6>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    }
+    e = hipGetLastError();
+  } else if (dma) {
     switch (d.bits) {
       case 2: e = launch_dma<2>(a, s.bm, stream); break;
       case 3: e = launch_dma<3>(a, s.bm, stream); break;
