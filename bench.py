@@ -163,6 +163,73 @@ def cpu_baseline(wl, rows: int, chunks: int):
     }
 
 
+def dequant_gemm_measure(gq, buf, X, m, n, q, stream):
+    """The quantized layer used: Y = X W_q^T from its packed codes (gptq_dequant_gemm).
+
+    prefill: one 2048-token calibration sequence, bound by bf16 MFMA (2 tokens m n
+    flop); decode: 16 tokens, bound by HBM (codes b/8 B, scale and zero 8 B per
+    group, X and Y once per weight).  The decode launches are replayed from a
+    HIP graph so that the host's launch cost is not timed."""
+    import torch
+
+    out = {}
+    ng = buf.scales.shape[1]
+    for name, tokens, reps in (("prefill_2048", 2048, 20), ("decode_16", 16, 200)):
+        Xt = X[:tokens]
+        Y = torch.empty((tokens, m), dtype=torch.float32, device=X.device)
+        nws = gq.gptq_dequant_gemm_workspace_size(tokens, m, n, False)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=X.device)
+
+        def call():
+            gq.gptq_dequant_gemm(Xt, buf.packed, q.bits, q.group_size, buf.scales, buf.zeros,
+                                 Y, ws=ws, stream=torch.cuda.current_stream())
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        graph = None
+        if tokens <= 32:
+            try:
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(side):
+                    with torch.cuda.graph(graph, stream=side):
+                        for _ in range(reps):
+                            call()
+                torch.cuda.current_stream().wait_stream(side)
+                graph.replay()
+                torch.cuda.synchronize()
+            except Exception as exc:  # capture refused: time plain launches instead
+                graph = None
+                out[name + "_graph_error"] = str(exc)[:200]
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for _ in range(reps):
+                call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flop = 2.0 * tokens * m * n
+        byts = m * n * q.bits / 8 + m * ng * 8 + tokens * n * 2 + tokens * m * 4
+        rec = {"tokens": tokens, "us": round(us, 3), "tflops": round(flop / us / 1e6, 2),
+               "gbs": round(byts / us / 1e3, 1), "timed": "hip graph replay" if graph else
+               "stream launches"}
+        if tokens > 32:
+            rec["roofline"] = {"bound": "mfma", "achieved": rec["tflops"], "peak": BF16_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(rec["tflops"] / BF16_PEAK_TFLOPS, 4)}
+        else:
+            rec["roofline"] = {"bound": "hbm", "achieved": rec["gbs"], "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(rec["gbs"] / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": int(byts)}
+        out[name] = rec
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_record:
@@ -347,6 +414,7 @@ def main():
         "layer_roofline_frac": round(roof_ms / ms_per_step, 4),
         "input_setup_s": round(t_gen, 1),
     }
+    out["dequant_gemm"] = dequant_gemm_measure(gq, buf, X, m, n, q, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_sample_chunks)
     else:
