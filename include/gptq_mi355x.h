@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00010001u /* major 1, minor 1 */
+#define GPTQ_ABI_VERSION 0x00010002u /* major 1, minor 2 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -198,6 +198,27 @@ gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int
                               int32_t group_size, const float* scales, const float* zeros,
                               const int32_t* perm, int64_t m, void* Y, gptq_dtype ydt,
                               int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Forward steps between quantized layers -- "GPTQ deep dive", section 3.1
+ * step 4, and "AWQ, MinMax, GPTQ calibration in Model Optimizer", section 4:
+ * layers are quantized in order and each layer's calibration inputs are the
+ * outputs of the layers already quantized.  In a Llama-style MLP block the
+ * dequantized-weight products are joined by two elementwise steps:
+ *
+ *   gptq_swiglu:       h = bf16(silu(gate) * up), silu(g) = g / (1 + e^-g)
+ *   gptq_residual_add: out = bf16(x + y)
+ *
+ * gate, up, y: fp32 [tokens, n] (row strides ldg, ldu, ldy >= n), as
+ * gptq_dequant_gemm writes them; x, h, out: bf16 [tokens, n] (strides >= n).
+ * fp32 arithmetic, rounded once to bf16 (nearest even).  out may alias x.
+ * tokens == 0 or n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_swiglu(const float* gate, int64_t ldg, const float* up, int64_t ldu,
+                        int64_t tokens, int64_t n, void* h, int64_t ldh, hipStream_t stream);
+gptq_status gptq_residual_add(const void* x, int64_t ldx, const float* y, int64_t ldy,
+                              int64_t tokens, int64_t n, void* out, int64_t ldo,
+                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Round-to-nearest baseline -- "GPTQ deep dive", section 1.2 (RTN rounds each

@@ -23,7 +23,9 @@ from ._lib import (  # noqa: F401
     gptq_prepare_workspace_size,
     gptq_quantize_layer,
     gptq_quantize_workspace_size,
+    gptq_residual_add,
     gptq_status_str,
+    gptq_swiglu,
     make_config,
     rtn_minmax,
 )

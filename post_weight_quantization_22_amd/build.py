@@ -1,6 +1,8 @@
 """Build step: compile the gfx950 HIP sources into libgptq_mi355x.so (in-tree).
 
-Usable as ``python -m post_weight_quantization_22_amd.build``.  Object files go
+Run as a script, ``python post_weight_quantization_22_amd/build.py`` (it uses
+only the standard library, so it does not import the package, which loads the
+library it builds).  Object files go
 to ``_build/`` at the repository root; the shared library lands next to this
 file, where the binding loads it.
 """

@@ -198,6 +198,23 @@ gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int
   return hip_status(launch_dequant_gemm(d, stream));
 }
 
+gptq_status gptq_swiglu(const float* gate, int64_t ldg, const float* up, int64_t ldu,
+                        int64_t tokens, int64_t n, void* h, int64_t ldh, hipStream_t stream) {
+  if (tokens < 0 || bad_dim(tokens) || n < 0 || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0 || n == 0) return GPTQ_OK;
+  if (!gate || !up || !h || ldg < n || ldu < n || ldh < n) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_swiglu(gate, ldg, up, ldu, tokens, n, h, ldh, stream));
+}
+
+gptq_status gptq_residual_add(const void* x, int64_t ldx, const float* y, int64_t ldy,
+                              int64_t tokens, int64_t n, void* out, int64_t ldo,
+                              hipStream_t stream) {
+  if (tokens < 0 || bad_dim(tokens) || n < 0 || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0 || n == 0) return GPTQ_OK;
+  if (!x || !y || !out || ldx < n || ldy < n || ldo < n) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_residual_add(x, ldx, y, ldy, tokens, n, out, ldo, stream));
+}
+
 gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
                        int32_t bits, int32_t group_size, int32_t sym, uint8_t* codes,
                        float* scales, float* zeros, hipStream_t stream) {

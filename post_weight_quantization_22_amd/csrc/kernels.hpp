@@ -66,4 +66,10 @@ struct DequantArgs {
 size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm);
 hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream);
 
+// ---- forward.hip ----------------------------------------------------------
+hipError_t launch_swiglu(const float* G, int64_t ldg, const float* U, int64_t ldu, int64_t rows,
+                         int64_t n, void* H, int64_t ldh, hipStream_t stream);
+hipError_t launch_residual_add(const void* X, int64_t ldx, const float* Y, int64_t ldy,
+                               int64_t rows, int64_t n, void* O, int64_t ldo, hipStream_t stream);
+
 }  // namespace gptq
