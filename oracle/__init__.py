@@ -22,7 +22,8 @@ It is a plain, slow, obviously-correct restatement of the method on these pages:
   (dequantization r = (q - zero_point) * scale), used by the dequantized-weight
   product of "LLM quantization principles" §5.2.
 * "AWQ, MinMax, GPTQ calibration in Model Optimizer" (gtnt.cn news 115337):
-  §4 (block_size a multiple of group_size, perc_damp 0.01).
+  §4 (block_size a multiple of group_size, perc_damp 0.01; layers quantized in
+  order on the quantized network's activations, in ``stack.py``).
 
 Floating point is fp64 throughout, except where a floating value decides an
 integer (a code, a zero-point): there the decision is taken in fp32, the
@@ -55,3 +56,4 @@ from .gptq import (  # noqa: F401
 )
 from .pack import pack_ref, unpack_ref  # noqa: F401
 from .dequant import dequant_weights, dequant_matmul  # noqa: F401
+from . import stack  # noqa: F401,E402  (layer-sequential MLP stack)

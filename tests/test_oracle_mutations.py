@@ -20,11 +20,13 @@ HESS_MOD = sys.modules["oracle.hessian"]
 PREP_MOD = sys.modules["oracle.prepare"]
 QUANT_MOD = sys.modules["oracle.quantizer"]
 DEQ_MOD = sys.modules["oracle.dequant"]
+STACK_MOD = sys.modules["oracle.stack"]
 
 import test_oracle_gptq as tg
 import test_oracle_hessian_prepare as th
 import test_oracle_quantizer as tq
 import test_oracle_dequant as td
+import test_oracle_stack as tst
 
 
 def _mutant(mod, old, new):
@@ -79,6 +81,14 @@ MUTANTS = [
     (DEQ_MOD, "s = np.asarray(scales, dtype=np.float64)[:, g]",
      "s = np.asarray(scales, dtype=np.float64)[:, np.sort(g)]", ["dequant_matmul"],
      lambda gd: td.test_dequant_matmul_brute_force(3)),
+    (STACK_MOD, "h = to_bf16(silu(x @ gate.Wq.T) * (x @ up.Wq.T))",
+     "h = to_bf16(silu(x @ np.asarray(Wg, np.float64).T) * (x @ up.Wq.T))", ["stack"],
+     lambda gd: tst.test_hessians_come_from_the_quantized_network(False)),
+    (STACK_MOD, "x_next = to_bf16(x + h @ down.Wq.T)", "x_next = to_bf16(h @ down.Wq.T)",
+     ["stack"], lambda gd: tst.test_zero_weights_pass_the_input_through()),
+    (STACK_MOD, "return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+     "return np.ldexp(np.rint(np.ldexp(m, 9)), e - 9)", ["stack"],
+     lambda gd: tst.test_to_bf16_hand_values()),
 ]
 
 
@@ -86,6 +96,12 @@ MUTANTS = [
 def test_pins_catch_planted_mistake(idx, monkeypatch, golden_dir):
     mod, old, new, names, pin = MUTANTS[idx]
     m = _mutant(mod, old, new)
+    if mod is STACK_MOD:
+        # the stack pins call the module's functions by name and through oracle.stack
+        monkeypatch.setattr(oracle, "stack", m)
+        for nm in ("quantize_stack", "float_stack", "silu", "to_bf16"):
+            monkeypatch.setattr(tst, nm, getattr(m, nm))
+        names = []
     for nm in names:
         monkeypatch.setattr(oracle, nm, getattr(m, nm))
     # quantizer mutants must also reach the loop, which imported the name directly
