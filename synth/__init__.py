@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     get_workload,
     outlier_channels,
     round_to_bf16,
+    stack_workload,
     weight,
     x_all,
     x_chunk,

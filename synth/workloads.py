@@ -173,6 +173,36 @@ def custom_workload(name: str, m: int, n: int, tokens: int, chunk_len: int, *,
         description=f"custom {m}x{n}, {tokens} tokens")
 
 
+def stack_workload(name: str, d: int, f: int, blocks: int, tokens: int, chunk_len: int, *,
+                   w_sigma: float = 0.02, x_dist: str = "student_t4",
+                   outlier_frac: float = 0.0, outlier_mult: float = 1.0, bits: int = 4,
+                   group_size: int = 128, block_size: int = 128, perc_damp: float = 0.01,
+                   desc_act: bool = True, sym: bool = False, workload_id: int = 200,
+                   seed: int = 0) -> Workload:
+    """A stack of Llama-style MLP blocks: per block k the layers gate_k, up_k
+    ([f, d]) and down_k ([d, f]), bf16 N(0, w_sigma^2); the stack's input stream
+    "x0" [tokens, d] bf16.  Only the input is drawn: the inputs of later layers
+    are what the quantized layers before them produce."""
+    if tokens % chunk_len:
+        raise ValueError("tokens must be a multiple of chunk_len")
+    layers = []
+    for k in range(blocks):
+        layers += [LayerSpec(f"gate_{k}", f, d, w_sigma, "bf16", 20 + 3 * k, "x0"),
+                   LayerSpec(f"up_{k}", f, d, w_sigma, "bf16", 21 + 3 * k, "x0"),
+                   LayerSpec(f"down_{k}", d, f, w_sigma, "bf16", 22 + 3 * k, "x0")]
+    return Workload(
+        name=name, workload_id=workload_id, seed=seed, layers=tuple(layers),
+        xs={"x0": XSpec(2, d, tokens // chunk_len, chunk_len, x_dist, outlier_frac,
+                        outlier_mult, "bf16")},
+        quant=QuantSpec(bits, group_size, block_size, perc_damp, desc_act, sym),
+        description=f"{blocks} MLP blocks d={d} f={f}, {tokens} tokens")
+
+
+# A two-block stack of Llama-7B MLP blocks (d 4096, f 11008) on the MLP
+# workload's activation recipe, 4-bit g128 desc_act: the layer-sequential case.
+_register(stack_workload("llama7b_mlp_stack", 4096, 11008, 2, 128 * 2048, 2048, workload_id=6))
+
+
 # ----------------------------------------------------------------------------
 # generators
 # ----------------------------------------------------------------------------
