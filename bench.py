@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the layer-sequential MLP-stack measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=128)
     ap.add_argument("--cpu-sample-chunks", type=int, default=2)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -228,6 +230,52 @@ def dequant_gemm_measure(gq, buf, X, m, n, q, stream):
                                "algorithmic_bytes": int(byts)}
         out[name] = rec
     return out
+
+
+def stack_measure(gq, dev):
+    """Layer-sequential GPTQ of a two-block Llama-7B MLP stack (d 4096, f 11008,
+    128 x 2048 calibration tokens, 4-bit g128 desc_act): each layer quantized on
+    the activations the already-quantized layers produce, gate and up on one
+    Hessian.  One warm-up run (allocations), then one timed run with events at
+    the phase boundaries on the stream."""
+    import numpy as np
+    import torch
+
+    import synth
+    from post_weight_quantization_22_amd import stack
+
+    wl = synth.get_workload("llama7b_mlp_stack")
+    xs = wl.xs["x0"]
+    q = wl.quant
+    t0 = time.time()
+    x0 = torch.empty((xs.tokens, xs.n), dtype=torch.bfloat16, device=dev)
+    for c0 in range(0, xs.chunks, 16):
+        idx = list(range(c0, min(xs.chunks, c0 + 16)))
+        x0[c0 * xs.chunk_len:(c0 + len(idx)) * xs.chunk_len].copy_(
+            torch.from_numpy(synth.x_all(wl, "x0", chunks=idx)).to(torch.bfloat16))
+    blocks = len(wl.layers) // 3
+    W = [tuple(torch.from_numpy(synth.weight(wl, f"{nm}_{k}")).to(dev).to(torch.bfloat16)
+               for nm in ("gate", "up", "down")) for k in range(blocks)]
+    t_gen = time.time() - t0
+    cfg = gq.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
+    stack.quantize_stack(x0, W, cfg)
+    torch.cuda.synchronize()
+    marks = []
+    stack.quantize_stack(x0, W, cfg, marks=marks)
+    torch.cuda.synchronize()
+    phases = {}
+    for (_, e0), (nm, e1) in zip(marks[:-1], marks[1:]):
+        phases[nm] = phases.get(nm, 0.0) + e0.elapsed_time(e1)
+    total = marks[0][1].elapsed_time(marks[-1][1])
+    weights = sum(l.m * l.n for l in wl.layers)
+    return {
+        "workload": f"{blocks} Llama-7B MLP blocks (gate/up 11008x4096, down 4096x11008), "
+                    f"{xs.tokens} calibration tokens, {q.bits}-bit g{q.group_size}, desc_act",
+        "ms": round(total, 2),
+        "weights_per_s": round(weights / (total * 1e-3), 1),
+        "phase_ms": {k: round(v, 2) for k, v in phases.items()},
+        "input_setup_s": round(t_gen, 1),
+    }
 
 
 def main():
@@ -415,6 +463,10 @@ def main():
         "input_setup_s": round(t_gen, 1),
     }
     out["dequant_gemm"] = dequant_gemm_measure(gq, buf, X, m, n, q, stream)
+    if not args.no_stack:
+        del X
+        torch.cuda.empty_cache()
+        out["layer_sequential"] = stack_measure(gq, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_sample_chunks)
     else:

@@ -81,20 +81,30 @@ def _product(prod: _Products, X: torch.Tensor, L: QuantizedLayer, slot: str,
 def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch.Tensor,
                                                              torch.Tensor]],
                    cfg: _lib.GPTQConfig, chunk_tokens: int = 16384, keep: bool = False,
-                   stream=None) -> Tuple[List[QuantizedBlock], torch.Tensor]:
+                   stream=None, marks: Optional[list] = None
+                   ) -> Tuple[List[QuantizedBlock], torch.Tensor]:
     """Quantize every block of the stack in order; returns the blocks and the
     quantized network's output activations (bf16 [tokens, d]).
 
     x0: bf16 [tokens, d] calibration activations (device).  weights: per block
     (Wg [f, d], Wu [f, d], Wd [d, f]) bf16 or fp32 device tensors.  Enqueued on
-    ``stream`` (default: the current stream); the data-error words are checked
-    (a synchronization) after each layer's quantization."""
+    ``stream`` (default: the current stream); the data-error words of a block's
+    three layers are checked (a synchronization) at the end of the block.  ``marks``: if a list,
+    (phase, event) pairs are appended, each event recorded on ``stream`` at the
+    end of the phase (timing only)."""
     if stream is None:
         stream = torch.cuda.current_stream()
     dev = x0.device
     T, d = x0.shape
     desc = bool(cfg.desc_act)
     prod = _Products(dev)
+    def mark(name):
+        if marks is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            marks.append((name, ev))
+
+    mark("start")
     x = x0
     blocks = []
     for Wg, Wu, Wd in weights:
@@ -104,13 +114,14 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
         bu = pipeline.allocate(f, d, cfg, 0, device=dev)
         bg.S.zero_()
         pipeline.accumulate(bg, [x], stream)
+        mark("hessian")
         pipeline.prepare(bg, T, stream)
+        mark("prepare")
         bu.S, bu.U, bu.perm, bu.dead = bg.S, bg.U, bg.perm, bg.dead  # shared Hessian
         pipeline.quantize(bg, Wg, stream)
         pipeline.quantize(bu, Wu, stream)
-        pipeline.check_info(bg)
-        pipeline.check_info(bu)
         gate, up = _packed(bg, desc, stream), _packed(bu, desc, stream)
+        mark("quantize")
         # h = silu(x Wg_q^T) * (x Wu_q^T), chunk by chunk
         h = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
         for t0 in range(0, T, chunk_tokens):
@@ -118,20 +129,26 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
             g = _product(prod, x[t0:t1], gate, "g", stream)
             u = _product(prod, x[t0:t1], up, "u", stream)
             _lib.gptq_swiglu(g, u, h[t0:t1], stream=stream)
+        mark("forward")
         # down: Hessian of h
         bd = pipeline.allocate(d, f, cfg, T, device=dev)
         bd.S.zero_()
         pipeline.accumulate(bd, [h], stream)
+        mark("hessian")
         pipeline.prepare(bd, T, stream)
+        mark("prepare")
         pipeline.quantize(bd, Wd, stream)
-        pipeline.check_info(bd)
         down = _packed(bd, desc, stream)
+        mark("quantize")
         # x' = x + h Wd_q^T
         x_next = torch.empty_like(x)
         for t0 in range(0, T, chunk_tokens):
             t1 = min(T, t0 + chunk_tokens)
             y = _product(prod, h[t0:t1], down, "y", stream)
             _lib.gptq_residual_add(x[t0:t1], y, x_next[t0:t1], stream=stream)
+        mark("forward")
+        for b in (bg, bu, bd):
+            pipeline.check_info(b)
         blocks.append(QuantizedBlock(gate, up, down, x if keep else None, h if keep else None))
         x = x_next
     return blocks, x
