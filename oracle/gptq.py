@@ -26,6 +26,14 @@ Readings of the pages adopted here:
   block are deferred.  This is the reading under which the result does not
   depend on the block size.
 
+* Static groups (a variant the pages do not describe; the plain reading of
+  the name): every group's parameters are computed once, before the loop,
+  from the original weights, for groups of consecutive original columns.
+* A group spanning several blocks (group_size a multiple of block_size) is
+  read as block_size = group_size ("AWQ, MinMax, GPTQ calibration in Model
+  Optimizer" §4): its parameters come from the current values of its columns
+  at its first column, which is a block start.
+
 ``gptq_obs_literal`` is a second, independent route: it keeps H_d^-1
 explicitly and applies the §2.2 compensation formula column by column, with
 the inverse downdated after each column; it shares only the quantizer.
@@ -58,14 +66,26 @@ def _ngroups(n: int, G: int) -> int:
 def _check_grouping(n: int, G: int, B: int) -> None:
     if B <= 0:
         raise ValueError("block_size must be positive")
-    if G > 0 and B % G != 0:
-        raise ValueError("block_size must be a multiple of group_size")
+    if G > 0 and B % G != 0 and G % B != 0:
+        raise ValueError("block_size must be a multiple of group_size (or group_size of "
+                         "block_size, which computes the same result as block_size = group_size)")
 
 
 def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
                   block_size: int = 128, perm: Optional[np.ndarray] = None,
-                  dead: Optional[np.ndarray] = None, sym: bool = False) -> GPTQResult:
-    """Blocked GPTQ of W [m, n] (original column order) with U from ``prepare``."""
+                  dead: Optional[np.ndarray] = None, sym: bool = False,
+                  static_groups: bool = False) -> GPTQResult:
+    """Blocked GPTQ of W [m, n] (original column order) with U from ``prepare``.
+
+    ``static_groups``: the group parameters are computed once, before the loop,
+    from the original W (dead columns zeroed), for groups of consecutive
+    ORIGINAL columns; a column uses the parameters of its original group, so
+    with desc_act g_idx stays c // G.  Otherwise (dynamic) a group is G
+    consecutive processing positions and its parameters come from the current,
+    compensated values when its first column is reached.  A group larger than
+    the block (G a multiple of B) starts at a block start, where every earlier
+    column's error has been applied to all later columns, so its parameters are
+    those block_size = G would give."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     G, B = group_size, block_size
@@ -83,15 +103,25 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
     if G <= 0:  # one group per row, taken from the whole (unmodified) row
         scale, zero = group_params(Wp, bits, sym)
         scales[:, 0], zeros[:, 0] = scale, zero
+    elif static_groups:
+        W0 = W.copy()
+        if dead is not None:
+            W0[:, np.asarray(dead)] = 0.0
+        for g in range(ng):
+            scales[:, g], zeros[:, g] = group_params(W0[:, g * G:(g + 1) * G], bits, sym)
     for i in range(0, n, B):
         i1 = min(i + B, n)
         W1 = Wp[:, i:i1].copy()
         E = np.zeros((m, i1 - i))
         for j in range(i1 - i):
             c = i + j
-            if G > 0 and c % G == 0:
+            if G > 0 and static_groups:
+                g = int(perm[c]) // G
+                scale, zero = scales[:, g], zeros[:, g]
+            elif G > 0 and c % G == 0:
                 glen = min(G, n - c)
-                scale, zero = group_params(W1[:, j:j + glen], bits, sym)
+                cur = W1[:, j:j + glen] if G <= B else Wp[:, c:c + glen]  # c == i when G > B
+                scale, zero = group_params(cur, bits, sym)
                 scales[:, c // G], zeros[:, c // G] = scale, zero
             w = W1[:, j]
             q = quantize_codes(w, scale, zero, bits)
@@ -105,7 +135,10 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
     codes = np.empty_like(Q)
     codes[:, perm] = Q
     g_idx = np.empty(n, dtype=np.int64)
-    g_idx[perm] = (np.arange(n) // G) if G > 0 else 0
+    if G > 0 and static_groups:
+        g_idx[:] = np.arange(n) // G
+    else:
+        g_idx[perm] = (np.arange(n) // G) if G > 0 else 0
     return GPTQResult(codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, perm=perm,
                       E=Eall, codes_proc=Q)
 
@@ -211,7 +244,8 @@ class ReplayReport:
 def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block_size: int,
                  perm: Optional[np.ndarray], dead: Optional[np.ndarray],
                  codes_proc: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
-                 tau: float = 1e-3, sym: bool = False) -> ReplayReport:
+                 tau: float = 1e-3, sym: bool = False,
+                 static_groups: bool = False) -> ReplayReport:
     """Validate a candidate result column by column against the oracle's own loop.
 
     At a rounding tie both neighbours are correct, and everything downstream
@@ -264,14 +298,25 @@ def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block
 
     if G <= 0:
         scale, zero = take_params(Wp, 0)
+    elif static_groups:
+        W0 = W.copy()
+        if dead is not None:
+            W0[:, np.asarray(dead)] = 0.0
+        for g in range((n + G - 1) // G):
+            take_params(W0[:, g * G:(g + 1) * G], g)
     for i in range(0, n, B):
         i1 = min(i + B, n)
         W1 = Wp[:, i:i1].copy()
         E = np.zeros((m, i1 - i))
         for j in range(i1 - i):
             c = i + j
-            if G > 0 and c % G == 0:
-                scale, zero = take_params(W1[:, j:j + min(G, n - c)], c // G)
+            if G > 0 and static_groups:
+                g = int(perm[c]) // G
+                scale = np.asarray(scales[:, g], np.float64)
+                zero = np.asarray(zeros[:, g], np.float64)
+            elif G > 0 and c % G == 0:
+                cur = W1[:, j:j + min(G, n - c)] if G <= B else Wp[:, c:c + min(G, n - c)]
+                scale, zero = take_params(cur, c // G)
             w = W1[:, j]
             q_o = quantize_codes(w, scale, zero, bits)
             q_c = cq[:, c]

@@ -57,8 +57,8 @@ MUTANTS = [
     (GPTQ_MOD, "e = (w - dequantize(q, scale, zero)) / U[c, c]",
      "e = (w - dequantize(q, scale, zero)) * U[c, c]", ["gptq_quantize"],
      lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
-    (GPTQ_MOD, "scale, zero = group_params(W1[:, j:j + glen], bits, sym)",
-     "scale, zero = group_params(W[:, perm][:, c:c + glen], bits, sym)", ["gptq_quantize"],
+    (GPTQ_MOD, "cur = W1[:, j:j + glen] if G <= B else Wp[:, c:c + glen]",
+     "cur = W[:, perm][:, c:c + glen]", ["gptq_quantize"],
      lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
     (QUANT_MOD, "zero = np.rint(f32(f32(-xmin * maxq) / span))",
      "zero = np.rint(f32(f32(xmin * maxq) / span))", ["group_params"],
