@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00010002u /* major 1, minor 2 */
+#define GPTQ_ABI_VERSION 0x00020000u /* major 2, minor 0 (gptq_config grew) */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -58,12 +58,21 @@ typedef enum gptq_dtype { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
  * gtnt.cn news 115337, section 4). */
 typedef struct gptq_config {
   int32_t bits;       /* 2..8                                                  */
-  int32_t group_size; /* 8, 16, 32, 64 or 128 dividing block_size; -1 = one
-                         group per row spanning all columns                   */
+  int32_t group_size; /* 8, 16, 32, 64 or 128 (dividing block_size), 256 or 512
+                         (a multiple of block_size: computed as block_size =
+                         group_size would, the group's parameters taken where it
+                         starts); -1 = one group per row spanning all columns  */
   int32_t block_size; /* 128 (the only block width built)                      */
   float perc_damp;    /* damping fraction (default 0.01); used by gptq_prepare  */
   int32_t desc_act;   /* 0/1: columns in descending Hessian-diagonal order      */
   int32_t sym;        /* 0 = asymmetric min-max; 1 = symmetric (zero = 2^(b-1)) */
+  int32_t static_groups; /* 0 = a group is group_size consecutive processing
+                         positions, parameters from the current (compensated)
+                         values at its first column; 1 = groups of group_size
+                         consecutive ORIGINAL columns, parameters computed once
+                         from the original weights (dead columns as 0), so that
+                         with desc_act g_idx stays c / group_size.  Not on the
+                         pages; the plain reading of the name.                  */
 } gptq_config;
 
 /* Version of this ABI (GPTQ_ABI_VERSION of the built library). */
@@ -126,8 +135,8 @@ gptq_status gptq_prepare(const float* S, int64_t n, int64_t lds, int64_t tokens,
  * Outputs, all in ORIGINAL column order except where stated:
  *   codes[m, n]  uint8 in [0, 2^bits - 1], row stride n;
  *   scales[m, ngroups], zeros[m, ngroups] fp32 (zeros hold integers), groups
- *                numbered in processing order; ngroups = ceil(n / group_size)
- *                (1 when group_size == -1);
+ *                numbered in processing order (static groups: in original
+ *                order); ngroups = ceil(n / group_size) (1 when group_size == -1);
  *   g_idx[n]     int32 group of each original column (may be NULL);
  *   row_err[m]   fp32 sum over columns of e_c^2 = delta^T H_d delta for the
  *                row's error delta = W - dequant(Q) (may be NULL).

@@ -53,6 +53,7 @@ class GPTQConfig(ctypes.Structure):
         ("perc_damp", ctypes.c_float),
         ("desc_act", ctypes.c_int32),
         ("sym", ctypes.c_int32),
+        ("static_groups", ctypes.c_int32),
     ]
 
 
@@ -214,8 +215,10 @@ def gptq_prepare(S, tokens: int, perc_damp: float, desc_act: bool, U, perm=None,
 
 
 def make_config(bits: int, group_size: int, block_size: int = 128, perc_damp: float = 0.01,
-                desc_act: bool = False, sym: bool = False) -> GPTQConfig:
-    return GPTQConfig(bits, group_size, block_size, perc_damp, int(desc_act), int(sym))
+                desc_act: bool = False, sym: bool = False,
+                static_groups: bool = False) -> GPTQConfig:
+    return GPTQConfig(bits, group_size, block_size, perc_damp, int(desc_act), int(sym),
+                      int(static_groups))
 
 
 def gptq_quantize_workspace_size(m: int, n: int, cfg: GPTQConfig) -> int:

@@ -17,7 +17,7 @@ inline gptq_status hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK :
 inline bool valid_dtype(int dt) { return dt == GPTQ_F32 || dt == GPTQ_BF16; }
 
 inline bool quant_group_ok(int32_t g) {
-  return g == -1 || g == 8 || g == 16 || g == 32 || g == 64 || g == 128;
+  return g == -1 || g == 8 || g == 16 || g == 32 || g == 64 || g == 128 || g == 256 || g == 512;
 }
 
 gptq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -99,8 +99,11 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_
                                 int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!cfg || bad_dim(m) || bad_dim(n) || !valid_dtype(wdt)) return GPTQ_ERR_INVALID_ARG;
   if (cfg->bits < 2 || cfg->bits > 8 || cfg->block_size <= 0 || cfg->group_size == 0 ||
-      (cfg->group_size > 0 && cfg->block_size % cfg->group_size != 0) ||
-      (cfg->desc_act != 0 && cfg->desc_act != 1) || (cfg->sym != 0 && cfg->sym != 1))
+      cfg->group_size < -1 ||
+      (cfg->group_size > 0 && cfg->block_size % cfg->group_size != 0 &&
+       cfg->group_size % cfg->block_size != 0) ||
+      (cfg->desc_act != 0 && cfg->desc_act != 1) || (cfg->sym != 0 && cfg->sym != 1) ||
+      (cfg->static_groups != 0 && cfg->static_groups != 1))
     return GPTQ_ERR_INVALID_ARG;
   if (cfg->block_size != 128 || !quant_group_ok(cfg->group_size)) return GPTQ_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) return GPTQ_OK;
@@ -123,6 +126,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_
   a.block_size = cfg->block_size;
   a.desc_act = cfg->desc_act;
   a.sym = cfg->sym;
+  a.static_groups = cfg->group_size > 0 ? cfg->static_groups : 0;
   a.codes = codes;
   a.scales = scales;
   a.zeros = zeros;

@@ -35,7 +35,7 @@ struct QuantArgs {
   int64_t ldu;
   const int32_t* perm;  // used only when desc_act
   const uint8_t* dead;  // may be null
-  int bits, group_size, block_size, desc_act, sym;
+  int bits, group_size, block_size, desc_act, sym, static_groups;
   uint8_t* codes;
   float* scales;
   float* zeros;

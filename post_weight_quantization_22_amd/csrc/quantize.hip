@@ -112,15 +112,19 @@ __global__ __launch_bounds__(256) void prep_weights_bf16_kernel(const uint16_t* 
   if (bad && info) *info = -1;
 }
 
-// One group per row: parameters from the whole row.
+// Parameters of one group per row from the current values of columns
+// [c0, c0 + len) of W': the whole row (one group per row), or a group that
+// spans several blocks (its first column is a block start).  Written to
+// scales/zeros[r * ngroups + g].
 __global__ __launch_bounds__(256) void row_params_kernel(const float* __restrict__ Wp, int64_t m,
-                                                         int64_t n, float maxq, int sym,
-                                                         float* __restrict__ scales,
+                                                         int64_t n, int64_t c0, int64_t len,
+                                                         int64_t g, int64_t ngroups, float maxq,
+                                                         int sym, float* __restrict__ scales,
                                                          float* __restrict__ zeros) {
   __shared__ float smin[4], smax[4];
   for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
     float vmin = 0.0f, vmax = 0.0f;
-    for (int64_t c = threadIdx.x; c < n; c += blockDim.x) {
+    for (int64_t c = c0 + threadIdx.x; c < c0 + len; c += blockDim.x) {
       const float v = Wp[r * n + c];
       vmin = fminf(vmin, v);
       vmax = fmaxf(vmax, v);
@@ -144,11 +148,38 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* __restrict
       float scale, zero;
       if (sym) sym_params(fmaxf(fabsf(smin[0]), fabsf(smax[0])), maxq, scale, zero);
       else minmax_params(smin[0], smax[0], maxq, scale, zero);
-      scales[r] = scale;
-      zeros[r] = zero;
+      scales[r * ngroups + g] = scale;
+      zeros[r * ngroups + g] = zero;
     }
     __syncthreads();
   }
+}
+
+// Static groups: parameters of every group of G consecutive ORIGINAL columns
+// from the original weights (dead columns as 0), before the loop.  One thread
+// per (row, group).
+__global__ __launch_bounds__(256) void static_params_kernel(const void* __restrict__ W, int dt,
+                                                            int64_t m, int64_t n, int64_t ldw,
+                                                            const uint8_t* __restrict__ dead,
+                                                            int64_t G, int64_t ngroups,
+                                                            float maxq, int sym,
+                                                            float* __restrict__ scales,
+                                                            float* __restrict__ zeros) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= m * ngroups) return;
+  const int64_t r = i / ngroups, g = i - r * ngroups;
+  float vmin = 0.0f, vmax = 0.0f;
+  const int64_t c1 = min(n, (g + 1) * G);
+  for (int64_t c = g * G; c < c1; ++c) {
+    const float v = (dead && dead[c]) ? 0.0f : load_elem(W, dt, r * ldw + c);
+    vmin = fminf(vmin, v);
+    vmax = fmaxf(vmax, v);
+  }
+  float scale, zero;
+  if (sym) sym_params(fmaxf(fabsf(vmin), fabsf(vmax)), maxq, scale, zero);
+  else minmax_params(vmin, vmax, maxq, scale, zero);
+  scales[i] = scale;
+  zeros[i] = zero;
 }
 
 // q = clamp(rne(w / scale) + zero, 0, maxq) with the IEEE quotient w / scale,
@@ -164,15 +195,19 @@ __device__ __forceinline__ float quant_code_fast(float w, float scale, float rsc
   return fminf(fmaxf(q + zero, 0.0f), maxq);
 }
 
-// One 128-column block.  G > 0: group size (8..128, divides 128); G < 0: one
-// group per row with parameters already in scales/zeros (ngroups == 1).
+// One 128-column block.  G > 0: group size (8..128, divides 128), parameters
+// computed here at each group's first column.  G < 0: parameters given in
+// scales/zeros before the block; processing column k takes group
+// (gperm ? gperm[k] : k) / gdiv (one group per row: gdiv = n; a group spanning
+// several blocks: gdiv = its size; static groups: gperm = perm, gdiv = its size).
 // Errors go to E[r, e0 + c] (row stride lde), c < 128.
 template <int G>
 __global__ __launch_bounds__(256) void block_quant_kernel(
     float* __restrict__ Wp, int64_t m, int64_t n, const float* __restrict__ U, int64_t ldu,
     int64_t i0, float maxq, int sym, uint8_t* __restrict__ codes, float* __restrict__ scales,
     float* __restrict__ zeros, int64_t ngroups, float* __restrict__ E, int64_t lde, int64_t e0,
-    float* __restrict__ row_err, int first_block) {
+    float* __restrict__ row_err, int first_block, const int32_t* __restrict__ gperm,
+    int64_t gdiv) {
   __shared__ __align__(16) float Us[BLK][BLK + UPAD];
   __shared__ __align__(16) float uinv[BLK];
   const int tid = threadIdx.x;
@@ -243,12 +278,18 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
   }
 
   float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
+  // given parameters: each lane holds those of its own 8 columns (only the
+  // owner lane's result of a column is used)
+  float sc_own[CPL], z_own[CPL], rs_own[CPL];
   if constexpr (G < 0) {
-    if (rv) {
-      scale = scales[r];
-      zero = zeros[r];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int64_t k = min(cbase + t, n - 1);
+      const int64_t gi = (gperm ? (int64_t)gperm[k] : k) / gdiv;
+      sc_own[t] = rv ? scales[r * ngroups + gi] : 1.0f;
+      z_own[t] = rv ? zeros[r * ngroups + gi] : 0.0f;
+      rs_own[t] = 1.0f / sc_own[t];
     }
-    rscale = 1.0f / scale;
   }
   float e_own[CPL], q_own[CPL];
 #pragma unroll
@@ -292,6 +333,11 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
           zeros[r * ngroups + g] = zero;
         }
       }
+    }
+    if constexpr (G < 0) {
+      scale = sc_own[s];
+      zero = z_own[s];
+      rscale = rs_own[s];
     }
     const float wj = w[s];
     const float q = quant_code_fast(wj, scale, rscale, zero, maxq);
@@ -508,17 +554,18 @@ __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
   if (p >= 0 && p < n) inv[p] = (int32_t)k;
 }
 
-// codes[r, c] = codes_proc[r, inv[c]]; g_idx[c] = inv[c] / G.
+// codes[r, c] = codes_proc[r, inv[c]]; g_idx[c] = inv[c] / G (static groups:
+// c / G, the groups being runs of original columns).
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ cproc,
                                                         const int32_t* __restrict__ inv,
                                                         int64_t m, int64_t n, int64_t G,
-                                                        uint8_t* __restrict__ codes,
+                                                        int gstatic, uint8_t* __restrict__ codes,
                                                         int32_t* __restrict__ g_idx) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
   int64_t k = inv ? inv[c] : c;
   if (k < 0 || k >= n) k = c;
-  if (g_idx && blockIdx.y == 0) g_idx[c] = G > 0 ? (int32_t)(k / G) : 0;
+  if (g_idx && blockIdx.y == 0) g_idx[c] = G > 0 ? (int32_t)((gstatic ? c : k) / G) : 0;
   if (!codes) return;
   for (int64_t r = blockIdx.y; r < m; r += gridDim.y) codes[r * n + c] = cproc[r * n + k];
 }
@@ -568,20 +615,39 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(prep_weights_kernel, grid, dim3(256), 0, stream, a.W, a.wdt, m, n, a.ldw,
                        a.desc_act ? a.perm : nullptr, a.dead, Wp, a.info);
   }
+  // where the parameters come from: computed in the block at each group's
+  // first column (G divides the block), or given: from the whole row (G < 0),
+  // from the original weights (static groups), or, for a group spanning
+  // several blocks, from W' at the block where it starts
+  const bool given = G < 0 || a.static_groups || G > BLK;
+  const int64_t gdiv = G > 0 ? G : n;
+  const int32_t* gperm = (a.static_groups && a.desc_act) ? a.perm : nullptr;
   if (G < 0) {
     hipLaunchKernelGGL(row_params_kernel, dim3((unsigned)hmin(m, 4096)), dim3(256), 0,
-                       stream, Wp, m, n, maxq, a.sym, a.scales, a.zeros);
+                       stream, Wp, m, n, (int64_t)0, n, (int64_t)0, (int64_t)1, maxq, a.sym,
+                       a.scales, a.zeros);
+  } else if (a.static_groups) {
+    hipLaunchKernelGGL(static_params_kernel, dim3((unsigned)ceil_div(m * ngroups, 256)),
+                       dim3(256), 0, stream, a.W, a.wdt, m, n, a.ldw, a.dead, (int64_t)G, ngroups,
+                       maxq, a.sym, a.scales, a.zeros);
   }
   const dim3 qgrid((unsigned)ceil_div(m, QROWS));
   for (int64_t s0 = 0; s0 < n; s0 += SB) {
     const int64_t s1 = hmin(n, s0 + SB);
     for (int64_t i0 = s0; i0 < s1; i0 += BLK) {
       const int first = i0 == 0;
+      if (!a.static_groups && G > BLK && i0 % G == 0) {
+        // a group spanning several blocks starts here: every earlier error
+        // has been applied to its columns (G divides the super-block)
+        hipLaunchKernelGGL(row_params_kernel, dim3((unsigned)hmin(m, 4096)), dim3(256), 0,
+                           stream, Wp, m, n, i0, hmin((int64_t)G, n - i0), i0 / G, ngroups, maxq,
+                           a.sym, a.scales, a.zeros);
+      }
 #define GPTQ_BQ(GV)                                                                              \
   hipLaunchKernelGGL(block_quant_kernel<GV>, qgrid, dim3(256), 0, stream, Wp, m, n, a.U, a.ldu,  \
                      i0, maxq, a.sym, cproc, a.scales, a.zeros, ngroups, E, SB, i0 - s0,        \
-                     a.row_err, first)
-      switch (G) {
+                     a.row_err, first, gperm, gdiv)
+      switch (given ? -1 : G) {
         case 8: GPTQ_BQ(8); break;
         case 16: GPTQ_BQ(16); break;
         case 32: GPTQ_BQ(32); break;
@@ -602,11 +668,11 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
                        a.perm, n, inv);
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(m, 1024));
     hipLaunchKernelGGL(unpermute_kernel, grid, dim3(256), 0, stream, cproc, inv, m, n,
-                       (int64_t)G, a.codes, a.g_idx);
+                       (int64_t)G, a.static_groups, a.codes, a.g_idx);
   } else if (a.g_idx) {
     hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)ceil_div(n, 256), 1), dim3(256), 0, stream,
                        (const uint8_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, n, (int64_t)G,
-                       (uint8_t*)nullptr, a.g_idx);
+                       a.static_groups, (uint8_t*)nullptr, a.g_idx);
   }
   return hipGetLastError();
 }

@@ -85,7 +85,10 @@ def test_quantize_argument_validation(lib):
     assert _quant(so, C(9, 128)) == lib.GPTQ_ERR_INVALID_ARG          # bits > 8
     assert _quant(so, C(1, 128)) == lib.GPTQ_ERR_INVALID_ARG          # bits < 2
     assert _quant(so, C(4, 96)) == lib.GPTQ_ERR_INVALID_ARG           # 128 % 96 != 0
-    assert _quant(so, C(4, 256)) == lib.GPTQ_ERR_INVALID_ARG          # block not a multiple
+    assert _quant(so, C(4, 192)) == lib.GPTQ_ERR_INVALID_ARG          # neither divides the other
+    assert _quant(so, C(4, 384)) == lib.GPTQ_ERR_UNSUPPORTED          # a multiple of 128, not built
+    assert _quant(so, C(4, 128, static_groups=2)) == lib.GPTQ_ERR_INVALID_ARG
+    assert _quant(so, C(4, -2)) == lib.GPTQ_ERR_INVALID_ARG
     assert _quant(so, C(4, 0)) == lib.GPTQ_ERR_INVALID_ARG
     assert _quant(so, C(4, 64, block_size=64)) == lib.GPTQ_ERR_UNSUPPORTED
     assert _quant(so, C(4, 4)) == lib.GPTQ_ERR_UNSUPPORTED            # divides 128, not built

@@ -206,6 +206,37 @@ def test_device_gptq_output_feeds_dequant_gemm():
     assert rel < 0.2
 
 
+def test_static_groups_feed_the_product_without_a_permutation():
+    """With static groups and desc_act the groups are runs of original columns:
+    the codes are packed in original order and the product needs no gather."""
+    q = need_gpu()
+    from post_weight_quantization_22_amd import pipeline
+
+    rng = np.random.default_rng(14)
+    m, n, tokens_cal, bits, G = 80, 512, 1024, 4, 64
+    W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.02).astype(np.float32))
+    Xc = synth.round_to_bf16(rng.standard_normal((tokens_cal, n)).astype(np.float32))
+    cfg = q.make_config(bits, G, 128, 0.01, True, False, static_groups=True)
+    buf = pipeline.allocate(m, n, cfg, tokens_cal)
+    say("static groups -> dequant_gemm", m, n)
+    pipeline.run_layer(buf, dev(W, torch.bfloat16), [dev(Xc, torch.bfloat16)])
+    torch.cuda.synchronize()
+    pipeline.check_info(buf)
+    g_idx = host(buf.g_idx).astype(np.int64)
+    assert np.array_equal(g_idx, np.arange(n) // G)
+    X = synth.round_to_bf16(rng.standard_normal((300, n)).astype(np.float32))
+    Y = torch.empty((300, m), dtype=torch.float32, device="cuda")
+    q.gptq_dequant_gemm(dev(X, torch.bfloat16), buf.packed, bits, G, buf.scales, buf.zeros, Y)
+    torch.cuda.synchronize()
+    codes = host(buf.codes).astype(np.int64)
+    scales = host(buf.scales).astype(np.float64)
+    zeros = host(buf.zeros).astype(np.float64)
+    Yo = oracle.dequant_matmul(X, oracle.pack_ref(codes, bits), n, bits, scales, zeros, g_idx)
+    Wo = oracle.dequant_weights(oracle.pack_ref(codes, bits), n, bits, scales, zeros, g_idx)
+    bound = (2.0 ** -8 + 8.0 * np.sqrt(n) * EPS32) * (np.abs(X) @ np.abs(Wo).T)
+    assert np.all(np.abs(host(Y).astype(np.float64) - Yo) <= bound)
+
+
 FULL = [
     # name, m, n, bits, G, perm
     ("llama7b_attn", 4096, 4096, 4, 128, False),

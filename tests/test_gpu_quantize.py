@@ -31,7 +31,8 @@ QCASES = [
 ]
 
 
-def run_case(q, m, n, tokens, G, bits, desc, wdt, xdist, sym=False, dead_cols=()):
+def run_case(q, m, n, tokens, G, bits, desc, wdt, xdist, sym=False, dead_cols=(),
+             static=False):
     wl = synth.custom_workload("qc", m, n, tokens, min(tokens, 2048), w_dtype=wdt, x_dist=xdist,
                                outlier_frac=0.01, outlier_mult=20.0, bits=bits, group_size=G,
                                desc_act=desc, sym=sym, workload_id=300 + m + n)
@@ -42,8 +43,8 @@ def run_case(q, m, n, tokens, G, bits, desc, wdt, xdist, sym=False, dead_cols=()
     S = oracle.hessian_S([X])
     P = oracle.prepare(S, float(np.float32(0.01)), desc)
     U32 = f32(P.U)  # both sides get the same fp32 U
-    ref = oracle.gptq_quantize(W, U32, bits, G, 128, P.perm, P.dead, sym)
-    cfg = q.make_config(bits, G, desc_act=desc, sym=sym)
+    ref = oracle.gptq_quantize(W, U32, bits, G, 128, P.perm, P.dead, sym, static_groups=static)
+    cfg = q.make_config(bits, G, desc_act=desc, sym=sym, static_groups=static)
     ng = ref.scales.shape[1]
     codes = torch.empty((m, n), dtype=torch.uint8, device="cuda")
     scales = torch.empty((m, ng), dtype=torch.float32, device="cuda")
@@ -51,7 +52,7 @@ def run_case(q, m, n, tokens, G, bits, desc, wdt, xdist, sym=False, dead_cols=()
     g_idx = torch.empty(n, dtype=torch.int32, device="cuda")
     row_err = torch.empty(m, dtype=torch.float32, device="cuda")
     info = torch.full((1,), 5, dtype=torch.int32, device="cuda")
-    say("quantize", m, n, G, bits, desc, wdt, xdist, sym)
+    say("quantize", m, n, G, bits, desc, wdt, xdist, sym, static)
     q.gptq_quantize_layer(dev(W, storage_dtype(wdt)), dev(U32.astype(np.float32), torch.float32),
                           cfg, codes, scales, zeros, perm=dev(P.perm.astype(np.int32), torch.int32),
                           dead=dev(P.dead.astype(np.uint8), torch.uint8), g_idx=g_idx,
@@ -125,3 +126,38 @@ def test_quantize_deterministic():
     q = need_gpu()
     outs = [run_case(q, 96, 384, 1024, 128, 4, True, "bf16", "normal")[6] for _ in range(3)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+VCASES = [
+    # m, n, tokens, G, bits, desc_act, static, dead columns
+    (64, 256, 1024, 128, 4, True, True, ()),       # static groups with desc_act
+    (40, 384, 2048, 64, 3, True, True, (5, 200)),  # static, dead columns
+    (33, 200, 1024, 32, 4, False, True, ()),       # static, ragged last block
+    (16, 640, 1024, 256, 4, True, True, ()),       # static groups larger than a block
+    (24, 1024, 2048, 256, 4, True, False, ()),     # a group spanning two blocks
+    (20, 1280, 2048, 512, 3, False, False, ()),    # four blocks; last group cut at n
+    (12, 2304, 2048, 256, 4, True, False, (7,)),   # groups across a super-block boundary
+]
+
+
+@pytest.mark.parametrize("m,n,tokens,G,bits,desc,static,dead", VCASES)
+def test_quantize_grouping_variants(m, n, tokens, G, bits, desc, static, dead):
+    q = need_gpu()
+    W, X, S, P, U32, ref, codes, scales, zeros, g_idx, row_err, info = run_case(
+        q, m, n, tokens, G, bits, desc, "bf16", "student_t4", dead_cols=dead, static=static)
+    assert info == 0
+    assert np.array_equal(g_idx, ref.g_idx)
+    if static:
+        _, s_rtn, z_rtn = oracle.rtn_minmax(np.where(P.dead[None, :], 0.0, W), bits, G)
+        assert np.array_equal(scales.astype(np.float64), s_rtn)
+        assert np.array_equal(zeros.astype(np.float64), z_rtn)
+    rate = match_rate(codes, ref.codes)
+    print(f"match {rate:.6f}")
+    assert rate >= 0.999
+    rep = oracle.replay_check(W, U32, bits, G, 128, P.perm, P.dead,
+                              codes.astype(np.float64)[:, P.perm], scales, zeros,
+                              static_groups=static)
+    print(f"replay: mism {rep.mismatches} ties {rep.ties} hard {rep.hard} "
+          f"zero-hard {rep.zero_hard} scale rel {rep.scale_max_rel:.2e}")
+    assert rep.hard == 0 and rep.zero_hard == 0
+    assert rep.scale_max_rel <= 1e-4
