@@ -57,3 +57,4 @@ from .gptq import (  # noqa: F401
 from .pack import pack_ref, unpack_ref  # noqa: F401
 from .dequant import dequant_weights, dequant_matmul  # noqa: F401
 from . import stack  # noqa: F401,E402  (layer-sequential MLP stack)
+from . import awq  # noqa: F401,E402  (AWQ-lite scale search and clip)

@@ -21,12 +21,14 @@ PREP_MOD = sys.modules["oracle.prepare"]
 QUANT_MOD = sys.modules["oracle.quantizer"]
 DEQ_MOD = sys.modules["oracle.dequant"]
 STACK_MOD = sys.modules["oracle.stack"]
+AWQ_MOD = sys.modules["oracle.awq"]
 
 import test_oracle_gptq as tg
 import test_oracle_hessian_prepare as th
 import test_oracle_quantizer as tq
 import test_oracle_dequant as td
 import test_oracle_stack as tst
+import test_oracle_awq as tawq
 
 
 def _mutant(mod, old, new):
@@ -89,6 +91,13 @@ MUTANTS = [
     (STACK_MOD, "return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
      "return np.ldexp(np.rint(np.ldexp(m, 9)), e - 9)", ["stack"],
      lambda gd: tst.test_to_bf16_hand_values()),
+    (AWQ_MOD, "        q, sc, z = quantize_groups(W * s, bits, G, sym)\n        D = dequant_groups(q, sc, z, G) / s - W",
+     "        q, sc, z = quantize_groups(W / s, bits, G, sym)\n        D = dequant_groups(q, sc, z, G) * s - W",
+     ["awq"], lambda gd: tawq.test_alpha_search_against_brute_force()),
+    (AWQ_MOD, "D = dequant_groups(q, sc, z, G) / s - W", "D = dequant_groups(q, sc, z, G) - W",
+     ["awq"], lambda gd: tawq.test_rescaling_preserves_the_output_when_nothing_is_rounded()),
+    (AWQ_MOD, "best = int(np.argmin(losses))", "best = int(np.argmax(losses))", ["awq"],
+     lambda gd: tawq.test_alpha_search_against_brute_force()),
 ]
 
 
@@ -96,6 +105,9 @@ MUTANTS = [
 def test_pins_catch_planted_mistake(idx, monkeypatch, golden_dir):
     mod, old, new, names, pin = MUTANTS[idx]
     m = _mutant(mod, old, new)
+    if mod is AWQ_MOD:
+        monkeypatch.setattr(tawq, "awq", m)
+        names = []
     if mod is STACK_MOD:
         # the stack pins call the module's functions by name and through oracle.stack
         monkeypatch.setattr(oracle, "stack", m)
