@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00020000u /* major 2, minor 0 (gptq_config grew) */
+#define GPTQ_ABI_VERSION 0x00020001u /* major 2, minor 1 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -227,6 +227,51 @@ gptq_status gptq_swiglu(const float* gate, int64_t ldg, const float* up, int64_t
                         int64_t tokens, int64_t n, void* h, int64_t ldh, hipStream_t stream);
 gptq_status gptq_residual_add(const void* x, int64_t ldx, const float* y, int64_t ldy,
                               int64_t tokens, int64_t n, void* out, int64_t ldo,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * AWQ-lite and awq_clip -- "AWQ, MinMax, GPTQ calibration in Model
+ * Optimizer" (gtnt.cn news 115337), section 3, and "LLM quantization
+ * principles", section 3.2.  The weights are multiplied per input channel by
+ * s = x^alpha / w^(1 - alpha) and the activations divided by it (x, w: the
+ * channel's mean |activation| and mean |weight|, floored at 1e-8); alpha is
+ * searched on a grid of n_alpha points over [0, 1] (11 = steps of 0.1) for the
+ * smallest output error ||X (W_eff - W)^T||^2, W_eff = dequant(Q(W diag(s)))
+ * diag(1/s), Q the group min-max quantizer of rtn_minmax (groups of group_size
+ * consecutive columns, -1 = whole row).  The error is computed through
+ * S = X^T X (the lower triangle gptq_hessian_accumulate builds).  awq_clip
+ * then searches, per row and group of W' = W diag(s), the clip value
+ * c_k = (1 - 0.05 k) amax, k < n_steps (11 = down to 0.5 amax): the group's
+ * parameters come from its values clamped to [-c_k, c_k]; the error of a
+ * candidate is d S'_gg d^T, S' = diag(1/s) S diag(1/s), d the group's error
+ * in the rescaled space.  Ties keep the first candidate (smallest alpha,
+ * largest clip).  The quantized layer computes (X / s) dequant(codes)^T.
+ *
+ * awq_activation_absum: absum[n] += sum over tokens of |X[t, c]| (additive over
+ *   calls, like the Hessian); workspace awq_absum_workspace_size(n, tokens).
+ * awq_lite: from W [m, n], S (lower, lds), absum over `tokens` tokens: s_out[n],
+ *   alpha_out[1], losses[n_alpha] (fp32, device); workspace
+ *   awq_lite_workspace_size(m, n) (holds a full copy of S and two m x n fp32
+ *   matrices).  GPTQ_ERR_EMPTY when tokens == 0.
+ * awq_clip_quantize: codes[m, n] (uint8, of W diag(s)), scales/zeros
+ *   [m, ceil(n / group_size)] fp32, clip_idx [m, ngroups] (uint8 k, may be
+ *   NULL); s may be NULL (no rescaling: clip search on W itself).
+ *   group_size 1..128 (GPTQ_ERR_UNSUPPORTED above).
+ * ---------------------------------------------------------------------- */
+gptq_status awq_absum_workspace_size(int64_t n, int64_t tokens, size_t* bytes);
+gptq_status awq_activation_absum(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                                 int64_t ldx, float* absum, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+gptq_status awq_lite_workspace_size(int64_t m, int64_t n, size_t* bytes);
+gptq_status awq_lite(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                     const float* S, int64_t lds, const float* absum, int64_t tokens,
+                     int32_t bits, int32_t group_size, int32_t sym, int32_t n_alpha,
+                     float* s_out, float* alpha_out, float* losses, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+gptq_status awq_clip_quantize(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                              const float* S, int64_t lds, const float* s, int32_t bits,
+                              int32_t group_size, int32_t sym, int32_t n_steps, uint8_t* codes,
+                              float* scales, float* zeros, uint8_t* clip_idx,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------

@@ -26,7 +26,8 @@ Readings (the pages leave these open):
   * the error is the squared Frobenius norm ||X (W_eff - W)^T||^2 over the
     calibration tokens, W_eff = dequant(Q(W')) diag(1/s), computed through
     S = X^T X as sum((D S) * D) with D = W_eff - W (the same number);
-  * clip: the candidate c_k = (1 - 0.05 k) amax, k = 0..10, limits the range
+  * clip: the candidate c_k = (1 - 0.05 k) amax, k = 0..10 (formed in fp32,
+    like every value that decides a code), limits the range
     the group's parameters are computed from (values clamped to [-c_k, c_k]);
     the codes of the unclamped values are clamped to the code range as usual;
     the error of a candidate is that of the group alone, d S'_gg d^T with
@@ -141,21 +142,25 @@ def awq_clip(W: np.ndarray, S: np.ndarray, s: np.ndarray, bits: int, G: int, sym
     """Per (row, group) clip search on W' = W diag(s); S = X^T X (full)."""
     W = np.asarray(W, np.float64)
     s = np.asarray(s, np.float64)
-    Ws = W * s
+    # W' in the quantizer's decision precision (fp32), and the clip bounds with it
+    Ws = f32(W * s)
     Sp = S / np.outer(s, s)  # second moments of X' = X diag(1/s)
     m, n = Ws.shape
     gs = _groups(n, G)
     errs = np.zeros((m, len(gs), len(ratios)))
     amax = np.stack([np.abs(Ws[:, g0:g1]).max(axis=1) for g0, g1 in gs], axis=1)
+
+    def bound(r):
+        return f32(amax * f32(r))
+
     for k, ratio in enumerate(ratios):
-        q, sc, z = quantize_groups(Ws, bits, G, sym, ranges=amax * ratio)
+        q, sc, z = quantize_groups(Ws, bits, G, sym, ranges=bound(ratio))
         d = dequant_groups(q, sc, z, G) - Ws
         for gi, (g0, g1) in enumerate(gs):
             dg = d[:, g0:g1]
             errs[:, gi, k] = np.einsum("ri,ij,rj->r", dg, Sp[g0:g1, g0:g1], dg)
     ridx = np.argmin(errs, axis=2)  # first minimum: the largest clip
-    codes, scales, zeros = quantize_groups(Ws, bits, G, sym,
-                                           ranges=amax * ratios[ridx])
+    codes, scales, zeros = quantize_groups(Ws, bits, G, sym, ranges=bound(ratios[ridx]))
     return AWQClip(codes, scales, zeros, ridx, errs)
 
 

@@ -10,6 +10,9 @@ fallback implementation.
 from . import _lib
 from ._lib import (  # noqa: F401
     EXPORTED,
+    awq_activation_absum,
+    awq_clip_quantize,
+    awq_lite,
     GPTQConfig,
     GPTQError,
     gptq_abi_version,

@@ -41,6 +41,11 @@ EXPORTED = (
     "gptq_dequant_gemm",
     "gptq_swiglu",
     "gptq_residual_add",
+    "awq_absum_workspace_size",
+    "awq_activation_absum",
+    "awq_lite_workspace_size",
+    "awq_lite",
+    "awq_clip_quantize",
     "rtn_minmax",
 )
 
@@ -114,6 +119,18 @@ def load() -> ctypes.CDLL:
     lib.gptq_swiglu.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
     lib.gptq_residual_add.restype = _i32
     lib.gptq_residual_add.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
+    lib.awq_absum_workspace_size.restype = _i32
+    lib.awq_absum_workspace_size.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.awq_activation_absum.restype = _i32
+    lib.awq_activation_absum.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
+    lib.awq_lite_workspace_size.restype = _i32
+    lib.awq_lite_workspace_size.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.awq_lite.restype = _i32
+    lib.awq_lite.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
+                             _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.awq_clip_quantize.restype = _i32
+    lib.awq_clip_quantize.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i32, _i32,
+                                      _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.rtn_minmax.restype = _i32
     lib.rtn_minmax.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
     _lib = lib
@@ -293,6 +310,46 @@ def gptq_residual_add(x, y, out, stream=None) -> None:
     _check(load().gptq_residual_add(_ptr(x), _ld(x), _ptr(y), _ld(y), tokens, n, _ptr(out),
                                     _ld(out), _stream(stream)),
            "gptq_residual_add")
+
+
+def awq_activation_absum(X, absum, ws=None, stream=None) -> None:
+    """absum[n] += sum over tokens of |X[t, c]|."""
+    tokens, n = X.shape
+    if ws is None:
+        out = _sz(0)
+        _check(load().awq_absum_workspace_size(n, tokens, ctypes.byref(out)),
+               "awq_absum_workspace_size")
+        ws = _workspace(out.value, X.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().awq_activation_absum(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(absum),
+                                       _ptr(ws), nbytes, _stream(stream)),
+           "awq_activation_absum")
+
+
+def awq_lite(W, S, absum, tokens: int, bits: int, group_size: int, s_out, alpha_out, losses,
+             sym: bool = False, ws=None, stream=None) -> None:
+    """alpha search; s_out[n], alpha_out[1], losses[n_alpha] fp32 device tensors."""
+    m, n = W.shape
+    if ws is None:
+        out = _sz(0)
+        _check(load().awq_lite_workspace_size(m, n, ctypes.byref(out)), "awq_lite_workspace_size")
+        ws = _workspace(out.value, W.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().awq_lite(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(S), _ld(S), _ptr(absum),
+                           int(tokens), int(bits), int(group_size), int(sym), losses.numel(),
+                           _ptr(s_out), _ptr(alpha_out), _ptr(losses), _ptr(ws), nbytes,
+                           _stream(stream)),
+           "awq_lite")
+
+
+def awq_clip_quantize(W, S, s, bits: int, group_size: int, codes, scales, zeros, clip_idx=None,
+                      sym: bool = False, n_steps: int = 11, stream=None) -> None:
+    m, n = W.shape
+    _check(load().awq_clip_quantize(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(S), _ld(S),
+                                    _ptr(s), int(bits), int(group_size), int(sym), int(n_steps),
+                                    _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(clip_idx),
+                                    _stream(stream)),
+           "awq_clip_quantize")
 
 
 def rtn_minmax(W, bits: int, group_size: int, codes, scales, zeros, sym: bool = False,

@@ -219,6 +219,62 @@ gptq_status gptq_residual_add(const void* x, int64_t ldx, const float* y, int64_
   return hip_status(launch_residual_add(x, ldx, y, ldy, tokens, n, out, ldo, stream));
 }
 
+gptq_status awq_absum_workspace_size(int64_t n, int64_t tokens, size_t* bytes) {
+  if (!bytes || n <= 0 || bad_dim(n) || tokens < 0) return GPTQ_ERR_INVALID_ARG;
+  *bytes = awq_absum_ws_bytes(n, tokens);
+  return GPTQ_OK;
+}
+
+gptq_status awq_activation_absum(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                                 int64_t ldx, float* absum, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!absum || n <= 0 || bad_dim(n) || tokens < 0 || !valid_dtype(xdt))
+    return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (!X || ldx < n) return GPTQ_ERR_INVALID_ARG;
+  const gptq_status w = check_ws(ws, ws_bytes, awq_absum_ws_bytes(n, tokens));
+  if (w != GPTQ_OK) return w;
+  return hip_status(launch_awq_absum(X, xdt, tokens, n, ldx, absum, ws, stream));
+}
+
+gptq_status awq_lite_workspace_size(int64_t m, int64_t n, size_t* bytes) {
+  if (!bytes || m <= 0 || n <= 0 || bad_dim(m) || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  *bytes = awq_lite_ws_bytes(m, n);
+  return GPTQ_OK;
+}
+
+gptq_status awq_lite(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                     const float* S, int64_t lds, const float* absum, int64_t tokens,
+                     int32_t bits, int32_t group_size, int32_t sym, int32_t n_alpha,
+                     float* s_out, float* alpha_out, float* losses, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!W || !S || !absum || !s_out || !alpha_out || !losses || m <= 0 || n <= 0 ||
+      bad_dim(m) || bad_dim(n) || ldw < n || lds < n || !valid_dtype(wdt) || bits < 2 ||
+      bits > 8 || group_size == 0 || group_size < -1 || (sym != 0 && sym != 1) ||
+      n_alpha < 2 || n_alpha > 101)
+    return GPTQ_ERR_INVALID_ARG;
+  if (tokens <= 0) return GPTQ_ERR_EMPTY;
+  const gptq_status w = check_ws(ws, ws_bytes, awq_lite_ws_bytes(m, n));
+  if (w != GPTQ_OK) return w;
+  return hip_status(launch_awq_lite(W, wdt, m, n, ldw, S, lds, absum, tokens, bits, group_size,
+                                    sym, n_alpha, s_out, alpha_out, losses, ws, stream));
+}
+
+gptq_status awq_clip_quantize(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                              const float* S, int64_t lds, const float* s, int32_t bits,
+                              int32_t group_size, int32_t sym, int32_t n_steps, uint8_t* codes,
+                              float* scales, float* zeros, uint8_t* clip_idx,
+                              hipStream_t stream) {
+  if (!W || !S || !codes || !scales || !zeros || m < 0 || n <= 0 || bad_dim(m) || bad_dim(n) ||
+      ldw < n || lds < n || !valid_dtype(wdt) || bits < 2 || bits > 8 || group_size < 1 ||
+      (sym != 0 && sym != 1) || n_steps < 1 || n_steps > 11)
+    return GPTQ_ERR_INVALID_ARG;
+  if (group_size > 128) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0) return GPTQ_OK;
+  return hip_status(launch_awq_clip(W, wdt, m, n, ldw, S, lds, s, bits, group_size, sym, n_steps,
+                                    codes, scales, zeros, clip_idx, stream));
+}
+
 gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
                        int32_t bits, int32_t group_size, int32_t sym, uint8_t* codes,
                        float* scales, float* zeros, hipStream_t stream) {

@@ -1,0 +1,342 @@
+// AWQ-lite channel scaling and awq_clip.
+//
+// "AWQ, MinMax, GPTQ calibration in Model Optimizer" (gtnt.cn news 115337),
+// section 3: awq_lite rescales input channels and weights in opposite
+// directions by s = x^alpha / w^(1 - alpha) (x, w: per-channel mean absolute
+// values of the activations and of the weights), searching alpha over [0, 1] in
+// steps of 0.1 for the smallest error between the rescaled, quantized layer's
+// output and the true output; awq_clip then searches each group's clip value in
+// [0.5 amax, amax] in steps of 0.05 amax.  "LLM quantization principles"
+// section 3.2: the weights are multiplied by s and the activations divided.
+//
+// The output error of a candidate, ||X D^T||^2 with D = W_eff - W, is taken
+// through the calibration second moments S = X^T X that the Hessian step
+// accumulates: sum((D S) * D), one fp32 MFMA product per candidate alpha
+// (the trailing-update GEMM), instead of a pass over the tokens.  The clip
+// search is per (row, group) with the group's block of the rescaled S staged
+// in LDS.  Both are deterministic (fixed summation orders).
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+constexpr float kFloor = 1e-8f;
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) p[i] = 0.0f;
+}
+
+// ---- per-channel mean absolute activation --------------------------------
+__global__ __launch_bounds__(256) void absum_partial_kernel(const void* __restrict__ X, int dt,
+                                                            int64_t tokens, int64_t n,
+                                                            int64_t ldx, int64_t per,
+                                                            float* __restrict__ part) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  const int64_t t0 = (int64_t)blockIdx.y * per, t1 = min(tokens, t0 + per);
+  float s = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) s += fabsf(load_elem(X, dt, t * ldx + c));
+  part[(int64_t)blockIdx.y * n + c] = s;
+}
+
+__global__ __launch_bounds__(256) void absum_reduce_kernel(const float* __restrict__ part,
+                                                           int64_t P, int64_t n,
+                                                           float* __restrict__ absum) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  float s = absum[c];
+  for (int64_t p = 0; p < P; ++p) s += part[p * n + c];
+  absum[c] = s;
+}
+
+// ---- per-channel mean absolute weight --------------------------------------
+__global__ __launch_bounds__(256) void col_absmean_kernel(const void* __restrict__ W, int dt,
+                                                          int64_t m, int64_t n, int64_t ldw,
+                                                          float* __restrict__ wm) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  float s = 0.0f;
+  for (int64_t r = 0; r < m; ++r) s += fabsf(load_elem(W, dt, r * ldw + c));
+  wm[c] = s / (float)m;
+}
+
+// s[c] = x^a / w^(1 - a), x = absum[c] / tokens, both floored; a from
+// *alpha_dev when given (the searched value), else alpha
+__global__ __launch_bounds__(256) void awq_scales_kernel(const float* __restrict__ absum,
+                                                         float inv_tokens,
+                                                         const float* __restrict__ wm,
+                                                         int64_t n, const float* alpha_dev,
+                                                         float alpha, float* __restrict__ s) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  const float a = alpha_dev ? *alpha_dev : alpha;
+  const float x = fmaxf(absum[c] * inv_tokens, kFloor);
+  const float w = fmaxf(wm[c], kFloor);
+  s[c] = powf(x, a) / powf(w, 1.0f - a);
+}
+
+__global__ __launch_bounds__(256) void symmetrize_kernel(const float* __restrict__ S, int64_t lds,
+                                                         int64_t n, float* __restrict__ F) {
+  const int64_t i = blockIdx.y, j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  F[i * n + j] = j <= i ? S[i * lds + j] : S[j * lds + i];
+}
+
+// ---- one alpha: D = dequant(Q(W diag(s))) / s - W --------------------------
+// One wave per (row, group); lanes stride the group's columns.
+__global__ __launch_bounds__(256) void awq_qdq_kernel(const void* __restrict__ W, int dt,
+                                                      int64_t m, int64_t n, int64_t ldw,
+                                                      const float* __restrict__ s, int64_t G,
+                                                      int64_t ngroups, float maxq, int sym,
+                                                      float* __restrict__ D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= m * ngroups) return;
+  const int64_t r = pair / ngroups, g = pair - r * ngroups;
+  const int64_t c0 = g * G, c1 = min(n, c0 + G);
+  float vmin = 0.0f, vmax = 0.0f;
+  for (int64_t c = c0 + lane; c < c1; c += 64) {
+    const float v = __fmul_rn(load_elem(W, dt, r * ldw + c), s[c]);
+    vmin = fminf(vmin, v);
+    vmax = fmaxf(vmax, v);
+  }
+  for (int off = 1; off < 64; off <<= 1) {
+    vmin = fminf(vmin, __shfl_xor(vmin, off));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  }
+  float scale, zero;
+  if (sym) sym_params(fmaxf(fabsf(vmin), fabsf(vmax)), maxq, scale, zero);
+  else minmax_params(vmin, vmax, maxq, scale, zero);
+  for (int64_t c = c0 + lane; c < c1; c += 64) {
+    const float w = load_elem(W, dt, r * ldw + c);
+    const float v = __fmul_rn(w, s[c]);
+    const float q = quant_code(v, scale, zero, maxq);
+    D[r * n + c] = (scale * (q - zero)) / s[c] - w;
+  }
+}
+
+// sum of Z * D over the whole matrix: fixed per-block slices, then in order
+__global__ __launch_bounds__(256) void dot_partial_kernel(const float* __restrict__ Z,
+                                                          const float* __restrict__ D,
+                                                          int64_t total, int64_t per,
+                                                          float* __restrict__ part) {
+  __shared__ float red[256];
+  const int64_t i0 = (int64_t)blockIdx.x * per, i1 = min(total, i0 + per);
+  float acc = 0.0f;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) acc = fmaf(Z[i], D[i], acc);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// loss = -(sum of the partials), Z holding -(D S)
+__global__ void loss_final_kernel(const float* __restrict__ part, int64_t np,
+                                  float* __restrict__ loss) {
+  double acc = 0.0;
+  for (int64_t p = 0; p < np; ++p) acc += (double)part[p];
+  *loss = (float)(-acc);
+}
+
+// alpha of the first smallest loss
+__global__ void argmin_kernel(const float* __restrict__ losses, int na, float step,
+                              float* __restrict__ alpha_out) {
+  int best = 0;
+  for (int i = 1; i < na; ++i)
+    if (losses[i] < losses[best]) best = i;
+  *alpha_out = (float)best * step;
+}
+
+// ---- awq_clip: one group of columns per workgroup, one row per wave at a time
+constexpr int CLIP_MAXG = 128;
+
+__global__ __launch_bounds__(256) void awq_clip_kernel(
+    const void* __restrict__ W, int dt, int64_t m, int64_t n, int64_t ldw,
+    const float* __restrict__ S, int64_t lds, const float* __restrict__ s, int64_t G,
+    int64_t ngroups, float maxq, int sym, int nsteps, int64_t rows_per_wg,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ zeros,
+    uint8_t* __restrict__ clip_idx) {
+  __shared__ float Sg[CLIP_MAXG][CLIP_MAXG + 1];
+  __shared__ float dsh[4][CLIP_MAXG];
+  const int64_t g = blockIdx.x;
+  const int64_t c0 = g * G;
+  const int gl = (int)min(G, n - c0);  // this group's width
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // rescaled second moments of the group: S_ij / (s_i s_j)
+  for (int idx = tid; idx < gl * gl; idx += 256) {
+    const int i = idx / gl, j = idx - i * gl;
+    const int64_t a = c0 + max(i, j), b = c0 + min(i, j);
+    const float v = S[a * lds + b];
+    Sg[i][j] = s ? v / (s[c0 + i] * s[c0 + j]) : v;
+  }
+  __syncthreads();
+  const int64_t rbeg = (int64_t)blockIdx.y * rows_per_wg;
+  const int64_t rend = min(m, rbeg + rows_per_wg);
+  for (int64_t r = rbeg + wv; r < rend; r += 4) {
+    // this lane's columns: lane, lane + 64
+    float v[2], amax = 0.0f, vmin = 0.0f, vmax = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      float x = 0.0f;
+      if (j < gl) {
+        const float w = load_elem(W, dt, r * ldw + c0 + j);
+        x = s ? __fmul_rn(w, s[c0 + j]) : w;
+        vmin = fminf(vmin, x);
+        vmax = fmaxf(vmax, x);
+      }
+      v[h] = x;
+      amax = fmaxf(amax, fabsf(x));
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      amax = fmaxf(amax, __shfl_xor(amax, off));
+      vmin = fminf(vmin, __shfl_xor(vmin, off));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    }
+    float best = 0.0f;
+    int bk = 0;
+    for (int k = 0; k < nsteps; ++k) {
+      const float c = __fmul_rn(amax, (float)(1.0 - 0.05 * k));
+      float scale, zero;
+      if (sym) sym_params(fminf(amax, c), maxq, scale, zero);
+      else minmax_params(fmaxf(vmin, -c), fminf(vmax, c), maxq, scale, zero);
+      float d[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + 64 * h;
+        d[h] = 0.0f;
+        if (j < gl) d[h] = scale * (quant_code(v[h], scale, zero, maxq) - zero) - v[h];
+        if (j < CLIP_MAXG) dsh[wv][j] = d[h];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      float e = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + 64 * h;
+        if (j < gl) {
+          float t = 0.0f;
+          for (int i = 0; i < gl; ++i) t = fmaf(Sg[j][i], dsh[wv][i], t);
+          e = fmaf(d[h], t, e);
+        }
+      }
+      for (int off = 1; off < 64; off <<= 1) e += __shfl_xor(e, off);
+      if (k == 0 || e < best) {
+        best = e;
+        bk = k;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    // the chosen clip
+    const float c = __fmul_rn(amax, (float)(1.0 - 0.05 * bk));
+    float scale, zero;
+    if (sym) sym_params(fminf(amax, c), maxq, scale, zero);
+    else minmax_params(fmaxf(vmin, -c), fminf(vmax, c), maxq, scale, zero);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j < gl) codes[r * n + c0 + j] = (uint8_t)quant_code(v[h], scale, zero, maxq);
+    }
+    if (lane == 0) {
+      scales[r * ngroups + g] = scale;
+      zeros[r * ngroups + g] = zero;
+      if (clip_idx) clip_idx[r * ngroups + g] = (uint8_t)bk;
+    }
+  }
+}
+
+}  // namespace
+
+constexpr int64_t kAbsumSplit = 64;  // token slices of the activation statistics
+
+size_t awq_absum_ws_bytes(int64_t n, int64_t tokens) {
+  (void)tokens;
+  return (size_t)kAbsumSplit * (size_t)n * sizeof(float);
+}
+
+hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx,
+                            float* absum, void* ws, hipStream_t stream) {
+  float* part = static_cast<float*>(ws);
+  const int64_t per = ceil_div(tokens, kAbsumSplit);
+  const int64_t P = ceil_div(tokens, per);
+  hipLaunchKernelGGL(absum_partial_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)P),
+                     dim3(256), 0, stream, X, dt, tokens, n, ldx, per, part);
+  hipLaunchKernelGGL(absum_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
+                     part, P, n, absum);
+  return hipGetLastError();
+}
+
+namespace {
+constexpr int64_t kDotBlocks = 1024;
+inline size_t al(size_t b) { return align_up(b, 256); }
+}  // namespace
+
+size_t awq_lite_ws_bytes(int64_t m, int64_t n) {
+  return al((size_t)n * 4) + al((size_t)n * n * 4) + 2 * al((size_t)m * n * 4) +
+         al((size_t)kDotBlocks * 4);
+}
+
+hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
+                           const float* S, int64_t lds, const float* absum, int64_t tokens,
+                           int bits, int64_t G, int sym, int nalpha, float* s_out,
+                           float* alpha_out, float* losses, void* ws, hipStream_t stream) {
+  char* p = static_cast<char*>(ws);
+  float* wm = reinterpret_cast<float*>(p);
+  p += al((size_t)n * 4);
+  float* F = reinterpret_cast<float*>(p);
+  p += al((size_t)n * n * 4);
+  float* D = reinterpret_cast<float*>(p);
+  p += al((size_t)m * n * 4);
+  float* Z = reinterpret_cast<float*>(p);
+  p += al((size_t)m * n * 4);
+  float* part = reinterpret_cast<float*>(p);
+  const int64_t Geff = G > 0 ? G : n;
+  const int64_t ngroups = ceil_div(n, Geff);
+  const float maxq = (float)((1 << bits) - 1);
+  const float inv_tokens = 1.0f / (float)tokens;
+  const float step = 1.0f / (float)(nalpha - 1);
+  const dim3 cgrid((unsigned)ceil_div(n, 256));
+  hipLaunchKernelGGL(col_absmean_kernel, cgrid, dim3(256), 0, stream, W, wdt, m, n, ldw, wm);
+  hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256),
+                     0, stream, S, lds, n, F);
+  const int64_t total = m * n;
+  const int64_t per = ceil_div(total, kDotBlocks);
+  const int64_t nblk = ceil_div(total, per);
+  for (int a = 0; a < nalpha; ++a) {
+    hipLaunchKernelGGL(awq_scales_kernel, cgrid, dim3(256), 0, stream, absum, inv_tokens, wm, n,
+                       (const float*)nullptr, step * (float)a, s_out);
+    hipLaunchKernelGGL(awq_qdq_kernel, dim3((unsigned)ceil_div(m * ngroups, 4)), dim3(256), 0,
+                       stream, W, wdt, m, n, ldw, s_out, Geff, ngroups, maxq, sym, D);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream,
+                       Z, total);
+    const hipError_t e = gemm_f32_sub(Z, m, n, D, n, F, n, n, stream);  // Z = -D S
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dot_partial_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, Z, D, total,
+                       per, part);
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(1), 0, stream, part, nblk, losses + a);
+  }
+  hipLaunchKernelGGL(argmin_kernel, dim3(1), dim3(1), 0, stream, losses, nalpha, step, alpha_out);
+  hipLaunchKernelGGL(awq_scales_kernel, cgrid, dim3(256), 0, stream, absum, inv_tokens, wm, n,
+                     (const float*)alpha_out, 0.0f, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_clip(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
+                           const float* S, int64_t lds, const float* s, int bits, int64_t G,
+                           int sym, int nsteps, uint8_t* codes, float* scales, float* zeros,
+                           uint8_t* clip_idx, hipStream_t stream) {
+  const int64_t ngroups = ceil_div(n, G);
+  const float maxq = (float)((1 << bits) - 1);
+  const int64_t rows_per_wg = 16;
+  const dim3 grid((unsigned)ngroups, (unsigned)ceil_div(m, rows_per_wg));
+  hipLaunchKernelGGL(awq_clip_kernel, grid, dim3(256), 0, stream, W, wdt, m, n, ldw, S, lds, s, G,
+                     ngroups, maxq, sym, nsteps, rows_per_wg, codes, scales, zeros, clip_idx);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -46,6 +46,23 @@ struct QuantArgs {
 };
 size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// C[m, n] (row stride n) -= A[m, k] (row stride lda) B[k, n] (row stride ldb), fp32 MFMA
+hipError_t gemm_f32_sub(float* C, int64_t m, int64_t n, const float* A, int64_t lda,
+                        const float* B, int64_t ldb, int64_t k, hipStream_t stream);
+
+// ---- awq.hip --------------------------------------------------------------
+size_t awq_absum_ws_bytes(int64_t n, int64_t tokens);
+hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx,
+                            float* absum, void* ws, hipStream_t stream);
+size_t awq_lite_ws_bytes(int64_t m, int64_t n);
+hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
+                           const float* S, int64_t lds, const float* absum, int64_t tokens,
+                           int bits, int64_t G, int sym, int nalpha, float* s_out,
+                           float* alpha_out, float* losses, void* ws, hipStream_t stream);
+hipError_t launch_awq_clip(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
+                           const float* S, int64_t lds, const float* s, int bits, int64_t G,
+                           int sym, int nsteps, uint8_t* codes, float* scales, float* zeros,
+                           uint8_t* clip_idx, hipStream_t stream);
 
 // ---- dequant_gemm.hip -----------------------------------------------------
 struct DequantArgs {

@@ -190,3 +190,34 @@ def test_forward_steps_argument_validation(lib):
     assert so.gptq_residual_add(FAKE, 64, FAKE, 64, 8, 64, FAKE, 63, None) == lib.GPTQ_ERR_INVALID_ARG
     assert so.gptq_residual_add(FAKE, 64, None, 64, 8, 64, FAKE, 64, None) == lib.GPTQ_ERR_INVALID_ARG
     assert so.gptq_residual_add(FAKE, 64, FAKE, 64, 8, 0, FAKE, 64, None) == lib.GPTQ_OK
+
+
+def test_awq_argument_validation(lib):
+    so = lib.load()
+    n = ctypes.c_size_t(0)
+    assert so.awq_absum_workspace_size(4096, 1000, ctypes.byref(n)) == lib.GPTQ_OK and n.value > 0
+    assert so.awq_activation_absum(FAKE, 1, 100, 64, 32, FAKE, FAKE, 1 << 30, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldx < n
+    assert so.awq_activation_absum(FAKE, 1, 0, 64, 64, FAKE, None, 0, None) == lib.GPTQ_OK
+    assert so.awq_activation_absum(FAKE, 1, 100, 64, 64, FAKE, None, 0, None) == \
+        lib.GPTQ_ERR_WORKSPACE
+
+    def lite(tokens=100, bits=4, G=128, na=11, ws=1 << 40, ldw=256):
+        return so.awq_lite(FAKE, 1, 64, 256, ldw, FAKE, 256, FAKE, tokens, bits, G, 0, na, FAKE,
+                           FAKE, FAKE, FAKE, ws, None)
+
+    assert lite(tokens=0) == lib.GPTQ_ERR_EMPTY
+    assert lite(bits=9) == lib.GPTQ_ERR_INVALID_ARG
+    assert lite(G=0) == lib.GPTQ_ERR_INVALID_ARG
+    assert lite(na=1) == lib.GPTQ_ERR_INVALID_ARG
+    assert lite(ldw=100) == lib.GPTQ_ERR_INVALID_ARG
+    assert lite(ws=16) == lib.GPTQ_ERR_WORKSPACE
+
+    def clip(G=128, steps=11, m=64):
+        return so.awq_clip_quantize(FAKE, 1, m, 256, 256, FAKE, 256, None, 4, G, 0, steps, FAKE,
+                                    FAKE, FAKE, None, None)
+
+    assert clip(G=256) == lib.GPTQ_ERR_UNSUPPORTED
+    assert clip(G=0) == lib.GPTQ_ERR_INVALID_ARG
+    assert clip(steps=12) == lib.GPTQ_ERR_INVALID_ARG
+    assert clip(m=0) == lib.GPTQ_OK

@@ -1,0 +1,193 @@
+"""GPU parity: AWQ-lite scale search and awq_clip against the oracle.
+
+The activation statistics are checked against the oracle's fp64 sums.  The alpha
+search is checked on what must agree: every candidate's output error within
+1e-3 (both sides round W' the same way up to the last bit of s, computed with
+powf on the device and in fp64 here), the chosen alpha's error within 1e-3 of
+the smallest (near-equal candidates may go either way), and s within 1e-5.
+The clip search is checked given the device's s (so that both sides quantize
+the same W'): the chosen clip's error within 1e-4 of the group's smallest, and
+the codes, scales and zero-points bit-identical to the oracle's quantizer at the
+device's chosen clips.  AWQ must beat plain group min-max on a layer with
+outlier activation channels.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import awq
+
+from gpu_util import dev, host, need_gpu, say, torch
+
+pytestmark = pytest.mark.gpu
+
+EPS32 = 2.0 ** -24
+
+
+def _run(q, W, X, bits, G, sym=False):
+    m, n = W.shape
+    Wd = dev(W.astype(np.float32), torch.bfloat16)
+    Xd = dev(X.astype(np.float32), torch.bfloat16)
+    S = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    q.gptq_hessian_accumulate(S, Xd)
+    absum = torch.zeros(n, dtype=torch.float32, device="cuda")
+    q.awq_activation_absum(Xd, absum)
+    s = torch.empty(n, dtype=torch.float32, device="cuda")
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    losses = torch.empty(11, dtype=torch.float32, device="cuda")
+    q.awq_lite(Wd, S, absum, X.shape[0], bits, G, s, alpha, losses, sym=sym)
+    ng = -(-n // G)
+    codes = torch.empty((m, n), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((m, ng), dtype=torch.float32, device="cuda")
+    zeros = torch.empty((m, ng), dtype=torch.float32, device="cuda")
+    cidx = torch.empty((m, ng), dtype=torch.uint8, device="cuda")
+    q.awq_clip_quantize(Wd, S, s, bits, G, codes, scales, zeros, cidx, sym=sym)
+    torch.cuda.synchronize()
+    S_dev = host(S).astype(np.float64)
+    S_full = np.tril(S_dev) + np.tril(S_dev, -1).T
+    return dict(S=S_full, absum=host(absum).astype(np.float64), s=host(s).astype(np.float64),
+                alpha=float(host(alpha)[0]), losses=host(losses).astype(np.float64),
+                codes=host(codes).astype(np.int64), scales=host(scales).astype(np.float64),
+                zeros=host(zeros).astype(np.float64), cidx=host(cidx).astype(np.int64))
+
+
+def _check(r, W, X, bits, G, sym=False):
+    tokens, n = X.shape
+    absum_ref = np.abs(X).sum(axis=0)
+    assert np.all(np.abs(r["absum"] - absum_ref) <= 8 * np.sqrt(tokens) * EPS32 * absum_ref + 1e-30)
+    xm = r["absum"] / tokens
+    S = r["S"]  # the device Hessian (its parity is tested on its own)
+    lite = awq.awq_lite(W, S, xm, bits, G, sym)
+    rel = np.abs(r["losses"] - lite.losses) / lite.losses
+    k = int(round(r["alpha"] * 10))
+    print(f"  alpha device {r['alpha']:.2f} oracle {lite.alpha:.2f}; loss rel diff max "
+          f"{rel.max():.2e}", flush=True)
+    assert np.all(rel <= 1e-3)
+    assert abs(r["alpha"] - 0.1 * k) < 1e-6
+    assert lite.losses[k] <= lite.losses.min() * (1 + 1e-3)
+    s_ref = awq.awq_scales(xm, awq.weight_absmean(W), 0.1 * k)
+    assert np.all(np.abs(r["s"] - s_ref) <= 1e-5 * s_ref)
+    # the clip search on the device's W' = W diag(s)
+    clip = awq.awq_clip(W, S, r["s"], bits, G, sym)
+    errs = clip.errors
+    chosen = np.take_along_axis(errs, r["cidx"][:, :, None], axis=2)[:, :, 0]
+    best = errs.min(axis=2)
+    scale_err = np.abs(errs).max(axis=2)
+    assert np.all(chosen <= best + 1e-4 * scale_err + 1e-30)
+    agree = float(np.mean(r["cidx"] == clip.ratio_idx))
+    ratios = awq.CLIP_RATIOS[r["cidx"]]
+    Ws = oracle.f32(W * r["s"])
+    amax = np.stack([np.abs(Ws[:, g0:g0 + G]).max(axis=1) for g0 in range(0, n, G)], axis=1)
+    codes, scales, zeros = awq.quantize_groups(Ws, bits, G, sym,
+                                               ranges=oracle.f32(amax * oracle.f32(ratios)))
+    print(f"  clip choices equal to the oracle's {agree:.4f}", flush=True)
+    assert np.array_equal(r["codes"], codes)
+    assert np.array_equal(r["scales"], scales) and np.array_equal(r["zeros"], zeros)
+    return lite
+
+
+CASES = [
+    # m, n, tokens, bits, G, sym, outliers
+    (64, 256, 2048, 4, 128, False, 4),
+    (96, 512, 4096, 3, 64, False, 8),
+    (40, 384, 1024, 4, 32, True, 3),
+    (33, 200, 1000, 4, 40, False, 2),   # ragged group, odd sizes
+]
+
+
+@pytest.mark.parametrize("m,n,tokens,bits,G,sym,nout", CASES)
+def test_awq_against_oracle(m, n, tokens, bits, G, sym, nout):
+    q = need_gpu()
+    rng = np.random.default_rng(m + n + bits)
+    W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.02).astype(np.float32)).astype(np.float64)
+    X = rng.standard_normal((tokens, n))
+    X[:, rng.choice(n, nout, replace=False)] *= 30.0
+    X = synth.round_to_bf16(X.astype(np.float32)).astype(np.float64)
+    say("awq", m, n, tokens, bits, G, sym)
+    r = _run(q, W, X, bits, G, sym)
+    _check(r, W, X, bits, G, sym)
+
+
+def test_awq_beats_plain_minmax_on_outlier_channels():
+    q = need_gpu()
+    rng = np.random.default_rng(9)
+    m, n, tokens, bits, G = 128, 512, 4096, 3, 128
+    W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.02).astype(np.float32)).astype(np.float64)
+    X = rng.standard_normal((tokens, n))
+    X[:, rng.choice(n, 6, replace=False)] *= 40.0
+    X = synth.round_to_bf16(X.astype(np.float32)).astype(np.float64)
+    say("awq vs rtn", m, n)
+    r = _run(q, W, X, bits, G)
+    S = r["S"]
+    W_awq = awq.dequant_groups(r["codes"], r["scales"], r["zeros"], G) / r["s"]
+    c, sc, z = oracle.rtn_minmax(W, bits, G)
+    W_rtn = oracle.dequant_layer(c, sc, z, np.arange(n) // G)
+    e_awq = awq.output_error(W_awq - W, S)
+    e_rtn = awq.output_error(W_rtn - W, S)
+    print(f"  output error: AWQ {e_awq:.4e}, min-max {e_rtn:.4e}", flush=True)
+    assert r["alpha"] > 0 and e_awq < 0.8 * e_rtn
+
+
+@pytest.mark.timeout(900)
+def test_awq_full_size_llama7b_attention():
+    """The Llama-7B attention projection workload (4096 x 4096, 262144 tokens,
+    4-bit g128): every candidate's error, the chosen alpha and s, and the clip
+    search and codes on 32 sampled rows."""
+    q = need_gpu()
+    wl = synth.get_workload("llama7b_attn")
+    ls = wl.layer()
+    xs = wl.xs[ls.x]
+    n, N = ls.n, xs.tokens
+    W = synth.weight(wl, ls.name).astype(np.float64)
+    Xd = torch.empty((N, n), dtype=torch.bfloat16, device="cuda")
+    absum_ref = np.zeros(n)
+    for c0 in range(0, xs.chunks, 16):
+        idx = list(range(c0, min(xs.chunks, c0 + 16)))
+        Xh = synth.x_all(wl, ls.x, chunks=idx)
+        Xd[c0 * xs.chunk_len:(c0 + len(idx)) * xs.chunk_len].copy_(torch.from_numpy(Xh).to(torch.bfloat16))
+        absum_ref += np.abs(Xh.astype(np.float64)).sum(axis=0)
+    say("awq full size", ls.m, n, N)
+    Wd = dev(W.astype(np.float32), torch.bfloat16)
+    S = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    q.gptq_hessian_accumulate(S, Xd)
+    absum = torch.zeros(n, dtype=torch.float32, device="cuda")
+    q.awq_activation_absum(Xd, absum)
+    s = torch.empty(n, dtype=torch.float32, device="cuda")
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    losses = torch.empty(11, dtype=torch.float32, device="cuda")
+    q.awq_lite(Wd, S, absum, N, 4, 128, s, alpha, losses)
+    codes = torch.empty((ls.m, n), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((ls.m, n // 128), dtype=torch.float32, device="cuda")
+    zeros = torch.empty((ls.m, n // 128), dtype=torch.float32, device="cuda")
+    cidx = torch.empty((ls.m, n // 128), dtype=torch.uint8, device="cuda")
+    q.awq_clip_quantize(Wd, S, s, 4, 128, codes, scales, zeros, cidx)
+    torch.cuda.synchronize()
+    absum_d = host(absum).astype(np.float64)
+    assert np.all(np.abs(absum_d - absum_ref) <= 8 * np.sqrt(N) * EPS32 * absum_ref)
+    S_dev = host(S).astype(np.float64)
+    S_full = np.tril(S_dev) + np.tril(S_dev, -1).T
+    del Xd, S
+    xm = absum_d / N
+    lite = awq.awq_lite(W, S_full, xm, 4, 128)
+    L = host(losses).astype(np.float64)
+    a = float(host(alpha)[0])
+    k = int(round(a * 10))
+    print(f"  alpha device {a:.2f} oracle {lite.alpha:.2f}; loss rel diff "
+          f"{float(np.max(np.abs(L - lite.losses) / lite.losses)):.2e}", flush=True)
+    assert np.all(np.abs(L - lite.losses) <= 1e-3 * lite.losses)
+    assert lite.losses[k] <= lite.losses.min() * (1 + 1e-3)
+    s_d = host(s).astype(np.float64)
+    s_ref = awq.awq_scales(xm, awq.weight_absmean(W), 0.1 * k)
+    assert np.all(np.abs(s_d - s_ref) <= 1e-5 * s_ref)
+    rows = np.unique(np.linspace(0, ls.m - 1, 32).astype(int))
+    clip = awq.awq_clip(W[rows], S_full, s_d, 4, 128)
+    ci = host(cidx).astype(np.int64)[rows]
+    chosen = np.take_along_axis(clip.errors, ci[:, :, None], axis=2)[:, :, 0]
+    assert np.all(chosen <= clip.errors.min(axis=2) + 1e-4 * np.abs(clip.errors).max(axis=2))
+    Ws = oracle.f32(W[rows] * s_d)
+    amax = np.stack([np.abs(Ws[:, g0:g0 + 128]).max(axis=1) for g0 in range(0, n, 128)], axis=1)
+    c_ref, s_ref2, z_ref = awq.quantize_groups(
+        Ws, 4, 128, ranges=oracle.f32(amax * oracle.f32(awq.CLIP_RATIOS[ci])))
+    assert np.array_equal(host(codes).astype(np.int64)[rows], c_ref)
+    assert np.array_equal(host(scales).astype(np.float64)[rows], s_ref2)
