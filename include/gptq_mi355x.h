@@ -248,11 +248,13 @@ gptq_status gptq_residual_add(const void* x, int64_t ldx, const float* y, int64_
  * largest clip).  The quantized layer computes (X / s) dequant(codes)^T.
  *
  * awq_activation_absum: absum[n] += sum over tokens of |X[t, c]| (additive over
- *   calls, like the Hessian); workspace awq_absum_workspace_size(n, tokens).
+ *   calls, like the Hessian; each call sums in fp64 and rounds once into the
+ *   fp32 absum); workspace awq_absum_workspace_size(n, tokens).
  * awq_lite: from W [m, n], S (lower, lds), absum over `tokens` tokens: s_out[n],
  *   alpha_out[1], losses[n_alpha] (fp32, device); workspace
  *   awq_lite_workspace_size(m, n) (holds a full copy of S and two m x n fp32
- *   matrices).  GPTQ_ERR_EMPTY when tokens == 0.
+ *   matrices).  GPTQ_ERR_EMPTY when tokens == 0.  w is summed in fp64; s is
+ *   computed in fp32 with powf.  Inputs are only read; every output is written.
  * awq_clip_quantize: codes[m, n] (uint8, of W diag(s)), scales/zeros
  *   [m, ceil(n / group_size)] fp32, clip_idx [m, ngroups] (uint8 k, may be
  *   NULL); s may be NULL (no rescaling: clip search on W itself).

@@ -15,6 +15,8 @@
 // (the trailing-update GEMM), instead of a pass over the tokens.  The clip
 // search is per (row, group) with the group's block of the rescaled S staged
 // in LDS.  Both are deterministic (fixed summation orders).
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gptq {
@@ -29,26 +31,28 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 }
 
 // ---- per-channel mean absolute activation --------------------------------
+// fp64 sums (a pass over X that is bound by its reads), so that the statistic
+// is the correctly rounded sum whatever the token count
 __global__ __launch_bounds__(256) void absum_partial_kernel(const void* __restrict__ X, int dt,
                                                             int64_t tokens, int64_t n,
                                                             int64_t ldx, int64_t per,
-                                                            float* __restrict__ part) {
+                                                            double* __restrict__ part) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
   const int64_t t0 = (int64_t)blockIdx.y * per, t1 = min(tokens, t0 + per);
-  float s = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) s += fabsf(load_elem(X, dt, t * ldx + c));
+  double s = 0.0;
+  for (int64_t t = t0; t < t1; ++t) s += (double)fabsf(load_elem(X, dt, t * ldx + c));
   part[(int64_t)blockIdx.y * n + c] = s;
 }
 
-__global__ __launch_bounds__(256) void absum_reduce_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void absum_reduce_kernel(const double* __restrict__ part,
                                                            int64_t P, int64_t n,
                                                            float* __restrict__ absum) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
-  float s = absum[c];
+  double s = (double)absum[c];
   for (int64_t p = 0; p < P; ++p) s += part[p * n + c];
-  absum[c] = s;
+  absum[c] = (float)s;
 }
 
 // ---- per-channel mean absolute weight --------------------------------------
@@ -57,9 +61,9 @@ __global__ __launch_bounds__(256) void col_absmean_kernel(const void* __restrict
                                                           float* __restrict__ wm) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
-  float s = 0.0f;
-  for (int64_t r = 0; r < m; ++r) s += fabsf(load_elem(W, dt, r * ldw + c));
-  wm[c] = s / (float)m;
+  double s = 0.0;
+  for (int64_t r = 0; r < m; ++r) s += (double)fabsf(load_elem(W, dt, r * ldw + c));
+  wm[c] = (float)(s / (double)m);
 }
 
 // s[c] = x^a / w^(1 - a), x = absum[c] / tokens, both floored; a from
@@ -79,9 +83,10 @@ __global__ __launch_bounds__(256) void awq_scales_kernel(const float* __restrict
 
 __global__ __launch_bounds__(256) void symmetrize_kernel(const float* __restrict__ S, int64_t lds,
                                                          int64_t n, float* __restrict__ F) {
-  const int64_t i = blockIdx.y, j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
-  F[i * n + j] = j <= i ? S[i * lds + j] : S[j * lds + i];
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y)
+    F[i * n + j] = j <= i ? S[i * lds + j] : S[j * lds + i];
 }
 
 // ---- one alpha: D = dequant(Q(W diag(s))) / s - W --------------------------
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(256) void awq_qdq_kernel(const void* __restrict__ W
                                                       int64_t m, int64_t n, int64_t ldw,
                                                       const float* __restrict__ s, int64_t G,
                                                       int64_t ngroups, float maxq, int sym,
-                                                      float* __restrict__ D) {
+                                                      float* __restrict__ D, int64_t ldd) {
   const int lane = threadIdx.x & 63;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= m * ngroups) return;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(256) void awq_qdq_kernel(const void* __restrict__ W
     const float w = load_elem(W, dt, r * ldw + c);
     const float v = __fmul_rn(w, s[c]);
     const float q = quant_code(v, scale, zero, maxq);
-    D[r * n + c] = (scale * (q - zero)) / s[c] - w;
+    D[r * ldd + c] = (scale * (q - zero)) / s[c] - w;
   }
 }
 
@@ -175,7 +180,8 @@ __global__ __launch_bounds__(256) void awq_clip_kernel(
     Sg[i][j] = s ? v / (s[c0 + i] * s[c0 + j]) : v;
   }
   __syncthreads();
-  const int64_t rbeg = (int64_t)blockIdx.y * rows_per_wg;
+  for (int64_t rbeg = (int64_t)blockIdx.y * rows_per_wg; rbeg < m;
+       rbeg += (int64_t)gridDim.y * rows_per_wg) {
   const int64_t rend = min(m, rbeg + rows_per_wg);
   for (int64_t r = rbeg + wv; r < rend; r += 4) {
     // this lane's columns: lane, lane + 64
@@ -248,6 +254,7 @@ __global__ __launch_bounds__(256) void awq_clip_kernel(
       if (clip_idx) clip_idx[r * ngroups + g] = (uint8_t)bk;
     }
   }
+  }
 }
 
 }  // namespace
@@ -256,12 +263,12 @@ constexpr int64_t kAbsumSplit = 64;  // token slices of the activation statistic
 
 size_t awq_absum_ws_bytes(int64_t n, int64_t tokens) {
   (void)tokens;
-  return (size_t)kAbsumSplit * (size_t)n * sizeof(float);
+  return (size_t)kAbsumSplit * (size_t)n * sizeof(double);
 }
 
 hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx,
                             float* absum, void* ws, hipStream_t stream) {
-  float* part = static_cast<float*>(ws);
+  double* part = static_cast<double*>(ws);
   const int64_t per = ceil_div(tokens, kAbsumSplit);
   const int64_t P = ceil_div(tokens, per);
   hipLaunchKernelGGL(absum_partial_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)P),
@@ -276,8 +283,12 @@ constexpr int64_t kDotBlocks = 1024;
 inline size_t al(size_t b) { return align_up(b, 256); }
 }  // namespace
 
+// D and Z rows padded to a multiple of 4 floats (the product's A operand is read
+// in float4s)
+inline int64_t lite_ld(int64_t n) { return (int64_t)align_up((size_t)n, 4); }
+
 size_t awq_lite_ws_bytes(int64_t m, int64_t n) {
-  return al((size_t)n * 4) + al((size_t)n * n * 4) + 2 * al((size_t)m * n * 4) +
+  return al((size_t)n * 4) + al((size_t)n * n * 4) + 2 * al((size_t)m * lite_ld(n) * 4) +
          al((size_t)kDotBlocks * 4);
 }
 
@@ -290,10 +301,11 @@ hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t
   p += al((size_t)n * 4);
   float* F = reinterpret_cast<float*>(p);
   p += al((size_t)n * n * 4);
+  const int64_t ldd = lite_ld(n);
   float* D = reinterpret_cast<float*>(p);
-  p += al((size_t)m * n * 4);
+  p += al((size_t)m * ldd * 4);
   float* Z = reinterpret_cast<float*>(p);
-  p += al((size_t)m * n * 4);
+  p += al((size_t)m * ldd * 4);
   float* part = reinterpret_cast<float*>(p);
   const int64_t Geff = G > 0 ? G : n;
   const int64_t ngroups = ceil_div(n, Geff);
@@ -302,19 +314,23 @@ hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t
   const float step = 1.0f / (float)(nalpha - 1);
   const dim3 cgrid((unsigned)ceil_div(n, 256));
   hipLaunchKernelGGL(col_absmean_kernel, cgrid, dim3(256), 0, stream, W, wdt, m, n, ldw, wm);
-  hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256),
-                     0, stream, S, lds, n, F);
-  const int64_t total = m * n;
+  hipLaunchKernelGGL(symmetrize_kernel,
+                     dim3((unsigned)ceil_div(n, 256), (unsigned)std::min<int64_t>(n, 65535)),
+                     dim3(256), 0, stream, S, lds, n, F);
+  // the padding columns of D stay zero (they meet zero columns of Z in the dot)
+  const int64_t total = m * ldd;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream,
+                     D, total);
   const int64_t per = ceil_div(total, kDotBlocks);
   const int64_t nblk = ceil_div(total, per);
   for (int a = 0; a < nalpha; ++a) {
     hipLaunchKernelGGL(awq_scales_kernel, cgrid, dim3(256), 0, stream, absum, inv_tokens, wm, n,
                        (const float*)nullptr, step * (float)a, s_out);
     hipLaunchKernelGGL(awq_qdq_kernel, dim3((unsigned)ceil_div(m * ngroups, 4)), dim3(256), 0,
-                       stream, W, wdt, m, n, ldw, s_out, Geff, ngroups, maxq, sym, D);
+                       stream, W, wdt, m, n, ldw, s_out, Geff, ngroups, maxq, sym, D, ldd);
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream,
                        Z, total);
-    const hipError_t e = gemm_f32_sub(Z, m, n, D, n, F, n, n, stream);  // Z = -D S
+    const hipError_t e = gemm_f32_sub(Z, ldd, m, n, D, ldd, F, n, n, stream);  // Z = -D S
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dot_partial_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, Z, D, total,
                        per, part);
@@ -333,7 +349,7 @@ hipError_t launch_awq_clip(const void* W, int wdt, int64_t m, int64_t n, int64_t
   const int64_t ngroups = ceil_div(n, G);
   const float maxq = (float)((1 << bits) - 1);
   const int64_t rows_per_wg = 16;
-  const dim3 grid((unsigned)ngroups, (unsigned)ceil_div(m, rows_per_wg));
+  const dim3 grid((unsigned)ngroups, (unsigned)std::min<int64_t>(ceil_div(m, rows_per_wg), 65535));
   hipLaunchKernelGGL(awq_clip_kernel, grid, dim3(256), 0, stream, W, wdt, m, n, ldw, S, lds, s, G,
                      ngroups, maxq, sym, nsteps, rows_per_wg, codes, scales, zeros, clip_idx);
   return hipGetLastError();

@@ -46,8 +46,9 @@ struct QuantArgs {
 };
 size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
-// C[m, n] (row stride n) -= A[m, k] (row stride lda) B[k, n] (row stride ldb), fp32 MFMA
-hipError_t gemm_f32_sub(float* C, int64_t m, int64_t n, const float* A, int64_t lda,
+// C[m, n] (row stride ldc) -= A[m, k] (row stride lda, a multiple of 4, A 16-byte
+// aligned) B[k, n] (row stride ldb), fp32 MFMA
+hipError_t gemm_f32_sub(float* C, int64_t ldc, int64_t m, int64_t n, const float* A, int64_t lda,
                         const float* B, int64_t ldb, int64_t k, hipStream_t stream);
 
 // ---- awq.hip --------------------------------------------------------------

@@ -585,9 +585,9 @@ size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act) {
   return b;
 }
 
-hipError_t gemm_f32_sub(float* C, int64_t m, int64_t n, const float* A, int64_t lda,
+hipError_t gemm_f32_sub(float* C, int64_t ldc, int64_t m, int64_t n, const float* A, int64_t lda,
                         const float* B, int64_t ldb, int64_t k, hipStream_t stream) {
-  launch_update(C, m, n, A, lda, 0, k, B, ldb, 0, 0, n, stream);
+  launch_update(C, m, ldc, A, lda, 0, k, B, ldb, 0, 0, n, stream);
   return hipGetLastError();
 }
 
