@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-awq", action="store_true",
+                    help="skip the AWQ-lite / awq_clip measurement")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the layer-sequential MLP-stack measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=128)
@@ -230,6 +232,76 @@ def dequant_gemm_measure(gq, buf, X, m, n, q, stream):
                                "algorithmic_bytes": int(byts)}
         out[name] = rec
     return out
+
+
+def awq_measure(gq, W, X, S, m, n, q, stream):
+    """AWQ-lite then awq_clip on the same layer and calibration set (S = X^T X from
+    the Hessian step): the activation statistic (one pass over X, bound by HBM),
+    the alpha search (11 candidates, each one fp32 MFMA product D S of 2 m n^2
+    flop) and the clip search (11 candidates per row and group, each a quadratic
+    form d S'_gg d^T of 2 G^2 flop on the vector units).  Events on the stream;
+    one warm-up call each, then the mean of ``reps`` calls."""
+    import torch
+
+    N = X.shape[0]
+    G = q.group_size
+    ng = -(-n // G)
+    absum = torch.zeros(n, dtype=torch.float32, device=X.device)
+    ws_abs = torch.empty(gq.awq_absum_workspace_size(n, N), dtype=torch.uint8, device=X.device)
+    s = torch.empty(n, dtype=torch.float32, device=X.device)
+    alpha = torch.empty(1, dtype=torch.float32, device=X.device)
+    losses = torch.empty(11, dtype=torch.float32, device=X.device)
+    ws_lite = torch.empty(gq.awq_lite_workspace_size(m, n), dtype=torch.uint8, device=X.device)
+    codes = torch.empty((m, n), dtype=torch.uint8, device=X.device)
+    scales = torch.empty((m, ng), dtype=torch.float32, device=X.device)
+    zeros = torch.empty((m, ng), dtype=torch.float32, device=X.device)
+    cidx = torch.empty((m, ng), dtype=torch.uint8, device=X.device)
+
+    def absum_call():
+        absum.zero_()
+        gq.awq_activation_absum(X, absum, ws=ws_abs, stream=stream)
+
+    def lite_call():
+        gq.awq_lite(W, S, absum, N, q.bits, G, s, alpha, losses, ws=ws_lite, stream=stream)
+
+    def clip_call():
+        gq.awq_clip_quantize(W, S, s, q.bits, G, codes, scales, zeros, cidx, stream=stream)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_abs = timed(absum_call, 5)
+    t_lite = timed(lite_call, 3)
+    t_clip = timed(clip_call, 5)
+    abs_bytes = N * n * 2
+    lite_flop = 11 * 2.0 * m * n * n
+    clip_flop = 11 * 2.0 * m * ng * G * G
+    a = float(alpha.cpu()[0])
+    return {
+        "alpha": round(a, 2),
+        "activation_absum": {"ms": round(t_abs, 4), "gbs": round(abs_bytes / t_abs / 1e6, 1),
+                             "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": round(abs_bytes / t_abs / 1e6 / HBM_PEAK_GBS, 4),
+                                          "algorithmic_bytes": abs_bytes}},
+        "awq_lite": {"ms": round(t_lite, 4),
+                     "tflops": round(lite_flop / t_lite / 1e9, 2),
+                     "roofline": {"bound": "mfma", "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(lite_flop / t_lite / 1e9 / FP32_PEAK_TFLOPS, 4),
+                                  "algorithmic_work": f"11 x 2 m n^2 = {lite_flop:.4e} flop"}},
+        "awq_clip": {"ms": round(t_clip, 4), "tflops": round(clip_flop / t_clip / 1e9, 2),
+                     "roofline": {"bound": "alu", "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(clip_flop / t_clip / 1e9 / FP32_PEAK_TFLOPS, 4),
+                                  "algorithmic_work": f"11 x 2 m ngroups G^2 = {clip_flop:.4e} flop"}},
+    }
 
 
 def stack_measure(gq, dev):
@@ -463,6 +535,8 @@ def main():
         "input_setup_s": round(t_gen, 1),
     }
     out["dequant_gemm"] = dequant_gemm_measure(gq, buf, X, m, n, q, stream)
+    if not args.no_awq:
+        out["awq"] = awq_measure(gq, W, X, buf.S, m, n, q, stream)
     if not args.no_stack:
         del X
         torch.cuda.empty_cache()

@@ -10,9 +10,11 @@ fallback implementation.
 from . import _lib
 from ._lib import (  # noqa: F401
     EXPORTED,
+    awq_absum_workspace_size,
     awq_activation_absum,
     awq_clip_quantize,
     awq_lite,
+    awq_lite_workspace_size,
     GPTQConfig,
     GPTQError,
     gptq_abi_version,

@@ -312,14 +312,24 @@ def gptq_residual_add(x, y, out, stream=None) -> None:
            "gptq_residual_add")
 
 
+def awq_absum_workspace_size(n: int, tokens: int) -> int:
+    out = _sz(0)
+    _check(load().awq_absum_workspace_size(n, tokens, ctypes.byref(out)),
+           "awq_absum_workspace_size")
+    return out.value
+
+
+def awq_lite_workspace_size(m: int, n: int) -> int:
+    out = _sz(0)
+    _check(load().awq_lite_workspace_size(m, n, ctypes.byref(out)), "awq_lite_workspace_size")
+    return out.value
+
+
 def awq_activation_absum(X, absum, ws=None, stream=None) -> None:
     """absum[n] += sum over tokens of |X[t, c]|."""
     tokens, n = X.shape
     if ws is None:
-        out = _sz(0)
-        _check(load().awq_absum_workspace_size(n, tokens, ctypes.byref(out)),
-               "awq_absum_workspace_size")
-        ws = _workspace(out.value, X.device)
+        ws = _workspace(awq_absum_workspace_size(n, tokens), X.device)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().awq_activation_absum(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(absum),
                                        _ptr(ws), nbytes, _stream(stream)),
@@ -331,9 +341,7 @@ def awq_lite(W, S, absum, tokens: int, bits: int, group_size: int, s_out, alpha_
     """alpha search; s_out[n], alpha_out[1], losses[n_alpha] fp32 device tensors."""
     m, n = W.shape
     if ws is None:
-        out = _sz(0)
-        _check(load().awq_lite_workspace_size(m, n, ctypes.byref(out)), "awq_lite_workspace_size")
-        ws = _workspace(out.value, W.device)
+        ws = _workspace(awq_lite_workspace_size(m, n), W.device)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().awq_lite(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(S), _ld(S), _ptr(absum),
                            int(tokens), int(bits), int(group_size), int(sym), losses.numel(),

@@ -45,6 +45,60 @@ __global__ __launch_bounds__(256) void absum_partial_kernel(const void* __restri
   part[(int64_t)blockIdx.y * n + c] = s;
 }
 
+// bf16 rows, 8 channels per lane (one 16-byte load), the workgroup's four waves
+// on interleaved tokens of the slice, combined through LDS in a fixed order
+__global__ __launch_bounds__(256) void absum_partial_bf16x8_kernel(
+    const uint16_t* __restrict__ X, int64_t tokens, int64_t n, int64_t ldx, int64_t per,
+    double* __restrict__ part) {
+  __shared__ double red[3][64][8];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * 8;
+  const int64_t t0 = (int64_t)blockIdx.y * per, t1 = min(tokens, t0 + per);
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  if (c < n) {
+    int64_t t = t0 + wv;
+    for (; t + 12 < t1; t += 16) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = *reinterpret_cast<const uint4*>(X + (t + 4 * u) * ldx + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += (double)fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu));
+          acc[2 * e + 1] += (double)fabsf(bf16_bits_to_f32(w[e] >> 16));
+        }
+      }
+    }
+    for (; t < t1; t += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(X + t * ldx + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu));
+        acc[2 * e + 1] += (double)fabsf(bf16_bits_to_f32(w[e] >> 16));
+      }
+    }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wv - 1][lane][e] = acc[e];
+  }
+  __syncthreads();
+  if (wv == 0 && c < n) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += red[w][lane][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[(int64_t)blockIdx.y * n + c + e] = acc[e];
+  }
+}
+
 __global__ __launch_bounds__(256) void absum_reduce_kernel(const double* __restrict__ part,
                                                            int64_t P, int64_t n,
                                                            float* __restrict__ absum) {
@@ -157,109 +211,148 @@ __global__ void argmin_kernel(const float* __restrict__ losses, int na, float st
   *alpha_out = (float)best * step;
 }
 
-// ---- awq_clip: one group of columns per workgroup, one row per wave at a time
+// ---- awq_clip ---------------------------------------------------------------
+// One group of columns per workgroup, its block of the rescaled second moments
+// S'_gg in LDS; one row per wave at a time.  A wave forms the errors d_k of all
+// the candidate clips of its row (lane j holds columns j and j + 64), stages them
+// in LDS as [column][candidate], and then takes every quadratic form d_k S'_gg d_k
+// in one sweep over the group's columns: each S' value read from LDS serves all
+// the candidates.
 constexpr int CLIP_MAXG = 128;
+constexpr int CLIP_NK = 12;     // candidate slots (at most 11 used), three float4s
+constexpr int CLIP_WAVES = 8;
 
-__global__ __launch_bounds__(256) void awq_clip_kernel(
+__device__ __forceinline__ void clip_params(float amax, float vmin, float vmax, int k, float maxq,
+                                            int sym, float& scale, float& zero) {
+  const float c = __fmul_rn(amax, (float)(1.0 - 0.05 * k));
+  if (sym) sym_params(fminf(amax, c), maxq, scale, zero);
+  else minmax_params(fmaxf(vmin, -c), fminf(vmax, c), maxq, scale, zero);
+}
+
+__global__ __launch_bounds__(CLIP_WAVES * 64) void awq_clip_kernel(
     const void* __restrict__ W, int dt, int64_t m, int64_t n, int64_t ldw,
     const float* __restrict__ S, int64_t lds, const float* __restrict__ s, int64_t G,
     int64_t ngroups, float maxq, int sym, int nsteps, int64_t rows_per_wg,
     uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ zeros,
     uint8_t* __restrict__ clip_idx) {
   __shared__ float Sg[CLIP_MAXG][CLIP_MAXG + 1];
-  __shared__ float dsh[4][CLIP_MAXG];
+  __shared__ float4 dsh[CLIP_WAVES][CLIP_MAXG][CLIP_NK / 4];
   const int64_t g = blockIdx.x;
   const int64_t c0 = g * G;
   const int gl = (int)min(G, n - c0);  // this group's width
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // rescaled second moments of the group: S_ij / (s_i s_j)
-  for (int idx = tid; idx < gl * gl; idx += 256) {
-    const int i = idx / gl, j = idx - i * gl;
-    const int64_t a = c0 + max(i, j), b = c0 + min(i, j);
-    const float v = S[a * lds + b];
-    Sg[i][j] = s ? v / (s[c0 + i] * s[c0 + j]) : v;
+  // rescaled second moments of the group, S_ij / (s_i s_j); zero outside it
+  for (int idx = tid; idx < CLIP_MAXG * CLIP_MAXG; idx += CLIP_WAVES * 64) {
+    const int i = idx / CLIP_MAXG, j = idx - i * CLIP_MAXG;
+    float v = 0.0f;
+    if (i < gl && j < gl) {
+      const int64_t a = c0 + max(i, j), b = c0 + min(i, j);
+      v = S[a * lds + b];
+      if (s) v = v / (s[c0 + i] * s[c0 + j]);
+    }
+    Sg[i][j] = v;
   }
   __syncthreads();
   for (int64_t rbeg = (int64_t)blockIdx.y * rows_per_wg; rbeg < m;
        rbeg += (int64_t)gridDim.y * rows_per_wg) {
-  const int64_t rend = min(m, rbeg + rows_per_wg);
-  for (int64_t r = rbeg + wv; r < rend; r += 4) {
-    // this lane's columns: lane, lane + 64
-    float v[2], amax = 0.0f, vmin = 0.0f, vmax = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = lane + 64 * h;
-      float x = 0.0f;
-      if (j < gl) {
-        const float w = load_elem(W, dt, r * ldw + c0 + j);
-        x = s ? __fmul_rn(w, s[c0 + j]) : w;
-        vmin = fminf(vmin, x);
-        vmax = fmaxf(vmax, x);
-      }
-      v[h] = x;
-      amax = fmaxf(amax, fabsf(x));
-    }
-    for (int off = 1; off < 64; off <<= 1) {
-      amax = fmaxf(amax, __shfl_xor(amax, off));
-      vmin = fminf(vmin, __shfl_xor(vmin, off));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-    }
-    float best = 0.0f;
-    int bk = 0;
-    for (int k = 0; k < nsteps; ++k) {
-      const float c = __fmul_rn(amax, (float)(1.0 - 0.05 * k));
-      float scale, zero;
-      if (sym) sym_params(fminf(amax, c), maxq, scale, zero);
-      else minmax_params(fmaxf(vmin, -c), fminf(vmax, c), maxq, scale, zero);
-      float d[2];
+    const int64_t rend = min(m, rbeg + rows_per_wg);
+    for (int64_t r = rbeg + wv; r < rend; r += CLIP_WAVES) {
+      float v[2], amax = 0.0f, vmin = 0.0f, vmax = 0.0f;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = lane + 64 * h;
-        d[h] = 0.0f;
-        if (j < gl) d[h] = scale * (quant_code(v[h], scale, zero, maxq) - zero) - v[h];
-        if (j < CLIP_MAXG) dsh[wv][j] = d[h];
+        float x = 0.0f;
+        if (j < gl) {
+          const float w = load_elem(W, dt, r * ldw + c0 + j);
+          x = s ? __fmul_rn(w, s[c0 + j]) : w;
+          vmin = fminf(vmin, x);
+          vmax = fmaxf(vmax, x);
+        }
+        v[h] = x;
+        amax = fmaxf(amax, fabsf(x));
+      }
+      for (int off = 1; off < 64; off <<= 1) {
+        amax = fmaxf(amax, __shfl_xor(amax, off));
+        vmin = fminf(vmin, __shfl_xor(vmin, off));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+      }
+      // the errors of every candidate, in the rescaled space
+      float d0[CLIP_NK], d1[CLIP_NK];
+#pragma unroll
+      for (int k = 0; k < CLIP_NK; ++k) {
+        d0[k] = 0.0f;
+        d1[k] = 0.0f;
+        if (k < nsteps) {
+          float scale, zero;
+          clip_params(amax, vmin, vmax, k, maxq, sym, scale, zero);
+          if (lane < gl) d0[k] = scale * (quant_code(v[0], scale, zero, maxq) - zero) - v[0];
+          if (lane + 64 < gl) d1[k] = scale * (quant_code(v[1], scale, zero, maxq) - zero) - v[1];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < CLIP_NK / 4; ++q) {
+        dsh[wv][lane][q] = make_float4(d0[4 * q], d0[4 * q + 1], d0[4 * q + 2], d0[4 * q + 3]);
+        dsh[wv][lane + 64][q] = make_float4(d1[4 * q], d1[4 * q + 1], d1[4 * q + 2], d1[4 * q + 3]);
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      float e = 0.0f;
+      // t_k[j] = sum_i S'_ji d_k[i] for the lane's two columns, all k at once
+      float t0[CLIP_NK], t1[CLIP_NK];
+#pragma unroll
+      for (int k = 0; k < CLIP_NK; ++k) {
+        t0[k] = 0.0f;
+        t1[k] = 0.0f;
+      }
+#pragma unroll 4
+      for (int i = 0; i < gl; ++i) {
+        const float s0 = Sg[lane][i], s1 = Sg[lane + 64][i];
+#pragma unroll
+        for (int q = 0; q < CLIP_NK / 4; ++q) {
+          const float4 dk = dsh[wv][i][q];
+          t0[4 * q] = fmaf(s0, dk.x, t0[4 * q]);
+          t0[4 * q + 1] = fmaf(s0, dk.y, t0[4 * q + 1]);
+          t0[4 * q + 2] = fmaf(s0, dk.z, t0[4 * q + 2]);
+          t0[4 * q + 3] = fmaf(s0, dk.w, t0[4 * q + 3]);
+          t1[4 * q] = fmaf(s1, dk.x, t1[4 * q]);
+          t1[4 * q + 1] = fmaf(s1, dk.y, t1[4 * q + 1]);
+          t1[4 * q + 2] = fmaf(s1, dk.z, t1[4 * q + 2]);
+          t1[4 * q + 3] = fmaf(s1, dk.w, t1[4 * q + 3]);
+        }
+      }
+      // e_k = sum_j d_k[j] t_k[j]; the first smallest wins
+      float best = 0.0f;
+      int bk = 0;
+#pragma unroll
+      for (int k = 0; k < CLIP_NK; ++k) {
+        if (k < nsteps) {
+          float e = fmaf(d1[k], t1[k], d0[k] * t0[k]);
+          for (int off = 1; off < 64; off <<= 1) e += __shfl_xor(e, off);
+          if (k == 0 || e < best) {
+            best = e;
+            bk = k;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // dsh is rewritten by the wave's next row
+      float scale, zero;
+      clip_params(amax, vmin, vmax, bk, maxq, sym, scale, zero);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = lane + 64 * h;
-        if (j < gl) {
-          float t = 0.0f;
-          for (int i = 0; i < gl; ++i) t = fmaf(Sg[j][i], dsh[wv][i], t);
-          e = fmaf(d[h], t, e);
-        }
+        if (j < gl) codes[r * n + c0 + j] = (uint8_t)quant_code(v[h], scale, zero, maxq);
       }
-      for (int off = 1; off < 64; off <<= 1) e += __shfl_xor(e, off);
-      if (k == 0 || e < best) {
-        best = e;
-        bk = k;
+      if (lane == 0) {
+        scales[r * ngroups + g] = scale;
+        zeros[r * ngroups + g] = zero;
+        if (clip_idx) clip_idx[r * ngroups + g] = (uint8_t)bk;
       }
-      __builtin_amdgcn_wave_barrier();
     }
-    // the chosen clip
-    const float c = __fmul_rn(amax, (float)(1.0 - 0.05 * bk));
-    float scale, zero;
-    if (sym) sym_params(fminf(amax, c), maxq, scale, zero);
-    else minmax_params(fmaxf(vmin, -c), fminf(vmax, c), maxq, scale, zero);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = lane + 64 * h;
-      if (j < gl) codes[r * n + c0 + j] = (uint8_t)quant_code(v[h], scale, zero, maxq);
-    }
-    if (lane == 0) {
-      scales[r * ngroups + g] = scale;
-      zeros[r * ngroups + g] = zero;
-      if (clip_idx) clip_idx[r * ngroups + g] = (uint8_t)bk;
-    }
-  }
   }
 }
 
 }  // namespace
 
-constexpr int64_t kAbsumSplit = 64;  // token slices of the activation statistics
+constexpr int64_t kAbsumSplit = 256;  // token slices of the activation statistics
 
 size_t awq_absum_ws_bytes(int64_t n, int64_t tokens) {
   (void)tokens;
@@ -271,8 +364,15 @@ hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, in
   double* part = static_cast<double*>(ws);
   const int64_t per = ceil_div(tokens, kAbsumSplit);
   const int64_t P = ceil_div(tokens, per);
-  hipLaunchKernelGGL(absum_partial_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)P),
-                     dim3(256), 0, stream, X, dt, tokens, n, ldx, per, part);
+  const bool vec = dt == GPTQ_BF16 && n % 8 == 0 && ldx % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(absum_partial_bf16x8_kernel, dim3((unsigned)ceil_div(n, 512), (unsigned)P),
+                       dim3(256), 0, stream, static_cast<const uint16_t*>(X), tokens, n, ldx, per,
+                       part);
+  else
+    hipLaunchKernelGGL(absum_partial_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)P),
+                       dim3(256), 0, stream, X, dt, tokens, n, ldx, per, part);
   hipLaunchKernelGGL(absum_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
                      part, P, n, absum);
   return hipGetLastError();
@@ -348,9 +448,9 @@ hipError_t launch_awq_clip(const void* W, int wdt, int64_t m, int64_t n, int64_t
                            uint8_t* clip_idx, hipStream_t stream) {
   const int64_t ngroups = ceil_div(n, G);
   const float maxq = (float)((1 << bits) - 1);
-  const int64_t rows_per_wg = 16;
+  const int64_t rows_per_wg = 64;
   const dim3 grid((unsigned)ngroups, (unsigned)std::min<int64_t>(ceil_div(m, rows_per_wg), 65535));
-  hipLaunchKernelGGL(awq_clip_kernel, grid, dim3(256), 0, stream, W, wdt, m, n, ldw, S, lds, s, G,
+  hipLaunchKernelGGL(awq_clip_kernel, grid, dim3(CLIP_WAVES * 64), 0, stream, W, wdt, m, n, ldw, S, lds, s, G,
                      ngroups, maxq, sym, nsteps, rows_per_wg, codes, scales, zeros, clip_idx);
   return hipGetLastError();
 }
