@@ -99,25 +99,23 @@ __global__ __launch_bounds__(256) void absum_partial_bf16x8_kernel(
   }
 }
 
+// out[c] = out[c] + sum (accumulate) or sum / div.  32 channels per workgroup,
+// 8 threads per channel on interleaved partials, combined in a fixed order.
 __global__ __launch_bounds__(256) void absum_reduce_kernel(const double* __restrict__ part,
-                                                           int64_t P, int64_t n,
-                                                           float* __restrict__ absum) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n) return;
-  double s = (double)absum[c];
-  for (int64_t p = 0; p < P; ++p) s += part[p * n + c];
-  absum[c] = (float)s;
-}
-
-// ---- per-channel mean absolute weight --------------------------------------
-__global__ __launch_bounds__(256) void col_absmean_kernel(const void* __restrict__ W, int dt,
-                                                          int64_t m, int64_t n, int64_t ldw,
-                                                          float* __restrict__ wm) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n) return;
+                                                           int64_t P, int64_t n, int accumulate,
+                                                           double div, float* __restrict__ out) {
+  __shared__ double red[8][32];
+  const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int64_t c = (int64_t)blockIdx.x * 32 + cl;
   double s = 0.0;
-  for (int64_t r = 0; r < m; ++r) s += (double)fabsf(load_elem(W, dt, r * ldw + c));
-  wm[c] = (float)(s / (double)m);
+  if (c < n)
+    for (int64_t p = grp; p < P; p += 8) s += part[p * n + c];
+  red[grp][cl] = s;
+  __syncthreads();
+  if (grp == 0 && c < n) {
+    for (int g = 1; g < 8; ++g) s += red[g][cl];
+    out[c] = accumulate ? (float)((double)out[c] + s) : (float)(s / div);
+  }
 }
 
 // s[c] = x^a / w^(1 - a), x = absum[c] / tokens, both floored; a from
@@ -194,12 +192,21 @@ __global__ __launch_bounds__(256) void dot_partial_kernel(const float* __restric
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// loss = -(sum of the partials), Z holding -(D S)
-__global__ void loss_final_kernel(const float* __restrict__ part, int64_t np,
-                                  float* __restrict__ loss) {
+// loss = -(sum of the partials), Z holding -(D S); one workgroup, fixed order
+__global__ __launch_bounds__(256) void loss_final_kernel(const float* __restrict__ part,
+                                                         int64_t np, float* __restrict__ loss) {
+  __shared__ double red[256];
+  const int64_t per = (np + 255) / 256;
+  const int64_t p0 = (int64_t)threadIdx.x * per, p1 = min(np, p0 + per);
   double acc = 0.0;
-  for (int64_t p = 0; p < np; ++p) acc += (double)part[p];
-  *loss = (float)(-acc);
+  for (int64_t p = p0; p < p1; ++p) acc += (double)part[p];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = (float)(-red[0]);
 }
 
 // alpha of the first smallest loss
@@ -359,9 +366,10 @@ size_t awq_absum_ws_bytes(int64_t n, int64_t tokens) {
   return (size_t)kAbsumSplit * (size_t)n * sizeof(double);
 }
 
-hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx,
-                            float* absum, void* ws, hipStream_t stream) {
-  double* part = static_cast<double*>(ws);
+namespace {
+// out[c] (+)= sum over rows of |A[r, c]| (accumulate), or that sum / div
+void launch_colsum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx, double* part,
+                   float* out, int accumulate, double div, hipStream_t stream) {
   const int64_t per = ceil_div(tokens, kAbsumSplit);
   const int64_t P = ceil_div(tokens, per);
   const bool vec = dt == GPTQ_BF16 && n % 8 == 0 && ldx % 8 == 0 &&
@@ -373,8 +381,14 @@ hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, in
   else
     hipLaunchKernelGGL(absum_partial_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)P),
                        dim3(256), 0, stream, X, dt, tokens, n, ldx, per, part);
-  hipLaunchKernelGGL(absum_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
-                     part, P, n, absum);
+  hipLaunchKernelGGL(absum_reduce_kernel, dim3((unsigned)ceil_div(n, 32)), dim3(256), 0, stream,
+                     part, P, n, accumulate, div, out);
+}
+}  // namespace
+
+hipError_t launch_awq_absum(const void* X, int dt, int64_t tokens, int64_t n, int64_t ldx,
+                            float* absum, void* ws, hipStream_t stream) {
+  launch_colsum(X, dt, tokens, n, ldx, static_cast<double*>(ws), absum, 1, 1.0, stream);
   return hipGetLastError();
 }
 
@@ -389,7 +403,7 @@ inline int64_t lite_ld(int64_t n) { return (int64_t)align_up((size_t)n, 4); }
 
 size_t awq_lite_ws_bytes(int64_t m, int64_t n) {
   return al((size_t)n * 4) + al((size_t)n * n * 4) + 2 * al((size_t)m * lite_ld(n) * 4) +
-         al((size_t)kDotBlocks * 4);
+         al((size_t)kDotBlocks * 4) + al(awq_absum_ws_bytes(n, m));
 }
 
 hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
@@ -407,13 +421,15 @@ hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t
   float* Z = reinterpret_cast<float*>(p);
   p += al((size_t)m * ldd * 4);
   float* part = reinterpret_cast<float*>(p);
+  p += al((size_t)kDotBlocks * 4);
+  double* colpart = reinterpret_cast<double*>(p);
   const int64_t Geff = G > 0 ? G : n;
   const int64_t ngroups = ceil_div(n, Geff);
   const float maxq = (float)((1 << bits) - 1);
   const float inv_tokens = 1.0f / (float)tokens;
   const float step = 1.0f / (float)(nalpha - 1);
   const dim3 cgrid((unsigned)ceil_div(n, 256));
-  hipLaunchKernelGGL(col_absmean_kernel, cgrid, dim3(256), 0, stream, W, wdt, m, n, ldw, wm);
+  launch_colsum(W, wdt, m, n, ldw, colpart, wm, 0, (double)m, stream);
   hipLaunchKernelGGL(symmetrize_kernel,
                      dim3((unsigned)ceil_div(n, 256), (unsigned)std::min<int64_t>(n, 65535)),
                      dim3(256), 0, stream, S, lds, n, F);
@@ -434,7 +450,7 @@ hipError_t launch_awq_lite(const void* W, int wdt, int64_t m, int64_t n, int64_t
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dot_partial_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, Z, D, total,
                        per, part);
-    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(1), 0, stream, part, nblk, losses + a);
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, stream, part, nblk, losses + a);
   }
   hipLaunchKernelGGL(argmin_kernel, dim3(1), dim3(1), 0, stream, losses, nalpha, step, alpha_out);
   hipLaunchKernelGGL(awq_scales_kernel, cgrid, dim3(256), 0, stream, absum, inv_tokens, wm, n,
