@@ -910,6 +910,114 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
   else hipLaunchKernelGGL((gemm_splitk_kernel<TILE, false>), grid, dim3(256), 0, stream, g);
 }
 
+// The two products on the factorization's critical path, the panel
+// L_k = A_k X_kk^T and the next column's update A[:, k+1] -= L_k L_{k+1,k}^T,
+// are M x 128 x 128 (M up to n - 128): C[M, 128] = alpha A[M, 128] op(B) + beta
+// C with op(B)(k, j) = B[j * ldb + k].  A workgroup takes TR rows and all 128
+// columns: its A rows are staged in LDS (row stride 132 doubles: the 16 rows x
+// 4 k of an operand read land on distinct bank pairs); 8 waves, wave w takes
+// columns 32 (w % 4) .. + 31 over half of K (w / 4), keeps that part of op(B)
+// in registers (32 doubles a lane, every load in flight at once) and runs its
+// 16 k-steps back to back; the upper half's sums are added through LDS in a
+// fixed order.  Triangular operands are read whole (their zero parts are
+// stored zeros).  beta == 0 never reads C.
+constexpr int TALL_LDA = 132;
+
+template <int TR>
+__global__ __launch_bounds__(512) void gemm_tall128_kernel(const double* __restrict__ A,
+                                                           int64_t lda,
+                                                           const double* __restrict__ B,
+                                                           int64_t ldb, double* C, int64_t ldc,
+                                                           int64_t M, double alpha, double beta) {
+  constexpr int TA = TR / 16;
+  __shared__ double As[TR][TALL_LDA];
+  __shared__ double red[4][TA * 2 * 4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wc = wv & 3, kh = wv >> 2;
+  const int r = lane & 15, kq = lane >> 4;
+  const int64_t i0 = (int64_t)blockIdx.x * TR;
+  // this wave's part of op(B): bf[b][s] = op(B)(64 kh + 4 s + kq, 32 wc + 16 b + r)
+  double bf[2][16];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const double* src = B + (int64_t)(32 * wc + 16 * b + r) * ldb + 64 * kh + kq;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) bf[b][st] = src[4 * st];
+  }
+  // the workgroup's rows of A (rows past M as zeros): thread t covers row
+  // t / 8 (+ 64 q), k 16 (t % 8) .. + 15
+  {
+    const int rr = tid >> 3;
+    if (rr < TR) {
+      const int kk = 16 * (tid & 7);
+      const int64_t gi = i0 + rr;
+      const double* src = A + (gi < M ? gi : 0) * lda + kk;
+      double2 v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const double2*>(src + 2 * e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        As[rr][kk + 2 * e] = gi < M ? v[e].x : 0.0;
+        As[rr][kk + 2 * e + 1] = gi < M ? v[e].y : 0.0;
+      }
+    }
+  }
+  __syncthreads();
+  f64x4 acc[TA][2];
+#pragma unroll
+  for (int a = 0; a < TA; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    double af[TA];
+#pragma unroll
+    for (int a = 0; a < TA; ++a) af[a] = As[16 * a + r][64 * kh + 4 * st + kq];
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b][st], acc[a][b], 0, 0, 0);
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[wc][(a * 2 + b) * 4 + q][lane] = acc[a][b][q];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int a = 0; a < TA; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = i0 + 16 * a + kq + 4 * q;
+        const int64_t j = 32 * wc + 16 * b + r;
+        if (i < M) {
+          double v = alpha * (acc[a][b][q] + red[wc][(a * 2 + b) * 4 + q][lane]);
+          if (beta != 0.0) v = fma(beta, C[i * ldc + j], v);
+          C[i * ldc + j] = v;
+        }
+      }
+}
+
+// C[M, 128] = alpha A[M, 128] B^T-indexed (op(B)(k, j) = B[j * ldb + k]) + beta C;
+// A's rows 16-byte aligned (lda even, A 16-byte aligned).
+void gemm_tall128(const double* A, int64_t lda, const double* B, int64_t ldb, double* C,
+                  int64_t ldc, int64_t M, double alpha, double beta, hipStream_t stream) {
+  if (M <= 0) return;
+  if (ceil_div(M, 32) >= 256)
+    hipLaunchKernelGGL(gemm_tall128_kernel<32>, dim3((unsigned)ceil_div(M, 32)), dim3(512), 0,
+                       stream, A, lda, B, ldb, C, ldc, M, alpha, beta);
+  else
+    hipLaunchKernelGGL(gemm_tall128_kernel<16>, dim3((unsigned)ceil_div(M, 16)), dim3(512), 0,
+                       stream, A, lda, B, ldb, C, ldc, M, alpha, beta);
+}
+
 hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t ldb, bool tb,
                 double* C, int64_t ldc, int64_t M, int64_t N, int64_t K, double alpha, double beta,
                 int kmode, bool lower, hipStream_t stream, int64_t max_wg = 0) {
@@ -1001,14 +1109,30 @@ hipError_t factor_invert(const PrepWs& w, int64_t n, int32_t* info, hipStream_t 
     const int64_t s1 = hmin(rows, (int64_t)NODE);  // width of block k + 1
     double* Lk = w.X + r1 * n + bk;                 // panel k: rows r1.., 128 columns
     // L_ik = A_ik X_kk^T  (X_kk(j, c) = 0 for c > j)
-    e = gemm(w.A + r1 * n + bk, n, false, w.X + bk * n + bk, n, true, Lk, n, rows, NODE, NODE,
-             1.0, 0.0, KHI_J, false, stream);
+    // (X_kk's upper part is stored as zeros, so the whole-K product is exact)
+    // the whole-K product wins over the split-K one at the first steps' tall
+    // panels (measured: 10.7 vs 13.3 us at 3968 rows, 9.9 vs 8.4 us at 512);
+    // it needs 16-byte aligned rows for its staged loads
+    const bool tall = n % 2 == 0;
+    if (tall && rows >= 3072) {
+      gemm_tall128(w.A + r1 * n + bk, n, w.X + bk * n + bk, n, Lk, n, rows, 1.0, 0.0, stream);
+      e = hipGetLastError();
+    } else {
+      e = gemm(w.A + r1 * n + bk, n, false, w.X + bk * n + bk, n, true, Lk, n, rows, NODE, NODE,
+               1.0, 0.0, KHI_J, false, stream);
+    }
     // column k + 1 is also written by the trailing update of step k - 1
     if (e == hipSuccess && pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
     // A[:, k+1] -= L_k L_{k+1,k}^T  (rows r1..; the diagonal block's upper part is not read)
-    if (e == hipSuccess)
-      e = gemm(Lk, n, false, Lk, n, true, w.A + r1 * n + r1, n, rows, s1, NODE, -1.0, 1.0, 0,
-               false, stream);
+    if (e == hipSuccess) {
+      if (tall && s1 == NODE && rows >= 1024) {  // 11.8 vs 25.8 us at 3968 rows, 10.7 vs 10.1 at 512
+        gemm_tall128(Lk, n, Lk, n, w.A + r1 * n + r1, n, rows, -1.0, 1.0, stream);
+        e = hipGetLastError();
+      } else {
+        e = gemm(Lk, n, false, Lk, n, true, w.A + r1 * n + r1, n, rows, s1, NODE, -1.0, 1.0, 0,
+                 false, stream);
+      }
+    }
     if (e == hipSuccess) e = hipEventRecord(side->step_done, stream);
     if (e == hipSuccess) e = node(k + 1);
     const int64_t r2 = r1 + NODE;
