@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00020001u /* major 2, minor 1 */
+#define GPTQ_ABI_VERSION 0x00020002u /* major 2, minor 2 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -200,6 +200,17 @@ gptq_status gptq_pack_ordered(const uint8_t* codes, int64_t m, int64_t n, int32_
  * Workspace: gptq_dequant_gemm_workspace_size(tokens, m, n, perm != NULL)
  * bytes (may be 0).  tokens == 0 or m == 0 is a no-op.
  * ---------------------------------------------------------------------- */
+/* gptq_gather_columns: Xp[t, p] = X[t, perm[p]] for p < n, 0 for n <= p < ldxp --
+ * the processing-order activations the product reads when perm is given,
+ * formed once so that several layers with the same order (layers sharing an
+ * input, hence a Hessian and its order: "GPTQ deep dive" section 3.1 step 4)
+ * can be multiplied with perm = NULL.  X, Xp bf16 [tokens, *] device, row
+ * strides ldx >= n and ldxp >= n (ldxp a multiple of 8, Xp 16-byte aligned);
+ * perm int32 [n] device, a permutation of 0..n-1 (an entry outside it reads
+ * as 0).  No workspace.  GPTQ_ERR_UNSUPPORTED for fp32 X. */
+gptq_status gptq_gather_columns(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                                int64_t ldx, const int32_t* perm, void* Xp, int64_t ldxp,
+                                hipStream_t stream);
 gptq_status gptq_dequant_gemm_workspace_size(int64_t tokens, int64_t m, int64_t n,
                                              int32_t has_perm, size_t* bytes);
 gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     gptq_abi_version,
     gptq_dequant_gemm,
     gptq_dequant_gemm_workspace_size,
+    gptq_gather_columns,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_size,
     gptq_pack,

@@ -39,6 +39,7 @@ EXPORTED = (
     "gptq_pack_ordered",
     "gptq_dequant_gemm_workspace_size",
     "gptq_dequant_gemm",
+    "gptq_gather_columns",
     "gptq_swiglu",
     "gptq_residual_add",
     "awq_absum_workspace_size",
@@ -115,6 +116,8 @@ def load() -> ctypes.CDLL:
     lib.gptq_dequant_gemm.restype = _i32
     lib.gptq_dequant_gemm.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp,
                                       _vp, _vp, _i64, _vp, _i32, _i64, _vp, _sz, _vp]
+    lib.gptq_gather_columns.restype = _i32
+    lib.gptq_gather_columns.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp]
     lib.gptq_swiglu.restype = _i32
     lib.gptq_swiglu.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
     lib.gptq_residual_add.restype = _i32
@@ -294,6 +297,14 @@ def gptq_dequant_gemm(X, packed, bits: int, group_size: int, scales, zeros, Y, p
                                     _ptr(zeros), _ptr(perm), m, _ptr(Y), _dtype_code(Y), _ld(Y),
                                     _ptr(ws), nbytes, _stream(stream)),
            "gptq_dequant_gemm")
+
+
+def gptq_gather_columns(X, perm, Xp, stream=None) -> None:
+    """Xp[t, p] = X[t, perm[p]] (bf16; Xp's columns past n are zeroed)."""
+    tokens, n = X.shape
+    _check(load().gptq_gather_columns(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(perm),
+                                      _ptr(Xp), _ld(Xp), _stream(stream)),
+           "gptq_gather_columns")
 
 
 def gptq_swiglu(gate, up, h, stream=None) -> None:

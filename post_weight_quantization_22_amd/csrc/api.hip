@@ -162,6 +162,21 @@ gptq_status gptq_dequant_gemm_workspace_size(int64_t tokens, int64_t m, int64_t 
   return GPTQ_OK;
 }
 
+gptq_status gptq_gather_columns(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
+                                int64_t ldx, const int32_t* perm, void* Xp, int64_t ldxp,
+                                hipStream_t stream) {
+  if (tokens < 0 || bad_dim(tokens) || n <= 0 || bad_dim(n) || !valid_dtype(xdt))
+    return GPTQ_ERR_INVALID_ARG;
+  if (xdt != GPTQ_BF16) return GPTQ_ERR_UNSUPPORTED;
+  if (tokens == 0) return GPTQ_OK;
+  if (!X || !perm || !Xp || ldx < n || ldxp < n || ldxp % 8 != 0 ||
+      (reinterpret_cast<uintptr_t>(Xp) & 15) != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  launch_gather(static_cast<const uint16_t*>(X), ldx, perm, tokens, n, ldxp,
+                static_cast<uint16_t*>(Xp), stream);
+  return hip_status(hipGetLastError());
+}
+
 gptq_status gptq_dequant_gemm(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
                               int64_t ldx, const uint32_t* packed, int64_t ldp, int32_t bits,
                               int32_t group_size, const float* scales, const float* zeros,

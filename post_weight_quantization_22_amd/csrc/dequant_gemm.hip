@@ -914,6 +914,65 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
   *reinterpret_cast<uint4*>(Xp + t * ldxp + p0) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// The same gather with every row staged in LDS: a workgroup walks a run of
+// rows; a row arrives with 16-byte loads (coalesced; the next row's loads are
+// in flight while this one is permuted) and leaves permuted, 8 positions per
+// thread and 16-byte store, the permuted reads served by the LDS.  n and ldx
+// multiples of 8, X 16-byte aligned, n <= NCAP.  Out-of-range perm entries
+// read as zero.
+template <int NCAP>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X,
+                                                          int64_t ldx,
+                                                          const int32_t* __restrict__ perm,
+                                                          int64_t tokens, int64_t n, int64_t ldxp,
+                                                          int64_t rows_per_wg,
+                                                          uint16_t* __restrict__ Xp) {
+  constexpr int CH = NCAP / 8 / 256;  // 16-byte chunks of a row per thread
+  __shared__ __align__(16) uint16_t buf[2][NCAP];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t t1 = min(tokens, t0 + rows_per_wg);
+  if (t0 >= t1) return;
+  const int nch = (int)(n / 8);
+  uint4 v[CH];
+  auto fetch = [&](int64_t t) {
+    const uint4* src = reinterpret_cast<const uint4*>(X + t * ldx);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      if (idx < nch) v[c] = src[idx];
+    }
+  };
+  fetch(t0);
+  for (int64_t t = t0; t < t1; ++t) {
+    uint16_t* b = buf[(t - t0) & 1];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      if (idx < nch) reinterpret_cast<uint4*>(b)[idx] = v[c];
+    }
+    if (t + 1 < t1) fetch(t + 1);
+    __syncthreads();
+    for (int64_t sg = tid; sg < ldxp / 8; sg += 256) {
+      const int64_t p0 = 8 * sg;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int64_t p = p0 + 2 * q + e;
+          const int32_t src = p < n ? perm[p] : -1;
+          h[e] = (src >= 0 && src < n) ? (uint32_t)b[src] : 0u;
+        }
+        w[q] = h[0] | (h[1] << 16);
+      }
+      *reinterpret_cast<uint4*>(Xp + t * ldxp + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // buffer (t - t0) & 1 is written again two rows on, after the next barrier
+  }
+}
+
 struct Shape {
   int bm, bn;
   int64_t ks;
@@ -987,6 +1046,28 @@ hipError_t launch_bits(const DqArgs& a, int bm, hipStream_t stream) {
 
 }  // namespace
 
+void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t tokens,
+                   int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream) {
+  if (tokens <= 0) return;
+  const bool rows = n % 8 == 0 && ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+                    n <= 32768;
+  if (rows) {
+    // about 1024 workgroups, at least 4 rows each
+    const int64_t rpw = hmax((int64_t)4, ceil_div(tokens, (int64_t)1024));
+    const dim3 grid((unsigned)ceil_div(tokens, rpw));
+    if (n <= 16384)
+      hipLaunchKernelGGL(gather_rows_kernel<16384>, grid, dim3(256), 0, stream, X, ldx, perm,
+                         tokens, n, ldxp, rpw, Xp);
+    else
+      hipLaunchKernelGGL(gather_rows_kernel<32768>, grid, dim3(256), 0, stream, X, ldx, perm,
+                         tokens, n, ldxp, rpw, Xp);
+  } else {
+    const int64_t total = tokens * (ldxp / 8);
+    hipLaunchKernelGGL(gather_columns_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                       stream, X, ldx, perm, tokens, n, ldxp, Xp);
+  }
+}
+
 size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm) {
   const Shape s = choose_shape(tokens, m, n);
   size_t bytes = 0;
@@ -1005,9 +1086,7 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
     const int64_t ldxp = (int64_t)align_up((size_t)d.n, 8);
     uint16_t* Xp = reinterpret_cast<uint16_t*>(ws);
     ws += align_up((size_t)d.tokens * (size_t)ldxp * 2, 256);
-    const int64_t total = d.tokens * (ldxp / 8);
-    hipLaunchKernelGGL(gather_columns_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
-                       stream, a.X, d.ldx, d.perm, d.tokens, d.n, ldxp, Xp);
+    launch_gather(a.X, d.ldx, d.perm, d.tokens, d.n, ldxp, Xp, stream);
     a.X = Xp;
     a.ldx = ldxp;
   }

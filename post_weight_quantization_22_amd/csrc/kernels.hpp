@@ -82,6 +82,9 @@ struct DequantArgs {
   void* ws;
 };
 size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm);
+// Xp[t, p] = X[t, perm[p]] (p < n), 0 for n <= p < ldxp (bf16)
+void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t tokens,
+                   int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream);
 hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream);
 
 // ---- forward.hip ----------------------------------------------------------

@@ -50,6 +50,7 @@ class _Products:
         self.device = device
         self.ws = {}
         self.out = {}
+        self.xp = {}
 
     def get(self, tokens: int, m: int, n: int, has_perm: bool, slot: str):
         key = (tokens, m, n, has_perm)
@@ -70,11 +71,28 @@ def _packed(buf: pipeline.LayerBuffers, desc_act: bool, stream) -> QuantizedLaye
     return QuantizedLayer(buf, packed, perm)
 
 
-def _product(prod: _Products, X: torch.Tensor, L: QuantizedLayer, slot: str,
+def _gathered(prod: _Products, X: torch.Tensor, perm: Optional[torch.Tensor], slot: str,
+              stream) -> torch.Tensor:
+    """X in the layers' processing order (X itself without desc_act), formed
+    once for every layer that reads it."""
+    if perm is None:
+        return X
+    key = (X.shape[0], X.shape[1], slot)
+    if key not in prod.xp:
+        ldxp = -(-X.shape[1] // 8) * 8
+        prod.xp[key] = torch.empty((X.shape[0], ldxp), dtype=torch.bfloat16,
+                                   device=prod.device)[:, :X.shape[1]]
+    Xp = prod.xp[key]
+    _lib.gptq_gather_columns(X, perm, Xp, stream=stream)
+    return Xp
+
+
+def _product(prod: _Products, Xp: torch.Tensor, L: QuantizedLayer, slot: str,
              stream) -> torch.Tensor:
-    ws, Y = prod.get(X.shape[0], L.buf.m, L.buf.n, L.perm is not None, slot)
-    _lib.gptq_dequant_gemm(X, L.packed, L.buf.cfg.bits, L.buf.cfg.group_size, L.buf.scales,
-                           L.buf.zeros, Y, perm=L.perm, ws=ws, stream=stream)
+    """Y = X W_q^T from the activations already in L's processing order."""
+    ws, Y = prod.get(Xp.shape[0], L.buf.m, L.buf.n, False, slot)
+    _lib.gptq_dequant_gemm(Xp, L.packed, L.buf.cfg.bits, L.buf.cfg.group_size, L.buf.scales,
+                           L.buf.zeros, Y, perm=None, ws=ws, stream=stream)
     return Y
 
 
@@ -126,8 +144,9 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
         h = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
         for t0 in range(0, T, chunk_tokens):
             t1 = min(T, t0 + chunk_tokens)
-            g = _product(prod, x[t0:t1], gate, "g", stream)
-            u = _product(prod, x[t0:t1], up, "u", stream)
+            xp = _gathered(prod, x[t0:t1], gate.perm, "x", stream)  # gate and up: one order
+            g = _product(prod, xp, gate, "g", stream)
+            u = _product(prod, xp, up, "u", stream)
             _lib.gptq_swiglu(g, u, h[t0:t1], stream=stream)
         mark("forward")
         # down: Hessian of h
@@ -144,7 +163,8 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
         x_next = torch.empty_like(x)
         for t0 in range(0, T, chunk_tokens):
             t1 = min(T, t0 + chunk_tokens)
-            y = _product(prod, h[t0:t1], down, "y", stream)
+            y = _product(prod, _gathered(prod, h[t0:t1], down.perm, "h", stream), down, "y",
+                         stream)
             _lib.gptq_residual_add(x[t0:t1], y, x_next[t0:t1], stream=stream)
         mark("forward")
         for b in (bg, bu, bd):

@@ -221,3 +221,28 @@ def test_awq_argument_validation(lib):
     assert clip(G=0) == lib.GPTQ_ERR_INVALID_ARG
     assert clip(steps=12) == lib.GPTQ_ERR_INVALID_ARG
     assert clip(m=0) == lib.GPTQ_OK
+
+
+def test_gather_argument_validation(lib):
+    so = lib.load()
+    bf, f32 = lib.GPTQ_BF16, lib.GPTQ_F32
+    assert so.gptq_gather_columns(FAKE, bf, 0, 64, 64, FAKE, FAKE, 64, None) == lib.GPTQ_OK
+    assert so.gptq_gather_columns(FAKE, f32, 4, 64, 64, FAKE, FAKE, 64, None) == \
+        lib.GPTQ_ERR_UNSUPPORTED
+    assert so.gptq_gather_columns(FAKE, bf, 4, 64, 64, FAKE, FAKE, 68, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldxp not a multiple of 8
+    assert so.gptq_gather_columns(FAKE, bf, 4, 64, 32, FAKE, FAKE, 64, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldx < n
+    assert so.gptq_gather_columns(FAKE, bf, 4, 64, 64, None, FAKE, 64, None) == \
+        lib.GPTQ_ERR_INVALID_ARG
+
+
+def test_every_binding_declares_its_signature(lib):
+    """Without argtypes ctypes passes Python ints as C int, masked to 32 bits:
+    device pointers would arrive truncated.  Every exported function used by
+    the binding must declare its argument and result types."""
+    so = lib.load()
+    for name in lib.EXPORTED:
+        fn = getattr(so, name)
+        assert fn.argtypes is not None, name
+        assert fn.restype is not None, name

@@ -265,3 +265,27 @@ def test_dequant_gemm_full_size(name, m, n, bits, G, perm_on, tokens):
     Y, _ = _run(q, X, codes, scales, zeros, perm, bits, G, perm_on)
     rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 22, replace=False)]))
     _check(Y, X, codes.astype(np.int64), scales, zeros, perm, bits, G, rows=rows)
+
+
+@pytest.mark.parametrize("tokens,n,ldx,ldxp", [
+    (37, 4096, 4096, 4096),      # rows staged in LDS (n <= 16384)
+    (9, 11008, 11016, 11008),    # row stride past n
+    (5, 20000, 20000, 20008),    # the 32768-position LDS variant, zeroed tail of Xp
+    (3, 77, 77, 80),             # n not a multiple of 8: the per-element gather
+    (1000, 256, 256, 256),       # many rows per workgroup
+])
+def test_gather_columns_exact(tokens, n, ldx, ldxp):
+    """gptq_gather_columns: Xp[t, p] = X[t, perm[p]] bit for bit, zeros past n."""
+    q = need_gpu()
+    rng = np.random.default_rng(tokens * 7 + n)
+    X = rng.standard_normal((tokens, ldx)).astype(np.float32)
+    perm = rng.permutation(n).astype(np.int32)
+    say("gather", tokens, n, ldx, ldxp)
+    Xd = dev(X, torch.bfloat16)[:, :n]
+    Xp = torch.full((tokens, ldxp), 7.0, dtype=torch.bfloat16, device="cuda")
+    q.gptq_gather_columns(Xd, dev(perm, torch.int32), Xp[:, :n])
+    torch.cuda.synchronize()
+    Xb = host(Xd.view(torch.int16)).astype(np.int64)
+    got = host(Xp.view(torch.int16)).astype(np.int64)
+    assert np.array_equal(got[:, :n], Xb[:, perm])
+    assert np.all(got[:, n:] == 0)
