@@ -229,3 +229,40 @@ def test_awq_full_size_llama7b_attention():
         Ws, 4, 128, ranges=oracle.f32(amax * oracle.f32(awq.CLIP_RATIOS[ci])))
     assert np.array_equal(host(codes).astype(np.int64)[rows], c_ref)
     assert np.array_equal(host(scales).astype(np.float64)[rows], s_ref2)
+
+
+def test_awq_layer_through_the_packed_product():
+    """The AWQ-quantized layer runs on the packed format and the product as they
+    are: codes of W diag(s) in groups of consecutive columns (gptq_pack, no
+    permutation), activations X diag(1/s) (formed here on the host and rounded
+    to bf16, as the previous operator would hand them over), and
+    gptq_dequant_gemm gives X W_eff^T, W_eff = dequant(codes) diag(1/s) the
+    oracle's effective weights, within the bf16 roundings of X/s and of the
+    weights (2^-8 of each term, twice) and the fp32 sums."""
+    q = need_gpu()
+    rng = np.random.default_rng(21)
+    m, n, tokens, bits, G = 256, 512, 2048, 4, 128
+    W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.02).astype(np.float32)).astype(np.float64)
+    X = rng.standard_normal((tokens, n))
+    X[:, rng.choice(n, 5, replace=False)] *= 30.0
+    X = synth.round_to_bf16(X.astype(np.float32)).astype(np.float64)
+    say("awq layer product", m, n, tokens)
+    r = _run(q, W, X, bits, G)
+    codes = dev(r["codes"].astype(np.uint8), torch.uint8)
+    packed = torch.empty((m, n * bits // 32), dtype=torch.int32, device="cuda")
+    q.gptq_pack(codes, bits, packed)
+    Xs = synth.round_to_bf16((X / r["s"]).astype(np.float32)).astype(np.float64)
+    Y = torch.empty((64, m), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(q.gptq_dequant_gemm_workspace_size(64, m, n, False), 1), dtype=torch.uint8,
+                     device="cuda")
+    q.gptq_dequant_gemm(dev(Xs[:64].astype(np.float32), torch.bfloat16), packed, bits, G,
+                        dev(r["scales"].astype(np.float32), torch.float32),
+                        dev(r["zeros"].astype(np.float32), torch.float32), Y, ws=ws)
+    torch.cuda.synchronize()
+    W_eff = awq.dequant_groups(r["codes"], r["scales"], r["zeros"], G) / r["s"]
+    Y_ref = X[:64] @ W_eff.T
+    Wq = awq.dequant_groups(r["codes"], r["scales"], r["zeros"], G)
+    bound = (2 * 2.0 ** -8 + 8 * np.sqrt(n) * EPS32) * (np.abs(Xs[:64]) @ np.abs(Wq).T) + 1e-6
+    diff = np.abs(host(Y).astype(np.float64) - Y_ref)
+    print(f"  max |Y - X W_eff^T| / bound {float((diff / bound).max()):.3f}", flush=True)
+    assert np.all(diff <= bound)
