@@ -664,6 +664,94 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode batches of at most 16 tokens, n a multiple of 128, every 32-position
+// run in one group: one workgroup per 16 weight rows over the whole K range, so
+// no second kernel adds split partial sums and no partials go through HBM.
+// The eight waves take an eighth of the 128-position chunks each (at n = 4096
+// four chunks, whose loads are all in flight at once).  Per chunk a
+// lane (weight row l % 16 and token l % 16, run g = l / 16) loads the 32 codes
+// of run g of its row (BITS words) and the 32 activations of run g of its
+// token (four 16-byte loads), both straight into registers, and feeds four
+// v_mfma_f32_16x16x32_bf16 whose k slots of
+// lane group g hold positions 8 j .. 8 j + 7 of run g on both sides.  The
+// waves' 16 x 16 sums are added through LDS in wave order.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int GV16_WAVES = 8;
+
+template <int BITS>
+__global__ __launch_bounds__(GV16_WAVES * 64) void dequant_gemv16_kernel(DqArgs a) {
+  constexpr int CB = 4;  // chunks whose loads are in flight together
+  __shared__ f32x4_t red[GV16_WAVES - 1][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rl = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t r = min(row0 + rl, a.m - 1);
+  const int64_t t = min((int64_t)rl, a.tokens - 1);
+  const int nch = (int)(a.n / 128);
+  const int cw = (nch + GV16_WAVES - 1) / GV16_WAVES;
+  const int c0 = wv * cw, c1 = min(nch, c0 + cw);
+  const uint32_t* prow = a.P + r * a.ldp;
+  const uint16_t* xrow = a.X + t * a.ldx;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int cb = c0; cb < c1; cb += CB) {
+    uint32_t w[CB][BITS];
+    uint4 xv[CB][4];
+    float sc[CB], nz[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = min(cb + u, c1 - 1);  // a valid chunk; unused past c1
+      const int64_t pos = 128 * (int64_t)c + 32 * g;
+#pragma unroll
+      for (int i = 0; i < BITS; ++i) w[u][i] = prow[(pos >> 5) * BITS + i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[u][i] = *reinterpret_cast<const uint4*>(xrow + pos + 8 * i);
+      const int64_t grp = a.G > 0 ? pos / a.G : 0;
+      const float s = a.scales[r * a.ngroups + grp];
+      sc[u] = s;
+      nz[u] = -(a.zeros[r * a.ngroups + grp] * s);
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (cb + u < c1) {  // uniform in the workgroup
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float f[8];
+          decode8<BITS>(w[u], j, f);
+          uint4 bw;
+          bw.x = bf16x2_bits(fmaf(f[0], sc[u], nz[u]), fmaf(f[1], sc[u], nz[u]));
+          bw.y = bf16x2_bits(fmaf(f[2], sc[u], nz[u]), fmaf(f[3], sc[u], nz[u]));
+          bw.z = bf16x2_bits(fmaf(f[4], sc[u], nz[u]), fmaf(f[5], sc[u], nz[u]));
+          bw.w = bf16x2_bits(fmaf(f[6], sc[u], nz[u]), fmaf(f[7], sc[u], nz[u]));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u][j]),
+                                                        __builtin_bit_cast(bf16x8, bw), acc, 0, 0,
+                                                        0);
+        }
+      }
+    }
+  }
+  if (wv > 0) red[wv - 1][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int w = 0; w < GV16_WAVES - 1; ++w) acc += red[w][lane];
+  // element q of lane l: token 4 (l / 16) + q, weight row row0 + l % 16
+  const int64_t row = row0 + rl;
+  if (row >= a.m) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tok = 4 * g + q;
+    if (tok < a.tokens) {
+      if (a.ybf16)
+        reinterpret_cast<uint16_t*>(a.Y)[tok * a.ldy + row] =
+            (uint16_t)(bf16x2_bits(acc[q], 0.0f) & 0xFFFFu);
+      else
+        reinterpret_cast<float*>(a.Y)[tok * a.ldy + row] = acc[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode batches (<= 32 tokens), n a multiple of 128: bound by the codes' HBM
 // traffic and by how many cache lines the loads touch, so the codes never go
 // through LDS.  A workgroup of 4 waves owns 128 weight rows (32 per wave) and a
@@ -988,11 +1076,13 @@ Shape choose_shape(int64_t tokens, int64_t m, int64_t n) {
   const int64_t nchunks = ceil_div(n, BK);
   s.ks = 1;
   if (tokens <= 32) {
-    // decode batches: 128-row workgroups, K split until ~2 workgroups per CU,
-    // >= 2 steps of 128 positions per split (both steps' codes in flight at once)
+    // decode batches (the split path, 17..32 tokens or shapes the 16-token
+    // kernel does not take): 128-row workgroups, K split until ~1 workgroup per
+    // CU (measured at 4096 x 4096: 11.9 us at 32 tokens against 14.4 us with
+    // ~2 per CU), >= 2 steps of 128 positions per split
     const int64_t tiles = ceil_div(m, 128);
     const int64_t steps = ceil_div(n, 128);
-    while (tiles * s.ks * 2 <= 512 && steps / (s.ks * 2) >= 2) s.ks *= 2;
+    while (tiles * s.ks * 2 <= 256 && steps / (s.ks * 2) >= 2) s.ks *= 2;
     // the group parameters of a split are staged in LDS: at most 16 steps
     // (2048 positions, 32 groups of 64) per split
     while (ceil_div(steps, s.ks) > 16) s.ks *= 2;
@@ -1123,6 +1213,20 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
                    (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 && a.ldx < (int64_t(1) << 23) &&
                    d.ldp < (int64_t(1) << 23);
   hipError_t e;
+  // up to 16 tokens: the single-kernel path (whole K per workgroup)
+  const bool gv16 = dma && d.tokens <= 16 && d.n % 128 == 0 &&
+                    (d.group_size <= 0 || d.group_size % 32 == 0);
+  if (gv16) {
+    const dim3 grid((unsigned)ceil_div(d.m, 16));
+    switch (d.bits) {
+      case 2: hipLaunchKernelGGL(dequant_gemv16_kernel<2>, grid, dim3(GV16_WAVES * 64), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(dequant_gemv16_kernel<3>, grid, dim3(GV16_WAVES * 64), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(dequant_gemv16_kernel<4>, grid, dim3(GV16_WAVES * 64), 0, stream, a); break;
+      case 5: hipLaunchKernelGGL(dequant_gemv16_kernel<5>, grid, dim3(GV16_WAVES * 64), 0, stream, a); break;
+      default: hipLaunchKernelGGL(dequant_gemv16_kernel<6>, grid, dim3(GV16_WAVES * 64), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   const int64_t gv_steps = d.n / GV_STEP;
   const int64_t gv_per_split = ceil_div(gv_steps, s.ks);
   const bool gv = dma && s.bm == 32 && d.n % GV_STEP == 0 &&
