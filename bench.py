@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one Hessian accumulate of the workload and one 2 GiB device copy, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    ap.add_argument("--dequant-probe", action="store_true",
+                    help="run the quantized layer's product 10 times at 2048 and at 16 tokens "
+                         "(4096 x 4096, random 4-bit codes, group 128), for rocprofv3 counter "
+                         "runs, then exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter files of two --traffic-probe runs into "
                          "profiles/traffic_hessian_llama7b_attn.json, then exit")
@@ -304,6 +308,31 @@ def awq_measure(gq, W, X, S, m, n, q, stream):
     }
 
 
+def dequant_probe(gq, dev):
+    """Ten products at 2048 tokens, then ten at 16, on a 4096 x 4096 4-bit g128
+    layer of random codes packed in processing order (identity order)."""
+    import numpy as np
+    import torch
+
+    m = n = 4096
+    bits, G = 4, 128
+    rng = np.random.default_rng(0)
+    codes = torch.from_numpy(rng.integers(0, 16, size=(m, n), dtype=np.uint8)).to(dev)
+    packed = torch.empty((m, n * bits // 32), dtype=torch.int32, device=dev)
+    gq.gptq_pack_ordered(codes, bits, None, packed)
+    scales = torch.from_numpy(rng.uniform(1e-3, 1e-2, size=(m, n // G)).astype(np.float32)).to(dev)
+    zeros = torch.from_numpy(rng.integers(0, 16, size=(m, n // G)).astype(np.float32)).to(dev)
+    X = torch.from_numpy(rng.standard_normal((2048, n)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    for tokens in (2048, 16):
+        Y = torch.empty((tokens, m), dtype=torch.float32, device=dev)
+        nws = gq.gptq_dequant_gemm_workspace_size(tokens, m, n, False)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        for _ in range(10):
+            gq.gptq_dequant_gemm(X[:tokens], packed, bits, G, scales, zeros, Y, ws=ws)
+        torch.cuda.synchronize()
+    print("dequant probe: 10 products at 2048 and 10 at 16 tokens done", flush=True)
+
+
 def stack_measure(gq, dev):
     """Layer-sequential GPTQ of a two-block Llama-7B MLP stack (d 4096, f 11008,
     128 x 2048 calibration tokens, 4-bit g128 desc_act): each layer quantized on
@@ -396,6 +425,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dequant_probe:
+        dequant_probe(gq, dev)
+        return
 
     wl = synth.get_workload(WORKLOAD)
     ls = wl.layer()
