@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00020002u /* major 2, minor 2 */
+#define GPTQ_ABI_VERSION 0x00020003u /* major 2, minor 3 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -200,6 +200,26 @@ gptq_status gptq_pack_ordered(const uint8_t* codes, int64_t m, int64_t n, int32_
  * Workspace: gptq_dequant_gemm_workspace_size(tokens, m, n, perm != NULL)
  * bytes (may be 0).  tokens == 0 or m == 0 is a no-op.
  * ---------------------------------------------------------------------- */
+/* gptq_dequantize: W[m, n] bf16 (row stride ldw, a multiple of 8, 16-byte
+ * aligned) = the weights gptq_dequant_gemm forms, bf16(fma(q, s, -(z s))) with
+ * the fma in fp32 and round to nearest even ("Quantized deployment, 1.5 TB to
+ * 250 GB" section 2.1: r = (q - zero) * scale), from codes packed in
+ * processing order as gptq_dequant_gemm reads them (same packed, ldp, bits,
+ * group_size, scales, zeros).  n a multiple of 8 (GPTQ_ERR_UNSUPPORTED
+ * otherwise).  For products over many tokens the weights are dequantized
+ * once and multiplied with gptq_gemm_bf16.
+ *
+ * gptq_gemm_bf16: Y[tokens, m] = X[tokens, n] W[m, n]^T, X and W bf16 device
+ * (row strides multiples of 8 below 2^23, 16-byte aligned), products exact,
+ * fp32 sums in a fixed order; Y fp32 or bf16 (round to nearest even), row
+ * stride ldy >= m.  n a multiple of 8.  No workspace. */
+gptq_status gptq_dequantize(const uint32_t* packed, int64_t ldp, int32_t bits,
+                            int32_t group_size, const float* scales, const float* zeros,
+                            int64_t m, int64_t n, void* W, int64_t ldw, hipStream_t stream);
+gptq_status gptq_gemm_bf16(const void* X, int64_t tokens, int64_t n, int64_t ldx, const void* W,
+                           int64_t m, int64_t ldw, void* Y, gptq_dtype ydt, int64_t ldy,
+                           hipStream_t stream);
+
 /* gptq_gather_columns: Xp[t, p] = X[t, perm[p]] for p < n, 0 for n <= p < ldxp --
  * the processing-order activations the product reads when perm is given,
  * formed once so that several layers with the same order (layers sharing an

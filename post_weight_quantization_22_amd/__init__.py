@@ -20,7 +20,9 @@ from ._lib import (  # noqa: F401
     gptq_abi_version,
     gptq_dequant_gemm,
     gptq_dequant_gemm_workspace_size,
+    gptq_dequantize,
     gptq_gather_columns,
+    gptq_gemm_bf16,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_size,
     gptq_pack,

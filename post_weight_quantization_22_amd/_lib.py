@@ -40,6 +40,8 @@ EXPORTED = (
     "gptq_dequant_gemm_workspace_size",
     "gptq_dequant_gemm",
     "gptq_gather_columns",
+    "gptq_dequantize",
+    "gptq_gemm_bf16",
     "gptq_swiglu",
     "gptq_residual_add",
     "awq_absum_workspace_size",
@@ -116,6 +118,10 @@ def load() -> ctypes.CDLL:
     lib.gptq_dequant_gemm.restype = _i32
     lib.gptq_dequant_gemm.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp,
                                       _vp, _vp, _i64, _vp, _i32, _i64, _vp, _sz, _vp]
+    lib.gptq_dequantize.restype = _i32
+    lib.gptq_dequantize.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]
+    lib.gptq_gemm_bf16.restype = _i32
+    lib.gptq_gemm_bf16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp]
     lib.gptq_gather_columns.restype = _i32
     lib.gptq_gather_columns.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp]
     lib.gptq_swiglu.restype = _i32
@@ -297,6 +303,25 @@ def gptq_dequant_gemm(X, packed, bits: int, group_size: int, scales, zeros, Y, p
                                     _ptr(zeros), _ptr(perm), m, _ptr(Y), _dtype_code(Y), _ld(Y),
                                     _ptr(ws), nbytes, _stream(stream)),
            "gptq_dequant_gemm")
+
+
+def gptq_dequantize(packed, bits: int, group_size: int, scales, zeros, n: int, W,
+                    stream=None) -> None:
+    """W[m, n] (bf16) = the product's weights from processing-order packed codes."""
+    m = packed.shape[0]
+    _check(load().gptq_dequantize(_ptr(packed), _ld(packed), int(bits), int(group_size),
+                                  _ptr(scales), _ptr(zeros), m, int(n), _ptr(W), _ld(W),
+                                  _stream(stream)),
+           "gptq_dequantize")
+
+
+def gptq_gemm_bf16(X, W, Y, stream=None) -> None:
+    """Y[tokens, m] = X[tokens, n] W[m, n]^T (bf16 operands, Y fp32 or bf16)."""
+    tokens, n = X.shape
+    m = W.shape[0]
+    _check(load().gptq_gemm_bf16(_ptr(X), tokens, n, _ld(X), _ptr(W), m, _ld(W), _ptr(Y),
+                                 _dtype_code(Y), _ld(Y), _stream(stream)),
+           "gptq_gemm_bf16")
 
 
 def gptq_gather_columns(X, perm, Xp, stream=None) -> None:

@@ -162,6 +162,38 @@ gptq_status gptq_dequant_gemm_workspace_size(int64_t tokens, int64_t m, int64_t 
   return GPTQ_OK;
 }
 
+gptq_status gptq_dequantize(const uint32_t* packed, int64_t ldp, int32_t bits,
+                            int32_t group_size, const float* scales, const float* zeros,
+                            int64_t m, int64_t n, void* W, int64_t ldw, hipStream_t stream) {
+  if (bad_dim(m) || n <= 0 || bad_dim(n) || bits < 2 || bits > 8 ||
+      !(group_size == -1 || (group_size >= 8 && group_size % 8 == 0)))
+    return GPTQ_ERR_INVALID_ARG;
+  if (n % 8 != 0) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0) return GPTQ_OK;
+  if (!packed || !scales || !zeros || !W || ldp < ceil_div(n * bits, 32) || ldw < n ||
+      ldw % 8 != 0 || (reinterpret_cast<uintptr_t>(W) & 15) != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  return hip_status(launch_dequantize(packed, ldp, bits, m, n, scales, zeros, group_size,
+                                      static_cast<uint16_t*>(W), ldw, stream));
+}
+
+gptq_status gptq_gemm_bf16(const void* X, int64_t tokens, int64_t n, int64_t ldx, const void* W,
+                           int64_t m, int64_t ldw, void* Y, gptq_dtype ydt, int64_t ldy,
+                           hipStream_t stream) {
+  if (tokens < 0 || bad_dim(tokens) || bad_dim(m) || n <= 0 || bad_dim(n) || !valid_dtype(ydt))
+    return GPTQ_ERR_INVALID_ARG;
+  if (n % 8 != 0) return GPTQ_ERR_UNSUPPORTED;
+  if (tokens == 0 || m == 0) return GPTQ_OK;
+  if (!X || !W || !Y || ldx < n || ldw < n || ldy < m || ldx % 8 != 0 || ldw % 8 != 0 ||
+      (reinterpret_cast<uintptr_t>(X) & 15) != 0 || (reinterpret_cast<uintptr_t>(W) & 15) != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  // the DMA offsets within a tile are 32-bit
+  if (ldx >= (int64_t(1) << 23) || ldw >= (int64_t(1) << 23)) return GPTQ_ERR_UNSUPPORTED;
+  return hip_status(launch_dense_gemm(static_cast<const uint16_t*>(X), ldx, tokens, n,
+                                      static_cast<const uint16_t*>(W), ldw, m, Y, ldy,
+                                      ydt == GPTQ_BF16 ? 1 : 0, stream));
+}
+
 gptq_status gptq_gather_columns(const void* X, gptq_dtype xdt, int64_t tokens, int64_t n,
                                 int64_t ldx, const int32_t* perm, void* Xp, int64_t ldxp,
                                 hipStream_t stream) {

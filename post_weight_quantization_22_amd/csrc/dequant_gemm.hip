@@ -664,6 +664,255 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense bf16 product Y = X W^T (X [tokens, n], W [m, n], both bf16 with n
+// contiguous) on the same tiles as the DMA product above, without the
+// dequantization: 256 tokens x 128 rows per workgroup, 4 waves of 128 x 64,
+// X and W tiles both arriving by LDS DMA in the swizzled 128-byte rows, three
+// stages each, issued two chunks ahead, one explicit vmcnt and one barrier per
+// chunk.  For the calibration forward of a quantized layer over many tokens
+// the weights are dequantized once (gptq_dequantize) and multiplied here, so
+// no tile re-dequantizes them.
+struct DenseArgs {
+  const uint16_t* X;
+  int64_t ldx, tokens, n;
+  const uint16_t* W;
+  int64_t ldw, m;
+  void* Y;
+  int64_t ldy;
+  int ybf16;
+  int64_t nrb, ntiles, nchunks;
+};
+
+constexpr int DD_STAGES = 3;
+constexpr int DD_TM = 256;
+
+struct DenseLayout {
+  static constexpr int X_BYTES = DD_TM * ROWB;  // 32 KB
+  static constexpr int W_BYTES = DN * ROWB;     // 16 KB
+  static constexpr int X_OFF = 0;
+  static constexpr int W_OFF = DD_STAGES * X_BYTES;
+  static constexpr int TOTAL = W_OFF + DD_STAGES * W_BYTES;
+  static constexpr int WM = DD_TM / 2, WN = DN / 2;
+  static constexpr int X_PER_WAVE = X_BYTES / 1024 / 4;  // 8
+  static constexpr int W_PER_WAVE = W_BYTES / 1024 / 4;  // 4
+  static constexpr int ISSUE = X_PER_WAVE + W_PER_WAVE;  // DMAs per wave and chunk
+};
+
+__global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
+  using Lay = DenseLayout;
+  static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
+  constexpr int DWM = Lay::WM, DWN = Lay::WN;
+  constexpr int XPW = Lay::X_PER_WAVE, WPW = Lay::W_PER_WAVE;
+  __shared__ __align__(16) uint8_t smem[Lay::TOTAL];
+
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, idx = b / kXcds;
+  const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return;
+  const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int64_t rb = L % a.nrb;
+  const int64_t tb = L / a.nrb;
+  const int64_t tok0 = tb * DD_TM, row0 = rb * DN;
+  const int c_end = (int)a.nchunks;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int n32 = (int)a.n;
+  const int tmax = (int)(a.tokens - 1 - tok0);
+  const int rmax = (int)(a.m - 1 - row0);
+
+  // DMA sources: instruction j of wave wv fills rows 8 (wv PER + j) .. + 8;
+  // lane l lands on row + l / 8, physical segment l % 8, so it loads the
+  // logical segment (l % 8) ^ swz(row); rows past the end re-read the last one
+  uint32_t xoff[XPW], woff[WPW];
+  int xseg[XPW], wseg[WPW];
+#pragma unroll
+  for (int j = 0; j < XPW; ++j) {
+    const int row = 8 * (wv * XPW + j) + (lane >> 3);
+    xseg[j] = (lane & 7) ^ swz(row);
+    xoff[j] = (uint32_t)(2 * ((int64_t)min(row, tmax) * a.ldx + 8 * xseg[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < WPW; ++j) {
+    const int row = 8 * (wv * WPW + j) + (lane >> 3);
+    wseg[j] = (lane & 7) ^ swz(row);
+    woff[j] = (uint32_t)(2 * ((int64_t)min(row, rmax) * a.ldw + 8 * wseg[j]));
+  }
+  const char* xbase = reinterpret_cast<const char*>(a.X + tok0 * a.ldx);
+  const char* wbase = reinterpret_cast<const char*>(a.W + row0 * a.ldw);
+  const uint32_t lds0 = lds_addr(smem);
+
+  auto issue = [&](int c) {
+    const int k0 = c * BK;
+    const int st = c % DD_STAGES;
+    const uint32_t xdst = lds0 + Lay::X_OFF + st * Lay::X_BYTES + wv * XPW * 1024;
+    const uint32_t wdst = lds0 + Lay::W_OFF + st * Lay::W_BYTES + wv * WPW * 1024;
+    const char* xs = xbase + 2 * (int64_t)k0;
+    const char* ws = wbase + 2 * (int64_t)k0;
+    if (k0 + BK <= n32) {
+#pragma unroll
+      for (int j = 0; j < XPW; ++j) lds_dma16(xs, xoff[j], xdst + 1024 * j);
+#pragma unroll
+      for (int j = 0; j < WPW; ++j) lds_dma16(ws, woff[j], wdst + 1024 * j);
+    } else {  // last chunk: segments past n re-read the last valid one
+#pragma unroll
+      for (int j = 0; j < XPW; ++j) {
+        const int clamp = 2 * (min(8 * xseg[j], n32 - 8 - k0) - 8 * xseg[j]);
+        lds_dma16(xs, xoff[j] + (uint32_t)clamp, xdst + 1024 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < WPW; ++j) {
+        const int clamp = 2 * (min(8 * wseg[j], n32 - 8 - k0) - 8 * wseg[j]);
+        lds_dma16(ws, woff[j] + (uint32_t)clamp, wdst + 1024 * j);
+      }
+    }
+  };
+
+  f32x16 acc[DWM / 32][DWN / 32];
+#pragma unroll
+  for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  struct Ops {
+    bf16x8 a[DWM / 32], b[DWN / 32];
+  };
+  auto read_ops = [&](const uint8_t* xt, const uint8_t* wt, int kk, Ops& o) {
+    const int sg = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < DWM / 32; ++i)
+      o.a[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(DWM * wm + 32 * i + (lane & 31), sg));
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j)
+      o.b[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(DWN * wn + 32 * j + (lane & 31), sg));
+  };
+  auto compute = [&](int c) {
+    const int st = c % DD_STAGES;
+    const uint8_t* xt = smem + Lay::X_OFF + st * Lay::X_BYTES;
+    const uint8_t* wt = smem + Lay::W_OFF + st * Lay::W_BYTES;
+    Ops o[2];
+    read_ops(xt, wt, 0, o[0]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) read_ops(xt, wt, kk + 1, o[(kk + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < DWN / 32; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[kk & 1].a[i], o[kk & 1].b[j],
+                                                              acc[i][j], 0, 0, 0);
+    }
+  };
+  // columns past n of the last chunk are set to 0 in X's tile, so whatever
+  // the weights there, the products are 0
+  auto zero_x_tail = [&](int c) {
+    uint8_t* xt = smem + Lay::X_OFF + (c % DD_STAGES) * Lay::X_BYTES;
+    const int k0 = c * BK;
+    for (int i = tid; i < DD_TM * 8; i += 256) {
+      const int row = i >> 3, sg = i & 7;
+      if (k0 + 8 * sg >= n32) *reinterpret_cast<uint4*>(xt + seg_off(row, sg)) = make_uint4(0, 0, 0, 0);
+    }
+  };
+  constexpr int VM = 0x0070 | (Lay::ISSUE & 15) | ((Lay::ISSUE >> 4) << 14);  // vmcnt(ISSUE), lgkmcnt(0)
+
+  if (c_end > 0) {
+    issue(0);
+    if (1 < c_end) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(VM);  // chunk 0 landed, chunk 1 may be in flight
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    }
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < c_end; ++c) {
+      if (c + 2 < c_end) issue(c + 2);  // into the stage chunk c - 1 used
+      compute(c);
+      if (c + 2 < c_end) {
+        __builtin_amdgcn_s_waitcnt(VM);  // chunk c + 1 landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+      }
+      __syncthreads();
+    }
+    if (c_end * BK > n32) {
+      zero_x_tail(c);
+      __syncthreads();
+    }
+    compute(c);
+  }
+
+  const int64_t tw = tok0 + DWM * wm + 4 * (lane >> 5);
+  const int64_t rw = row0 + DWN * wn + (lane & 31);
+  const bool fulltile = tok0 + DWM * (wm + 1) <= a.tokens && row0 + DWN * (wn + 1) <= a.m;
+  float* outf = reinterpret_cast<float*>(a.Y);
+  __bf16* outh = reinterpret_cast<__bf16*>(a.Y);
+#pragma unroll
+  for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < DWN / 32; ++j) {
+      const int64_t base = (tw + 32 * i) * a.ldy + rw + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int dt = 8 * (q >> 2) + (q & 3);
+        if (!fulltile && (tw + 32 * i + dt >= a.tokens || rw + 32 * j >= a.m)) continue;
+        const int64_t o = base + (int64_t)dt * a.ldy;
+        if (a.ybf16) {
+          outh[o] = (__bf16)acc[i][j][q];
+        } else {
+          outf[o] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+// W[r, p] = bf16(fma(q[r, p], s, -(z s))) from codes packed in processing order:
+// the weights the products above form, written once (one thread per 8
+// positions, one 16-byte store; n a multiple of 8).
+template <int BITS>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t* __restrict__ P,
+                                                         int64_t ldp, int64_t m, int64_t n,
+                                                         const float* __restrict__ scales,
+                                                         const float* __restrict__ zeros,
+                                                         int64_t G, int64_t ngroups,
+                                                         uint16_t* __restrict__ W, int64_t ldw) {
+  const int64_t segs = n / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= m * segs) return;
+  const int64_t r = i / segs, p0 = 8 * (i - r * segs);
+  // the 32-code run holding positions p0 .. p0 + 7 (BITS words; the last run of
+  // a row may end past n, its words past the row's are not read)
+  const int64_t run = p0 >> 5;
+  const int s8 = (int)((p0 >> 3) & 3);
+  const int64_t nwr = (n * BITS + 31) / 32;
+  uint32_t w[BITS];
+#pragma unroll
+  for (int q = 0; q < BITS; ++q) {
+    const int64_t wi = run * BITS + q;
+    w[q] = wi < nwr ? P[r * ldp + wi] : 0u;
+  }
+  float f[8];
+  decode8<BITS>(w, s8, f);
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t p = p0 + 2 * e + h;
+      const int64_t g = G > 0 ? p / G : 0;
+      const float sc = scales[r * ngroups + g];
+      v[h] = fmaf(f[2 * e + h], sc, -(zeros[r * ngroups + g] * sc));
+    }
+    o[e] = bf16x2_bits(v[0], v[1]);
+  }
+  *reinterpret_cast<uint4*>(W + r * ldw + p0) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
 // Decode batches of at most 16 tokens, n a multiple of 128, every 32-position
 // run in one group: one workgroup per 16 weight rows over the whole K range, so
 // no second kernel adds split partial sums and no partials go through HBM.
@@ -1277,6 +1526,43 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
   const int64_t total = d.tokens * ceil_div(d.m, 4);
   hipLaunchKernelGGL(dequant_reduce_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
                      stream, a.part, s.ks, d.tokens, d.m, d.Y, d.ldy, a.ybf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_gemm(const uint16_t* X, int64_t ldx, int64_t tokens, int64_t n,
+                             const uint16_t* W, int64_t ldw, int64_t m, void* Y, int64_t ldy,
+                             int ybf16, hipStream_t stream) {
+  DenseArgs a;
+  a.X = X; a.ldx = ldx; a.tokens = tokens; a.n = n;
+  a.W = W; a.ldw = ldw; a.m = m;
+  a.Y = Y; a.ldy = ldy; a.ybf16 = ybf16;
+  a.nrb = ceil_div(m, DN);
+  a.ntiles = ceil_div(tokens, DD_TM) * a.nrb;
+  a.nchunks = ceil_div(n, BK);
+  const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
+  hipLaunchKernelGGL(dense_gemm_dma_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint32_t* P, int64_t ldp, int bits, int64_t m, int64_t n,
+                             const float* scales, const float* zeros, int64_t group_size,
+                             uint16_t* W, int64_t ldw, hipStream_t stream) {
+  const int64_t G = group_size > 0 ? group_size : 0;
+  const int64_t ngroups = G > 0 ? ceil_div(n, G) : 1;
+  const dim3 grid((unsigned)ceil_div(m * (n / 8), 256));
+#define GPTQ_DQ(B)                                                                            \
+  hipLaunchKernelGGL(dequantize_kernel<B>, grid, dim3(256), 0, stream, P, ldp, m, n, scales, \
+                     zeros, G, ngroups, W, ldw)
+  switch (bits) {
+    case 2: GPTQ_DQ(2); break;
+    case 3: GPTQ_DQ(3); break;
+    case 4: GPTQ_DQ(4); break;
+    case 5: GPTQ_DQ(5); break;
+    case 6: GPTQ_DQ(6); break;
+    case 7: GPTQ_DQ(7); break;
+    default: GPTQ_DQ(8); break;
+  }
+#undef GPTQ_DQ
   return hipGetLastError();
 }
 

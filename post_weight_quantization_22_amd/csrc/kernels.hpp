@@ -82,6 +82,15 @@ struct DequantArgs {
   void* ws;
 };
 size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm);
+// Y[tokens, m] = X W^T, X [tokens, n] and W [m, n] bf16 (n % 8 == 0, strides
+// multiples of 8, 16-byte aligned, strides < 2^23); Y fp32 or bf16 (ybf16)
+hipError_t launch_dense_gemm(const uint16_t* X, int64_t ldx, int64_t tokens, int64_t n,
+                             const uint16_t* W, int64_t ldw, int64_t m, void* Y, int64_t ldy,
+                             int ybf16, hipStream_t stream);
+// W[m, n] bf16 = the product's weights from processing-order packed codes (n % 8 == 0)
+hipError_t launch_dequantize(const uint32_t* P, int64_t ldp, int bits, int64_t m, int64_t n,
+                             const float* scales, const float* zeros, int64_t group_size,
+                             uint16_t* W, int64_t ldw, hipStream_t stream);
 // Xp[t, p] = X[t, perm[p]] (p < n), 0 for n <= p < ldxp (bf16)
 void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t tokens,
                    int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream);

@@ -12,10 +12,14 @@ Hessian.  The block is a Llama-style MLP with a residual:
     x' = bf16(x + y)                 gptq_residual_add
 
 Every step runs in libgptq_mi355x.so (Hessian, prepare, quantize, processing-
-order packing, the dequantized-weight products, the elementwise steps); this
-module allocates the caller-owned buffers and issues the calls on one stream.
-Activations stay resident in HBM (x and h of the current block); the products
-run over token chunks so their fp32 outputs stay small.
+order packing, the products, the elementwise steps); this module allocates the
+caller-owned buffers and issues the calls on one stream.  Activations stay
+resident in HBM (x and h of the current block); the products run over token
+chunks so their fp32 outputs stay small.  The products multiply by the
+quantized weights either as a dense bf16 matrix dequantized once per layer
+(gptq_dequantize + gptq_gemm_bf16, the default: the calibration set is large,
+so no tile should dequantize again) or straight from the packed codes
+(gptq_dequant_gemm); both form the same weights, bf16(fma(q, s, -(z s))).
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ class QuantizedLayer:
     buf: pipeline.LayerBuffers  # codes, scales, zeros, g_idx (original order), U, perm
     packed: torch.Tensor        # processing-order packing, the product's input
     perm: Optional[torch.Tensor]  # None when the processing order is the identity
+    wq: Optional[torch.Tensor] = None  # dense bf16 weights, processing order (dense products)
 
 
 @dataclasses.dataclass
@@ -52,23 +57,29 @@ class _Products:
         self.out = {}
         self.xp = {}
 
-    def get(self, tokens: int, m: int, n: int, has_perm: bool, slot: str):
+    def get(self, tokens: int, m: int, n: int, has_perm: bool, slot: str, need_ws: bool = True):
         key = (tokens, m, n, has_perm)
-        if key not in self.ws:
+        if need_ws and key not in self.ws:
             nb = _lib.gptq_dequant_gemm_workspace_size(tokens, m, n, has_perm)
             self.ws[key] = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
         okey = (tokens, m, slot)
         if okey not in self.out:
             self.out[okey] = torch.empty((tokens, m), dtype=torch.float32, device=self.device)
-        return self.ws[key], self.out[okey]
+        return self.ws.get(key), self.out[okey]
 
 
-def _packed(buf: pipeline.LayerBuffers, desc_act: bool, stream) -> QuantizedLayer:
+def _packed(buf: pipeline.LayerBuffers, desc_act: bool, dense: bool, stream) -> QuantizedLayer:
     nw = -(-(buf.n * buf.cfg.bits) // 32)
     packed = torch.empty((buf.m, nw), dtype=torch.int32, device=buf.codes.device)
     perm = buf.perm if desc_act else None
     _lib.gptq_pack_ordered(buf.codes, buf.cfg.bits, perm, packed, stream=stream)
-    return QuantizedLayer(buf, packed, perm)
+    wq = None
+    if dense:
+        ldw = -(-buf.n // 8) * 8
+        wq = torch.empty((buf.m, ldw), dtype=torch.bfloat16, device=packed.device)[:, :buf.n]
+        _lib.gptq_dequantize(packed, buf.cfg.bits, buf.cfg.group_size, buf.scales, buf.zeros,
+                             buf.n, wq, stream=stream)
+    return QuantizedLayer(buf, packed, perm, wq)
 
 
 def _gathered(prod: _Products, X: torch.Tensor, perm: Optional[torch.Tensor], slot: str,
@@ -90,16 +101,19 @@ def _gathered(prod: _Products, X: torch.Tensor, perm: Optional[torch.Tensor], sl
 def _product(prod: _Products, Xp: torch.Tensor, L: QuantizedLayer, slot: str,
              stream) -> torch.Tensor:
     """Y = X W_q^T from the activations already in L's processing order."""
-    ws, Y = prod.get(Xp.shape[0], L.buf.m, L.buf.n, False, slot)
-    _lib.gptq_dequant_gemm(Xp, L.packed, L.buf.cfg.bits, L.buf.cfg.group_size, L.buf.scales,
-                           L.buf.zeros, Y, perm=None, ws=ws, stream=stream)
+    ws, Y = prod.get(Xp.shape[0], L.buf.m, L.buf.n, False, slot, need_ws=L.wq is None)
+    if L.wq is not None:
+        _lib.gptq_gemm_bf16(Xp, L.wq, Y, stream=stream)
+    else:
+        _lib.gptq_dequant_gemm(Xp, L.packed, L.buf.cfg.bits, L.buf.cfg.group_size, L.buf.scales,
+                               L.buf.zeros, Y, perm=None, ws=ws, stream=stream)
     return Y
 
 
 def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch.Tensor,
                                                              torch.Tensor]],
                    cfg: _lib.GPTQConfig, chunk_tokens: int = 16384, keep: bool = False,
-                   stream=None, marks: Optional[list] = None
+                   stream=None, marks: Optional[list] = None, dense: bool = True
                    ) -> Tuple[List[QuantizedBlock], torch.Tensor]:
     """Quantize every block of the stack in order; returns the blocks and the
     quantized network's output activations (bf16 [tokens, d]).
@@ -109,7 +123,8 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
     ``stream`` (default: the current stream); the data-error words of a block's
     three layers are checked (a synchronization) at the end of the block.  ``marks``: if a list,
     (phase, event) pairs are appended, each event recorded on ``stream`` at the
-    end of the phase (timing only)."""
+    end of the phase (timing only).  ``dense``: multiply by the dequantized bf16
+    weights (gptq_gemm_bf16) instead of the packed codes (gptq_dequant_gemm)."""
     if stream is None:
         stream = torch.cuda.current_stream()
     dev = x0.device
@@ -138,7 +153,7 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
         bu.S, bu.U, bu.perm, bu.dead = bg.S, bg.U, bg.perm, bg.dead  # shared Hessian
         pipeline.quantize(bg, Wg, stream)
         pipeline.quantize(bu, Wu, stream)
-        gate, up = _packed(bg, desc, stream), _packed(bu, desc, stream)
+        gate, up = _packed(bg, desc, dense, stream), _packed(bu, desc, dense, stream)
         mark("quantize")
         # h = silu(x Wg_q^T) * (x Wu_q^T), chunk by chunk
         h = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
@@ -157,7 +172,7 @@ def quantize_stack(x0: torch.Tensor, weights: Sequence[Tuple[torch.Tensor, torch
         pipeline.prepare(bd, T, stream)
         mark("prepare")
         pipeline.quantize(bd, Wd, stream)
-        down = _packed(bd, desc, stream)
+        down = _packed(bd, desc, dense, stream)
         mark("quantize")
         # x' = x + h Wd_q^T
         x_next = torch.empty_like(x)

@@ -246,3 +246,26 @@ def test_every_binding_declares_its_signature(lib):
         fn = getattr(so, name)
         assert fn.argtypes is not None, name
         assert fn.restype is not None, name
+
+
+def test_dense_and_dequantize_argument_validation(lib):
+    so = lib.load()
+    bf, f32 = lib.GPTQ_BF16, lib.GPTQ_F32
+    # gptq_gemm_bf16(X, tokens, n, ldx, W, m, ldw, Y, ydt, ldy, stream)
+    assert so.gptq_gemm_bf16(FAKE, 0, 64, 64, FAKE, 8, 64, FAKE, f32, 8, None) == lib.GPTQ_OK
+    assert so.gptq_gemm_bf16(FAKE, 4, 60, 64, FAKE, 8, 64, FAKE, f32, 8, None) == \
+        lib.GPTQ_ERR_UNSUPPORTED  # n % 8
+    assert so.gptq_gemm_bf16(FAKE, 4, 64, 68, FAKE, 8, 64, FAKE, f32, 8, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldx % 8
+    assert so.gptq_gemm_bf16(FAKE, 4, 64, 64, FAKE, 8, 64, FAKE, f32, 4, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldy < m
+    assert so.gptq_gemm_bf16(FAKE, 4, 64, 64, FAKE, 8, 64, FAKE, 7, 8, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # dtype
+    # gptq_dequantize(packed, ldp, bits, G, scales, zeros, m, n, W, ldw, stream)
+    assert so.gptq_dequantize(FAKE, 8, 4, 64, FAKE, FAKE, 0, 64, FAKE, 64, None) == lib.GPTQ_OK
+    assert so.gptq_dequantize(FAKE, 8, 4, 64, FAKE, FAKE, 4, 60, FAKE, 64, None) == \
+        lib.GPTQ_ERR_UNSUPPORTED
+    assert so.gptq_dequantize(FAKE, 7, 4, 64, FAKE, FAKE, 4, 64, FAKE, 64, None) == \
+        lib.GPTQ_ERR_INVALID_ARG  # ldp < n bits / 32
+    assert so.gptq_dequantize(FAKE, 8, 9, 64, FAKE, FAKE, 4, 64, FAKE, 64, None) == \
+        lib.GPTQ_ERR_INVALID_ARG

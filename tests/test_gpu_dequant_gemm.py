@@ -289,3 +289,51 @@ def test_gather_columns_exact(tokens, n, ldx, ldxp):
     got = host(Xp.view(torch.int16)).astype(np.int64)
     assert np.array_equal(got[:, :n], Xb[:, perm])
     assert np.all(got[:, n:] == 0)
+
+
+@pytest.mark.parametrize("m,n,bits,G", [(130, 512, 4, 128), (64, 392, 3, 8), (33, 2048, 2, -1),
+                                        (7, 96, 8, 32), (256, 4096, 5, 64)])
+def test_dequantize_matches_the_product_weights(m, n, bits, G):
+    """gptq_dequantize writes bf16(fma(q, s, -(z s))) bit for bit (the weights
+    every product kernel forms), from the oracle-packed codes."""
+    q = need_gpu()
+    rng = np.random.default_rng(m * 13 + n + bits)
+    codes = rng.integers(0, 2 ** bits, size=(m, n)).astype(np.float64)
+    ng = -(-n // G) if G > 0 else 1
+    scales = rng.uniform(1e-3, 2e-2, size=(m, ng)).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(m, ng)).astype(np.float32)
+    packed = oracle.pack_ref(codes, bits).astype(np.uint32)
+    say("dequantize", m, n, bits, G)
+    W = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    q.gptq_dequantize(dev(packed.view(np.int32), torch.int32), bits, G, dev(scales, torch.float32),
+                      dev(zeros, torch.float32), n, W)
+    torch.cuda.synchronize()
+    got = host(W.view(torch.int16)).astype(np.uint16)
+    ref = _weights_model(codes, scales, zeros, G).astype(np.float32)
+    ref_bits = (ref.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(got, ref_bits)
+
+
+@pytest.mark.parametrize("tokens,m,n,ydt", [(600, 300, 520, "f32"), (256, 128, 64, "f32"),
+                                            (1000, 513, 4096, "bf16"), (17, 40, 136, "f32")])
+def test_gemm_bf16_against_fp64(tokens, m, n, ydt):
+    """gptq_gemm_bf16 against the fp64 product of the same bf16 operands, within
+    the fp32 summation bound 8 sqrt(n) 2^-24 sum |x w| (plus half a bf16 unit
+    of the result for bf16 output); ragged token, row and chunk tails."""
+    q = need_gpu()
+    rng = np.random.default_rng(tokens + m + n)
+    X = synth.round_to_bf16(rng.standard_normal((tokens, n)).astype(np.float32)).astype(np.float64)
+    W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.05).astype(np.float32)).astype(np.float64)
+    say("gemm_bf16", tokens, m, n, ydt)
+    Y = torch.empty((tokens, m), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32,
+                    device="cuda")
+    q.gptq_gemm_bf16(dev(X.astype(np.float32), torch.bfloat16),
+                     dev(W.astype(np.float32), torch.bfloat16), Y)
+    torch.cuda.synchronize()
+    ref = X @ W.T
+    bound = 8 * np.sqrt(n) * EPS32 * (np.abs(X) @ np.abs(W).T) + 1e-30
+    if ydt == "bf16":
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+    diff = np.abs(host(Y.float()).astype(np.float64) - ref)
+    print(f"  max diff / bound {float((diff / bound).max()):.3f}", flush=True)
+    assert np.all(diff <= bound)

@@ -94,8 +94,12 @@ def _check_layer(name, buf, W, q, damp):
                           host(buf.g_idx).astype(np.int64))
 
 
+@pytest.mark.parametrize("dense", [True, False])
 @pytest.mark.parametrize("desc_act", [True, False])
-def test_mlp_stack_layer_by_layer(desc_act):
+def test_mlp_stack_layer_by_layer(desc_act, dense):
+    """dense: products from the once-dequantized bf16 weights (gptq_gemm_bf16),
+    else straight from the packed codes (gptq_dequant_gemm); both form the same
+    weights, so the same checks hold."""
     q_ = need_gpu()
     from post_weight_quantization_22_amd import stack
 
@@ -108,10 +112,11 @@ def test_mlp_stack_layer_by_layer(desc_act):
     Ws = [tuple(synth.weight(wl, f"{nm}_{k}").astype(np.float64) for nm in ("gate", "up", "down"))
           for k in range(blocks)]
     cfg = q_.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
-    say("mlp stack", d, f, blocks, T, desc_act)
+    say("mlp stack", d, f, blocks, T, desc_act, dense)
     res, x_out = stack.quantize_stack(dev(x0.astype(np.float32), torch.bfloat16),
                                       [tuple(dev(w.astype(np.float32), torch.bfloat16) for w in Wk)
-                                       for Wk in Ws], cfg, chunk_tokens=768, keep=True)
+                                       for Wk in Ws], cfg, chunk_tokens=768, keep=True,
+                                      dense=dense)
     torch.cuda.synchronize()
     for k, b in enumerate(res):
         x = host(b.x_in.float()).astype(np.float64)
