@@ -116,6 +116,10 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t n, int64_t lds, const void
  * 1-based processing position of the first non-positive pivot (raise
  * perc_damp, as "GPTQ deep dive" section 3.3 advises), -1 = a non-finite
  * value in S.  Returns GPTQ_ERR_EMPTY synchronously when tokens == 0.
+ * The factorization also runs on two library-owned streams of the device
+ * (created on first use, default priority), ordered against `stream` by
+ * events: the call behaves as work on `stream`.  Calls from several host
+ * threads on one device are serialized while they enqueue.
  * ---------------------------------------------------------------------- */
 gptq_status gptq_prepare_workspace_size(int64_t n, size_t* bytes);
 gptq_status gptq_prepare(const float* S, int64_t n, int64_t lds, int64_t tokens,

@@ -96,6 +96,7 @@ struct SideStream {
   hipEvent_t trailing_done;   // s -> main: trailing update k is applied
   hipEvent_t last_node;       // main -> inv: the last node is done
   hipEvent_t inv_done;        // inv -> main: the last group of X is written
+  std::mutex run;             // one call at a time enqueues on a device's side streams
 };
 
 hipError_t side_stream(SideStream*& out) {
@@ -1205,6 +1206,9 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   SideStream* side = nullptr;
   hipError_t e = side_stream(side);
   if (e != hipSuccess) return e;
+  // the side streams and their events are shared by every call on the device:
+  // two host threads enqueueing at once would interleave the event records
+  std::lock_guard<std::mutex> lock(side->run);
   e = factor_invert(w, n, info, stream, side);
   if (e != hipSuccess) return e;
   {
