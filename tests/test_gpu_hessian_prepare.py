@@ -178,3 +178,46 @@ def test_prepare_empty_calibration_is_refused():
     with pytest.raises(q.GPTQError) as ei:
         q.gptq_prepare(S, 0, 0.01, False, U, info=info)
     assert ei.value.status == 4
+
+
+def test_prepare_from_concurrent_host_threads():
+    """Two host threads run prepare on their own streams at once (the library's
+    side streams are shared by the device): each U equals the one a single
+    call gives, bit for bit (the factorization has a fixed order)."""
+    import threading
+
+    q = need_gpu()
+    n, tokens = 640, 3000
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((tokens, n)).astype(np.float32)
+    S = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    q.gptq_hessian_accumulate(S, dev(X, torch.bfloat16))
+    say("prepare concurrent", n)
+
+    def run(stream, out):
+        U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        perm = torch.empty(n, dtype=torch.int32, device="cuda")
+        info = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = torch.empty(q.gptq_prepare_workspace_size(n), dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                q.gptq_prepare(S, tokens, 0.01, True, U, perm=perm, info=info, ws=ws,
+                               stream=stream)
+        stream.synchronize()
+        assert int(host(info)[0]) == 0
+        out.append((host(U), host(perm)))
+
+    ref = []
+    run(torch.cuda.current_stream(), ref)
+    outs = [[], []]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=run, args=(streams[i], outs[i])) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert len(o) == 1
+        assert np.array_equal(o[0][0], ref[0][0]) and np.array_equal(o[0][1], ref[0][1])
