@@ -1254,9 +1254,10 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
 // The same gather with every row staged in LDS: a workgroup walks a run of
 // rows; a row arrives with 16-byte loads (coalesced; the next row's loads are
 // in flight while this one is permuted) and leaves permuted, 8 positions per
-// thread and 16-byte store, the permuted reads served by the LDS.  n and ldx
-// multiples of 8, X 16-byte aligned, n <= NCAP.  Out-of-range perm entries
-// read as zero.
+// thread and 16-byte store, the permuted reads served by the LDS.  The
+// permutation is read once per workgroup into registers (16-bit entries, two
+// to a word), not once per row.  n and ldx multiples of 8, X 16-byte aligned,
+// n <= NCAP.  Out-of-range perm entries read as zero.
 template <int NCAP>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X,
                                                           int64_t ldx,
@@ -1265,12 +1266,32 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
                                                           int64_t rows_per_wg,
                                                           uint16_t* __restrict__ Xp) {
   constexpr int CH = NCAP / 8 / 256;  // 16-byte chunks of a row per thread
+  constexpr int SEG = NCAP / 8 / 256; // output segments per thread (ldxp <= NCAP)
+  static_assert(NCAP <= 65535 + 1, "16-bit permutation entries");
   __shared__ __align__(16) uint16_t buf[2][NCAP];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * rows_per_wg;
   const int64_t t1 = min(tokens, t0 + rows_per_wg);
   if (t0 >= t1) return;
   const int nch = (int)(n / 8);
+  const int nseg = (int)(ldxp / 8);
+  // this thread's segments tid + 256 i: source positions, 0xFFFF = zero
+  uint32_t pk[SEG][4];
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int sg = tid + 256 * i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t p = 8 * (int64_t)sg + 2 * q + e;
+        const int32_t src = (sg < nseg && p < n) ? perm[p] : -1;
+        h[e] = (src >= 0 && src < n) ? (uint32_t)src : 0xFFFFu;
+      }
+      pk[i][q] = h[0] | (h[1] << 16);
+    }
+  }
   uint4 v[CH];
   auto fetch = [&](int64_t t) {
     const uint4* src = reinterpret_cast<const uint4*>(X + t * ldx);
@@ -1290,21 +1311,21 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     }
     if (t + 1 < t1) fetch(t + 1);
     __syncthreads();
-    for (int64_t sg = tid; sg < ldxp / 8; sg += 256) {
-      const int64_t p0 = 8 * sg;
-      uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t h[2];
+    for (int i = 0; i < SEG; ++i) {
+      const int sg = tid + 256 * i;
+      if (sg < nseg) {
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int64_t p = p0 + 2 * q + e;
-          const int32_t src = p < n ? perm[p] : -1;
-          h[e] = (src >= 0 && src < n) ? (uint32_t)b[src] : 0u;
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t s0 = pk[i][q] & 0xFFFFu, s1 = pk[i][q] >> 16;
+          const uint32_t lo = s0 != 0xFFFFu ? (uint32_t)b[s0] : 0u;
+          const uint32_t hi = s1 != 0xFFFFu ? (uint32_t)b[s1] : 0u;
+          w[q] = lo | (hi << 16);
         }
-        w[q] = h[0] | (h[1] << 16);
+        *reinterpret_cast<uint4*>(Xp + t * ldxp + 8 * (int64_t)sg) =
+            make_uint4(w[0], w[1], w[2], w[3]);
       }
-      *reinterpret_cast<uint4*>(Xp + t * ldxp + p0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     // buffer (t - t0) & 1 is written again two rows on, after the next barrier
   }
@@ -1388,13 +1409,14 @@ hipError_t launch_bits(const DqArgs& a, int bm, hipStream_t stream) {
 void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t tokens,
                    int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream) {
   if (tokens <= 0) return;
+  // (ldxp bounds the output segments a thread holds positions for)
   const bool rows = n % 8 == 0 && ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
-                    n <= 32768;
+                    ldxp <= 32768;
   if (rows) {
     // about 1024 workgroups, at least 4 rows each
     const int64_t rpw = hmax((int64_t)4, ceil_div(tokens, (int64_t)1024));
     const dim3 grid((unsigned)ceil_div(tokens, rpw));
-    if (n <= 16384)
+    if (ldxp <= 16384)
       hipLaunchKernelGGL(gather_rows_kernel<16384>, grid, dim3(256), 0, stream, X, ldx, perm,
                          tokens, n, ldxp, rpw, Xp);
     else
