@@ -665,11 +665,14 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 
 // ---------------------------------------------------------------------------
 // Dense bf16 product Y = X W^T (X [tokens, n], W [m, n], both bf16 with n
-// contiguous) on the same tiles as the DMA product above, without the
-// dequantization: 256 tokens x 128 rows per workgroup, 4 waves of 128 x 64,
-// X and W tiles both arriving by LDS DMA in the swizzled 128-byte rows, three
-// stages each, issued two chunks ahead, one explicit vmcnt and one barrier per
-// chunk.  For the calibration forward of a quantized layer over many tokens
+// contiguous) on the tile machinery of the DMA product above, without the
+// dequantization: X and W tiles both arrive by LDS DMA in the swizzled
+// 128-byte rows, one explicit vmcnt and one barrier per chunk.  The tile is
+// 256 tokens x TN rows, 4 waves of 128 x TN/2.  Used with TN = 256 and two
+// stages (the next chunk in flight while one multiplies): 128 x 128 wave tiles
+// read half the LDS bytes per MFMA that 128 x 64 ones do, and the LDS, not the
+// matrix cores, is what bounds the 128-row tile (measured: the layer-
+// sequential forward 195 -> 175 ms).  For the calibration forward of a quantized layer over many tokens
 // the weights are dequantized once (gptq_dequantize) and multiplied here, so
 // no tile re-dequantizes them.
 struct DenseArgs {
@@ -683,23 +686,25 @@ struct DenseArgs {
   int64_t nrb, ntiles, nchunks;
 };
 
-constexpr int DD_STAGES = 3;
 constexpr int DD_TM = 256;
 
+template <int TN, int NST>
 struct DenseLayout {
   static constexpr int X_BYTES = DD_TM * ROWB;  // 32 KB
-  static constexpr int W_BYTES = DN * ROWB;     // 16 KB
+  static constexpr int W_BYTES = TN * ROWB;
   static constexpr int X_OFF = 0;
-  static constexpr int W_OFF = DD_STAGES * X_BYTES;
-  static constexpr int TOTAL = W_OFF + DD_STAGES * W_BYTES;
-  static constexpr int WM = DD_TM / 2, WN = DN / 2;
+  static constexpr int W_OFF = NST * X_BYTES;
+  static constexpr int TOTAL = W_OFF + NST * W_BYTES;
+  static constexpr int WM = DD_TM / 2, WN = TN / 2;
   static constexpr int X_PER_WAVE = X_BYTES / 1024 / 4;  // 8
-  static constexpr int W_PER_WAVE = W_BYTES / 1024 / 4;  // 4
+  static constexpr int W_PER_WAVE = W_BYTES / 1024 / 4;
   static constexpr int ISSUE = X_PER_WAVE + W_PER_WAVE;  // DMAs per wave and chunk
 };
 
+template <int TN, int NST>
 __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
-  using Lay = DenseLayout;
+  using Lay = DenseLayout<TN, NST>;
+  constexpr int DD_STAGES = NST;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
   constexpr int DWM = Lay::WM, DWN = Lay::WN;
   constexpr int XPW = Lay::X_PER_WAVE, WPW = Lay::W_PER_WAVE;
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
   const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int64_t rb = L % a.nrb;
   const int64_t tb = L / a.nrb;
-  const int64_t tok0 = tb * DD_TM, row0 = rb * DN;
+  const int64_t tok0 = tb * DD_TM, row0 = rb * TN;
   const int c_end = (int)a.nchunks;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -724,24 +729,17 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
 
   // DMA sources: instruction j of wave wv fills rows 8 (wv PER + j) .. + 8;
   // lane l lands on row + l / 8, physical segment l % 8, so it loads the
-  // logical segment (l % 8) ^ swz(row); rows past the end re-read the last one
-  uint32_t xoff[XPW], woff[WPW];
-  int xseg[XPW], wseg[WPW];
-#pragma unroll
-  for (int j = 0; j < XPW; ++j) {
-    const int row = 8 * (wv * XPW + j) + (lane >> 3);
-    xseg[j] = (lane & 7) ^ swz(row);
-    xoff[j] = (uint32_t)(2 * ((int64_t)min(row, tmax) * a.ldx + 8 * xseg[j]));
-  }
-#pragma unroll
-  for (int j = 0; j < WPW; ++j) {
-    const int row = 8 * (wv * WPW + j) + (lane >> 3);
-    wseg[j] = (lane & 7) ^ swz(row);
-    woff[j] = (uint32_t)(2 * ((int64_t)min(row, rmax) * a.ldw + 8 * wseg[j]));
-  }
+  // logical segment (l % 8) ^ swz(row); rows past the end re-read the last one.
+  // The offsets are formed at each issue (registers go to the accumulators).
   const char* xbase = reinterpret_cast<const char*>(a.X + tok0 * a.ldx);
   const char* wbase = reinterpret_cast<const char*>(a.W + row0 * a.ldw);
   const uint32_t lds0 = lds_addr(smem);
+  auto src_off = [&](int row, int rmaxv, int64_t ld, int k0, int& seg) -> uint32_t {
+    seg = (lane & 7) ^ swz(row);
+    int s8 = 8 * seg;
+    if (k0 + BK > n32) s8 = min(s8, n32 - 8 - k0);  // last chunk: past n re-read the last valid segment
+    return (uint32_t)(2 * ((int64_t)min(row, rmaxv) * ld + s8));
+  };
 
   auto issue = [&](int c) {
     const int k0 = c * BK;
@@ -750,23 +748,15 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
     const uint32_t wdst = lds0 + Lay::W_OFF + st * Lay::W_BYTES + wv * WPW * 1024;
     const char* xs = xbase + 2 * (int64_t)k0;
     const char* ws = wbase + 2 * (int64_t)k0;
-    if (k0 + BK <= n32) {
+    int seg;
 #pragma unroll
-      for (int j = 0; j < XPW; ++j) lds_dma16(xs, xoff[j], xdst + 1024 * j);
+    for (int j = 0; j < XPW; ++j)
+      lds_dma16(xs, src_off(8 * (wv * XPW + j) + (lane >> 3), tmax, a.ldx, k0, seg),
+                xdst + 1024 * j);
 #pragma unroll
-      for (int j = 0; j < WPW; ++j) lds_dma16(ws, woff[j], wdst + 1024 * j);
-    } else {  // last chunk: segments past n re-read the last valid one
-#pragma unroll
-      for (int j = 0; j < XPW; ++j) {
-        const int clamp = 2 * (min(8 * xseg[j], n32 - 8 - k0) - 8 * xseg[j]);
-        lds_dma16(xs, xoff[j] + (uint32_t)clamp, xdst + 1024 * j);
-      }
-#pragma unroll
-      for (int j = 0; j < WPW; ++j) {
-        const int clamp = 2 * (min(8 * wseg[j], n32 - 8 - k0) - 8 * wseg[j]);
-        lds_dma16(ws, woff[j] + (uint32_t)clamp, wdst + 1024 * j);
-      }
-    }
+    for (int j = 0; j < WPW; ++j)
+      lds_dma16(ws, src_off(8 * (wv * WPW + j) + (lane >> 3), rmax, a.ldw, k0, seg),
+                wdst + 1024 * j);
   };
 
   f32x16 acc[DWM / 32][DWN / 32];
@@ -793,17 +783,31 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
     const int st = c % DD_STAGES;
     const uint8_t* xt = smem + Lay::X_OFF + st * Lay::X_BYTES;
     const uint8_t* wt = smem + Lay::W_OFF + st * Lay::W_BYTES;
-    Ops o[2];
-    read_ops(xt, wt, 0, o[0]);
+    if constexpr (TN <= 128) {  // operands of step kk + 1 read while step kk multiplies
+      Ops o[2];
+      read_ops(xt, wt, 0, o[0]);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) read_ops(xt, wt, kk + 1, o[(kk + 1) & 1]);
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) read_ops(xt, wt, kk + 1, o[(kk + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < DWM / 32; ++i)
+        for (int i = 0; i < DWM / 32; ++i)
 #pragma unroll
-        for (int j = 0; j < DWN / 32; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[kk & 1].a[i], o[kk & 1].b[j],
-                                                              acc[i][j], 0, 0, 0);
+          for (int j = 0; j < DWN / 32; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[kk & 1].a[i], o[kk & 1].b[j],
+                                                                acc[i][j], 0, 0, 0);
+      }
+    } else {  // 16 MFMAs a step cover the next step's reads; one operand set fits
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        Ops o;
+        read_ops(xt, wt, kk, o);
+#pragma unroll
+        for (int i = 0; i < DWM / 32; ++i)
+#pragma unroll
+          for (int j = 0; j < DWN / 32; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0,
+                                                                0);
+      }
     }
   };
   // columns past n of the last chunk are set to 0 in X's tile, so whatever
@@ -818,7 +822,7 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
   };
   constexpr int VM = 0x0070 | (Lay::ISSUE & 15) | ((Lay::ISSUE >> 4) << 14);  // vmcnt(ISSUE), lgkmcnt(0)
 
-  if (c_end > 0) {
+  if (c_end > 0 && NST == 3) {
     issue(0);
     if (1 < c_end) {
       issue(1);
@@ -836,6 +840,22 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
       } else {
         __builtin_amdgcn_s_waitcnt(0x0070);
       }
+      __syncthreads();
+    }
+    if (c_end * BK > n32) {
+      zero_x_tail(c);
+      __syncthreads();
+    }
+    compute(c);
+  } else if (c_end > 0) {  // two stages: the next chunk in flight while this one multiplies
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < c_end; ++c) {
+      issue(c + 1);  // into the stage chunk c - 1 used
+      compute(c);
+      __builtin_amdgcn_s_waitcnt(0x0070);
       __syncthreads();
     }
     if (c_end * BK > n32) {
@@ -1558,11 +1578,13 @@ hipError_t launch_dense_gemm(const uint16_t* X, int64_t ldx, int64_t tokens, int
   a.X = X; a.ldx = ldx; a.tokens = tokens; a.n = n;
   a.W = W; a.ldw = ldw; a.m = m;
   a.Y = Y; a.ldy = ldy; a.ybf16 = ybf16;
-  a.nrb = ceil_div(m, DN);
+  constexpr int TN = 256, NST = 2;
+  a.nrb = ceil_div(m, TN);
   a.ntiles = ceil_div(tokens, DD_TM) * a.nrb;
   a.nchunks = ceil_div(n, BK);
   const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
-  hipLaunchKernelGGL(dense_gemm_dma_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dense_gemm_dma_kernel<TN, NST>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
