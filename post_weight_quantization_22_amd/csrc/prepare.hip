@@ -379,17 +379,25 @@ __device__ __forceinline__ void leaf32(const double* P, double* Q, int s, double
 // sum_{kmin <= k < kmax} P(i0 + i, k) Q(k, j0 + j), P(i, k) = P[i * PS + k],
 // Q(k, j) = QT ? Qm[j * PS + k] : Qm[k * PS + j].  Element q of lane l is
 // (i0 + l/16 + 4q, j0 + l%16).
+// (At most 8 k-steps: every operand read is issued before the first MFMA.)
 template <bool QT>
 __device__ __forceinline__ f64x4 tile16(const double* P, const double* Qm, int i0, int j0,
                                         int kmin, int kmax) {
   const int lane = threadIdx.x & 63;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kmin; k0 < kmax; k0 += 4) {
-    const int kl = k0 + (lane >> 4);
-    const double av = P[(i0 + (lane & 15)) * PS + kl];
-    const double bv = QT ? Qm[(j0 + (lane & 15)) * PS + kl] : Qm[kl * PS + j0 + (lane & 15)];
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+  double av[8], bv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int k0 = kmin + 4 * t;
+    if (k0 < kmax) {  // uniform in the wave
+      const int kl = k0 + (lane >> 4);
+      av[t] = P[(i0 + (lane & 15)) * PS + kl];
+      bv[t] = QT ? Qm[(j0 + (lane & 15)) * PS + kl] : Qm[kl * PS + j0 + (lane & 15)];
+    }
   }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if (kmin + 4 * t < kmax) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[t], bv[t], acc, 0, 0, 0);
   return acc;
 }
 
