@@ -314,9 +314,10 @@ def test_dequantize_matches_the_product_weights(m, n, bits, G):
     assert np.array_equal(got, ref_bits)
 
 
-@pytest.mark.parametrize("tokens,m,n,ydt", [(600, 300, 520, "f32"), (256, 128, 64, "f32"),
-                                            (1000, 513, 4096, "bf16"), (17, 40, 136, "f32")])
-def test_gemm_bf16_against_fp64(tokens, m, n, ydt):
+@pytest.mark.parametrize("tokens,m,n,ydt,pad", [(600, 300, 520, "f32", 0), (256, 128, 64, "f32", 0),
+                                                (1000, 513, 4096, "bf16", 0),
+                                                (17, 40, 136, "f32", 0), (300, 260, 264, "f32", 24)])
+def test_gemm_bf16_against_fp64(tokens, m, n, ydt, pad):
     """gptq_gemm_bf16 against the fp64 product of the same bf16 operands, within
     the fp32 summation bound 8 sqrt(n) 2^-24 sum |x w| (plus half a bf16 unit
     of the result for bf16 output); ragged token, row and chunk tails."""
@@ -324,11 +325,15 @@ def test_gemm_bf16_against_fp64(tokens, m, n, ydt):
     rng = np.random.default_rng(tokens + m + n)
     X = synth.round_to_bf16(rng.standard_normal((tokens, n)).astype(np.float32)).astype(np.float64)
     W = synth.round_to_bf16((rng.standard_normal((m, n)) * 0.05).astype(np.float32)).astype(np.float64)
-    say("gemm_bf16", tokens, m, n, ydt)
+    say("gemm_bf16", tokens, m, n, ydt, pad)
     Y = torch.empty((tokens, m), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32,
                     device="cuda")
-    q.gptq_gemm_bf16(dev(X.astype(np.float32), torch.bfloat16),
-                     dev(W.astype(np.float32), torch.bfloat16), Y)
+    # pad > 0: operands as views into wider rows (row strides n + pad)
+    Xw = np.zeros((tokens, n + pad), dtype=np.float32)
+    Xw[:, :n] = X
+    Ww = np.zeros((m, n + pad), dtype=np.float32)
+    Ww[:, :n] = W
+    q.gptq_gemm_bf16(dev(Xw, torch.bfloat16)[:, :n], dev(Ww, torch.bfloat16)[:, :n], Y)
     torch.cuda.synchronize()
     ref = X @ W.T
     bound = 8 * np.sqrt(n) * EPS32 * (np.abs(X) @ np.abs(W).T) + 1e-30
