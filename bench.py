@@ -48,8 +48,8 @@ def parse():
                     help="skip the AWQ-lite / awq_clip measurement")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the layer-sequential MLP-stack measurement")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
-    ap.add_argument("--cpu-sample-chunks", type=int, default=32)
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=64)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one Hessian accumulate of the workload and one 2 GiB device copy, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
