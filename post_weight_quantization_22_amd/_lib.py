@@ -183,12 +183,63 @@ def _ld(t) -> int:
     return t.stride(0)
 
 
-def _workspace(nbytes: int, device):
+def _workspace(nbytes: int, device, stream=None):
+    """A per-call workspace allocated on the stream the call is enqueued on, so
+    that torch's caching allocator does not hand the memory to other work
+    before the library's kernels on that stream are done with it."""
     import torch
 
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+_INT32_LIKE = ("int32", "uint32")
+
+
+def _buf(t, name: str, shape, dtypes, device, optional: bool = True, min_rows=None):
+    """Check an output or index buffer before its pointer goes to the library:
+    the kernels write ``shape`` elements with the row stride the ABI states, so
+    a smaller, strided, mistyped or foreign-device tensor would be written out
+    of bounds.  ``shape`` entries of None are not checked; ``dtypes`` are torch
+    dtype names."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if len(shape) == 1:
+        if t.numel() < shape[0]:
+            raise ValueError(f"{name}: {t.numel()} elements, need {shape[0]}")
+        return
+    if t.dim() != len(shape) or any(s is not None and d != s for d, s in zip(t.shape, shape)):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _mat(t, name: str, rows: int, cols: int, dtypes, device):
+    """A 2-D operand read or written with an explicit row stride: unit column
+    stride, at least ``rows`` x ``cols``, on ``device``."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != 2 or t.stride(1) != 1 or t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name}: expected a 2-D tensor of at least {rows} x {cols} with unit "
+                         f"column stride, got shape {tuple(t.shape)} strides {t.stride()}")
+
+
+def _ngroups(n: int, group_size: int) -> int:
+    return 1 if group_size <= 0 else -(-n // group_size)
 
 
 # ---------------------------------------------------------------------------
@@ -213,9 +264,11 @@ def gptq_hessian_accumulate(S, X, ws=None, stream=None) -> None:
     """S[n, n] (fp32, lower triangle) += X^T X for X[tokens, n] (bf16 or fp32)."""
     n = S.shape[0]
     tokens = X.shape[0]
+    _mat(S, "S", n, n, ("float32",), S.device)
+    _mat(X, "X", tokens, n, ("bfloat16", "float32"), S.device)
     need = gptq_hessian_workspace_size(n, tokens) if _dtype_code(X) == GPTQ_BF16 else 0
     if ws is None:
-        ws = _workspace(need, S.device)
+        ws = _workspace(need, S.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().gptq_hessian_accumulate(_ptr(S), n, _ld(S), _ptr(X), _dtype_code(X), tokens,
                                           _ld(X), _ptr(ws), nbytes, _stream(stream)),
@@ -231,8 +284,15 @@ def gptq_prepare_workspace_size(n: int) -> int:
 def gptq_prepare(S, tokens: int, perc_damp: float, desc_act: bool, U, perm=None, dead=None,
                  lambda_out=None, info=None, ws=None, stream=None) -> None:
     n = S.shape[0]
+    d = S.device
+    _mat(S, "S", n, n, ("float32",), d)
+    _mat(U, "U", n, n, ("float32",), d)
+    _buf(perm, "perm", (n,), _INT32_LIKE, d)
+    _buf(dead, "dead", (n,), ("uint8", "bool"), d)
+    _buf(lambda_out, "lambda_out", (1,), ("float32",), d)
+    _buf(info, "info", (1,), ("int32",), d, optional=False)
     if ws is None:
-        ws = _workspace(gptq_prepare_workspace_size(n), S.device)
+        ws = _workspace(gptq_prepare_workspace_size(n), S.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().gptq_prepare(_ptr(S), n, _ld(S), int(tokens), float(perc_damp), int(desc_act),
                                _ptr(U), _ld(U), _ptr(perm), _ptr(dead), _ptr(lambda_out),
@@ -257,8 +317,20 @@ def gptq_quantize_workspace_size(m: int, n: int, cfg: GPTQConfig) -> int:
 def gptq_quantize_layer(W, U, cfg: GPTQConfig, codes, scales, zeros, perm=None, dead=None,
                         g_idx=None, row_err=None, info=None, ws=None, stream=None) -> None:
     m, n = W.shape
+    d = W.device
+    ng = _ngroups(n, cfg.group_size)
+    _mat(W, "W", m, n, ("bfloat16", "float32"), d)
+    _mat(U, "U", n, n, ("float32",), d)
+    _buf(codes, "codes", (m, n), ("uint8",), d, optional=False)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _buf(perm, "perm", (n,), _INT32_LIKE, d)
+    _buf(dead, "dead", (n,), ("uint8", "bool"), d)
+    _buf(g_idx, "g_idx", (n,), _INT32_LIKE, d)
+    _buf(row_err, "row_err", (m,), ("float32",), d)
+    _buf(info, "info", (1,), ("int32",), d)
     if ws is None:
-        ws = _workspace(gptq_quantize_workspace_size(m, n, cfg), W.device)
+        ws = _workspace(gptq_quantize_workspace_size(m, n, cfg), W.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(U), _ld(U),
                                       _ptr(perm), _ptr(dead), ctypes.byref(cfg), _ptr(codes),
@@ -269,6 +341,9 @@ def gptq_quantize_layer(W, U, cfg: GPTQConfig, codes, scales, zeros, perm=None, 
 
 def gptq_pack(codes, bits: int, packed, stream=None) -> None:
     m, n = codes.shape
+    _buf(codes, "codes", (m, n), ("uint8",), codes.device, optional=False)
+    _buf(packed, "packed", (m, -(-(n * int(bits)) // 32)), _INT32_LIKE, codes.device,
+         optional=False)
     _check(load().gptq_pack(_ptr(codes), m, n, int(bits), _ptr(packed), _stream(stream)),
            "gptq_pack")
 
@@ -276,6 +351,10 @@ def gptq_pack(codes, bits: int, packed, stream=None) -> None:
 def gptq_pack_ordered(codes, bits: int, perm, packed, stream=None) -> None:
     """packed[r] = codes[r, perm[0]], codes[r, perm[1]], ... in the gptq_pack layout."""
     m, n = codes.shape
+    _buf(codes, "codes", (m, n), ("uint8",), codes.device, optional=False)
+    _buf(perm, "perm", (n,), _INT32_LIKE, codes.device)
+    _buf(packed, "packed", (m, -(-(n * int(bits)) // 32)), _INT32_LIKE, codes.device,
+         optional=False)
     _check(load().gptq_pack_ordered(_ptr(codes), m, n, int(bits), _ptr(perm), _ptr(packed),
                                     _stream(stream)),
            "gptq_pack_ordered")
@@ -294,9 +373,16 @@ def gptq_dequant_gemm(X, packed, bits: int, group_size: int, scales, zeros, Y, p
     """Y[tokens, m] = X[tokens, n] W_q^T with W_q from processing-order packed codes."""
     tokens, n = X.shape
     m = packed.shape[0]
+    d = X.device
+    ng = _ngroups(n, group_size)
+    _mat(packed, "packed", m, -(-(n * int(bits)) // 32), _INT32_LIKE, d)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _buf(perm, "perm", (n,), _INT32_LIKE, d)
+    _mat(Y, "Y", tokens, m, ("float32", "bfloat16"), d)
     if ws is None:
         ws = _workspace(gptq_dequant_gemm_workspace_size(tokens, m, n, perm is not None),
-                        X.device)
+                        X.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().gptq_dequant_gemm(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(packed),
                                     _ld(packed), int(bits), int(group_size), _ptr(scales),
@@ -309,6 +395,12 @@ def gptq_dequantize(packed, bits: int, group_size: int, scales, zeros, n: int, W
                     stream=None) -> None:
     """W[m, n] (bf16) = the product's weights from processing-order packed codes."""
     m = packed.shape[0]
+    d = packed.device
+    ng = _ngroups(int(n), group_size)
+    _mat(packed, "packed", m, -(-(int(n) * int(bits)) // 32), _INT32_LIKE, d)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _mat(W, "W", m, int(n), ("bfloat16",), d)
     _check(load().gptq_dequantize(_ptr(packed), _ld(packed), int(bits), int(group_size),
                                   _ptr(scales), _ptr(zeros), m, int(n), _ptr(W), _ld(W),
                                   _stream(stream)),
@@ -319,6 +411,8 @@ def gptq_gemm_bf16(X, W, Y, stream=None) -> None:
     """Y[tokens, m] = X[tokens, n] W[m, n]^T (bf16 operands, Y fp32 or bf16)."""
     tokens, n = X.shape
     m = W.shape[0]
+    _mat(W, "W", m, n, ("bfloat16",), X.device)
+    _mat(Y, "Y", tokens, m, ("float32", "bfloat16"), X.device)
     _check(load().gptq_gemm_bf16(_ptr(X), tokens, n, _ld(X), _ptr(W), m, _ld(W), _ptr(Y),
                                  _dtype_code(Y), _ld(Y), _stream(stream)),
            "gptq_gemm_bf16")
@@ -327,6 +421,8 @@ def gptq_gemm_bf16(X, W, Y, stream=None) -> None:
 def gptq_gather_columns(X, perm, Xp, stream=None) -> None:
     """Xp[t, p] = X[t, perm[p]] (bf16; Xp's columns past n are zeroed)."""
     tokens, n = X.shape
+    _buf(perm, "perm", (n,), _INT32_LIKE, X.device, optional=False)
+    _mat(Xp, "Xp", tokens, n, ("bfloat16",), X.device)
     _check(load().gptq_gather_columns(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(perm),
                                       _ptr(Xp), _ld(Xp), _stream(stream)),
            "gptq_gather_columns")
@@ -335,6 +431,8 @@ def gptq_gather_columns(X, perm, Xp, stream=None) -> None:
 def gptq_swiglu(gate, up, h, stream=None) -> None:
     """h[tokens, n] (bf16) = silu(gate) * up for fp32 gate, up."""
     tokens, n = gate.shape
+    _mat(up, "up", tokens, n, ("float32",), gate.device)
+    _mat(h, "h", tokens, n, ("bfloat16",), gate.device)
     _check(load().gptq_swiglu(_ptr(gate), _ld(gate), _ptr(up), _ld(up), tokens, n, _ptr(h),
                               _ld(h), _stream(stream)),
            "gptq_swiglu")
@@ -343,6 +441,8 @@ def gptq_swiglu(gate, up, h, stream=None) -> None:
 def gptq_residual_add(x, y, out, stream=None) -> None:
     """out[tokens, n] (bf16) = x (bf16) + y (fp32); out may be x."""
     tokens, n = x.shape
+    _mat(y, "y", tokens, n, ("float32",), x.device)
+    _mat(out, "out", tokens, n, ("bfloat16",), x.device)
     _check(load().gptq_residual_add(_ptr(x), _ld(x), _ptr(y), _ld(y), tokens, n, _ptr(out),
                                     _ld(out), _stream(stream)),
            "gptq_residual_add")
@@ -364,8 +464,9 @@ def awq_lite_workspace_size(m: int, n: int) -> int:
 def awq_activation_absum(X, absum, ws=None, stream=None) -> None:
     """absum[n] += sum over tokens of |X[t, c]|."""
     tokens, n = X.shape
+    _buf(absum, "absum", (n,), ("float32",), X.device, optional=False)
     if ws is None:
-        ws = _workspace(awq_absum_workspace_size(n, tokens), X.device)
+        ws = _workspace(awq_absum_workspace_size(n, tokens), X.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().awq_activation_absum(_ptr(X), _dtype_code(X), tokens, n, _ld(X), _ptr(absum),
                                        _ptr(ws), nbytes, _stream(stream)),
@@ -376,8 +477,14 @@ def awq_lite(W, S, absum, tokens: int, bits: int, group_size: int, s_out, alpha_
              sym: bool = False, ws=None, stream=None) -> None:
     """alpha search; s_out[n], alpha_out[1], losses[n_alpha] fp32 device tensors."""
     m, n = W.shape
+    d = W.device
+    _mat(S, "S", n, n, ("float32",), d)
+    _buf(absum, "absum", (n,), ("float32",), d, optional=False)
+    _buf(s_out, "s_out", (n,), ("float32",), d, optional=False)
+    _buf(alpha_out, "alpha_out", (1,), ("float32",), d, optional=False)
+    _buf(losses, "losses", (1,), ("float32",), d, optional=False)
     if ws is None:
-        ws = _workspace(awq_lite_workspace_size(m, n), W.device)
+        ws = _workspace(awq_lite_workspace_size(m, n), W.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().awq_lite(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(S), _ld(S), _ptr(absum),
                            int(tokens), int(bits), int(group_size), int(sym), losses.numel(),
@@ -389,6 +496,14 @@ def awq_lite(W, S, absum, tokens: int, bits: int, group_size: int, s_out, alpha_
 def awq_clip_quantize(W, S, s, bits: int, group_size: int, codes, scales, zeros, clip_idx=None,
                       sym: bool = False, n_steps: int = 11, stream=None) -> None:
     m, n = W.shape
+    d = W.device
+    ng = _ngroups(n, group_size)
+    _mat(S, "S", n, n, ("float32",), d)
+    _buf(s, "s", (n,), ("float32",), d)
+    _buf(codes, "codes", (m, n), ("uint8",), d, optional=False)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _buf(clip_idx, "clip_idx", (m, ng), ("uint8",), d)
     _check(load().awq_clip_quantize(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(S), _ld(S),
                                     _ptr(s), int(bits), int(group_size), int(sym), int(n_steps),
                                     _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(clip_idx),
@@ -399,6 +514,11 @@ def awq_clip_quantize(W, S, s, bits: int, group_size: int, codes, scales, zeros,
 def rtn_minmax(W, bits: int, group_size: int, codes, scales, zeros, sym: bool = False,
                stream=None) -> None:
     m, n = W.shape
+    d = W.device
+    ng = _ngroups(n, group_size)
+    _buf(codes, "codes", (m, n), ("uint8",), d, optional=False)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
     _check(load().rtn_minmax(_ptr(W), _dtype_code(W), m, n, _ld(W), int(bits), int(group_size),
                              int(sym), _ptr(codes), _ptr(scales), _ptr(zeros), _stream(stream)),
            "rtn_minmax")

@@ -62,6 +62,7 @@ struct PrepWs {
   double* diag;            // [n]
   double* lam;             // [1]
   int32_t* perm;           // [n]
+  int32_t* rank;           // [n] descending-order rank of each column (desc_act)
 };
 
 constexpr int GRP = 4;  // blocks per group of the inverse
@@ -83,6 +84,8 @@ PrepWs carve(void* ws, int64_t n) {
   w.lam = reinterpret_cast<double*>(p);
   p += 256;
   w.perm = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)n * sizeof(int32_t), 256);
+  w.rank = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -132,6 +135,7 @@ __global__ __launch_bounds__(1024) void diag_damp_kernel(const float* __restrict
                                                          uint8_t* __restrict__ dead,
                                                          double* __restrict__ lam,
                                                          float* __restrict__ lambda_out,
+                                                         int32_t* __restrict__ rank,
                                                          int32_t* __restrict__ info) {
   __shared__ double part[1024];
   __shared__ int bad;
@@ -145,6 +149,7 @@ __global__ __launch_bounds__(1024) void diag_damp_kernel(const float* __restrict
     const bool is_dead = d == 0.0;
     if (is_dead) d = 1.0;
     if (dead) dead[i] = is_dead ? 1 : 0;
+    if (rank) rank[i] = 0;
     diag[i] = d;
     sum += d;
   }
@@ -162,26 +167,41 @@ __global__ __launch_bounds__(1024) void diag_damp_kernel(const float* __restrict
   }
 }
 
-// Stable descending order of diag: rank_i = #{j: d_j > d_i or (d_j == d_i and j < i)}.
-__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ diag, int64_t n,
-                                                   int32_t* __restrict__ perm) {
-  __shared__ double key[1024];
+// Stable descending order of diag.  The key of column i is its diagonal
+// entry, with a NaN taken as -inf, so that the keys are totally ordered and
+// rank_i = #{j : key_j > key_i or (key_j == key_i and j < i)} is a
+// permutation of 0 .. n-1 whatever the values (a non-finite diagonal is
+// reported through info by diag_damp_kernel; the order stays well formed).
+// The count is split over a 2-D grid: blockIdx.x takes 256 columns i,
+// blockIdx.y a chunk of RANK_CHUNK columns j staged in LDS (every lane reads
+// the same key: an LDS broadcast); each partial count is added to rank[i]
+// (zeroed by diag_damp_kernel).  rank_scatter_kernel then writes perm.
+constexpr int RANK_CHUNK = 2048;
+
+__device__ __forceinline__ double order_key(double d) { return d != d ? -INFINITY : d; }
+
+__global__ __launch_bounds__(256) void rank_count_kernel(const double* __restrict__ diag,
+                                                         int64_t n, int32_t* __restrict__ rank) {
+  __shared__ double key[RANK_CHUNK];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const double di = i < n ? diag[i] : 0.0;
-  int64_t rank = 0;
-  for (int64_t base = 0; base < n; base += 1024) {
-    __syncthreads();
-    for (int t = threadIdx.x; t < 1024; t += blockDim.x)
-      key[t] = base + t < n ? diag[base + t] : 0.0;
-    __syncthreads();
-    const int cnt = (int)min<int64_t>(1024, n - base);
-    for (int t = 0; t < cnt; ++t) {
-      const double dj = key[t];
-      const int64_t j = base + t;
-      rank += (dj > di) || (dj == di && j < i);
-    }
-  }
-  if (i < n) perm[rank] = (int32_t)i;
+  const int64_t base = (int64_t)blockIdx.y * RANK_CHUNK;
+  const int cnt = (int)min<int64_t>(RANK_CHUNK, n - base);
+  for (int t = threadIdx.x; t < cnt; t += blockDim.x) key[t] = order_key(diag[base + t]);
+  __syncthreads();
+  if (i >= n) return;
+  const double ki = order_key(diag[i]);
+  int r = 0;
+  // j < i inside the chunk: ties count; j >= i: only strictly greater keys
+  const int split = (int)max<int64_t>(0, min<int64_t>(cnt, i - base));
+  for (int t = 0; t < split; ++t) r += key[t] >= ki;
+  for (int t = split; t < cnt; ++t) r += key[t] > ki;
+  if (r) atomicAdd(rank + i, r);
+}
+
+__global__ __launch_bounds__(256) void rank_scatter_kernel(const int32_t* __restrict__ rank,
+                                                           int64_t n, int32_t* __restrict__ perm) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) perm[rank[i]] = (int32_t)i;
 }
 
 __global__ void iota_kernel(int32_t* __restrict__ perm, int64_t n) {
@@ -209,7 +229,10 @@ __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ 
     const int64_t a = a0 + tx, b = b0 + r;
     double v = 0.0;
     if (a < n && b <= a) {
-      const int64_t p = perm[n - 1 - a], q = perm[n - 1 - b];
+      // perm comes from this library's own order kernels, but an index
+      // outside 0 .. n-1 must never address S
+      const int64_t p = min<int64_t>(max<int64_t>(perm[n - 1 - a], 0), n - 1);
+      const int64_t q = min<int64_t>(max<int64_t>(perm[n - 1 - b], 0), n - 1);
       if (a == b) {
         v = diag[p] + l;
       } else {
@@ -1189,7 +1212,7 @@ size_t prepare_ws_bytes(int64_t n) {
   b += align_up((size_t)m_elems(n) * sizeof(double), 256);
   b += align_up((size_t)n * sizeof(double), 256);
   b += 256;
-  b += align_up((size_t)n * sizeof(int32_t), 256);
+  b += 2 * align_up((size_t)n * sizeof(int32_t), 256);  // perm, rank
   return b;
 }
 
@@ -1199,10 +1222,13 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   PrepWs w = carve(ws, n);
   int32_t* pm = perm ? perm : w.perm;
   hipLaunchKernelGGL(diag_damp_kernel, dim3(1), dim3(1024), 0, stream, S, n, lds, perc_damp,
-                     w.diag, dead, w.lam, lambda_out, info);
+                     w.diag, dead, w.lam, lambda_out, desc_act ? w.rank : nullptr, info);
   if (desc_act) {
-    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, w.diag,
-                       n, pm);
+    hipLaunchKernelGGL(rank_count_kernel,
+                       dim3((unsigned)ceil_div(n, 256), (unsigned)ceil_div(n, RANK_CHUNK)),
+                       dim3(256), 0, stream, w.diag, n, w.rank);
+    hipLaunchKernelGGL(rank_scatter_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
+                       w.rank, n, pm);
   } else {
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, pm, n);
   }

@@ -170,6 +170,52 @@ def test_prepare_reports_non_finite():
     assert int(host(info)[0]) == -1
 
 
+def test_prepare_nan_on_diagonal_with_desc_act():
+    """A NaN on S's diagonal with desc_act: info reports the non-finite input
+    and the processing order is still a permutation (a NaN key orders as the
+    smallest value, ties by index), so nothing downstream reads S or W through
+    an unwritten perm slot."""
+    q = need_gpu()
+    n = 300
+    S = _S_case(n, 512, seed=4)
+    S[7, 7] = np.nan
+    S[123, 123] = np.nan
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    perm = torch.full((n,), -5, dtype=torch.int32, device="cuda")
+    say("prepare NaN diagonal desc_act", n)
+    q.gptq_prepare(dev(S.astype(np.float32), torch.float32), 512, 0.01, True, U, perm=perm,
+                   info=info)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == -1
+    p = host(perm).astype(np.int64)
+    assert np.array_equal(np.sort(p), np.arange(n))
+    d = np.diag(S).astype(np.float64)
+    key = np.where(np.isnan(d), -np.inf, d)
+    assert np.array_equal(p, np.argsort(-key, kind="stable"))
+    assert p[-1] == 123 and p[-2] == 7  # the two NaN columns last, lower index first
+
+
+def test_prepare_desc_act_order_with_exact_ties_over_several_chunks():
+    """The order kernel counts over column chunks of 2048: at n = 4500 (three
+    chunks) with a diagonal of exactly tied values the device order equals the
+    stable descending argsort bit for bit."""
+    q = need_gpu()
+    n = 4500
+    rng = np.random.default_rng(9)
+    dvals = rng.integers(1, 6, size=n).astype(np.float32)
+    S = torch.from_numpy(np.diag(dvals)).cuda()
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    say("prepare tied desc_act order", n)
+    q.gptq_prepare(S, 1000, 0.01, True, U, perm=perm, info=info)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0
+    assert np.array_equal(host(perm).astype(np.int64), np.argsort(-dvals.astype(np.float64),
+                                                                   kind="stable"))
+
+
 def test_prepare_empty_calibration_is_refused():
     q = need_gpu()
     S = torch.zeros((8, 8), dtype=torch.float32, device="cuda")
