@@ -1,21 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark: GPTQ quantization of one linear layer on one MI355X.
 
-Workload (one step = the whole layer path over one calibration set):
-  Llama-7B-shaped attention projection, W 4096 x 4096 bf16 ~ N(0, 0.02^2),
-  calibration X = 128 sequences x 2048 tokens x 4096 bf16 ~ N(0, 1) with 0.5 %
-  outlier channels x30, 4-bit asymmetric, group 128, block 128, damp 0.01.
-  Inputs are synthetic, seeded, and resident in HBM before timing starts.
+Headline workload (one step = the whole layer path over one calibration set):
+  70B-shaped down projection, W 8192 x 28672 bf16 ~ N(0, 0.01^2), calibration
+  X = 256 sequences x 2048 tokens x 28672 bf16 ~ Laplace(0, 1), 4-bit
+  asymmetric, group 64, block 128, damp 0.01, desc_act on (columns by
+  descending Hessian diagonal).  The largest of the five workloads; the other
+  four (256^2 fp32; Llama-7B attention 4096^2; Llama-7B MLP gate/up 11008 x
+  4096 sharing one Hessian plus down 4096 x 11008; 70B square 8192^2 3-bit)
+  are measured the same way and reported under ``configs``.  Inputs are
+  synthetic, seeded, and resident in HBM before timing starts.
 
-  step = S := 0; S += X^T X (all 262144 tokens); prepare (damp, Cholesky,
+  step = S := 0; S += X^T X (all tokens); prepare (damp, order, Cholesky,
          inverse, upper factor); quantize (blocked column loop + lazy trailing
-         update); pack to 4-bit words; plus the group min-max RTN baseline.
+         update) of every layer sharing the Hessian; pack; plus the group
+         min-max RTN baseline of each layer.
 
 Prints ONE JSON line.  The metric is weights quantized per second
 (m * n / step time).  ``roofline`` reports the dominant kernel (the bf16 MFMA
 Hessian) against the MI355X dense bf16 MFMA peak, timed with HIP events on the
-stream it runs on.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
-of the same workload on the host cores and scales it to the same unit.
+stream it runs on.  ``breakdown`` sums the durations of every kernel of one
+extra step by kernel (from the profiler's activity trace), which separates the
+column loop's block chain from its trailing-update products.  ``cpu_baseline``
+times the fp64 oracle on a bounded sample of the headline workload on the host
+cores and scales it to the same unit.
 """
 from __future__ import annotations
 
@@ -25,41 +33,57 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-WORKLOAD = "llama7b_attn"
+HEADLINE = "llama70b_down"
+EXTRA = ("layer256", "llama7b_attn", "llama7b_mlp", "llama70b_square")
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 FP64_PEAK_TFLOPS = 78.6
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hessian_llama7b_attn.json")
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_22_amd", "csrc", "hessian.hip")
+EXTRA_STEPS = {"layer256": (20, 3), "llama7b_attn": (10, 2), "llama7b_mlp": (5, 1),
+               "llama70b_square": (5, 1)}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_hessian_{workload}.json")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="headline workload (default: the 70B down projection)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel breakdown of one extra step")
     ap.add_argument("--no-awq", action="store_true",
                     help="skip the AWQ-lite / awq_clip measurement")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the layer-sequential MLP-stack measurement")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
-    ap.add_argument("--cpu-sample-chunks", type=int, default=64)
+    ap.add_argument("--no-dequant", action="store_true",
+                    help="skip the dequantized-weight product measurement")
+    ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=2)
+    ap.add_argument("--cpu-prepare-n", type=int, default=8192)
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run one Hessian accumulate of the workload and one 2 GiB device copy, "
-                         "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+                    help="run one Hessian accumulate of the workload, one whole layer step "
+                         "and one 2 GiB device copy, for rocprofv3 --pmc runs, then exit")
     ap.add_argument("--dequant-probe", action="store_true",
                     help="run the quantized layer's product 10 times at 2048 and at 16 tokens "
                          "(4096 x 4096, random 4-bit codes, group 128), for rocprofv3 counter "
                          "runs, then exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn the counter files of two --traffic-probe runs into "
-                         "profiles/traffic_hessian_llama7b_attn.json, then exit")
+                    help="turn the counter files of two --traffic-probe runs of --workload into "
+                         "profiles/traffic_hessian_<workload>.json, then exit")
     return ap.parse_args()
 
 
@@ -68,12 +92,13 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per Hessian launch from committed rocprofv3 counter runs, if current."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != source_hash(HESSIAN_SRC):
@@ -90,8 +115,10 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
 
     Each counter (KiB per dispatch, summed over the L2 channels) is scaled by
     the ratio of the known bytes of the 2 GiB device copy to what the same
-    counter reads for that copy; the launch is the last pair of Hessian
-    dispatches (interior SYRK + split reduction) in each file.
+    counter reads for that copy; the launch is the first dispatch of each
+    Hessian kernel in the file (the probe's lone accumulate).  Every other
+    kernel of the probe's layer step is summed by name as well
+    (``per_kernel``), for the quantize, pack and RTN bandwidths.
     """
     import csv
     from collections import defaultdict
@@ -114,45 +141,359 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
         if not copies:
             raise SystemExit(f"{path}: no copy dispatch")
         copy_kib = val[max(copies)]
-        hess = 0.0
-        for k in HESS_KERNELS:
-            ds = [d for d in val if k in name[d]]
-            if not ds:
-                raise SystemExit(f"{path}: no {k} dispatch")
-            hess += val[max(ds)]
         factor = COPY_BYTES / (copy_kib * 1024.0)
+        hess = 0.0
+        found = False
+        for k in HESS_KERNELS:
+            ds = sorted(d for d in val if k in name[d])
+            if ds:
+                hess += val[ds[0]]
+                found = True
+        if not found:
+            raise SystemExit(f"{path}: no Hessian dispatch")
+        per_kernel = defaultdict(float)
+        for d, v in val.items():
+            if "copyBuffer" in name[d]:
+                continue
+            per_kernel[name[d].split("(")[0]] += v * 1024.0 * factor
         out[counter] = {"hessian_kib": hess, "copy_kib": copy_kib, "scale": factor,
-                        "bytes": hess * 1024.0 * factor}
+                        "bytes": hess * 1024.0 * factor, "per_kernel_bytes": dict(per_kernel)}
     return out
 
 
-def cpu_baseline(wl, rows: int, chunks: int):
-    """Time the fp64 oracle on a bounded sample and scale to weights/s for the full layer."""
+def upload_x(wl, xname, dev):
+    """The calibration stream X [tokens, n] on the device (bf16 or fp32).
+
+    Chunks are drawn on host threads (synth's generators), reduced to their
+    storage bits there (the values are already bf16-exact), and copied in
+    order while later chunks are still being drawn."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    xs = wl.xs[xname]
+    bf16 = xs.dtype == "bf16"
+    X = torch.empty((xs.tokens, xs.n), dtype=torch.bfloat16 if bf16 else torch.float32,
+                    device=dev)
+    outl = synth.outlier_channels(wl, xname)
+
+    def draw(c):
+        a = synth.x_chunk(wl, xname, c, outl)
+        if bf16:
+            a = (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        return a
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(threads) as ex:
+        futs = {}
+        nxt = 0
+        for c in range(xs.chunks):
+            while nxt < xs.chunks and nxt < c + 2 * threads:
+                futs[nxt] = ex.submit(draw, nxt)
+                nxt += 1
+            a = futs.pop(c).result()
+            t = torch.from_numpy(a)
+            if bf16:
+                t = t.view(torch.bfloat16)
+            X[c * xs.chunk_len:(c + 1) * xs.chunk_len].copy_(t)
+    torch.cuda.synchronize()
+    return X
+
+
+def layer_groups(wl):
+    """Layers that share a calibration stream share one Hessian and prepare."""
+    groups = {}
+    for l in wl.layers:
+        groups.setdefault(l.x, []).append(l)
+    return list(groups.items())
+
+
+def stage_roof_ms(m, n, N, q, prep_peak=FP32_PEAK_TFLOPS, with_hessian=True):
+    """A layer's time at roofline: Hessian n(n+1)N flop at the bf16 MFMA peak,
+    prepare 2n^3/3 at ``prep_peak``, trailing update m n (n - 128) at the fp32
+    MFMA peak, quantize + pack (9 + 8/G + 1 + b/8 bytes per weight) at HBM."""
+    G = q.group_size if q.group_size > 0 else n
+    t = 0.0
+    if with_hessian:
+        t += n * (n + 1) * N / (BF16_PEAK_TFLOPS * 1e12)
+        t += 2 * n ** 3 / 3 / (prep_peak * 1e12)
+    t += m * n * max(n - q.block_size, 0) / (FP32_PEAK_TFLOPS * 1e12)
+    t += m * n * (9 + 8 / G + 1 + q.bits / 8) / (HBM_PEAK_GBS * 1e9)
+    return t * 1e3
+
+
+KERNEL_STAGE = (
+    ("hessian", ("syrk_", "reduce_full_partials", "reduce_partials")),
+    ("prepare", ("diag_damp", "rank_", "iota_kernel", "build_a", "node_kernel", "gemm_f64",
+                 "gemm_splitk", "gemm_tall128", "write_u")),
+    ("quantize", ("prep_weights", "block_quant", "update_gemm", "unpermute", "static_params",
+                  "row_params", "invert_perm", "fill_i32", "zero_f32")),
+    ("pack", ("pack_",)),
+    ("rtn", ("rtn_",)),
+)
+
+
+def kernel_breakdown(run_once):
+    """Per-kernel duration sums of one call of ``run_once`` from torch's
+    profiler (its activity trace records every kernel the process dispatches,
+    the library's included).  Returns None when the trace holds no kernels."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        run_once()
+        torch.cuda.synchronize()
+    per = {}
+    for ev in prof.key_averages():
+        dt = getattr(ev, "device_time_total", None)
+        if dt is None:
+            dt = getattr(ev, "cuda_time_total", 0.0)
+        if not dt:
+            continue
+        name = ev.key
+        if name.startswith("void "):
+            name = name[5:]
+        name = name.split("(")[0]
+        rec = per.setdefault(name, [0.0, 0])
+        rec[0] += dt / 1e3
+        rec[1] += ev.count
+    if not per:
+        return None
+    return {k: {"ms": round(v[0], 4), "calls": v[1]} for k, v in
+            sorted(per.items(), key=lambda kv: -kv[1][0])}
+
+
+def stage_of(kernel: str):
+    for st, prefixes in KERNEL_STAGE:
+        if any(kernel.startswith(p) for p in prefixes):
+            return st
+    return None
+
+
+def run_workload(gq, wl, dev, steps, warmup, breakdown=False, keep=False):
+    """Time the whole path of a workload: per calibration stream one Hessian and
+    one prepare, then quantize + pack + RTN of every layer that reads it.
+    Returns (record, resident state of the last stream if ``keep``)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from post_weight_quantization_22_amd import pipeline
+
+    q = wl.quant
+    cfg = gq.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
+    stream = torch.cuda.current_stream()
+    groups_out = []
+    total_ms = 0.0
+    total_weights = 0
+    roof_ms = 0.0
+    roof64_ms = 0.0
+    t_setup = 0.0
+    state = None
+    for xname, layers in layer_groups(wl):
+        xs = wl.xs[xname]
+        n, N = xs.n, xs.tokens
+        t0 = time.time()
+        X = upload_x(wl, xname, dev)
+        Ws = []
+        for l in layers:
+            Wh = synth.weight(wl, l.name)
+            dt = torch.bfloat16 if l.w_dtype == "bf16" else torch.float32
+            if l.w_dtype == "bf16":
+                Ws.append(torch.from_numpy((Wh.view(np.uint32) >> np.uint32(16))
+                                           .astype(np.uint16)).view(dt).to(dev))
+            else:
+                Ws.append(torch.from_numpy(Wh).to(dev))
+            del Wh
+        torch.cuda.synchronize()
+        t_setup += time.time() - t0
+        bufs = [pipeline.allocate(layers[0].m, n, cfg, N, device=dev)]
+        for l in layers[1:]:
+            b = pipeline.allocate(l.m, n, cfg, 0, device=dev)
+            b.S, b.U, b.perm, b.dead = bufs[0].S, bufs[0].U, bufs[0].perm, bufs[0].dead
+            bufs.append(b)
+        rtn = []
+        for l in layers:
+            ng = pipeline.ngroups(n, q.group_size)
+            rtn.append((torch.empty((l.m, n), dtype=torch.uint8, device=dev),
+                        torch.empty((l.m, ng), dtype=torch.float32, device=dev),
+                        torch.empty((l.m, ng), dtype=torch.float32, device=dev)))
+        b0 = bufs[0]
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            b0.S.zero_()
+            gq.gptq_hessian_accumulate(b0.S, X, ws=b0.ws_hess, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            pipeline.prepare(b0, N, stream)
+            if ev:
+                ev[2].record(stream)
+            for b, W in zip(bufs, Ws):
+                pipeline.quantize(b, W, stream)
+            if ev:
+                ev[3].record(stream)
+            for b in bufs:
+                pipeline.pack(b, stream)
+            if ev:
+                ev[4].record(stream)
+            for (c, s_, z), W in zip(rtn, Ws):
+                gq.rtn_minmax(W, q.bits, q.group_size, c, s_, z, stream=stream)
+            if ev:
+                ev[5].record(stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        for b in bufs:
+            pipeline.check_info(b)
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            step(events[k])
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        for b in bufs:
+            pipeline.check_info(b)
+        names = ["hessian", "prepare", "quantize", "pack", "rtn"]
+        stage_ms = {nm: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
+                                       for k in range(steps)])) for i, nm in enumerate(names)}
+        weights = sum(l.m for l in layers) * n
+        hess_flops = n * (n + 1) * N
+        prep_flops = 2 * n ** 3 / 3
+        upd_flops = sum(l.m for l in layers) * n * max(n - q.block_size, 0)
+        g_roof = stage_roof_ms(layers[0].m, n, N, q)
+        g_roof64 = stage_roof_ms(layers[0].m, n, N, q, prep_peak=FP64_PEAK_TFLOPS)
+        for l in layers[1:]:
+            g_roof += stage_roof_ms(l.m, n, N, q, with_hessian=False)
+            g_roof64 += stage_roof_ms(l.m, n, N, q, with_hessian=False)
+        rec = {
+            "layers": [f"{l.name} {l.m}x{l.n}" for l in layers],
+            "tokens": N,
+            "ms_per_step": round(ms, 4),
+            "weights_per_s": round(weights / (ms * 1e-3), 1),
+            "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "hessian_tflops": round(hess_flops / (stage_ms["hessian"] * 1e-3) / 1e12, 2),
+            "hessian_frac_bf16_peak": round(hess_flops / (stage_ms["hessian"] * 1e-3) / 1e12
+                                            / BF16_PEAK_TFLOPS, 4),
+            "prepare_tflops_f64": round(prep_flops / (stage_ms["prepare"] * 1e-3) / 1e12, 3),
+            "quantize_update_tflops_incl_block_loop": round(
+                upd_flops / (stage_ms["quantize"] * 1e-3) / 1e12, 2),
+            "layer_roofline_ms": round(g_roof, 4),
+            "layer_roofline_frac": round(g_roof / ms, 4),
+            "layer_roofline_ms_f64_prepare": round(g_roof64, 4),
+            "layer_roofline_frac_f64_prepare": round(g_roof64 / ms, 4),
+        }
+        if breakdown:
+            try:
+                per = kernel_breakdown(step)
+            except Exception as exc:  # the trace is optional evidence
+                per = None
+                rec["breakdown_error"] = str(exc)[:200]
+            if per:
+                rec["breakdown"] = per
+                upd = sum(v["ms"] for k, v in per.items() if k.startswith("update_gemm"))
+                chain = sum(v["ms"] for k, v in per.items() if k.startswith("block_quant"))
+                rec["quantize_split"] = {
+                    "block_chain_ms": round(chain, 4),
+                    "update_gemm_ms": round(upd, 4),
+                    "update_gemm_tflops": round(upd_flops / (upd * 1e-3) / 1e12, 2)
+                    if upd else None,
+                    "update_gemm_frac_fp32_peak": round(upd_flops / (upd * 1e-3) / 1e12
+                                                        / FP32_PEAK_TFLOPS, 4) if upd else None,
+                    "other_quantize_kernels_ms": round(sum(
+                        v["ms"] for k, v in per.items() if stage_of(k) == "quantize") - upd
+                        - chain, 4),
+                }
+                prep_gemm = sum(v["ms"] for k, v in per.items() if k.startswith("gemm_"))
+                if prep_gemm:
+                    rec["prepare_products_tflops_f64"] = round(
+                        prep_flops / (prep_gemm * 1e-3) / 1e12, 2)
+        groups_out.append(rec)
+        total_ms += ms
+        total_weights += weights
+        roof_ms += g_roof
+        roof64_ms += g_roof64
+        if keep:
+            state = dict(X=X, W=Ws[0], buf=b0, stream=stream, hess_flops=hess_flops, N=N, n=n,
+                         m=layers[0].m, q=q)
+        else:
+            del X, Ws, bufs, rtn, b0
+            torch.cuda.empty_cache()
+    out = {
+        "workload": wl.description,
+        "ms_per_step": round(total_ms, 4),
+        "weights_per_s": round(total_weights / (total_ms * 1e-3), 1),
+        "layer_roofline_ms": round(roof_ms, 4),
+        "layer_roofline_frac": round(roof_ms / total_ms, 4),
+        "layer_roofline_ms_f64_prepare": round(roof64_ms, 4),
+        "layer_roofline_frac_f64_prepare": round(roof64_ms / total_ms, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "input_setup_s": round(t_setup, 1),
+        "streams": groups_out,
+    }
+    return out, state
+
+
+def cpu_baseline(wl, rows: int, chunks: int, prep_n: int):
+    """Time the fp64 oracle on a bounded sample and scale to weights/s for the
+    whole workload: the Hessian over ``chunks`` calibration sequences (cost
+    linear in tokens), prepare at n' = min(n, prep_n) on that sample's leading
+    n' x n' block (cost ~ n^3), and the column loop on ``rows`` rows (rows are
+    independent given U; the loop's work does not depend on U's values, so a
+    unit upper factor stands in where n' < n)."""
     import numpy as np
 
     import oracle
     import synth
 
-    ls = wl.layer()
-    xs = wl.xs[ls.x]
     q = wl.quant
-    # Hessian on `chunks` calibration sequences: cost is linear in tokens
-    Xs = synth.x_all(wl, ls.x, chunks=list(range(chunks)))
-    t0 = time.perf_counter()
-    S = oracle.hessian_S([Xs])
-    t_h = time.perf_counter() - t0
-    t_h_full = t_h * xs.chunks / chunks
-    # prepare at full size (the sample's S stands in for the full one)
-    t0 = time.perf_counter()
-    P = oracle.prepare(S, q.perc_damp, q.desc_act)
-    t_p = time.perf_counter() - t0
-    # column loop on a row sample: rows are independent given U, cost linear in rows
-    W = synth.weight(wl, ls.name, rows=slice(0, rows))
-    t0 = time.perf_counter()
-    oracle.gptq_quantize(W, P.U, q.bits, q.group_size, q.block_size, P.perm, P.dead)
-    t_q = time.perf_counter() - t0
-    t_q_full = t_q * ls.m / rows
-    total = t_h_full + t_p + t_q_full
+    total = 0.0
+    parts = []
+    for xname, layers in layer_groups(wl):
+        xs = wl.xs[xname]
+        n = xs.n
+        c = min(chunks, xs.chunks)
+        Xs = synth.x_all(wl, xname, chunks=list(range(c)))
+        t0 = time.perf_counter()
+        S = oracle.hessian_S([Xs])
+        t_h = time.perf_counter() - t0
+        del Xs
+        t_h_full = t_h * xs.chunks / c
+        npr = min(n, prep_n)
+        t0 = time.perf_counter()
+        P = oracle.prepare(np.ascontiguousarray(S[:npr, :npr]), q.perc_damp, q.desc_act)
+        t_p = time.perf_counter() - t0
+        t_p_full = t_p * (n / npr) ** 3
+        del S
+        if npr == n:
+            U, perm, dead = P.U, P.perm, P.dead
+        else:
+            U, perm, dead = np.eye(n), np.arange(n), None
+        t_q_full = 0.0
+        for l in layers:
+            r = min(rows, l.m)
+            W = synth.weight(wl, l.name, rows=slice(0, r))
+            t0 = time.perf_counter()
+            oracle.gptq_quantize(W, U, q.bits, q.group_size, q.block_size, perm, dead, q.sym)
+            t_q = time.perf_counter() - t0
+            t_q_full += t_q * l.m / r
+        del U
+        total += t_h_full + t_p_full + t_q_full
+        parts.append(f"{xname}: Hessian over {c} of {xs.chunks} sequences ({t_h:.2f} s, scaled "
+                     f"x{xs.chunks / c:g}), prepare at n={npr} ({t_p:.2f} s, scaled "
+                     f"x{(n / npr) ** 3:.4g}), column loop on {min(rows, layers[0].m)} rows of "
+                     f"each of {len(layers)} layer(s) (scaled to all rows"
+                     + ("" if npr == n else "; unit upper factor") + ")")
+    weights = sum(l.m * l.n for l in wl.layers)
     try:
         from threadpoolctl import threadpool_info
 
@@ -160,14 +501,12 @@ def cpu_baseline(wl, rows: int, chunks: int):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     return {
-        "value": ls.m * ls.n / total,
+        "value": weights / total,
         "unit": "weights/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 numpy/scipy oracle: Hessian over {chunks} of {xs.chunks} sequences "
-                   f"({t_h:.2f} s, scaled x{xs.chunks / chunks:g}), prepare at full n={ls.n} "
-                   f"({t_p:.2f} s), column loop on {rows} of {ls.m} rows ({t_q:.2f} s, scaled "
-                   f"x{ls.m / rows:g}); estimated full-layer time {total:.1f} s"),
+        "sample": "fp64 numpy/scipy oracle; " + "; ".join(parts)
+                  + f"; estimated whole-workload time {total:.1f} s",
     }
 
 
@@ -385,25 +724,30 @@ def main():
         t = traffic_record(*args.traffic_record)
         rec = {
             "kernel": "gptq_hessian_accumulate: " + " + ".join(HESS_KERNELS),
-            "workload": WORKLOAD,
+            "workload": args.workload,
             "bytes_per_launch": round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]),
-            "fetch": t["FETCH_SIZE"],
-            "write": t["WRITE_SIZE"],
+            "fetch": {k: v for k, v in t["FETCH_SIZE"].items() if k != "per_kernel_bytes"},
+            "write": {k: v for k, v in t["WRITE_SIZE"].items() if k != "per_kernel_bytes"},
+            "per_kernel_step_bytes": {
+                k: {"fetch": round(t["FETCH_SIZE"]["per_kernel_bytes"].get(k, 0.0)),
+                    "write": round(t["WRITE_SIZE"]["per_kernel_bytes"].get(k, 0.0))}
+                for k in sorted(set(t["FETCH_SIZE"]["per_kernel_bytes"])
+                                | set(t["WRITE_SIZE"]["per_kernel_bytes"]))},
             "calibration": f"device copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write "
                            f"{COPY_BYTES})",
             "commands": [
                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format "
-                "csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py "
-                "--traffic-probe",
+                f"csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py "
+                f"--traffic-probe --workload {args.workload}",
                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format "
-                "csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py "
-                "--traffic-probe",
+                f"csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py "
+                f"--traffic-probe --workload {args.workload}",
                 "python3 bench.py --traffic-record gpurun_out/pmc_fetch/run_counter_collection.csv "
-                "gpurun_out/pmc_write/run_counter_collection.csv",
+                f"gpurun_out/pmc_write/run_counter_collection.csv --workload {args.workload}",
             ],
             "kernel_source_sha256": source_hash(HESSIAN_SRC),
         }
-        with open(TRAFFIC_FILE, "w") as f:
+        with open(traffic_file(args.workload), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
@@ -413,12 +757,10 @@ def main():
               "(the multi-GPU split of the path is described, not built)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
     import post_weight_quantization_22_amd as gq
-    from post_weight_quantization_22_amd import pipeline
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -429,155 +771,149 @@ def main():
         dequant_probe(gq, dev)
         return
 
-    wl = synth.get_workload(WORKLOAD)
+    wl = synth.get_workload(args.workload)
+    if args.traffic_probe:
+        traffic_probe(gq, wl, dev)
+        return
+
+    print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
+    head, _ = run_workload(gq, wl, dev, args.steps, args.warmup,
+                           breakdown=not args.no_breakdown)
+    g0 = head["streams"][0]
     ls = wl.layer()
     xs = wl.xs[ls.x]
-    q = wl.quant
-    m, n, N = ls.m, ls.n, xs.tokens
-
-    # ---- inputs, resident in HBM before any timing -------------------------------
-    t0 = time.time()
-    W = torch.from_numpy(synth.weight(wl, ls.name)).to(dev).to(torch.bfloat16)
-    X = torch.empty((N, n), dtype=torch.bfloat16, device=dev)
-    per = 16
-    for c0 in range(0, xs.chunks, per):
-        idx = list(range(c0, min(xs.chunks, c0 + per)))
-        host = synth.x_all(wl, ls.x, chunks=idx)
-        X[c0 * xs.chunk_len:(c0 + len(idx)) * xs.chunk_len].copy_(
-            torch.from_numpy(host).to(torch.bfloat16))
-    torch.cuda.synchronize()
-    t_gen = time.time() - t0
-
-    cfg = gq.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
-    buf = pipeline.allocate(m, n, cfg, N)
-    if args.traffic_probe:
-        stream = torch.cuda.current_stream()
-        for _ in range(2):
-            buf.S.zero_()
-            gq.gptq_hessian_accumulate(buf.S, X, ws=buf.ws_hess, stream=stream)
-        torch.cuda.synchronize()
-        del X
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print("traffic probe: 2 Hessian accumulates and one device copy of "
-              f"{COPY_BYTES} bytes done", flush=True)
-        return
-    ng = pipeline.ngroups(n, q.group_size)
-    rtn_codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
-    rtn_scales = torch.empty((m, ng), dtype=torch.float32, device=dev)
-    rtn_zeros = torch.empty((m, ng), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        buf.S.zero_()
-        gq.gptq_hessian_accumulate(buf.S, X, ws=buf.ws_hess, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        pipeline.prepare(buf, N, stream)
-        if ev:
-            ev[2].record(stream)
-        pipeline.quantize(buf, W, stream)
-        if ev:
-            ev[3].record(stream)
-        pipeline.pack(buf, stream)
-        if ev:
-            ev[4].record(stream)
-        gq.rtn_minmax(W, q.bits, q.group_size, rtn_codes, rtn_scales, rtn_zeros, stream=stream)
-        if ev:
-            ev[5].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    pipeline.check_info(buf)
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for k in range(args.steps):
-        step(events[k])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    pipeline.check_info(buf)
-
-    names = ["hessian", "prepare", "quantize", "pack", "rtn"]
-    stage_ms = {nm: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
-                                   for k in range(args.steps)])) for i, nm in enumerate(names)}
+    n, N, q = xs.n, xs.tokens, wl.quant
     hess_flops = n * (n + 1) * N
-    prep_flops = 2 * n ** 3 / 3
-    upd_flops = m * n * (n - q.block_size)
-    hess_tf = hess_flops / (stage_ms["hessian"] * 1e-3) / 1e12
-    value = m * n / (ms_per_step * 1e-3)
-
+    hess_ms = g0["stages_ms"]["hessian"]
+    hess_tf = hess_flops / (hess_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "hessian: gptq_hessian_accumulate (syrk_bf16_dma_kernel + reduce_full_partials_kernel)",
+        "kernel": "hessian: gptq_hessian_accumulate (syrk_bf16_dma_kernel"
+                  + (" + reduce_full_partials_kernel" if gq.gptq_hessian_workspace_size(n, N)
+                     else "") + ")",
         "achieved": round(hess_tf, 2),
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(hess_tf / BF16_PEAK_TFLOPS, 4),
-        "traffic": measured_traffic(),
+        "traffic": measured_traffic(args.workload),
         "algorithmic_work": f"n(n+1)N = {hess_flops:.4e} flop per launch",
-        "launch_ms": round(stage_ms["hessian"], 4),
+        "launch_ms": round(hess_ms, 4),
     }
-    stages = {
-        nm: {"ms": round(v, 4)} for nm, v in stage_ms.items()
-    }
-    stages["hessian"]["tflops"] = round(hess_tf, 2)
-    stages["prepare"]["tflops_f64"] = round(prep_flops / (stage_ms["prepare"] * 1e-3) / 1e12, 3)
-    stages["quantize"]["update_tflops_incl_block_loop"] = round(
-        upd_flops / (stage_ms["quantize"] * 1e-3) / 1e12, 2)
-    # the layer's roofline time: each stage at its own peak
-    roof_ms = (hess_flops / (BF16_PEAK_TFLOPS * 1e12) + prep_flops / (FP64_PEAK_TFLOPS * 1e12)
-               + upd_flops / (FP32_PEAK_TFLOPS * 1e12)
-               + (m * n * (2 + 4 + 4 + 1) + m * n * (1 + q.bits / 8)) / (HBM_PEAK_GBS * 1e9)) * 1e3
-
+    weights = sum(l.m * l.n for l in wl.layers)
     out = {
         "metric": "GPTQ layer weights quantized/sec; Hessian+update TFLOP/s as % MFMA peak",
-        "value": round(value, 1),
+        "value": round(weights / (head["ms_per_step"] * 1e-3), 1),
         "unit": "weights/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16->f32 MFMA (Hessian), f64 (prepare), f32 (column loop)",
-        "data": "synthetic, seeded (normal activations, 0.5% outlier channels x30)",
+        "data": "synthetic, seeded (" + {
+            "normal": "normal activations", "laplace": "Laplace(0, 1) activations",
+            "student_t4": "Student-t (nu = 4) activations"}[xs.dist] + ")",
         "config": {
-            "workload": "Llama-7B-shaped attention projection 4096x4096, 128x2048 calibration "
-                        "tokens, 4-bit asymmetric, group 128, block 128, damp 0.01, desc_act off",
-            "m": m, "n": n, "tokens": N, "bits": q.bits, "group_size": q.group_size,
+            "workload": WORKLOAD_LABEL.get(args.workload, wl.description),
+            "m": ls.m, "n": n, "tokens": N, "bits": q.bits, "group_size": q.group_size,
             "block_size": q.block_size, "perc_damp": q.perc_damp, "desc_act": q.desc_act,
             "parallelism": "single GPU",
         },
         "roofline": roofline,
-        "stages": stages,
-        "layer_roofline_ms": round(roof_ms, 4),
-        "layer_roofline_frac": round(roof_ms / ms_per_step, 4),
-        "input_setup_s": round(t_gen, 1),
+        "stages": g0["stages_ms"],
+        "layer_roofline_ms": head["layer_roofline_ms"],
+        "layer_roofline_frac": head["layer_roofline_frac"],
+        "layer_roofline_ms_f64_prepare": head["layer_roofline_ms_f64_prepare"],
+        "layer_roofline_frac_f64_prepare": head["layer_roofline_frac_f64_prepare"],
+        "input_setup_s": head["input_setup_s"],
+        "detail": g0,
     }
-    out["dequant_gemm"] = dequant_gemm_measure(gq, buf, X, m, n, q, stream)
-    if not args.no_awq:
-        out["awq"] = awq_measure(gq, W, X, buf.S, m, n, q, stream)
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        configs = {}
+        for name in EXTRA:
+            if name == args.workload:
+                continue
+            print(f"bench: workload {name}", file=sys.stderr, flush=True)
+            st, wu = EXTRA_STEPS[name]
+            keep = name == "llama7b_attn" and not (args.no_awq and args.no_dequant)
+            rec, state = run_workload(gq, synth.get_workload(name), dev, st, wu,
+                                      breakdown=not args.no_breakdown, keep=keep)
+            configs[name] = rec
+            if state is not None:
+                if not args.no_dequant:
+                    out["dequant_gemm"] = dequant_gemm_measure(
+                        gq, state["buf"], state["X"], state["m"], state["n"], state["q"],
+                        state["stream"])
+                if not args.no_awq:
+                    out["awq"] = awq_measure(gq, state["W"], state["X"], state["buf"].S,
+                                             state["m"], state["n"], state["q"], state["stream"])
+                del state
+            torch.cuda.empty_cache()
+        out["configs"] = configs
     if not args.no_stack:
-        del X
-        torch.cuda.empty_cache()
+        print("bench: layer-sequential stack", file=sys.stderr, flush=True)
         out["layer_sequential"] = stack_measure(gq, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_sample_chunks)
+        print("bench: oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_sample_chunks,
+                                           args.cpu_prepare_n)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+WORKLOAD_LABEL = {
+    "llama70b_down": "70B-shaped down projection 8192x28672 (28672^2 Hessian), 256x2048 "
+                     "Laplace(0,1) bf16 calibration tokens, 4-bit asymmetric, group 64, block "
+                     "128, damp 0.01, desc_act on",
+    "llama7b_attn": "Llama-7B-shaped attention projection 4096x4096, 128x2048 calibration "
+                    "tokens, 4-bit asymmetric, group 128, block 128, damp 0.01, desc_act off",
+}
+
+
+def traffic_probe(gq, wl, dev):
+    """One Hessian accumulate, one whole layer step (prepare, quantize, pack,
+    RTN of the first layer) and a 2 GiB device copy, for counter runs."""
+    import torch
+
+    import synth
+    from post_weight_quantization_22_amd import pipeline
+
+    ls = wl.layer()
+    xs = wl.xs[ls.x]
+    q = wl.quant
+    n, N = xs.n, xs.tokens
+    X = upload_x(wl, ls.x, dev)
+    W = torch.from_numpy(synth.weight(wl, ls.name)).to(dev)
+    if ls.w_dtype == "bf16":
+        W = W.to(torch.bfloat16)
+    cfg = gq.make_config(q.bits, q.group_size, q.block_size, q.perc_damp, q.desc_act, q.sym)
+    buf = pipeline.allocate(ls.m, n, cfg, N, device=dev)
+    stream = torch.cuda.current_stream()
+    buf.S.zero_()
+    gq.gptq_hessian_accumulate(buf.S, X, ws=buf.ws_hess, stream=stream)
+    torch.cuda.synchronize()
+    del X
+    torch.cuda.empty_cache()
+    pipeline.prepare(buf, N, stream)
+    pipeline.quantize(buf, W, stream)
+    pipeline.pack(buf, stream)
+    ng = pipeline.ngroups(n, q.group_size)
+    gq.rtn_minmax(W, q.bits, q.group_size, torch.empty((ls.m, n), dtype=torch.uint8, device=dev),
+                  torch.empty((ls.m, ng), dtype=torch.float32, device=dev),
+                  torch.empty((ls.m, ng), dtype=torch.float32, device=dev), stream=stream)
+    torch.cuda.synchronize()
+    pipeline.check_info(buf)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"traffic probe ({wl.name}): one Hessian accumulate, one layer step and one device "
+          f"copy of {COPY_BYTES} bytes done", flush=True)
 
 
 if __name__ == "__main__":

@@ -29,7 +29,9 @@ Floating point is fp64 throughout, except where a floating value decides an
 integer (a code, a zero-point): there the decision is taken in fp32, the
 precision of the device kernels, emulated exactly (each fp32 operation is the
 fp64 result rounded once to fp32, which is the correctly rounded fp32 result
-for +, -, *, / of fp32 operands).
+for +, -, *, / of fp32 operands).  The quantizer, the GPTQ loop, RTN and the
+replay also take ``exact=True``: every decision in plain fp64, the reference
+against which the fp32 decisions are shown to differ only at rounding ties.
 
 Every function below is pinned by ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, special cases and brute force; the module

@@ -74,7 +74,7 @@ def _check_grouping(n: int, G: int, B: int) -> None:
 def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
                   block_size: int = 128, perm: Optional[np.ndarray] = None,
                   dead: Optional[np.ndarray] = None, sym: bool = False,
-                  static_groups: bool = False) -> GPTQResult:
+                  static_groups: bool = False, exact: bool = False) -> GPTQResult:
     """Blocked GPTQ of W [m, n] (original column order) with U from ``prepare``.
 
     ``static_groups``: the group parameters are computed once, before the loop,
@@ -85,7 +85,10 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
     compensated values when its first column is reached.  A group larger than
     the block (G a multiple of B) starts at a block start, where every earlier
     column's error has been applied to all later columns, so its parameters are
-    those block_size = G would give."""
+    those block_size = G would give.
+
+    ``exact``: the quantizer's decisions (range, scale, zero-point, codes) in
+    plain fp64 instead of the fp32 decision precision."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     G, B = group_size, block_size
@@ -101,14 +104,14 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
     Q = np.zeros((m, n))
     Eall = np.zeros((m, n))
     if G <= 0:  # one group per row, taken from the whole (unmodified) row
-        scale, zero = group_params(Wp, bits, sym)
+        scale, zero = group_params(Wp, bits, sym, exact)
         scales[:, 0], zeros[:, 0] = scale, zero
     elif static_groups:
         W0 = W.copy()
         if dead is not None:
             W0[:, np.asarray(dead)] = 0.0
         for g in range(ng):
-            scales[:, g], zeros[:, g] = group_params(W0[:, g * G:(g + 1) * G], bits, sym)
+            scales[:, g], zeros[:, g] = group_params(W0[:, g * G:(g + 1) * G], bits, sym, exact)
     for i in range(0, n, B):
         i1 = min(i + B, n)
         W1 = Wp[:, i:i1].copy()
@@ -121,10 +124,10 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
             elif G > 0 and c % G == 0:
                 glen = min(G, n - c)
                 cur = W1[:, j:j + glen] if G <= B else Wp[:, c:c + glen]  # c == i when G > B
-                scale, zero = group_params(cur, bits, sym)
+                scale, zero = group_params(cur, bits, sym, exact)
                 scales[:, c // G], zeros[:, c // G] = scale, zero
             w = W1[:, j]
-            q = quantize_codes(w, scale, zero, bits)
+            q = quantize_codes(w, scale, zero, bits, exact)
             e = (w - dequantize(q, scale, zero)) / U[c, c]
             W1[:, j + 1:] -= np.outer(e, U[c, c + 1:i1])
             E[:, j] = e
@@ -144,7 +147,8 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int,
 
 
 def gptq_obs_literal(W: np.ndarray, Hd: np.ndarray, bits: int, group_size: int,
-                     perm: Optional[np.ndarray] = None, sym: bool = False):
+                     perm: Optional[np.ndarray] = None, sym: bool = False,
+                     exact: bool = False):
     """Fixed-order OBS route: explicit H_d^-1, compensation and downdate per column.
 
     ``Hd`` is the damped Hessian in processing order.  Returns (codes in original
@@ -162,13 +166,13 @@ def gptq_obs_literal(W: np.ndarray, Hd: np.ndarray, bits: int, group_size: int,
     zeros = np.zeros((m, ng))
     Q = np.zeros((m, n))
     if G <= 0:
-        scale, zero = group_params(Wp, bits, sym)
+        scale, zero = group_params(Wp, bits, sym, exact)
         scales[:, 0], zeros[:, 0] = scale, zero
     for c in range(n):
         if G > 0 and c % G == 0:
-            scale, zero = group_params(Wp[:, c:min(c + G, n)], bits, sym)
+            scale, zero = group_params(Wp[:, c:min(c + G, n)], bits, sym, exact)
             scales[:, c // G], zeros[:, c // G] = scale, zero
-        q = quantize_codes(Wp[:, c], scale, zero, bits)
+        q = quantize_codes(Wp[:, c], scale, zero, bits, exact)
         err = Wp[:, c] - dequantize(q, scale, zero)
         d = Hinv[c, c]
         # compensation: delta_F = -(err / [H^-1]_cc) * [H^-1]_{c, F}
@@ -182,7 +186,8 @@ def gptq_obs_literal(W: np.ndarray, Hd: np.ndarray, bits: int, group_size: int,
     return codes, scales, zeros
 
 
-def rtn_minmax(W: np.ndarray, bits: int, group_size: int, sym: bool = False):
+def rtn_minmax(W: np.ndarray, bits: int, group_size: int, sym: bool = False,
+               exact: bool = False):
     """Round-to-nearest with group min-max parameters from the original weights.
 
     The GPTQ loop with no compensation: "GPTQ deep dive" §1.2 (RTN rounds each
@@ -198,9 +203,9 @@ def rtn_minmax(W: np.ndarray, bits: int, group_size: int, sym: bool = False):
     zeros = np.zeros((m, ng))
     for g in range(ng):
         c0, c1 = g * G, min((g + 1) * G, n)
-        scale, zero = group_params(W[:, c0:c1], bits, sym)
+        scale, zero = group_params(W[:, c0:c1], bits, sym, exact)
         scales[:, g], zeros[:, g] = scale, zero
-        codes[:, c0:c1] = quantize_codes(W[:, c0:c1], scale[:, None], zero[:, None], bits)
+        codes[:, c0:c1] = quantize_codes(W[:, c0:c1], scale[:, None], zero[:, None], bits, exact)
     return codes, scales, zeros
 
 
@@ -245,7 +250,7 @@ def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block
                  perm: Optional[np.ndarray], dead: Optional[np.ndarray],
                  codes_proc: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
                  tau: float = 1e-3, sym: bool = False,
-                 static_groups: bool = False) -> ReplayReport:
+                 static_groups: bool = False, exact: bool = False) -> ReplayReport:
     """Validate a candidate result column by column against the oracle's own loop.
 
     At a rounding tie both neighbours are correct, and everything downstream
@@ -255,6 +260,7 @@ def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block
     within ``tau`` (in quantization steps) of a rounding boundary, the other
     neighbour.  Any other disagreement is "hard".  Group zero-points are checked
     the same way; scales must agree to ``scale_max_rel``, which is reported.
+    ``exact``: the oracle's side of every decision in plain fp64.
     """
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
@@ -273,19 +279,20 @@ def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block
 
     def take_params(vals, gidx):
         nonlocal zmis, zties, zhard, smax
-        s_o, z_o = group_params(vals, bits, sym)
+        s_o, z_o = group_params(vals, bits, sym, exact)
         s_c = np.asarray(scales[:, gidx], np.float64)
         z_c = np.asarray(zeros[:, gidx], np.float64)
         smax = max(smax, float(np.max(np.abs(s_c - s_o) / np.abs(s_o))))
         bad = z_c != z_o
         if np.any(bad) and not sym:
-            v32 = f32(vals)
+            rd = f32 if not exact else (lambda x: np.asarray(x, dtype=np.float64))
+            v32 = rd(vals)
             xmin = np.minimum(v32.min(axis=1), 0.0)
             xmax = np.maximum(v32.max(axis=1), 0.0)
             flat = xmin == xmax
             xmin = np.where(flat, -1.0, xmin)
-            span = f32(np.where(flat, 1.0, xmax) - xmin)
-            pre = f32(f32(-xmin * maxq) / span)
+            span = rd(np.where(flat, 1.0, xmax) - xmin)
+            pre = rd(rd(-xmin * maxq) / span)
             frac = np.abs(pre - np.floor(pre) - 0.5)
             tie = bad & (frac < tau) & (np.abs(z_c - z_o) == 1)
             zmis += int(bad.sum())
@@ -318,11 +325,11 @@ def replay_check(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block
                 cur = W1[:, j:j + min(G, n - c)] if G <= B else Wp[:, c:c + min(G, n - c)]
                 scale, zero = take_params(cur, c // G)
             w = W1[:, j]
-            q_o = quantize_codes(w, scale, zero, bits)
+            q_o = quantize_codes(w, scale, zero, bits, exact)
             q_c = cq[:, c]
             bad = q_c != q_o
             if np.any(bad):
-                pre = pre_round_value(w, scale)
+                pre = pre_round_value(w, scale, exact)
                 frac = np.abs(pre - np.floor(pre) - 0.5)
                 tie = bad & (frac < tau) & (np.abs(q_c - q_o) == 1)
                 mism += int(bad.sum())

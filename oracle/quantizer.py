@@ -18,7 +18,10 @@ followed by the device path):
 * codes are unsigned in [0, 2^bits - 1], clamped after adding the zero-point;
 * rounding is round-half-to-even (IEEE rint) and every division is a true
   division, never a multiplication by a reciprocal;
-* the decision precision is fp32 (see the package docstring).
+* the decision precision is fp32 (see the package docstring); with
+  ``exact=True`` every step is plain fp64 instead (no rounding to fp32
+  anywhere), the reference against which an fp32 decision is shown to differ
+  only at rounding ties.
 """
 from __future__ import annotations
 
@@ -30,20 +33,30 @@ def f32(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def group_params(v: np.ndarray, bits: int, sym: bool = False):
+def _rounder(exact: bool):
+    """The rounding applied after each step: to fp32 (the kernels' decision
+    precision), or none (plain fp64)."""
+    if exact:
+        return lambda x: np.asarray(x, dtype=np.float64)
+    return f32
+
+
+def group_params(v: np.ndarray, bits: int, sym: bool = False, exact: bool = False):
     """Scale and zero-point of each row of ``v`` ([rows, group_len] current values).
 
-    Returns (scale, zero), both fp64 arrays holding fp32 values; zero is integral.
-    Asymmetric: min-max range with 0 included.  Symmetric: zero-point fixed at
-    the middle of the code range, scale = 2*max|v| / maxq (the symmetric variant
-    of "LLM quantization principles" §2.3, expressed on unsigned codes).
+    Returns (scale, zero), both fp64 arrays holding fp32 values (fp64 values
+    with ``exact``); zero is integral.  Asymmetric: min-max range with 0
+    included.  Symmetric: zero-point fixed at the middle of the code range,
+    scale = 2*max|v| / maxq (the symmetric variant of "LLM quantization
+    principles" §2.3, expressed on unsigned codes).
     """
+    r = _rounder(exact)
     maxq = float(2 ** bits - 1)
-    v32 = f32(v)
+    v32 = r(v)
     if sym:
         amax = np.abs(v32).max(axis=1)
         amax = np.where(amax == 0.0, 1.0, amax)
-        scale = f32(f32(2.0 * amax) / maxq)
+        scale = r(r(2.0 * amax) / maxq)
         zero = np.full_like(scale, np.floor((maxq + 1.0) / 2.0))
         return scale, zero
     xmin = np.minimum(v32.min(axis=1), 0.0)
@@ -51,21 +64,24 @@ def group_params(v: np.ndarray, bits: int, sym: bool = False):
     degenerate = xmin == xmax
     xmin = np.where(degenerate, -1.0, xmin)
     xmax = np.where(degenerate, 1.0, xmax)
-    span = f32(xmax - xmin)
-    scale = f32(span / maxq)
-    zero = np.rint(f32(f32(-xmin * maxq) / span))
+    span = r(xmax - xmin)
+    scale = r(span / maxq)
+    zero = np.rint(r(r(-xmin * maxq) / span))
     return scale, zero
 
 
-def pre_round_value(w: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """w / scale in fp32 (the value whose rounding gives the code before the offset)."""
-    return f32(f32(w) / scale)
+def pre_round_value(w: np.ndarray, scale: np.ndarray, exact: bool = False) -> np.ndarray:
+    """w / scale in fp32 (fp64 with ``exact``): the value whose rounding gives
+    the code before the offset."""
+    r = _rounder(exact)
+    return r(r(w) / scale)
 
 
-def quantize_codes(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int) -> np.ndarray:
+def quantize_codes(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int,
+                   exact: bool = False) -> np.ndarray:
     """q = clamp(round(w / scale) + zero, 0, maxq), ties to even; fp64 integral values."""
     maxq = float(2 ** bits - 1)
-    return np.clip(np.rint(pre_round_value(w, scale)) + zero, 0.0, maxq)
+    return np.clip(np.rint(pre_round_value(w, scale, exact)) + zero, 0.0, maxq)
 
 
 def dequantize(q: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:

@@ -89,6 +89,19 @@ def test_layer_end_to_end(name, wl, layer):
     assert rate >= 0.999
     assert rep.hard == 0 and rep.zero_hard == 0
     assert rep.scale_max_rel <= 1e-4
+    # against the plain-fp64 oracle: every decision (range, scale, zero-point, code)
+    # in fp64; the device's fp32 decisions may differ only at rounding ties
+    ref64 = oracle.gptq_quantize(W, P.U, qs.bits, qs.group_size, qs.block_size, P.perm, P.dead,
+                                 exact=True)
+    rate64 = match_rate(codes, ref64.codes)
+    rep64 = oracle.replay_check(W, P.U, qs.bits, qs.group_size, qs.block_size, P.perm, P.dead,
+                                codes.astype(np.float64)[:, P.perm], scales, zeros, exact=True)
+    print(f"{name}: vs plain-fp64 oracle: match {rate64:.6f} | replay mism {rep64.mismatches} "
+          f"ties {rep64.ties} hard {rep64.hard} zero-hard {rep64.zero_hard} scale rel "
+          f"{rep64.scale_max_rel:.2e}")
+    assert rate64 >= 0.999
+    assert rep64.hard == 0 and rep64.zero_hard == 0
+    assert rep64.scale_max_rel <= 1e-4
     Wq = oracle.dequant_layer(codes.astype(np.float64), scales.astype(np.float64),
                               zeros.astype(np.float64), g_idx)
     Wq_ref = oracle.dequant_layer(ref.codes, ref.scales, ref.zeros, ref.g_idx)

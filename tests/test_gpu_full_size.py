@@ -79,6 +79,20 @@ def test_llama7b_attn_full_size():
     assert rate >= 0.999
     assert rep.hard == 0 and rep.zero_hard == 0
     assert rep.scale_max_rel <= 1e-4
+    # against the plain-fp64 oracle (every decision in fp64)
+    t0 = time.time()
+    ref64 = oracle.gptq_quantize(W, P.U, qs.bits, qs.group_size, qs.block_size, P.perm, P.dead,
+                                 exact=True)
+    rate64 = match_rate(codes, ref64.codes)
+    roots64, casc64 = root_cascade(codes, ref64.codes, P.perm)
+    rep64 = oracle.replay_check(W, P.U, qs.bits, qs.group_size, qs.block_size, P.perm, P.dead,
+                                codes.astype(np.float64), scales, zeros, exact=True)
+    print(f"vs plain-fp64 oracle ({time.time() - t0:.1f} s): match {rate64:.6f} roots "
+          f"{roots64} cascaded {casc64} | replay ties {rep64.ties} hard {rep64.hard} zero-hard "
+          f"{rep64.zero_hard} scale rel {rep64.scale_max_rel:.2e}", flush=True)
+    assert rate64 >= 0.999
+    assert rep64.hard == 0 and rep64.zero_hard == 0
+    assert rep64.scale_max_rel <= 1e-4
     # free running, rows whose codes all agree must agree on every group's scale and
     # zero; rows downstream of a tie follow another (equally valid) trajectory, which
     # the replay above has checked

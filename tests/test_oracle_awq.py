@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from oracle import awq
+from oracle.quantizer import f32
 
 
 def _layer(rng, m, n, t, outliers=()):
@@ -86,6 +87,60 @@ def test_clip_ratio_one_is_plain_minmax_and_the_search_never_worse():
     chosen = np.take_along_axis(clip.errors, clip.ratio_idx[:, :, None], axis=2)[:, :, 0]
     assert np.all(chosen <= clip.errors[:, :, 0])
     assert np.all(chosen == clip.errors.min(axis=2))
+
+
+def test_clip_group_error_over_tokens_with_rescaled_inputs():
+    """errors[r, g, k] is the group's share of the output error over the
+    calibration tokens, with the activations divided by s: the sum over tokens
+    of (X'[t, g] . d_g)^2, X' = X diag(1/s), d_g the candidate's rounding error
+    in the rescaled space, summed here term by term."""
+    rng = np.random.default_rng(6)
+    m, n, t, G, bits = 3, 16, 40, 8, 3
+    W, X = _layer(rng, m, n, t, outliers=(2,))
+    s = rng.uniform(0.5, 2.0, n)
+    clip = awq.awq_clip(W, X.T @ X, s, bits, G)
+    Ws = f32(W * s)
+    amax = np.stack([np.abs(Ws[:, g0:g0 + G]).max(axis=1) for g0 in range(0, n, G)], axis=1)
+    for k, ratio in enumerate(awq.CLIP_RATIOS):
+        bound = f32(amax * f32(ratio))
+        q, sc, z = awq.quantize_groups(Ws, bits, G, ranges=bound)
+        d = awq.dequant_groups(q, sc, z, G) - Ws
+        for r in range(m):
+            for gi, g0 in enumerate(range(0, n, G)):
+                err = 0.0
+                for tt in range(t):
+                    acc = 0.0
+                    for c in range(g0, g0 + G):
+                        acc += (X[tt, c] / s[c]) * d[r, c]
+                    err += acc * acc
+                assert abs(clip.errors[r, gi, k] - err) <= 1e-10 * max(err, 1e-30), (r, gi, k)
+
+
+def test_clip_parameters_come_from_the_clamped_range():
+    """The chosen clip c bounds the range the group's parameters are computed
+    from: scale = (min(c, max v) - max(-c, min v)) / maxq with 0 kept in the
+    range (fp32, as every decision), while the values themselves are not
+    clamped (a weight beyond c takes the end code)."""
+    rng = np.random.default_rng(8)
+    m, n, G, bits = 6, 32, 32, 3
+    W = rng.standard_normal((m, n)) * 0.01
+    W[:, 5] = 0.5
+    clip = awq.awq_clip(W, np.eye(n) * 100.0, np.ones(n), bits, G)
+    maxq = 2 ** bits - 1
+    Ws = f32(W)
+    for r in range(m):
+        k = int(clip.ratio_idx[r, 0])
+        assert k > 0
+        c = f32(np.abs(Ws[r]).max() * f32(awq.CLIP_RATIOS[k]))
+        hi = max(0.0, min(c, Ws[r].max()))
+        lo = min(0.0, max(-c, Ws[r].min()))
+        assert clip.scales[r, 0] == f32(f32(hi - lo) / maxq)
+        assert clip.codes[r, 5] == maxq  # 0.5 lies beyond c: the top code
+        # the unclamped value 0.5 alone decides its code: an in-range weight keeps
+        # the code of its own value
+        j = int(np.argmin(np.abs(Ws[r])))
+        pre = f32(Ws[r, j] / clip.scales[r, 0])
+        assert clip.codes[r, j] == np.clip(np.rint(pre) + clip.zeros[r, 0], 0, maxq)
 
 
 def test_clip_cuts_a_planted_outlier():

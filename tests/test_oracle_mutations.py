@@ -29,6 +29,7 @@ import test_oracle_quantizer as tq
 import test_oracle_dequant as td
 import test_oracle_stack as tst
 import test_oracle_awq as tawq
+import test_oracle_exact as tex
 
 
 def _mutant(mod, old, new):
@@ -62,11 +63,17 @@ MUTANTS = [
     (GPTQ_MOD, "cur = W1[:, j:j + glen] if G <= B else Wp[:, c:c + glen]",
      "cur = W[:, perm][:, c:c + glen]", ["gptq_quantize"],
      lambda gd: tg.test_cholesky_route_equals_literal_obs_route()),
-    (QUANT_MOD, "zero = np.rint(f32(f32(-xmin * maxq) / span))",
-     "zero = np.rint(f32(f32(xmin * maxq) / span))", ["group_params"],
+    (QUANT_MOD, "zero = np.rint(r(r(-xmin * maxq) / span))",
+     "zero = np.rint(r(r(xmin * maxq) / span))", ["group_params"],
      lambda gd: tq.test_codes_and_zero_in_range(4)),
-    (QUANT_MOD, "scale = f32(span / maxq)", "scale = f32(span / (maxq + 1.0))",
+    (QUANT_MOD, "scale = r(span / maxq)", "scale = r(span / (maxq + 1.0))",
      ["group_params"], lambda gd: tq.test_worked_example_minmax_int8(gd)),
+    # the fp64 decision mode silently rounding to fp32 after all
+    (QUANT_MOD, "return lambda x: np.asarray(x, dtype=np.float64)", "return f32",
+     ["group_params"], lambda gd: tex.test_worked_example_exact(gd)),
+    (QUANT_MOD, "return np.clip(np.rint(pre_round_value(w, scale, exact)) + zero, 0.0, maxq)",
+     "return np.clip(np.floor(pre_round_value(w, scale, exact)) + zero, 0.0, maxq)",
+     ["quantize_codes"], lambda gd: tex.test_exact_rtn_is_the_nearest_grid_point()),
     (PREP_MOD, "lam = float(perc_damp) * float(np.mean(np.diag(H)))",
      "lam = float(perc_damp) * float(np.sum(np.diag(H)))", ["prepare"],
      lambda gd: th.test_damping_closed_form_on_diagonal_S()),
@@ -98,6 +105,13 @@ MUTANTS = [
      ["awq"], lambda gd: tawq.test_rescaling_preserves_the_output_when_nothing_is_rounded()),
     (AWQ_MOD, "best = int(np.argmin(losses))", "best = int(np.argmax(losses))", ["awq"],
      lambda gd: tawq.test_alpha_search_against_brute_force()),
+    # awq_clip's group error without the 1/s rescaling of the inputs' second moments
+    (AWQ_MOD, "Sp = S / np.outer(s, s)", "Sp = S", ["awq"],
+     lambda gd: tawq.test_clip_group_error_over_tokens_with_rescaled_inputs()),
+    # clip candidates that clamp the values instead of the range
+    (AWQ_MOD, "        scale, zero = group_params(basis, bits, sym)\n        scales[:, k], zeros[:, k] = scale, zero\n        codes[:, g0:g1] = quantize_codes(v, scale[:, None], zero[:, None], bits)",
+     "        scale, zero = group_params(v, bits, sym)\n        scales[:, k], zeros[:, k] = scale, zero\n        codes[:, g0:g1] = quantize_codes(basis, scale[:, None], zero[:, None], bits)",
+     ["awq"], lambda gd: tawq.test_clip_parameters_come_from_the_clamped_range()),
 ]
 
 
