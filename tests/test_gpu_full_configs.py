@@ -9,9 +9,13 @@ and on properties that hold at any size:
   - S on a sample of channel pairs (every token, fp64);
   - the processing order is a descending order of diag(H);
   - U on a sample of rows: U H_d U^T = I, to the fp32 rounding of U;
-  - the column loop, scales, zeros, codes and packed words on a sample of rows,
-    from the oracle's loop given the device's U and order (rows are independent
-    given U), with the replay check for rounding ties.
+  - the column loop on EVERY row: codes, scales and zeros from the oracle's
+    loop given the device's U and order (rows are independent given U, so the
+    oracle runs row-parallel in spawned worker processes), free-running match
+    rate with its root and cascade counts, and the replay check for rounding
+    ties on every row;
+  - the packed words on a sample of rows, and the reconstruction error on all
+    rows (a sample of 1024 rows for the 28672-wide layer).
 """
 import time
 
@@ -19,9 +23,10 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_rows
 import synth
 
-from gpu_util import host, match_rate, need_gpu, root_cascade, say, torch
+from gpu_util import host, match_rate, need_gpu, say, torch
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
 
@@ -65,7 +70,8 @@ def _check_hessian(buf, S_ref, chans, tokens):
 
 
 def _check_order_and_U(buf, S_dev, perc_damp, desc_act):
-    """H_d in the device's order; U H_d U^T = I on sampled rows."""
+    """H_d in the device's order; U H_d U^T = I on sampled rows.  Returns the
+    device's U (fp32), its order and the dead columns."""
     n = S_dev.shape[0]
     H = np.tril(S_dev) + np.tril(S_dev, -1).T
     H *= 2.0
@@ -81,11 +87,12 @@ def _check_order_and_U(buf, S_dev, perc_damp, desc_act):
     else:
         assert np.array_equal(perm, np.arange(n))
     Hp = H[np.ix_(perm, perm)]
+    del H
     lam = float(np.float32(perc_damp)) * float(np.mean(np.diag(Hp)))
     Hp[np.diag_indices(n)] += lam
-    U = host(buf.U).astype(np.float64)
+    U32 = host(buf.U)
     rows = _sample_rows(n, 12)
-    Ur = U[rows]
+    Ur = U32[rows].astype(np.float64)
     Q = Ur @ Hp @ Ur.T
     bound = 8 * EPS32 * (np.abs(Ur) @ np.abs(Hp) @ np.abs(Ur).T) + 1e-10
     dev_ = np.abs(Q - np.eye(len(rows)))
@@ -94,47 +101,59 @@ def _check_order_and_U(buf, S_dev, perc_damp, desc_act):
     assert np.all(dev_ <= bound)
     # U is upper triangular with a positive diagonal
     for r in rows:
-        assert np.all(U[r, :r] == 0.0) and U[r, r] > 0.0
-    return U, perm, dead
+        assert np.all(U32[r, :r] == 0.0) and U32[r, r] > 0.0
+    return U32, perm, dead
 
 
-def _check_rows(wl, lname, buf, U, perm, dead):
+def _check_rows(wl, lname, buf, pool, perm, dead, S_dev):
+    """The column loop on every row, given the device's U (in ``pool``)."""
     q = wl.quant
     ls = wl.layer(lname)
-    rows = _sample_rows(ls.m)
-    W = np.concatenate([synth.weight(wl, lname, rows=slice(r, r + 1)) for r in rows])
+    W = synth.weight(wl, lname)
+    kw = dict(bits=q.bits, group_size=q.group_size, block_size=q.block_size, perm=perm,
+              dead=dead, sym=q.sym)
     t0 = time.time()
-    ref = oracle.gptq_quantize(W, U, q.bits, q.group_size, q.block_size, perm, dead, q.sym)
-    codes = host(buf.codes)[rows]
-    scales = host(buf.scales)[rows]
-    zeros = host(buf.zeros)[rows]
+    ref = pool.quantize(W, **kw)
+    t_loop = time.time() - t0
+    codes = host(buf.codes)
+    scales = host(buf.scales)
+    zeros = host(buf.zeros)
+    g_idx = host(buf.g_idx).astype(np.int64)
     rate = match_rate(codes, ref.codes)
-    roots, casc = root_cascade(codes, ref.codes, perm)
-    rep = oracle.replay_check(W, U, q.bits, q.group_size, q.block_size, perm, dead,
-                              codes.astype(np.float64)[:, perm], scales, zeros, sym=q.sym)
-    print(f"{lname}: {len(rows)} sampled rows, oracle loop {time.time() - t0:.1f} s: match "
-          f"{rate:.6f} roots {roots} cascaded {casc} | replay ties {rep.ties} hard {rep.hard} "
-          f"zero-hard {rep.zero_hard} scale rel {rep.scale_max_rel:.2e}", flush=True)
+    roots, mism, mean_c, max_c = oracle_rows.cascades(codes, ref.codes, perm)
+    t0 = time.time()
+    rep = pool.replay(W, codes.astype(np.float64)[:, perm], scales, zeros, **kw)
+    t_rep = time.time() - t0
+    print(f"{lname}: all {ls.m} rows x {ls.n} (oracle loop {t_loop:.1f} s, replay {t_rep:.1f} s "
+          f"on {pool.nproc} processes): free-running match {rate:.7f} ({mism} of {ls.m * ls.n} "
+          f"codes), {roots} rows diverge (cascade mean {mean_c:.1f}, max {max_c} codes) | "
+          f"replay ties {rep.ties} hard {rep.hard} zero-ties {rep.zero_ties} zero-hard "
+          f"{rep.zero_hard} scale rel {rep.scale_max_rel:.2e}", flush=True)
     assert rate >= 0.999
     assert rep.hard == 0 and rep.zero_hard == 0
     assert rep.scale_max_rel <= 1e-4
-    # g_idx and the packed words of the sampled rows
-    assert np.array_equal(host(buf.g_idx).astype(np.int64), ref.g_idx)
+    # free running, rows whose codes all agree must agree on every group's scale and zero
+    clean = np.all(codes == ref.codes, axis=1)
+    sc_rel = float((np.abs(scales[clean] - ref.scales[clean]) / ref.scales[clean]).max())
+    print(f"{lname}: {int(clean.sum())} rows without divergence, their max scale rel "
+          f"{sc_rel:.2e}", flush=True)
+    assert sc_rel <= 1e-4
+    assert np.array_equal(zeros[clean], ref.zeros[clean])
+    assert np.array_equal(g_idx, ref.g_idx)
+    rows = _sample_rows(ls.m)
     packed = host(buf.packed).view(np.uint32)[rows]
-    assert np.array_equal(packed, oracle.pack_ref(codes, q.bits))
-    # reconstruction error on the sampled rows, device codes vs the oracle's
-    Wq_dev = oracle.dequant_layer(codes, scales, zeros, host(buf.g_idx).astype(np.int64))
-    Wq_ref = oracle.dequant_layer(ref.codes, ref.scales, ref.zeros, ref.g_idx)
-    return W, Wq_dev, Wq_ref
-
-
-def _recon_close(W, Wq_dev, Wq_ref, S_dev):
+    assert np.array_equal(packed, oracle.pack_ref(codes[rows], q.bits))
+    # reconstruction error through the device's undamped H (all rows, or 1024)
+    er = np.arange(ls.m) if ls.n <= 11008 else np.unique(
+        np.random.default_rng(11).choice(ls.m, 1024, replace=False))
     H = 2.0 * (np.tril(S_dev) + np.tril(S_dev, -1).T)
-    e_dev = oracle.recon_error_from_H(W, Wq_dev, H)
-    e_ref = oracle.recon_error_from_H(W, Wq_ref, H)
+    Wq_dev = oracle.dequant_layer(codes[er], scales[er], zeros[er], g_idx)
+    Wq_ref = oracle.dequant_layer(ref.codes[er], ref.scales[er], ref.zeros[er], ref.g_idx)
+    e_dev = oracle.recon_error_from_H(W[er], Wq_dev, H)
+    e_ref = oracle.recon_error_from_H(W[er], Wq_ref, H)
     rel = abs(e_dev - e_ref) / e_ref
-    print(f"reconstruction error on sampled rows: device {e_dev:.6e} oracle {e_ref:.6e} "
-          f"rel {rel:.2e}", flush=True)
+    print(f"{lname}: reconstruction error on {len(er)} rows: device {e_dev:.6e} oracle "
+          f"{e_ref:.6e} rel {rel:.2e}", flush=True)
     assert rel <= 1e-3
 
 
@@ -165,21 +184,22 @@ def _run(wl_name, xname, layer_names):
     pipeline.check_info(buf)
     del Xd
     S_dev = _check_hessian(buf, S_ref, chans, N)
-    U, perm, dead = _check_order_and_U(buf, S_dev, q.perc_damp, q.desc_act)
-    for lname in layer_names:
-        ls = wl.layer(lname)
-        assert ls.m == m0 and ls.n == n
-        W = synth.weight(wl, lname)
-        Wd = torch.from_numpy(W).cuda().to(torch.bfloat16)
-        del W
-        say(wl_name, lname, "quantize + pack", ls.m, n)
-        pipeline.quantize(buf, Wd)
-        pipeline.pack(buf)
-        torch.cuda.synchronize()
-        pipeline.check_info(buf)
-        Wr, Wq_dev, Wq_ref = _check_rows(wl, lname, buf, U, perm, dead)
-        _recon_close(Wr, Wq_dev, Wq_ref, S_dev)
-        del Wd
+    U32, perm, dead = _check_order_and_U(buf, S_dev, q.perc_damp, q.desc_act)
+    with oracle_rows.RowPool(U32) as pool:
+        del U32
+        for lname in layer_names:
+            ls = wl.layer(lname)
+            assert ls.m == m0 and ls.n == n
+            W = synth.weight(wl, lname)
+            Wd = torch.from_numpy(W).cuda().to(torch.bfloat16)
+            del W
+            say(wl_name, lname, "quantize + pack", ls.m, n)
+            pipeline.quantize(buf, Wd)
+            pipeline.pack(buf)
+            torch.cuda.synchronize()
+            pipeline.check_info(buf)
+            _check_rows(wl, lname, buf, pool, perm, dead, S_dev)
+            del Wd
 
 
 def test_llama7b_mlp_gate_up_full_size():
