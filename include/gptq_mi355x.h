@@ -14,7 +14,9 @@
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer (HBM) owned by the caller.  The
  *    library never allocates device memory: scratch space comes from a
- *    caller-provided workspace whose size the *_workspace_size queries give.
+ *    caller-provided workspace whose size the *_workspace_size queries give
+ *    (gptq_quantize_layer_noalloc instead uses a fixed array of device memory
+ *    that is part of the library's device code).
  *  - Matrices are row-major with an explicit leading dimension (in elements).
  *  - All work is enqueued on `stream` (NULL = the default stream); calls return
  *    without synchronizing.  Argument errors are detected on the host and
@@ -36,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00020003u /* major 2, minor 3 */
+#define GPTQ_ABI_VERSION 0x00020004u /* major 2, minor 4 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -157,6 +159,32 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_
                                 const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
                                 float* scales, float* zeros, int32_t* g_idx, float* row_err,
                                 int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gptq_quantize_layer without allocation.  For callers that cannot allocate
+ * device memory or take a workspace from an allocator: code under HIP graph
+ * capture, tight loops, harnesses that forbid hipMalloc.  Same arguments,
+ * outputs and kernels as gptq_quantize_layer, minus the workspace: the
+ * column loop's scratch is a fixed array of GPTQ_NOALLOC_SCRATCH_BYTES of
+ * device memory owned by the library, one copy per GPU, held from the first
+ * call on that GPU until the process ends.  The call allocates nothing and
+ * frees nothing.
+ * Limit: layers whose gptq_quantize_workspace_size exceeds
+ * GPTQ_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. m * n up to about 11.7 M weights
+ * without desc_act, 9.4 M with it; 4096 x 2048 fits, 4096 x 4096 does not)
+ * return GPTQ_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch (it keeps the last call's
+ * contents; every part a call reads is written by the call first): calls
+ * that overlap in time on one GPU -- on different streams, or from several
+ * host threads without ordering -- race and must not be issued.
+ * ---------------------------------------------------------------------- */
+#define GPTQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+gptq_status gptq_quantize_layer_noalloc(const void* W, gptq_dtype wdt, int64_t m, int64_t n,
+                                        int64_t ldw, const float* U, int64_t ldu,
+                                        const int32_t* perm, const uint8_t* dead,
+                                        const gptq_config* cfg, uint8_t* codes, float* scales,
+                                        float* zeros, int32_t* g_idx, float* row_err,
+                                        int32_t* info, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Bit packing.  The pages fix the storage cost (b bits per weight plus the

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     awq_lite_workspace_size,
     GPTQConfig,
     GPTQError,
+    GPTQ_ERR_WORKSPACE,
+    GPTQ_NOALLOC_SCRATCH_BYTES,
     gptq_abi_version,
     gptq_dequant_gemm,
     gptq_dequant_gemm_workspace_size,
@@ -30,6 +32,7 @@ from ._lib import (  # noqa: F401
     gptq_prepare,
     gptq_prepare_workspace_size,
     gptq_quantize_layer,
+    gptq_quantize_layer_noalloc,
     gptq_quantize_workspace_size,
     gptq_residual_add,
     gptq_status_str,

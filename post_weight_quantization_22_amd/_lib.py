@@ -35,6 +35,7 @@ EXPORTED = (
     "gptq_prepare",
     "gptq_quantize_workspace_size",
     "gptq_quantize_layer",
+    "gptq_quantize_layer_noalloc",
     "gptq_pack",
     "gptq_pack_ordered",
     "gptq_dequant_gemm_workspace_size",
@@ -109,6 +110,10 @@ def load() -> ctypes.CDLL:
     lib.gptq_quantize_layer.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
                                         ctypes.POINTER(GPTQConfig), _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]
+    lib.gptq_quantize_layer_noalloc.restype = _i32
+    lib.gptq_quantize_layer_noalloc.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
+                                                ctypes.POINTER(GPTQConfig), _vp, _vp, _vp, _vp,
+                                                _vp, _vp, _vp]
     lib.gptq_pack.restype = _i32
     lib.gptq_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
     lib.gptq_pack_ordered.restype = _i32
@@ -337,6 +342,35 @@ def gptq_quantize_layer(W, U, cfg: GPTQConfig, codes, scales, zeros, perm=None, 
                                       _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_err),
                                       _ptr(info), _ptr(ws), nbytes, _stream(stream)),
            "gptq_quantize_layer")
+
+
+GPTQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gptq_quantize_layer_noalloc(W, U, cfg: GPTQConfig, codes, scales, zeros, perm=None,
+                                dead=None, g_idx=None, row_err=None, info=None,
+                                stream=None) -> None:
+    """gptq_quantize_layer on the library's fixed per-GPU scratch: allocates
+    nothing (GPTQ_ERR_WORKSPACE for layers whose workspace exceeds it)."""
+    m, n = W.shape
+    d = W.device
+    ng = _ngroups(n, cfg.group_size)
+    _mat(W, "W", m, n, ("bfloat16", "float32"), d)
+    _mat(U, "U", n, n, ("float32",), d)
+    _buf(codes, "codes", (m, n), ("uint8",), d, optional=False)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _buf(perm, "perm", (n,), _INT32_LIKE, d)
+    _buf(dead, "dead", (n,), ("uint8", "bool"), d)
+    _buf(g_idx, "g_idx", (n,), _INT32_LIKE, d)
+    _buf(row_err, "row_err", (m,), ("float32",), d)
+    _buf(info, "info", (1,), ("int32",), d)
+    _check(load().gptq_quantize_layer_noalloc(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(U),
+                                              _ld(U), _ptr(perm), _ptr(dead), ctypes.byref(cfg),
+                                              _ptr(codes), _ptr(scales), _ptr(zeros),
+                                              _ptr(g_idx), _ptr(row_err), _ptr(info),
+                                              _stream(stream)),
+           "gptq_quantize_layer_noalloc")
 
 
 def gptq_pack(codes, bits: int, packed, stream=None) -> None:

@@ -97,44 +97,8 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wdt, int64_t m, int64_
                                 const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
                                 float* scales, float* zeros, int32_t* g_idx, float* row_err,
                                 int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!cfg || bad_dim(m) || bad_dim(n) || !valid_dtype(wdt)) return GPTQ_ERR_INVALID_ARG;
-  if (cfg->bits < 2 || cfg->bits > 8 || cfg->block_size <= 0 || cfg->group_size == 0 ||
-      cfg->group_size < -1 ||
-      (cfg->group_size > 0 && cfg->block_size % cfg->group_size != 0 &&
-       cfg->group_size % cfg->block_size != 0) ||
-      (cfg->desc_act != 0 && cfg->desc_act != 1) || (cfg->sym != 0 && cfg->sym != 1) ||
-      (cfg->static_groups != 0 && cfg->static_groups != 1))
-    return GPTQ_ERR_INVALID_ARG;
-  if (cfg->block_size != 128 || !quant_group_ok(cfg->group_size)) return GPTQ_ERR_UNSUPPORTED;
-  if (m == 0 || n == 0) return GPTQ_OK;
-  if (!W || !U || !codes || !scales || !zeros || ldw < n || ldu < n) return GPTQ_ERR_INVALID_ARG;
-  if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
-  const gptq_status w = check_ws(ws, ws_bytes, quantize_ws_bytes(m, n, cfg->desc_act));
-  if (w != GPTQ_OK) return w;
-  QuantArgs a;
-  a.W = W;
-  a.wdt = wdt;
-  a.m = m;
-  a.n = n;
-  a.ldw = ldw;
-  a.U = U;
-  a.ldu = ldu;
-  a.perm = perm;
-  a.dead = dead;
-  a.bits = cfg->bits;
-  a.group_size = cfg->group_size;
-  a.block_size = cfg->block_size;
-  a.desc_act = cfg->desc_act;
-  a.sym = cfg->sym;
-  a.static_groups = cfg->group_size > 0 ? cfg->static_groups : 0;
-  a.codes = codes;
-  a.scales = scales;
-  a.zeros = zeros;
-  a.g_idx = g_idx;
-  a.row_err = row_err;
-  a.info = info;
-  a.ws = ws;
-  return hip_status(launch_quantize(a, stream));
+  return quantize_layer_checked(W, wdt, m, n, ldw, U, ldu, perm, dead, cfg, codes, scales, zeros,
+                                g_idx, row_err, info, ws, ws_bytes, stream);
 }
 
 gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int32_t bits, uint32_t* packed,
@@ -335,3 +299,50 @@ gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int6
 }
 
 }  // extern "C"
+
+// Argument checks and launch of gptq_quantize_layer, shared with its
+// no-allocation variant (which passes its static scratch as the workspace).
+gptq_status gptq::quantize_layer_checked(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                                const float* U, int64_t ldu, const int32_t* perm,
+                                const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
+                                float* scales, float* zeros, int32_t* g_idx, float* row_err,
+                                int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!cfg || bad_dim(m) || bad_dim(n) || !valid_dtype(wdt)) return GPTQ_ERR_INVALID_ARG;
+  if (cfg->bits < 2 || cfg->bits > 8 || cfg->block_size <= 0 || cfg->group_size == 0 ||
+      cfg->group_size < -1 ||
+      (cfg->group_size > 0 && cfg->block_size % cfg->group_size != 0 &&
+       cfg->group_size % cfg->block_size != 0) ||
+      (cfg->desc_act != 0 && cfg->desc_act != 1) || (cfg->sym != 0 && cfg->sym != 1) ||
+      (cfg->static_groups != 0 && cfg->static_groups != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (cfg->block_size != 128 || !quant_group_ok(cfg->group_size)) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros || ldw < n || ldu < n) return GPTQ_ERR_INVALID_ARG;
+  if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
+  const gptq_status w = check_ws(ws, ws_bytes, quantize_ws_bytes(m, n, cfg->desc_act));
+  if (w != GPTQ_OK) return w;
+  QuantArgs a;
+  a.W = W;
+  a.wdt = wdt;
+  a.m = m;
+  a.n = n;
+  a.ldw = ldw;
+  a.U = U;
+  a.ldu = ldu;
+  a.perm = perm;
+  a.dead = dead;
+  a.bits = cfg->bits;
+  a.group_size = cfg->group_size;
+  a.block_size = cfg->block_size;
+  a.desc_act = cfg->desc_act;
+  a.sym = cfg->sym;
+  a.static_groups = cfg->group_size > 0 ? cfg->static_groups : 0;
+  a.codes = codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.g_idx = g_idx;
+  a.row_err = row_err;
+  a.info = info;
+  a.ws = ws;
+  return hip_status(launch_quantize(a, stream));
+}

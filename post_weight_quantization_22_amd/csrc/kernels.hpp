@@ -46,6 +46,12 @@ struct QuantArgs {
 };
 size_t quantize_ws_bytes(int64_t m, int64_t n, int desc_act);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// gptq_quantize_layer's argument checks and launch, on the given workspace
+gptq_status quantize_layer_checked(const void* W, gptq_dtype wdt, int64_t m, int64_t n,
+                                   int64_t ldw, const float* U, int64_t ldu, const int32_t* perm,
+                                   const uint8_t* dead, const gptq_config* cfg, uint8_t* codes,
+                                   float* scales, float* zeros, int32_t* g_idx, float* row_err,
+                                   int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream);
 // C[m, n] (row stride ldc) -= A[m, k] (row stride lda, a multiple of 4, A 16-byte
 // aligned) B[k, n] (row stride ldb), fp32 MFMA
 hipError_t gemm_f32_sub(float* C, int64_t ldc, int64_t m, int64_t n, const float* A, int64_t lda,

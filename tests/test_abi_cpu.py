@@ -269,3 +269,27 @@ def test_dense_and_dequantize_argument_validation(lib):
         lib.GPTQ_ERR_INVALID_ARG  # ldp < n bits / 32
     assert so.gptq_dequantize(FAKE, 8, 9, 64, FAKE, FAKE, 4, 64, FAKE, 64, None) == \
         lib.GPTQ_ERR_INVALID_ARG
+
+
+def test_noalloc_quantize_validation(lib):
+    """The no-allocation variant refuses layers beyond its fixed scratch before
+    touching the GPU, and validates its arguments like gptq_quantize_layer."""
+    import ctypes
+
+    so = lib.load()
+    cfg = lib.make_config(4, 128)
+    FAKE = 0x1000
+    # 4096 x 4096: W' alone is 64 MiB, more than the scratch
+    assert so.gptq_quantize_layer_noalloc(FAKE, 1, 4096, 4096, 4096, FAKE, 4096, None, None,
+                                          ctypes.byref(cfg), FAKE, FAKE, FAKE, None, None, None,
+                                          None) == lib.GPTQ_ERR_WORKSPACE
+    assert so.gptq_quantize_layer_noalloc(FAKE, 1, 8, 8, 8, FAKE, 8, None, None, None, FAKE,
+                                          FAKE, FAKE, None, None, None, None) == \
+        lib.GPTQ_ERR_INVALID_ARG
+    assert so.gptq_quantize_layer_noalloc(FAKE, 1, -1, 8, 8, FAKE, 8, None, None,
+                                          ctypes.byref(cfg), FAKE, FAKE, FAKE, None, None, None,
+                                          None) == lib.GPTQ_ERR_INVALID_ARG
+    # the limit the header states
+    need = lib.gptq_quantize_workspace_size(4096, 2048, cfg)
+    assert need <= lib.GPTQ_NOALLOC_SCRATCH_BYTES < lib.gptq_quantize_workspace_size(4096, 4096,
+                                                                                       cfg)
