@@ -255,7 +255,9 @@ def kernel_breakdown(run_once):
         name = ev.key
         if name.startswith("void "):
             name = name[5:]
-        name = name.split("(")[0]
+        name = name.replace("(anonymous namespace)::", "").split("(")[0]
+        if name.startswith("gptq::"):
+            name = name[len("gptq::"):]
         rec = per.setdefault(name, [0.0, 0])
         rec[0] += dt / 1e3
         rec[1] += ev.count

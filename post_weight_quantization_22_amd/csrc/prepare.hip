@@ -19,15 +19,17 @@
 //
 // X = L^-1 in two phases, with 128-wide blocks (block k = rows 128k ..).
 //
-// 1. Blocked right-looking Cholesky.  Step k: the diagonal node kernel turns
-//    the (fully updated) block A_kk into X_kk = L_kk^-1 in one workgroup; the
-//    panel L_ik = A_ik X_kk^T (i > k) is a GEMM, stored in X's block (i, k);
-//    the rank-128 update A_ij -= L_ik L_jk^T (k < j <= i) follows from
-//    A = L L^T.  The update is split so that the next node can start early:
-//    block column k + 1 on the main stream, the rest of the trailing matrix
-//    (columns >= k + 2) on a side stream, where it overlaps node k + 1 and
-//    panel k + 1.  Before the main stream updates column k + 2 it waits for
-//    that side update (both write it).
+// 1. Blocked Cholesky in outer blocks of ob 128-wide blocks (ob = 4 for
+//    large n, else 1).  Step k: the diagonal node kernel turns the (fully
+//    updated) block A_kk into X_kk = L_kk^-1 in one workgroup; the panel
+//    L_ik = A_ik X_kk^T (i > k) is a GEMM, stored in X's block (i, k); the
+//    updates A_ij -= L_ik L_jk^T follow from A = L L^T.  Inside an outer
+//    block they are applied left-looking (block k's columns take the outer
+//    block's earlier panels just before its node); past it, once per outer
+//    block with K = 128 ob: the next outer block's columns on the main stream
+//    (the lookahead), the rest of the trailing matrix on a side stream, where
+//    it overlaps the next outer block.  Before its next lookahead the main
+//    stream waits for that side update (both write those columns).
 // 2. X = L^-1 by groups of GRP blocks (rows c .. c + 512), from L X = I:
 //    X[g, 0:c] = -X_gg L[g, 0:c] X[0:c, 0:c].  Per group, on a third stream:
 //      X_gg, the inverse of the group's own diagonal block, joins the nodes'
@@ -95,8 +97,8 @@ PrepWs carve(void* ws, int64_t n) {
 struct SideStream {
   hipStream_t s = nullptr;    // trailing updates
   hipStream_t inv = nullptr;  // block rows of X
-  hipEvent_t step_done;       // main -> s, inv: panel k and column k + 1 are done
-  hipEvent_t trailing_done;   // s -> main: trailing update k is applied
+  hipEvent_t step_done;       // main -> s, inv: an outer block's panels and lookahead are done
+  hipEvent_t trailing_done;   // s -> main: the trailing update is applied
   hipEvent_t last_node;       // main -> inv: the last node is done
   hipEvent_t inv_done;        // inv -> main: the last group of X is written
   std::mutex run;             // one call at a time enqueues on a device's side streams
@@ -942,6 +944,151 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
   else hipLaunchKernelGGL((gemm_splitk_kernel<TILE, false>), grid, dim3(256), 0, stream, g);
 }
 
+// Large products (the trailing updates and the inverse's block-row products
+// at large n): 128 x 128 output tiles, 4 waves of 64 x 64, each a 4 x 4 grid
+// of v_mfma_f64_16x16x4_f64 accumulators.  K goes through LDS in stages of 16,
+// double-buffered: a stage is fetched into registers (16-byte loads) while
+// the previous one is multiplied, then stored k-major (As[k][i], Bs[k][j]),
+// one barrier per stage.  The LDS row stride of 144 doubles puts two
+// consecutive k rows on opposite halves of the 64 banks, so the 16 x 4
+// operand reads of a half-wave are conflict-free.  op(A) is A itself
+// (row-major, A[i * lda + k]); op(B) as in gemm_f64_kernel.  Needs even
+// leading dimensions and 16-byte aligned A, B (checked by the caller).
+constexpr int BIG = 128;   // tile edge
+constexpr int BKC = 16;    // K per stage
+constexpr int BLD = 144;   // LDS row stride (doubles)
+
+template <bool TB>
+__global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
+  __shared__ __align__(16) double As[2][BKC][BLD];
+  __shared__ __align__(16) double Bs[2][BKC][BLD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wr = wv >> 1, wc = wv & 1;
+  // loader roles: "row" loads (8 consecutive k of one row i / column j) and
+  // "k-row" loads (8 consecutive i / j of one k)
+  const int rl_i = tid >> 1, rl_k = (tid & 1) * 8;   // row loads
+  const int kl_k = tid >> 4, kl_i = (tid & 15) * 8;  // k-row loads
+  for (int64_t bid = blockIdx.x; bid < g.tiles; bid += gridDim.x) {
+    int64_t ti, tj;
+    gemm_tile_of(g, bid, ti, tj);
+    const int64_t i0 = ti * BIG, j0 = tj * BIG;
+    int64_t kb = 0, ke = g.K;
+    if (g.kmode & KLO_J) kb = j0;
+    if (g.kmode & KHI_J) ke = min(ke, j0 + BIG);
+    if (g.kmode & KHI_I) ke = min(ke, i0 + BIG);
+    f64x4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double ra[8], rb[8];
+    // op(A) row i0 + rl_i, k = k0 + rl_k .. + 7
+    const int64_t ai = i0 + rl_i;
+    const bool a_ok = ai < g.M;
+    const double* arow = g.A + (a_ok ? ai : 0) * g.lda;
+    // op(B): TB -> row j0 + rl_i of B, k = k0 + rl_k ..; else k-row k0 + kl_k, j = j0 + kl_i ..
+    const int64_t bj = j0 + (TB ? rl_i : kl_i);
+    const bool b_ok = TB ? bj < g.N : true;
+    const double* brow = TB ? g.B + (b_ok ? bj : 0) * g.ldb : g.B;
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int64_t k = k0 + rl_k + 2 * p;
+        if (a_ok && k + 1 < ke) {
+          const double2 v = *reinterpret_cast<const double2*>(arow + k);
+          ra[2 * p] = v.x;
+          ra[2 * p + 1] = v.y;
+        } else {
+          ra[2 * p] = (a_ok && k < ke) ? arow[k] : 0.0;
+          ra[2 * p + 1] = 0.0;
+        }
+      }
+      if (TB) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int64_t k = k0 + rl_k + 2 * p;
+          if (b_ok && k + 1 < ke) {
+            const double2 v = *reinterpret_cast<const double2*>(brow + k);
+            rb[2 * p] = v.x;
+            rb[2 * p + 1] = v.y;
+          } else {
+            rb[2 * p] = (b_ok && k < ke) ? brow[k] : 0.0;
+            rb[2 * p + 1] = 0.0;
+          }
+        }
+      } else {
+        const int64_t k = k0 + kl_k;
+        const bool kin = k < ke;
+        const double* src = g.B + (kin ? k : kb) * g.ldb;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int64_t j = bj + 2 * p;
+          if (kin && j + 1 < g.N) {
+            const double2 v = *reinterpret_cast<const double2*>(src + j);
+            rb[2 * p] = v.x;
+            rb[2 * p + 1] = v.y;
+          } else {
+            rb[2 * p] = (kin && j < g.N) ? src[j] : 0.0;
+            rb[2 * p + 1] = 0.0;
+          }
+        }
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) As[buf][rl_k + e][rl_i] = ra[e];
+      if (TB) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bs[buf][rl_k + e][rl_i] = rb[e];
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          *reinterpret_cast<double2*>(&Bs[buf][kl_k][kl_i + 2 * p]) =
+              make_double2(rb[2 * p], rb[2 * p + 1]);
+      }
+    };
+    __syncthreads();  // the previous tile's last stage has been read by every wave
+    if (kb < ke) fetch(kb);
+    int buf = 0;
+    for (int64_t k0 = kb; k0 < ke; k0 += BKC, buf ^= 1) {
+      stash(buf);
+      __syncthreads();
+      if (k0 + BKC < ke) fetch(k0 + BKC);
+#pragma unroll
+      for (int ks = 0; ks < BKC; ks += 4) {
+        double af[4], bf[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) af[a] = As[buf][ks + (lane >> 4)][64 * wr + 16 * a + (lane & 15)];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][64 * wc + 16 * b + (lane & 15)];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
+      }
+    }
+    // D layout of the f64 16x16x4 MFMA: lane l, element q -> row l/16 + 4q, column l%16
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gi = i0 + 64 * wr + 16 * a + (lane >> 4) + 4 * q;
+          const int64_t gj = j0 + 64 * wc + 16 * b + (lane & 15);
+          if (gi >= g.M || gj >= g.N) continue;
+          if (g.lower && gj > gi) continue;
+          double* c = g.C + gi * g.ldc + gj;
+          const double v = g.alpha * acc[a][b][q];
+          *c = g.beta == 0.0 ? v : fma(g.beta, *c, v);
+        }
+  }
+}
+
+// Products with at least this many 128 x 128 tiles take gemm_f64_big_kernel.
+constexpr int64_t BIG_MIN_TILES = 256;
+
 // The two products on the factorization's critical path, the panel
 // L_k = A_k X_kk^T and the next column's update A[:, k+1] -= L_k L_{k+1,k}^T,
 // are M x 128 x 128 (M up to n - 128): C[M, 128] = alpha A[M, 128] op(B) + beta
@@ -1065,8 +1212,23 @@ hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t 
   // (Measured on products of 128 to 2048; 128-wide tiles lost at every size.)
   const int64_t t64 = lower ? ceil_div(M, 64) * (ceil_div(M, 64) + 1) / 2
                             : ceil_div(M, 64) * ceil_div(N, 64);
-  if (!ta && t64 < 256) launch_splitk<32>(g, tb, max_wg, stream);
-  else launch_gemm_tile<64>(g, ta, tb, max_wg, stream);
+  const int64_t tm = ceil_div(M, BIG), tn = ceil_div(N, BIG);
+  const int64_t t128 = lower ? tm * (tm + 1) / 2 : tm * tn;
+  const bool big_ok = !ta && lda % 2 == 0 && ldb % 2 == 0 &&
+                      reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(B) % 16 == 0;
+  if (big_ok && t128 >= BIG_MIN_TILES) {
+    g.tiles_m = tm;
+    g.tiles_n = tn;
+    g.tiles = t128;
+    const dim3 grid((unsigned)(max_wg > 0 ? hmin(t128, max_wg) : t128));
+    if (tb) hipLaunchKernelGGL(gemm_f64_big_kernel<true>, grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL(gemm_f64_big_kernel<false>, grid, dim3(256), 0, stream, g);
+  } else if (!ta && t64 < 256) {
+    launch_splitk<32>(g, tb, max_wg, stream);
+  } else {
+    launch_gemm_tile<64>(g, ta, tb, max_wg, stream);
+  }
   return hipGetLastError();
 }
 
@@ -1101,13 +1263,27 @@ hipError_t invert_group_diag(const PrepWs& w, int64_t n, int64_t b0, int64_t cnt
 }
 
 // Both phases: X's diagonal blocks from the nodes, L's panels into X's lower
-// blocks, then X group by group over them.  The node kernel needs a CU of its
-// own (most of the LDS), so the large products of the other two streams are
-// released only when the main stream reaches the node (after the column
-// update of step k): launched earlier they would fill every CU first.
+// blocks, then X group by group over them.
+//
+// The factorization runs in outer blocks of `ob` 128-wide blocks.  Inside an
+// outer block it is left-looking: before block k's node, its columns receive
+// the updates of the outer block's earlier panels in one product (K = 128 j
+// for the j-th block), then the node and the panel.  Past the outer block the
+// updates go out with K = 128 ob: the next outer block's columns on the main
+// stream (the lookahead, which the next nodes need) and everything beyond on
+// the side stream, overlapping the next outer block; the main stream waits
+// for the side stream's previous update before its lookahead (both write
+// those columns).  With ob = 4 (large n) the trailing matrix is read and
+// written once per 512 columns instead of once per 128, which is what bounds
+// the rank-128 update in fp64; with ob = 1 (small n) the chain per 128
+// columns is shortest.  The side products are released once the main stream
+// has finished its lookahead and is about to start the next node.
 hipError_t factor_invert(const PrepWs& w, int64_t n, int32_t* info, hipStream_t stream,
                          SideStream* side) {
   const int64_t nb = ceil_div(n, NODE);
+  // measured: 8192 x 8192 prepare 13.6 ms with 4, 15.2 ms with 1; 4096 x 4096 about the
+  // same either way (the node chain bounds it)
+  const int64_t ob = n >= 6144 ? 4 : 1;
   double* Mg = w.M;
   double* Mj = w.M + GRP * NODE * n;
   auto node = [&](int64_t k) {
@@ -1128,66 +1304,98 @@ hipError_t factor_invert(const PrepWs& w, int64_t n, int32_t* info, hipStream_t 
     return e;
   };
   // M_g = L[g, 0:c] X[0:c, 0:c] (X(r, j) = 0 for r < j): needs the groups above
-  // and the panels of L in the group's rows, the last of them by step c / 128 - 1
+  // and the panels of L in the group's rows, all written once group g - 1's
+  // last node and panel are
   auto group_head = [&](int64_t g) {
     const int64_t c = NODE * GRP * g, sg = hmin(n, c + GRP * NODE) - c;
     return gemm(w.X + c * n, n, false, w.X, n, false, Mg, c, sg, c, c, 1.0, 0.0, KLO_J, false,
                 side->inv);
   };
-  hipError_t e = node(0);
+  // the whole-K product needs 16-byte aligned rows for its staged loads
+  const bool tall = n % 2 == 0;
+  hipError_t e = hipSuccess;
   bool pending = false;  // a trailing update is queued on the side stream
-  for (int64_t k = 0; k + 1 < nb && e == hipSuccess; ++k) {
-    const int64_t bk = NODE * k, r1 = bk + NODE, rows = n - r1;
-    const int64_t s1 = hmin(rows, (int64_t)NODE);  // width of block k + 1
-    double* Lk = w.X + r1 * n + bk;                 // panel k: rows r1.., 128 columns
-    // L_ik = A_ik X_kk^T  (X_kk(j, c) = 0 for c > j)
-    // (X_kk's upper part is stored as zeros, so the whole-K product is exact)
-    // the whole-K product wins over the split-K one at the first steps' tall
-    // panels (measured: 10.7 vs 13.3 us at 3968 rows, 9.9 vs 8.4 us at 512);
-    // it needs 16-byte aligned rows for its staged loads
-    const bool tall = n % 2 == 0;
-    if (tall && rows >= 3072) {
-      gemm_tall128(w.A + r1 * n + bk, n, w.X + bk * n + bk, n, Lk, n, rows, 1.0, 0.0, stream);
-      e = hipGetLastError();
-    } else {
-      e = gemm(w.A + r1 * n + bk, n, false, w.X + bk * n + bk, n, true, Lk, n, rows, NODE, NODE,
-               1.0, 0.0, KHI_J, false, stream);
+  int64_t groups_done = 0;  // groups whose inverse is enqueued
+  for (int64_t k0 = 0; k0 < nb && e == hipSuccess; k0 += ob) {
+    const int64_t k1 = hmin(nb, k0 + ob);
+    const int64_t c0 = NODE * k0;  // first column of the outer block
+    for (int64_t k = k0; k < k1 && e == hipSuccess; ++k) {
+      const int64_t rk = NODE * k, sk = hmin(n - rk, (int64_t)NODE);
+      if (k > k0) {
+        // A[rk.., k] -= L[rk.., k0..k) L[k, k0..k)^T: the outer block's earlier panels
+        // (stored in X's blocks), the diagonal block's upper part included (never read)
+        const double* Lr = w.X + rk * n + c0;
+        const int64_t K = rk - c0;
+        if (tall && K == NODE && sk == NODE && n - rk >= 1024) {
+          gemm_tall128(Lr, n, Lr, n, w.A + rk * n + rk, n, n - rk, -1.0, 1.0, stream);
+          e = hipGetLastError();
+        } else {
+          e = gemm(Lr, n, false, Lr, n, true, w.A + rk * n + rk, n, n - rk, sk, K, -1.0, 1.0, 0,
+                   false, stream);
+        }
+      }
+      if (e == hipSuccess) e = node(k);
+      const int64_t r1 = rk + NODE;
+      if (e == hipSuccess && r1 < n) {
+        // L_ik = A_ik X_kk^T  (X_kk(j, c) = 0 for c > j, stored as zeros: whole-K exact)
+        const int64_t rows = n - r1;
+        double* Lk = w.X + r1 * n + rk;
+        if (tall && rows >= 3072) {
+          gemm_tall128(w.A + r1 * n + rk, n, w.X + rk * n + rk, n, Lk, n, rows, 1.0, 0.0, stream);
+          e = hipGetLastError();
+        } else {
+          e = gemm(w.A + r1 * n + rk, n, false, w.X + rk * n + rk, n, true, Lk, n, rows, NODE,
+                   NODE, 1.0, 0.0, KHI_J, false, stream);
+        }
+      }
     }
-    // column k + 1 is also written by the trailing update of step k - 1
-    if (e == hipSuccess && pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
-    // A[:, k+1] -= L_k L_{k+1,k}^T  (rows r1..; the diagonal block's upper part is not read)
+    if (e != hipSuccess) break;
+    const int64_t R = NODE * k1;  // first column past the outer block
+    if (R >= n) break;
+    const int64_t R2 = hmin(n, NODE * hmin(nb, k1 + ob));  // end of the next outer block
+    const double* Lo = w.X + R * n + c0;                   // L[R.., outer block]
+    const int64_t K = R - c0;
+    // lookahead: the next outer block's columns (also written by the previous
+    // trailing update, which must be applied first)
+    if (pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
     if (e == hipSuccess) {
-      if (tall && s1 == NODE && rows >= 1024) {  // 11.8 vs 25.8 us at 3968 rows, 10.7 vs 10.1 at 512
-        gemm_tall128(Lk, n, Lk, n, w.A + r1 * n + r1, n, rows, -1.0, 1.0, stream);
+      if (tall && K == NODE && R2 - R == NODE && n - R >= 1024) {
+        gemm_tall128(Lo, n, Lo, n, w.A + R * n + R, n, n - R, -1.0, 1.0, stream);
         e = hipGetLastError();
       } else {
-        e = gemm(Lk, n, false, Lk, n, true, w.A + r1 * n + r1, n, rows, s1, NODE, -1.0, 1.0, 0,
+        e = gemm(Lo, n, false, Lo, n, true, w.A + R * n + R, n, n - R, R2 - R, K, -1.0, 1.0, 0,
                  false, stream);
       }
     }
+    // release the side streams as the next node starts
     if (e == hipSuccess) e = hipEventRecord(side->step_done, stream);
-    if (e == hipSuccess) e = node(k + 1);
-    const int64_t r2 = r1 + NODE;
-    if (e == hipSuccess && r2 < n) {
-      // A[r2.., r2..] -= L_k L_k^T (lower tiles), off the critical path
+    // everything past the next outer block, off the critical path
+    if (e == hipSuccess && R2 < n) {
       e = hipStreamWaitEvent(side->s, side->step_done, 0);
+      const double* L2 = w.X + R2 * n + c0;
       if (e == hipSuccess)
-        e = gemm(w.X + r2 * n + bk, n, false, w.X + r2 * n + bk, n, true, w.A + r2 * n + r2, n,
-                 n - r2, n - r2, NODE, -1.0, 1.0, 0, true, side->s);
+        e = gemm(L2, n, false, L2, n, true, w.A + R2 * n + R2, n, n - R2, n - R2, K, -1.0, 1.0, 0,
+                 true, side->s);
       if (e == hipSuccess) e = hipEventRecord(side->trailing_done, side->s);
       pending = true;
     }
-    if (e == hipSuccess && k % GRP == GRP - 1) {  // node k closed group k / GRP
+    // groups whose blocks are all factored: their inverse, and the next group's head
+    const int64_t gready = k1 / GRP;
+    if (e == hipSuccess && gready > groups_done)
       e = hipStreamWaitEvent(side->inv, side->step_done, 0);
-      if (e == hipSuccess) e = group_tail(k / GRP);
-      if (e == hipSuccess) e = group_head(k / GRP + 1);
+    for (; groups_done < gready && e == hipSuccess; ++groups_done) {
+      e = group_tail(groups_done);
+      if (e == hipSuccess) e = group_head(groups_done + 1);
     }
   }
   if (e == hipSuccess && pending) e = hipStreamWaitEvent(stream, side->trailing_done, 0);
   // the last group, closed by node nb - 1
   if (e == hipSuccess) e = hipEventRecord(side->last_node, stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side->inv, side->last_node, 0);
-  if (e == hipSuccess) e = group_tail((nb - 1) / GRP);
+  for (; groups_done <= (nb - 1) / GRP && e == hipSuccess; ++groups_done) {
+    e = group_tail(groups_done);
+    if (e == hipSuccess && groups_done < (nb - 1) / GRP) e = group_head(groups_done + 1);
+  }
   if (e == hipSuccess) e = hipEventRecord(side->inv_done, side->inv);
   if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->inv_done, 0);
   return e;

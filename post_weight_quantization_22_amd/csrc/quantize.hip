@@ -112,6 +112,96 @@ __global__ __launch_bounds__(256) void prep_weights_bf16_kernel(const uint16_t* 
   if (bad && info) *info = -1;
 }
 
+// W' = W[:, perm] as fp32 for bf16 W with desc_act, a row at a time through
+// LDS: the row comes in by coalesced 16-byte loads (the next row's already in
+// flight), is staged in LDS, and leaves in processing order by 16-byte stores
+// of 8 fp32 values, the permuted reads served by the LDS.  Each thread keeps
+// the source columns of its output segments in registers for all its rows
+// (16-bit entries: the column in bits 0-14, the dead flag in bit 15), so the
+// permutation is read once per workgroup (512 threads).  Needs n % 8 == 0,
+// n <= NCAP <= 32768, 16-byte aligned rows.  Every weight is checked for finiteness (dead
+// columns included) before a dead column is zeroed.
+template <int NCAP>
+__global__ __launch_bounds__(512) void prep_rows_bf16_kernel(const uint16_t* __restrict__ W,
+                                                             int64_t ldw,
+                                                             const int32_t* __restrict__ perm,
+                                                             const uint8_t* __restrict__ dead,
+                                                             int64_t m, int64_t n,
+                                                             int64_t rows_per_wg,
+                                                             float* __restrict__ Wp,
+                                                             int32_t* __restrict__ info) {
+  constexpr int CH = NCAP / 8 / 512;  // 16-byte chunks (8 columns) of a row per thread
+  static_assert(NCAP <= 32768, "15-bit column entries");
+  __shared__ __align__(16) uint16_t buf[2][NCAP];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t r1 = min(m, r0 + rows_per_wg);
+  if (r0 >= r1) return;
+  const int nseg = (int)(n / 8);
+  uint32_t pk[CH][4];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int sg = tid + 512 * i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t p = 8 * (int64_t)sg + 2 * q + e;
+        uint32_t v = 0;
+        if (sg < nseg) {
+          int64_t src = perm[p];
+          if (src < 0 || src >= n) src = p;  // a malformed permutation must not address out of range
+          v = (uint32_t)src | ((dead && dead[src]) ? 0x8000u : 0u);
+        }
+        h[e] = v;
+      }
+      pk[i][q] = h[0] | (h[1] << 16);
+    }
+  }
+  uint4 v[CH];
+  auto fetch = [&](int64_t r) {
+    const uint4* src = reinterpret_cast<const uint4*>(W + r * ldw);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 512 * c;
+      if (idx < nseg) v[c] = src[idx];
+    }
+  };
+  bool bad = false;
+  fetch(r0);
+  for (int64_t r = r0; r < r1; ++r) {
+    uint16_t* b = buf[(r - r0) & 1];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 512 * c;
+      if (idx < nseg) reinterpret_cast<uint4*>(b)[idx] = v[c];
+    }
+    if (r + 1 < r1) fetch(r + 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int sg = tid + 512 * i;
+      if (sg < nseg) {
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t h = (pk[i][q] >> (16 * e)) & 0xFFFFu;
+            const float x = bf16_bits_to_f32(b[h & 0x7FFFu]);
+            bad |= !isfinite(x);
+            f[2 * q + e] = (h & 0x8000u) ? 0.0f : x;
+          }
+        float4* o = reinterpret_cast<float4*>(Wp + r * n + 8 * (int64_t)sg);
+        o[0] = make_float4(f[0], f[1], f[2], f[3]);
+        o[1] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+  }
+  if (bad && info) *info = -1;
+}
+
 // Parameters of one group per row from the current values of columns
 // [c0, c0 + len) of W': the whole row (one group per row), or a group that
 // spans several blocks (its first column is a block start).  Written to
@@ -554,6 +644,72 @@ __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
   if (p >= 0 && p < n) inv[p] = (int32_t)k;
 }
 
+// codes[r, c] = codes_proc[r, inv[c]] a row at a time through LDS: the
+// processing-order row comes in by coalesced 16-byte loads (the next row's in
+// flight), is staged in LDS, and leaves in original order by 16-byte stores
+// (16 codes), the permuted reads served by the LDS.  The source positions
+// (16-bit) sit in LDS too, read once per workgroup.  Needs n % 16 == 0, n <=
+// NCAP <= 32768.  g_idx is written by unpermute_kernel's g_idx-only form.
+template <int NCAP>
+__global__ __launch_bounds__(512) void unpermute_rows_kernel(const uint8_t* __restrict__ cproc,
+                                                             const int32_t* __restrict__ inv,
+                                                             int64_t m, int64_t n,
+                                                             int64_t rows_per_wg,
+                                                             uint8_t* __restrict__ codes) {
+  constexpr int CH = NCAP / 16 / 512;  // 16-byte chunks (16 codes) of a row per thread
+  static_assert(NCAP <= 32768, "16-bit position entries");
+  __shared__ __align__(16) uint8_t buf[2][NCAP];
+  __shared__ __align__(16) uint16_t pos[NCAP];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t r1 = min(m, r0 + rows_per_wg);
+  if (r0 >= r1) return;
+  const int nseg = (int)(n / 16);
+  for (int64_t c = tid; c < n; c += 512) {
+    int64_t k = inv[c];
+    if (k < 0 || k >= n) k = c;  // a malformed permutation must not address out of range
+    pos[c] = (uint16_t)k;
+  }
+  uint4 v[CH];
+  auto fetch = [&](int64_t r) {
+    const uint4* src = reinterpret_cast<const uint4*>(cproc + r * n);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 512 * c;
+      if (idx < nseg) v[c] = src[idx];
+    }
+  };
+  fetch(r0);
+  for (int64_t r = r0; r < r1; ++r) {
+    uint8_t* b = buf[(r - r0) & 1];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 512 * c;
+      if (idx < nseg) reinterpret_cast<uint4*>(b)[idx] = v[c];
+    }
+    if (r + 1 < r1) fetch(r + 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int sg = tid + 512 * i;
+      if (sg < nseg) {
+        const uint4 p0 = reinterpret_cast<const uint4*>(pos)[2 * sg];
+        const uint4 p1 = reinterpret_cast<const uint4*>(pos)[2 * sg + 1];
+        const uint32_t pk[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a = pk[2 * q], c2 = pk[2 * q + 1];
+          w[q] = (uint32_t)b[a & 0xFFFFu] | ((uint32_t)b[a >> 16] << 8) |
+                 ((uint32_t)b[c2 & 0xFFFFu] << 16) | ((uint32_t)b[c2 >> 16] << 24);
+        }
+        *reinterpret_cast<uint4*>(codes + r * n + 16 * (int64_t)sg) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
 // codes[r, c] = codes_proc[r, inv[c]]; g_idx[c] = inv[c] / G (static groups:
 // c / G, the groups being runs of original columns).
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ cproc,
@@ -616,6 +772,20 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)ceil_div(n, 8 * 256), (unsigned)hmin(m, 1024));
     hipLaunchKernelGGL(prep_weights_bf16_kernel, grid, dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(a.W), m, n, a.ldw, a.dead, Wp, a.info);
+  } else if (a.wdt == GPTQ_BF16 && a.desc_act && n % 8 == 0 && a.ldw % 8 == 0 &&
+             reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && n <= 32768) {
+    // permuted rows through LDS: 32 KB per workgroup up to 8192 columns, else 128 KB
+    const int64_t wgs = hmin(m, n <= 8192 ? 512 : 256);
+    const int64_t rpw = ceil_div(m, wgs);
+    const dim3 grid((unsigned)ceil_div(m, rpw));
+    if (n <= 8192)
+      hipLaunchKernelGGL(prep_rows_bf16_kernel<8192>, grid, dim3(512), 0, stream,
+                         reinterpret_cast<const uint16_t*>(a.W), a.ldw, a.perm, a.dead, m, n, rpw,
+                         Wp, a.info);
+    else
+      hipLaunchKernelGGL(prep_rows_bf16_kernel<32768>, grid, dim3(512), 0, stream,
+                         reinterpret_cast<const uint16_t*>(a.W), a.ldw, a.perm, a.dead, m, n, rpw,
+                         Wp, a.info);
   } else {
     const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(m, 1024));
     hipLaunchKernelGGL(prep_weights_kernel, grid, dim3(256), 0, stream, a.W, a.wdt, m, n, a.ldw,
@@ -672,9 +842,26 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   if (a.desc_act) {
     hipLaunchKernelGGL(invert_perm_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
                        a.perm, n, inv);
-    const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(m, 1024));
-    hipLaunchKernelGGL(unpermute_kernel, grid, dim3(256), 0, stream, cproc, inv, m, n,
-                       (int64_t)G, a.static_groups, a.codes, a.g_idx);
+    if (n % 16 == 0 && n <= 32768) {
+      // codes through LDS rows; g_idx by the per-column kernel alone
+      const int64_t wgs = hmin(m, n <= 16384 ? 512 : 256);
+      const int64_t rpw = ceil_div(m, wgs);
+      const dim3 grid((unsigned)ceil_div(m, rpw));
+      if (n <= 16384)
+        hipLaunchKernelGGL(unpermute_rows_kernel<16384>, grid, dim3(512), 0, stream, cproc, inv,
+                           m, n, rpw, a.codes);
+      else
+        hipLaunchKernelGGL(unpermute_rows_kernel<32768>, grid, dim3(512), 0, stream, cproc, inv,
+                           m, n, rpw, a.codes);
+      if (a.g_idx)
+        hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)ceil_div(n, 256), 1), dim3(256), 0,
+                           stream, (const uint8_t*)nullptr, inv, (int64_t)0, n, (int64_t)G,
+                           a.static_groups, (uint8_t*)nullptr, a.g_idx);
+    } else {
+      const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)hmin(m, 1024));
+      hipLaunchKernelGGL(unpermute_kernel, grid, dim3(256), 0, stream, cproc, inv, m, n,
+                         (int64_t)G, a.static_groups, a.codes, a.g_idx);
+    }
   } else if (a.g_idx) {
     hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)ceil_div(n, 256), 1), dim3(256), 0, stream,
                        (const uint8_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, n, (int64_t)G,

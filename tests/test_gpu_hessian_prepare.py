@@ -87,6 +87,8 @@ PREP_CASES = [
     (64, 256, False, 0.1),
     (1, 10, False, 0.01),
     (130, 2048, False, 0.0),
+    (4500, 9000, True, 0.01),    # trailing updates on the 128 x 128-tile product, ragged
+    (8448, 9000, False, 0.01),   # the inverse's block-row products on it as well
 ]
 
 
