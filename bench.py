@@ -110,6 +110,14 @@ COPY_BYTES = 1 << 31  # the calibration copy of --traffic-probe
 HESS_KERNELS = ("syrk_bf16_dma_kernel", "reduce_full_partials_kernel")
 
 
+def short_kernel_name(name: str) -> str:
+    """A kernel's name without return type, namespaces and argument list."""
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return name[len("gptq::"):] if name.startswith("gptq::") else name
+
+
 def traffic_record(fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes of one Hessian launch from two counter runs of --traffic-probe.
 
@@ -155,7 +163,7 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
         for d, v in val.items():
             if "copyBuffer" in name[d]:
                 continue
-            per_kernel[name[d].split("(")[0]] += v * 1024.0 * factor
+            per_kernel[short_kernel_name(name[d])] += v * 1024.0 * factor
         out[counter] = {"hessian_kib": hess, "copy_kib": copy_kib, "scale": factor,
                         "bytes": hess * 1024.0 * factor, "per_kernel_bytes": dict(per_kernel)}
     return out
@@ -252,12 +260,7 @@ def kernel_breakdown(run_once):
             dt = getattr(ev, "cuda_time_total", 0.0)
         if not dt:
             continue
-        name = ev.key
-        if name.startswith("void "):
-            name = name[5:]
-        name = name.replace("(anonymous namespace)::", "").split("(")[0]
-        if name.startswith("gptq::"):
-            name = name[len("gptq::"):]
+        name = short_kernel_name(ev.key)
         rec = per.setdefault(name, [0.0, 0])
         rec[0] += dt / 1e3
         rec[1] += ev.count

@@ -945,8 +945,9 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
 }
 
 // Large products (the trailing updates and the inverse's block-row products
-// at large n): 128 x 128 output tiles, 4 waves of 64 x 64, each a 4 x 4 grid
-// of v_mfma_f64_16x16x4_f64 accumulators.  K goes through LDS in stages of 16,
+// at large n): 128 x 128 output tiles, NW waves (8: waves of 64 x 32, four
+// per SIMD at two workgroups per CU; 4: waves of 64 x 64), each a grid of
+// v_mfma_f64_16x16x4_f64 accumulators.  K goes through LDS in stages of 16,
 // double-buffered: a stage is fetched into registers (16-byte loads) while
 // the previous one is multiplied, then stored k-major (As[k][i], Bs[k][j]),
 // one barrier per stage.  The LDS row stride of 144 doubles puts two
@@ -954,20 +955,31 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
 // operand reads of a half-wave are conflict-free.  op(A) is A itself
 // (row-major, A[i * lda + k]); op(B) as in gemm_f64_kernel.  Needs even
 // leading dimensions and 16-byte aligned A, B (checked by the caller).
+// (Measured, 20480-wide products: 8 waves 49 TF/s against 41 for 4 on the
+// K = 512 trailing update, 41 against 35 on the inverse's head product; an
+// LDS-DMA variant with four stages in flight at one workgroup per CU was
+// slower than both.)
 constexpr int BIG = 128;   // tile edge
 constexpr int BKC = 16;    // K per stage
 constexpr int BLD = 144;   // LDS row stride (doubles)
 
-template <bool TB>
-__global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
+template <bool TB, int NW>
+__global__ __launch_bounds__(64 * NW, NW / 2) void gemm_f64_big_kernel(GemmArgs g) {
+  // NW = 4: waves of 64 x 64 (2 x 2); NW = 8: waves of 64 x 32 (2 x 4)
+  constexpr int NT = 64 * NW;           // threads
+  constexpr int WCOL = 128 / (NW / 2);  // columns per wave
+  constexpr int NB = WCOL / 16;         // MFMA tiles per wave row
+  constexpr int PER = BIG * BKC / NT;   // doubles per thread per operand per stage
+  constexpr int RPT = BKC / PER;        // threads per row in the row loads
+  constexpr int KPT = BIG / PER;        // threads per k-row in the k-row loads
   __shared__ __align__(16) double As[2][BKC][BLD];
   __shared__ __align__(16) double Bs[2][BKC][BLD];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wr = wv >> 1, wc = wv & 1;
-  // loader roles: "row" loads (8 consecutive k of one row i / column j) and
-  // "k-row" loads (8 consecutive i / j of one k)
-  const int rl_i = tid >> 1, rl_k = (tid & 1) * 8;   // row loads
-  const int kl_k = tid >> 4, kl_i = (tid & 15) * 8;  // k-row loads
+  const int wr = wv / (NW / 2), wc = wv % (NW / 2);
+  // loader roles: "row" loads (PER consecutive k of one row i / column j) and
+  // "k-row" loads (PER consecutive i / j of one k)
+  const int rl_i = tid / RPT, rl_k = (tid % RPT) * PER;  // row loads
+  const int kl_k = tid / KPT, kl_i = (tid % KPT) * PER;  // k-row loads
   for (int64_t bid = blockIdx.x; bid < g.tiles; bid += gridDim.x) {
     int64_t ti, tj;
     gemm_tile_of(g, bid, ti, tj);
@@ -976,13 +988,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
     if (g.kmode & KLO_J) kb = j0;
     if (g.kmode & KHI_J) ke = min(ke, j0 + BIG);
     if (g.kmode & KHI_I) ke = min(ke, i0 + BIG);
-    f64x4 acc[4][4];
+    f64x4 acc[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-    double ra[8], rb[8];
-    // op(A) row i0 + rl_i, k = k0 + rl_k .. + 7
+      for (int b = 0; b < NB; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double ra[PER], rb[PER];
+    // op(A) row i0 + rl_i, k = k0 + rl_k .. + PER - 1
     const int64_t ai = i0 + rl_i;
     const bool a_ok = ai < g.M;
     const double* arow = g.A + (a_ok ? ai : 0) * g.lda;
@@ -992,7 +1004,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
     const double* brow = TB ? g.B + (b_ok ? bj : 0) * g.ldb : g.B;
     auto fetch = [&](int64_t k0) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int p = 0; p < PER / 2; ++p) {
         const int64_t k = k0 + rl_k + 2 * p;
         if (a_ok && k + 1 < ke) {
           const double2 v = *reinterpret_cast<const double2*>(arow + k);
@@ -1005,7 +1017,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
       }
       if (TB) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < PER / 2; ++p) {
           const int64_t k = k0 + rl_k + 2 * p;
           if (b_ok && k + 1 < ke) {
             const double2 v = *reinterpret_cast<const double2*>(brow + k);
@@ -1021,7 +1033,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
         const bool kin = k < ke;
         const double* src = g.B + (kin ? k : kb) * g.ldb;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < PER / 2; ++p) {
           const int64_t j = bj + 2 * p;
           if (kin && j + 1 < g.N) {
             const double2 v = *reinterpret_cast<const double2*>(src + j);
@@ -1036,13 +1048,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
     };
     auto stash = [&](int buf) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) As[buf][rl_k + e][rl_i] = ra[e];
+      for (int e = 0; e < PER; ++e) As[buf][rl_k + e][rl_i] = ra[e];
       if (TB) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Bs[buf][rl_k + e][rl_i] = rb[e];
+        for (int e = 0; e < PER; ++e) Bs[buf][rl_k + e][rl_i] = rb[e];
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < PER / 2; ++p)
           *reinterpret_cast<double2*>(&Bs[buf][kl_k][kl_i + 2 * p]) =
               make_double2(rb[2 * p], rb[2 * p + 1]);
       }
@@ -1056,15 +1068,16 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
       if (k0 + BKC < ke) fetch(k0 + BKC);
 #pragma unroll
       for (int ks = 0; ks < BKC; ks += 4) {
-        double af[4], bf[4];
+        double af[4], bf[NB];
 #pragma unroll
         for (int a = 0; a < 4; ++a) af[a] = As[buf][ks + (lane >> 4)][64 * wr + 16 * a + (lane & 15)];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][64 * wc + 16 * b + (lane & 15)];
+        for (int b = 0; b < NB; ++b)
+          bf[b] = Bs[buf][ks + (lane >> 4)][WCOL * wc + 16 * b + (lane & 15)];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+          for (int b = 0; b < NB; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
       }
     }
@@ -1072,11 +1085,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_big_kernel(GemmArgs g) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t gi = i0 + 64 * wr + 16 * a + (lane >> 4) + 4 * q;
-          const int64_t gj = j0 + 64 * wc + 16 * b + (lane & 15);
+          const int64_t gj = j0 + WCOL * wc + 16 * b + (lane & 15);
           if (gi >= g.M || gj >= g.N) continue;
           if (g.lower && gj > gi) continue;
           double* c = g.C + gi * g.ldc + gj;
@@ -1222,8 +1235,8 @@ hipError_t gemm(const double* A, int64_t lda, bool ta, const double* B, int64_t 
     g.tiles_n = tn;
     g.tiles = t128;
     const dim3 grid((unsigned)(max_wg > 0 ? hmin(t128, max_wg) : t128));
-    if (tb) hipLaunchKernelGGL(gemm_f64_big_kernel<true>, grid, dim3(256), 0, stream, g);
-    else hipLaunchKernelGGL(gemm_f64_big_kernel<false>, grid, dim3(256), 0, stream, g);
+    if (tb) hipLaunchKernelGGL((gemm_f64_big_kernel<true, 8>), grid, dim3(512), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_f64_big_kernel<false, 8>), grid, dim3(512), 0, stream, g);
   } else if (!ta && t64 < 256) {
     launch_splitk<32>(g, tb, max_wg, stream);
   } else {
