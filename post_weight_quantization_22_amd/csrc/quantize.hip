@@ -498,43 +498,55 @@ struct UpdArgs {
   int vec_u;
 };
 
-// TT x TT output tile per workgroup (4 waves of TT/2 x TT/2, (TT/32)^2 MFMA
-// tiles each); TT = 64 for the narrow updates inside a super-block, where
-// 128-wide tiles would leave most CUs idle.
-template <int TT>
-__global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
-  constexpr int HW = TT / 2;        // per-wave edge
-  constexpr int SUBT = HW / 16;     // MFMA tiles per wave edge
-  constexpr int AQ = TT * TK / 1024;  // float4 per thread per operand chunk
+// TT x TT output tile per workgroup of NW waves, 2 x NW/2 of them, each
+// TT/2 rows x TT/(NW/2) columns of 16 x 16 MFMA tiles: TT = 128 with 8 waves
+// (64 x 32 each, four waves per SIMD at two workgroups per CU) for the wide
+// updates; TT = 64 with 4 waves for the narrow updates inside a super-block,
+// where 128-wide tiles would leave most CUs idle.
+template <int TT, int NW>
+__global__ __launch_bounds__(64 * NW, NW / 2) void update_gemm_kernel(UpdArgs g) {
+  constexpr int NT = 64 * NW;            // threads
+  constexpr int HW = TT / 2;             // rows per wave
+  constexpr int WC = TT / (NW / 2);      // columns per wave
+  constexpr int SUBA = HW / 16, SUBB = WC / 16;  // MFMA tiles per wave edge
+  constexpr int AQ = TT * TK / (4 * NT);  // float4 per thread per operand chunk
   __shared__ float As[2][TT][TK + 1];
   __shared__ __align__(16) float Bs[2][TK][TT + 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wr = wv >> 1, wc = wv & 1;
+  const int wr = wv / (NW / 2), wc = wv % (NW / 2);
   const int64_t T8 = (g.tiles / 8) * 8;
   const int64_t bid = blockIdx.x;
   const int64_t t = bid < T8 ? (bid % 8) * (T8 / 8) + bid / 8 : bid;
-  const int64_t row0 = (t / g.tiles_n) * TT, col0 = (t % g.tiles_n) * TT;  // col0 relative to c0
+  // tiles in groups of 8 row blocks, column blocks outer and rows inner: the
+  // workgroups in flight on an XCD (a contiguous range of t) share a few
+  // column blocks of U and the group's rows of E, so U is read from beyond
+  // the L2 about once per group instead of once per row block
+  const int64_t tiles_m = g.tiles / g.tiles_n;
+  const int64_t grp = t / (8 * g.tiles_n);
+  const int64_t rig = min((int64_t)8, tiles_m - 8 * grp);  // row blocks in the group
+  const int64_t idx = t - grp * 8 * g.tiles_n;
+  const int64_t row0 = (grp * 8 + idx % rig) * TT, col0 = (idx / rig) * TT;  // col0 relative to c0
 
-  f32x4 acc[SUBT][SUBT];
+  f32x4 acc[SUBA][SUBB];
 #pragma unroll
-  for (int a = 0; a < SUBT; ++a)
+  for (int a = 0; a < SUBA; ++a)
 #pragma unroll
-    for (int b = 0; b < SUBT; ++b)
+    for (int b = 0; b < SUBB; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = row0 + HW * wr + 16 * a + 4 * (lane >> 4) + q;
-        const int64_t col = col0 + HW * wc + 16 * b + (lane & 15);
+        const int64_t col = col0 + WC * wc + 16 * b + (lane & 15);
         acc[a][b][q] = (row < g.m && col < g.nc) ? g.Wp[row * g.n + g.c0 + col] : 0.0f;
       }
 
-  // staging: A chunk TT x 32 (thread: rows tid/8 + 32q, k 4 (tid%8) .. +3),
-  //          B chunk 32 x TT (thread: k (tid / (TT/4)) + (1024/TT) q, cols 4 (tid % (TT/4)) .. +3)
+  // staging: A chunk TT x 32 (thread: rows tid/8 + (NT/8) q, k 4 (tid%8) .. +3),
+  //          B chunk 32 x TT (thread: k (tid / (TT/4)) + (4 NT/TT) q, cols 4 (tid % (TT/4)) .. +3)
   float4 ra[AQ], rb[AQ];
   auto fetch = [&](int64_t kk0) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-      const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
+      const int rr = (tid >> 3) + (NT / 8) * q, kk = 4 * (tid & 7);
       const int64_t row = row0 + rr;
       const int64_t k = kk0 + kk;
       if (row < g.m && k + 4 <= g.kc) {
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
     }
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-      const int kk = (tid / (TT / 4)) + (1024 / TT) * q, cc = 4 * (tid % (TT / 4));
+      const int kk = (tid / (TT / 4)) + (4 * NT / TT) * q, cc = 4 * (tid % (TT / 4));
       const int64_t k = kk0 + kk;
       const int64_t col = col0 + cc;
       const float* src = g.U + (g.u0 + (k < g.kc ? k : 0)) * g.ldu + g.c0 + col;
@@ -566,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
   auto stash = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-      const int rr = (tid >> 3) + 32 * q, kk = 4 * (tid & 7);
+      const int rr = (tid >> 3) + (NT / 8) * q, kk = 4 * (tid & 7);
       As[buf][rr][kk] = -ra[q].x;
       As[buf][rr][kk + 1] = -ra[q].y;
       As[buf][rr][kk + 2] = -ra[q].z;
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
     }
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-      const int kk = (tid / (TT / 4)) + (1024 / TT) * q, cc = 4 * (tid % (TT / 4));
+      const int kk = (tid / (TT / 4)) + (4 * NT / TT) * q, cc = 4 * (tid % (TT / 4));
       *reinterpret_cast<float4*>(&Bs[buf][kk][cc]) = rb[q];
     }
   };
@@ -589,15 +601,15 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
     if (more) fetch((int64_t)(c + 1) * TK);
 #pragma unroll
     for (int ks = 0; ks < TK; ks += 4) {
-      float af[SUBT], bf[SUBT];
+      float af[SUBA], bf[SUBB];
 #pragma unroll
-      for (int a = 0; a < SUBT; ++a) af[a] = As[buf][HW * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
+      for (int a = 0; a < SUBA; ++a) af[a] = As[buf][HW * wr + 16 * a + (lane & 15)][ks + (lane >> 4)];
 #pragma unroll
-      for (int b = 0; b < SUBT; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][HW * wc + 16 * b + (lane & 15)];
+      for (int b = 0; b < SUBB; ++b) bf[b] = Bs[buf][ks + (lane >> 4)][WC * wc + 16 * b + (lane & 15)];
 #pragma unroll
-      for (int a = 0; a < SUBT; ++a)
+      for (int a = 0; a < SUBA; ++a)
 #pragma unroll
-        for (int b = 0; b < SUBT; ++b)
+        for (int b = 0; b < SUBB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
     if (more) stash(buf ^ 1);
@@ -605,13 +617,13 @@ __global__ __launch_bounds__(256, 2) void update_gemm_kernel(UpdArgs g) {
   }
 
 #pragma unroll
-  for (int a = 0; a < SUBT; ++a)
+  for (int a = 0; a < SUBA; ++a)
 #pragma unroll
-    for (int b = 0; b < SUBT; ++b)
+    for (int b = 0; b < SUBB; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = row0 + HW * wr + 16 * a + 4 * (lane >> 4) + q;
-        const int64_t col = col0 + HW * wc + 16 * b + (lane & 15);
+        const int64_t col = col0 + WC * wc + 16 * b + (lane & 15);
         if (row < g.m && col < g.nc) g.Wp[row * g.n + g.c0 + col] = acc[a][b][q];
       }
 }
@@ -628,11 +640,13 @@ void launch_update(float* Wp, int64_t m, int64_t n, const float* E, int64_t lde,
   if (ceil_div(nc, 128) * ceil_div(m, 128) >= 256) {
     g.tiles_n = ceil_div(nc, 128);
     g.tiles = g.tiles_n * ceil_div(m, 128);
-    hipLaunchKernelGGL(update_gemm_kernel<128>, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((update_gemm_kernel<128, 8>), dim3((unsigned)g.tiles), dim3(512), 0, stream,
+                       g);
   } else {
     g.tiles_n = ceil_div(nc, 64);
     g.tiles = g.tiles_n * ceil_div(m, 64);
-    hipLaunchKernelGGL(update_gemm_kernel<64>, dim3((unsigned)g.tiles), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((update_gemm_kernel<64, 4>), dim3((unsigned)g.tiles), dim3(256), 0, stream,
+                       g);
   }
 }
 
