@@ -93,7 +93,8 @@ def source_hash(path: str) -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per Hessian launch from committed rocprofv3 counter runs, if current."""
+    """HBM bytes per Hessian kernel launch from committed rocprofv3 counter
+    runs (the probe's one accumulate call over its launches), if current."""
     path = traffic_file(workload)
     if not os.path.exists(path):
         return None
@@ -103,11 +104,14 @@ def measured_traffic(workload: str):
         return None
     if rec.get("kernel_source_sha256") != source_hash(HESSIAN_SRC):
         return None  # the kernel changed since the counters were taken
-    return rec.get("bytes_per_launch")
+    if "bytes_per_call" not in rec:
+        return None
+    return round(rec["bytes_per_call"] / max(1, rec.get("launches_per_call", 1)))
 
 
 COPY_BYTES = 1 << 31  # the calibration copy of --traffic-probe
 HESS_KERNELS = ("syrk_bf16_dma_kernel", "reduce_full_partials_kernel")
+HESS_LAUNCH_TOKENS = 65536  # tokens per launch of an unsplit Hessian product
 
 
 def short_kernel_name(name: str) -> str:
@@ -123,10 +127,11 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
 
     Each counter (KiB per dispatch, summed over the L2 channels) is scaled by
     the ratio of the known bytes of the 2 GiB device copy to what the same
-    counter reads for that copy; the launch is the first dispatch of each
-    Hessian kernel in the file (the probe's lone accumulate).  Every other
-    kernel of the probe's layer step is summed by name as well
-    (``per_kernel``), for the quantize, pack and RTN bandwidths.
+    counter reads for that copy; the call is every dispatch of the Hessian
+    kernels in the file (the probe's lone accumulate; the product kernel may
+    run as several launches, counted in ``launches``).  Every other kernel of
+    the probe's layer step is summed by name as well (``per_kernel``), for the
+    quantize, pack and RTN bandwidths.
     """
     import csv
     from collections import defaultdict
@@ -151,21 +156,20 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
         copy_kib = val[max(copies)]
         factor = COPY_BYTES / (copy_kib * 1024.0)
         hess = 0.0
-        found = False
-        for k in HESS_KERNELS:
-            ds = sorted(d for d in val if k in name[d])
-            if ds:
-                hess += val[ds[0]]
-                found = True
-        if not found:
+        ds = [d for d in val if HESS_KERNELS[0] in name[d]]
+        if not ds:
             raise SystemExit(f"{path}: no Hessian dispatch")
+        launches = len(ds)
+        for k in HESS_KERNELS:
+            hess += sum(val[d] for d in val if k in name[d])
         per_kernel = defaultdict(float)
         for d, v in val.items():
             if "copyBuffer" in name[d]:
                 continue
             per_kernel[short_kernel_name(name[d])] += v * 1024.0 * factor
         out[counter] = {"hessian_kib": hess, "copy_kib": copy_kib, "scale": factor,
-                        "bytes": hess * 1024.0 * factor, "per_kernel_bytes": dict(per_kernel)}
+                        "bytes": hess * 1024.0 * factor, "launches": launches,
+                        "per_kernel_bytes": dict(per_kernel)}
     return out
 
 
@@ -730,9 +734,12 @@ def main():
         rec = {
             "kernel": "gptq_hessian_accumulate: " + " + ".join(HESS_KERNELS),
             "workload": args.workload,
-            "bytes_per_launch": round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]),
-            "fetch": {k: v for k, v in t["FETCH_SIZE"].items() if k != "per_kernel_bytes"},
-            "write": {k: v for k, v in t["WRITE_SIZE"].items() if k != "per_kernel_bytes"},
+            "bytes_per_call": round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]),
+            "launches_per_call": t["FETCH_SIZE"]["launches"],
+            "fetch": {k: v for k, v in t["FETCH_SIZE"].items()
+                      if k not in ("per_kernel_bytes", "launches")},
+            "write": {k: v for k, v in t["WRITE_SIZE"].items()
+                      if k not in ("per_kernel_bytes", "launches")},
             "per_kernel_step_bytes": {
                 k: {"fetch": round(t["FETCH_SIZE"]["per_kernel_bytes"].get(k, 0.0)),
                     "write": round(t["WRITE_SIZE"]["per_kernel_bytes"].get(k, 0.0))}
@@ -791,18 +798,27 @@ def main():
     hess_flops = n * (n + 1) * N
     hess_ms = g0["stages_ms"]["hessian"]
     hess_tf = hess_flops / (hess_ms * 1e-3) / 1e12
+    split = gq.gptq_hessian_workspace_size(n, N) > 0
+    # launches of the product kernel per accumulate call: counted in the
+    # profiled step, else the library's rule (an unsplit product runs one
+    # launch per HESS_LAUNCH_TOKENS tokens)
+    launches = g0.get("breakdown", {}).get(HESS_KERNELS[0], {}).get("calls")
+    if not launches:
+        launches = 1 if split else -(-N // HESS_LAUNCH_TOKENS)
     roofline = {
         "bound": "mfma",
         "kernel": "hessian: gptq_hessian_accumulate (syrk_bf16_dma_kernel"
-                  + (" + reduce_full_partials_kernel" if gq.gptq_hessian_workspace_size(n, N)
-                     else "") + ")",
+                  + (" + reduce_full_partials_kernel" if split else "") + ")",
         "achieved": round(hess_tf, 2),
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(hess_tf / BF16_PEAK_TFLOPS, 4),
         "traffic": measured_traffic(args.workload),
-        "algorithmic_work": f"n(n+1)N = {hess_flops:.4e} flop per launch",
-        "launch_ms": round(hess_ms, 4),
+        "algorithmic_work": f"n(n+1)N/launches = {hess_flops / launches:.4e} flop per launch "
+                            f"({launches} launches per accumulate call, {N} tokens)",
+        "launches_per_call": launches,
+        "launch_ms": round(hess_ms / launches, 4),
+        "call_ms": round(hess_ms, 4),
     }
     weights = sum(l.m * l.n for l in wl.layers)
     out = {

@@ -22,7 +22,9 @@
 // Tiles are few when n is small, so the token axis is split P ways; each
 // split writes its partial tile to the workspace and a reduction kernel adds
 // the P partials to S in a fixed order (deterministic, no atomics).  With
-// P == 1 the tile is added to S directly.
+// P == 1 the tile is added to S directly, by one launch per 65,536 tokens
+// (shorter units keep an XCD's workgroups on the same token rows, so they
+// share them through its L2).
 //
 // fp32 path (fp32 activations; small layers): a SIMT fp32 SYRK, lower tiles.
 #include "kernels.hpp"
@@ -587,6 +589,17 @@ HessPlan plan_bf16(int64_t n, int64_t tokens) {
 
 // Interior tiling (256 x 256 tiles of the lower triangle).  P = 0: not usable
 // for these sizes (n not a multiple of 256, or not whole 64-token stages).
+//
+// A unit streams its tile's tokens from its start to its end, and the ~32
+// workgroups in flight on one XCD share their channel blocks through its L2
+// only while they stay near the same token rows.  Over a long token axis they
+// drift apart and the L2 stops serving them: with all 524,288 tokens of a
+// 28672-wide layer in one launch (8192 stages a unit) the L2 serves about a
+// third of the 3.4 TB the tiles request and the launch takes ~438 ms; as
+// launches of 32K-96K tokens, each adding its tiles to S, it takes ~387 ms
+// (the extra read and write of S, 3.3 GB a launch, is small beside that).
+// Split plans (P > 1) already give a unit tokens / P tokens.
+constexpr int64_t HCHUNK = 65536;  // tokens per launch of an unsplit plan
 struct FullPlan {
   int64_t ntiles, P, T2;
   size_t ws;
@@ -658,9 +671,14 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
     if (ws_bytes < fp.ws) return hipErrorInvalidValue;
     float* part = fp.P > 1 ? reinterpret_cast<float*>(ws) : nullptr;
     const int64_t units = (fp.ntiles - fp.T2) * fp.P + fp.T2 * 2 * fp.P;
-    hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)units), dim3(512), 0, stream,
-                       reinterpret_cast<const uint16_t*>(X), ldx, tokens, fp.P, fp.T2, S, lds,
-                       part, n / FT_I);
+    // Unsplit (many tiles): one launch per HCHUNK tokens, each adding to S.
+    // The tokens are whole stages (P == 1 plans need tokens % HK == 0).
+    const int64_t chunk = fp.P == 1 ? HCHUNK : tokens;
+    for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
+      hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)units), dim3(512), 0, stream,
+                         reinterpret_cast<const uint16_t*>(X) + t0 * ldx, ldx,
+                         hmin(chunk, tokens - t0), fp.P, fp.T2, S, lds, part, n / FT_I);
+    }
     if (fp.P > 1) {
       const int vec_s = (reinterpret_cast<uintptr_t>(S) % 16 == 0) && lds % 4 == 0;
       hipLaunchKernelGGL(reduce_full_partials_kernel,

@@ -174,30 +174,42 @@ __global__ __launch_bounds__(1024) void diag_damp_kernel(const float* __restrict
 // rank_i = #{j : key_j > key_i or (key_j == key_i and j < i)} is a
 // permutation of 0 .. n-1 whatever the values (a non-finite diagonal is
 // reported through info by diag_damp_kernel; the order stays well formed).
-// The count is split over a 2-D grid: blockIdx.x takes 256 columns i,
-// blockIdx.y a chunk of RANK_CHUNK columns j staged in LDS (every lane reads
-// the same key: an LDS broadcast); each partial count is added to rank[i]
-// (zeroed by diag_damp_kernel).  rank_scatter_kernel then writes perm.
-constexpr int RANK_CHUNK = 2048;
+// The count is split over a 2-D grid: blockIdx.x takes RANK_I columns i (4 a
+// thread, so each key read from LDS serves four comparisons), blockIdx.y a
+// chunk of RANK_CHUNK columns j staged in LDS (every lane reads the same key:
+// an LDS broadcast); each partial count is added to rank[i] (zeroed by
+// diag_damp_kernel).  rank_scatter_kernel then writes perm.
+constexpr int RANK_CHUNK = 1024;
+constexpr int RANK_I = 1024;  // columns i per workgroup (4 per thread)
 
 __device__ __forceinline__ double order_key(double d) { return d != d ? -INFINITY : d; }
 
 __global__ __launch_bounds__(256) void rank_count_kernel(const double* __restrict__ diag,
                                                          int64_t n, int32_t* __restrict__ rank) {
   __shared__ double key[RANK_CHUNK];
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t base = (int64_t)blockIdx.y * RANK_CHUNK;
   const int cnt = (int)min<int64_t>(RANK_CHUNK, n - base);
   for (int t = threadIdx.x; t < cnt; t += blockDim.x) key[t] = order_key(diag[base + t]);
   __syncthreads();
-  if (i >= n) return;
-  const double ki = order_key(diag[i]);
-  int r = 0;
-  // j < i inside the chunk: ties count; j >= i: only strictly greater keys
-  const int split = (int)max<int64_t>(0, min<int64_t>(cnt, i - base));
-  for (int t = 0; t < split; ++t) r += key[t] >= ki;
-  for (int t = split; t < cnt; ++t) r += key[t] > ki;
-  if (r) atomicAdd(rank + i, r);
+  int64_t iv[4];
+  double ki[4];
+  int r[4], split[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    iv[u] = (int64_t)blockIdx.x * RANK_I + threadIdx.x + 256 * u;
+    ki[u] = iv[u] < n ? order_key(diag[iv[u]]) : 0.0;
+    r[u] = 0;
+    // j < i inside the chunk: ties count; j >= i: only strictly greater keys
+    split[u] = (int)max<int64_t>(0, min<int64_t>(cnt, iv[u] - base));
+  }
+  for (int t = 0; t < cnt; ++t) {
+    const double kj = key[t];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] += t < split[u] ? (kj >= ki[u]) : (kj > ki[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (iv[u] < n && r[u]) atomicAdd(rank + iv[u], r[u]);
 }
 
 __global__ __launch_bounds__(256) void rank_scatter_kernel(const int32_t* __restrict__ rank,
@@ -1446,7 +1458,7 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
                      w.diag, dead, w.lam, lambda_out, desc_act ? w.rank : nullptr, info);
   if (desc_act) {
     hipLaunchKernelGGL(rank_count_kernel,
-                       dim3((unsigned)ceil_div(n, 256), (unsigned)ceil_div(n, RANK_CHUNK)),
+                       dim3((unsigned)ceil_div(n, RANK_I), (unsigned)ceil_div(n, RANK_CHUNK)),
                        dim3(256), 0, stream, w.diag, n, w.rank);
     hipLaunchKernelGGL(rank_scatter_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
                        w.rank, n, pm);

@@ -67,6 +67,39 @@ def test_hessian_is_additive_over_calls():
         assert np.abs(host(S) - S_ref)[low].max() <= 1e-5 * np.abs(S_ref).max()
 
 
+def test_hessian_long_token_axis_in_launches():
+    """Many tiles (n = 16384: 2080 lower-triangle tiles) run unsplit, one
+    launch per 65,536 tokens.  With 66,624 tokens (a second, short launch) S
+    equals, bit for bit, two calls on tokens [0, 65536) and [65536, 66624), and
+    sampled channel pairs agree with the fp64 sum within the fp32 accumulation
+    bound."""
+    q = need_gpu()
+    n, tokens, split = 16384, 66624, 65536
+    wl = synth.custom_workload("hlong", 8, n, tokens, 2082, outlier_frac=0.01,
+                               outlier_mult=20.0, workload_id=230)
+    X = synth.x_all(wl, "x")
+    rng = np.random.default_rng(3)
+    chans = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 62, replace=False)]))
+    Xc = X[:, chans].astype(np.float64)
+    S_ref = Xc.T @ Xc
+    A_ref = np.abs(Xc).T @ np.abs(Xc)
+    Xd = dev(X, torch.bfloat16)
+    del X, Xc
+    S1 = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    S2 = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    say("hessian long token axis", n, tokens)
+    q.gptq_hessian_accumulate(S1, Xd)
+    q.gptq_hessian_accumulate(S2, Xd[:split])
+    q.gptq_hessian_accumulate(S2, Xd[split:])
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2)
+    got = host(S1)[np.ix_(chans, chans)].astype(np.float64)
+    low = chans[:, None] >= chans[None, :]
+    err = np.abs(got - S_ref)[low]
+    bound = (tokens + 8) * 2.0 ** -24 * A_ref[low] + 1e-30
+    assert np.all(err <= bound)
+
+
 def test_hessian_deterministic():
     q = need_gpu()
     X = dev(_x(384, 8192, 2048, "bf16", seed=4), torch.bfloat16)
@@ -199,9 +232,10 @@ def test_prepare_nan_on_diagonal_with_desc_act():
 
 
 def test_prepare_desc_act_order_with_exact_ties_over_several_chunks():
-    """The order kernel counts over column chunks of 2048: at n = 4500 (three
-    chunks) with a diagonal of exactly tied values the device order equals the
-    stable descending argsort bit for bit."""
+    """The order kernel counts over column chunks of 1024 and rows of 1024
+    columns per workgroup: at n = 4500 (five of each, the last ragged) with a
+    diagonal of exactly tied values the device order equals the stable
+    descending argsort bit for bit."""
     q = need_gpu()
     n = 4500
     rng = np.random.default_rng(9)
