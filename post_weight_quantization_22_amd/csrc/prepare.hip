@@ -964,7 +964,13 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
 // the previous one is multiplied, then stored k-major (As[k][i], Bs[k][j]),
 // one barrier per stage.  The LDS row stride of 144 doubles puts two
 // consecutive k rows on opposite halves of the 64 banks, so the 16 x 4
-// operand reads of a half-wave are conflict-free.  op(A) is A itself
+// operand reads of a half-wave are conflict-free; k rows 4-7 and 12-15 of a
+// stage hold their columns XOR 16 (the other half of the banks), so the
+// transposing stores of the row loads, whose lanes write k rows 0, 4, 8, 12
+// at once, meet at most two to a bank, and the k-row loads of op(B) store
+// 16-byte pairs 2 KPT columns apart so 32 lanes cover all 64 banks.
+// (Measured before the swizzle: 4-6 bank-conflict cycles per LDS
+// instruction, MFMA pipes 0.57-0.68 busy.)  op(A) is A itself
 // (row-major, A[i * lda + k]); op(B) as in gemm_f64_kernel.  Needs even
 // leading dimensions and 16-byte aligned A, B (checked by the caller).
 // (Measured, 20480-wide products: 8 waves 49 TF/s against 41 for 4 on the
@@ -974,6 +980,62 @@ void launch_splitk(const GemmArgs& g0, bool tb, int64_t max_wg, hipStream_t stre
 constexpr int BIG = 128;   // tile edge
 constexpr int BKC = 16;    // K per stage
 constexpr int BLD = 144;   // LDS row stride (doubles)
+
+// Tile of workgroup `bid` for the 128 x 128 products, XCD-aware (workgroup b
+// runs on XCD b % 8, and the ~64 in flight on one XCD share its 4 MB L2):
+//  - lower (the trailing updates, one K for every tile): the triangle in bands
+//    of 8 tile rows, a band column by column, each XCD a contiguous range of
+//    that order, so an XCD's tiles in flight read ~8 row blocks and ~8 column
+//    blocks of the panel;
+//  - K from the column's start (the inverse's head products: long, unequal K):
+//    the tiles_m row tiles of a column on one XCD, columns in increasing order
+//    (longest K first), so those tiles read the column's op(B) panel together;
+//  - otherwise as gemm_tile_of.
+// (Measured in isolation, bit-identical: +4 % on a K = 512 trailing update,
+// +3-5 % on the head product.)
+__device__ __forceinline__ void big_tile_of(const GemmArgs& g, int64_t bid, int64_t& ti,
+                                            int64_t& tj) {
+  if (g.lower) {
+    const int64_t T = g.tiles_m, U = g.tiles, U8 = (U / 8) * 8;
+    const int64_t u = bid < U8 ? (bid % 8) * (U8 / 8) + bid / 8 : bid;
+    // band b (tile rows 8b .. 8b + 7) starts at 32 b^2 + 4 b: 64 tiles for
+    // each earlier band of 8 rows, plus the bands' 36-tile diagonal triangles
+    int64_t b = (int64_t)((-4.0 + sqrt(16.0 + 128.0 * (double)u)) / 64.0);
+    while (b > 0 && 32 * b * b + 4 * b > u) --b;
+    while (32 * (b + 1) * (b + 1) + 4 * (b + 1) <= u) ++b;
+    const int64_t r0 = 8 * b, h = min((int64_t)8, T - r0);
+    int64_t d = u - (32 * b * b + 4 * b);
+    if (d < r0 * h) {  // the band's full columns 0 .. r0 - 1
+      tj = d / h;
+      ti = r0 + d % h;
+      return;
+    }
+    d -= r0 * h;  // its diagonal triangle: column r0 + c has h - c tiles
+    int64_t c = 0;
+    while (d >= h - c) {
+      d -= h - c;
+      ++c;
+    }
+    tj = r0 + c;
+    ti = r0 + c + d;
+    return;
+  }
+  if (g.kmode & KLO_J) {
+    const int64_t tm = g.tiles_m, tn = g.tiles_n;
+    const int64_t full = (tn / 8) * 8 * tm;
+    if (bid < full) {
+      const int64_t s = bid / 8;
+      ti = s % tm;
+      tj = 8 * (s / tm) + bid % 8;
+    } else {
+      const int64_t u = bid - full;
+      ti = u % tm;
+      tj = (tn / 8) * 8 + u / tm;
+    }
+    return;
+  }
+  gemm_tile_of(g, bid, ti, tj);
+}
 
 template <bool TB, int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2) void gemm_f64_big_kernel(GemmArgs g) {
@@ -991,10 +1053,12 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void gemm_f64_big_kernel(GemmArgs 
   // loader roles: "row" loads (PER consecutive k of one row i / column j) and
   // "k-row" loads (PER consecutive i / j of one k)
   const int rl_i = tid / RPT, rl_k = (tid % RPT) * PER;  // row loads
-  const int kl_k = tid / KPT, kl_i = (tid % KPT) * PER;  // k-row loads
+  const int kl_k = tid / KPT, kl_i = (tid % KPT) * 2;    // k-row loads: pairs kl_i + 2 KPT p
+  // column swizzle of k row k (see above)
+  auto sw = [](int k) { return ((k >> 2) & 1) << 4; };
   for (int64_t bid = blockIdx.x; bid < g.tiles; bid += gridDim.x) {
     int64_t ti, tj;
-    gemm_tile_of(g, bid, ti, tj);
+    big_tile_of(g, bid, ti, tj);
     const int64_t i0 = ti * BIG, j0 = tj * BIG;
     int64_t kb = 0, ke = g.K;
     if (g.kmode & KLO_J) kb = j0;
@@ -1014,60 +1078,67 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void gemm_f64_big_kernel(GemmArgs 
     const int64_t bj = j0 + (TB ? rl_i : kl_i);
     const bool b_ok = TB ? bj < g.N : true;
     const double* brow = TB ? g.B + (b_ok ? bj : 0) * g.ldb : g.B;
+    // whole stages of a tile inside op(A) and op(B) take unchecked 16-byte
+    // loads (k0 and rl_k even, lda and ldb even); the others, per element
+    const bool full_tile = i0 + BIG <= g.M && j0 + BIG <= g.N;
     auto fetch = [&](int64_t k0) {
+      if (full_tile && k0 + BKC <= ke) {  // uniform over the workgroup
 #pragma unroll
-      for (int p = 0; p < PER / 2; ++p) {
-        const int64_t k = k0 + rl_k + 2 * p;
-        if (a_ok && k + 1 < ke) {
-          const double2 v = *reinterpret_cast<const double2*>(arow + k);
+        for (int p = 0; p < PER / 2; ++p) {
+          const double2 v = *reinterpret_cast<const double2*>(arow + k0 + rl_k + 2 * p);
           ra[2 * p] = v.x;
           ra[2 * p + 1] = v.y;
-        } else {
-          ra[2 * p] = (a_ok && k < ke) ? arow[k] : 0.0;
-          ra[2 * p + 1] = 0.0;
         }
+        if (TB) {
+#pragma unroll
+          for (int p = 0; p < PER / 2; ++p) {
+            const double2 v = *reinterpret_cast<const double2*>(brow + k0 + rl_k + 2 * p);
+            rb[2 * p] = v.x;
+            rb[2 * p + 1] = v.y;
+          }
+        } else {
+          const double* src = g.B + (k0 + kl_k) * g.ldb + bj;
+#pragma unroll
+          for (int p = 0; p < PER / 2; ++p) {
+            const double2 v = *reinterpret_cast<const double2*>(src + 2 * KPT * p);
+            rb[2 * p] = v.x;
+            rb[2 * p + 1] = v.y;
+          }
+        }
+        return;
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int64_t k = k0 + rl_k + e;
+        ra[e] = (a_ok && k < ke) ? arow[k] : 0.0;
       }
       if (TB) {
 #pragma unroll
-        for (int p = 0; p < PER / 2; ++p) {
-          const int64_t k = k0 + rl_k + 2 * p;
-          if (b_ok && k + 1 < ke) {
-            const double2 v = *reinterpret_cast<const double2*>(brow + k);
-            rb[2 * p] = v.x;
-            rb[2 * p + 1] = v.y;
-          } else {
-            rb[2 * p] = (b_ok && k < ke) ? brow[k] : 0.0;
-            rb[2 * p + 1] = 0.0;
-          }
+        for (int e = 0; e < PER; ++e) {
+          const int64_t k = k0 + rl_k + e;
+          rb[e] = (b_ok && k < ke) ? brow[k] : 0.0;
         }
       } else {
         const int64_t k = k0 + kl_k;
         const bool kin = k < ke;
         const double* src = g.B + (kin ? k : kb) * g.ldb;
 #pragma unroll
-        for (int p = 0; p < PER / 2; ++p) {
-          const int64_t j = bj + 2 * p;
-          if (kin && j + 1 < g.N) {
-            const double2 v = *reinterpret_cast<const double2*>(src + j);
-            rb[2 * p] = v.x;
-            rb[2 * p + 1] = v.y;
-          } else {
-            rb[2 * p] = (kin && j < g.N) ? src[j] : 0.0;
-            rb[2 * p + 1] = 0.0;
-          }
+        for (int e = 0; e < PER; ++e) {
+          const int64_t j = bj + 2 * KPT * (e / 2) + (e % 2);
+          rb[e] = (kin && j < g.N) ? src[j] : 0.0;
         }
       }
     };
     auto stash = [&](int buf) {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) As[buf][rl_k + e][rl_i] = ra[e];
+      for (int e = 0; e < PER; ++e) As[buf][rl_k + e][rl_i ^ sw(rl_k + e)] = ra[e];
       if (TB) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) Bs[buf][rl_k + e][rl_i] = rb[e];
+        for (int e = 0; e < PER; ++e) Bs[buf][rl_k + e][rl_i ^ sw(rl_k + e)] = rb[e];
       } else {
 #pragma unroll
         for (int p = 0; p < PER / 2; ++p)
-          *reinterpret_cast<double2*>(&Bs[buf][kl_k][kl_i + 2 * p]) =
+          *reinterpret_cast<double2*>(&Bs[buf][kl_k][(kl_i + 2 * KPT * p) ^ sw(kl_k)]) =
               make_double2(rb[2 * p], rb[2 * p + 1]);
       }
     };
@@ -1081,11 +1152,13 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void gemm_f64_big_kernel(GemmArgs 
 #pragma unroll
       for (int ks = 0; ks < BKC; ks += 4) {
         double af[4], bf[NB];
+        const int x = sw(ks);  // the same for the k-step's four rows
 #pragma unroll
-        for (int a = 0; a < 4; ++a) af[a] = As[buf][ks + (lane >> 4)][64 * wr + 16 * a + (lane & 15)];
+        for (int a = 0; a < 4; ++a)
+          af[a] = As[buf][ks + (lane >> 4)][(64 * wr + 16 * a + (lane & 15)) ^ x];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          bf[b] = Bs[buf][ks + (lane >> 4)][WCOL * wc + 16 * b + (lane & 15)];
+          bf[b] = Bs[buf][ks + (lane >> 4)][(WCOL * wc + 16 * b + (lane & 15)) ^ x];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
