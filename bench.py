@@ -237,9 +237,11 @@ def stage_roof_ms(m, n, N, q, prep_peak=FP32_PEAK_TFLOPS, with_hessian=True):
 
 KERNEL_STAGE = (
     ("hessian", ("syrk_", "reduce_full_partials", "reduce_partials")),
-    ("prepare", ("diag_damp", "rank_", "iota_kernel", "build_a", "node_kernel", "gemm_f64",
+    ("prepare", ("diag_damp", "rank_", "chunk_sort", "iota_kernel", "build_a", "sym_kernel",
+                 "gather_a", "node_kernel", "gemm_f64",
                  "gemm_splitk", "gemm_tall128", "write_u")),
-    ("quantize", ("prep_weights", "block_quant", "update_gemm", "unpermute", "static_params",
+    ("quantize", ("prep_weights", "prep_rows", "block_quant", "update_gemm", "unpermute",
+                  "static_params",
                   "row_params", "invert_perm", "fill_i32", "zero_f32")),
     ("pack", ("pack_",)),
     ("rtn", ("rtn_",)),

@@ -1272,34 +1272,37 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
 }
 
 // The same gather with every row staged in LDS: a workgroup walks a run of
-// rows; a row arrives with 16-byte loads (coalesced; the next row's loads are
-// in flight while this one is permuted) and leaves permuted, 8 positions per
-// thread and 16-byte store, the permuted reads served by the LDS.  The
+// rows; a row arrives with 16-byte loads (coalesced) straight into LDS and
+// leaves permuted, 8 positions per thread and 16-byte store, the permuted
+// reads served by the LDS.  One row buffer (two barriers a row), so several
+// workgroups share a CU and one's loads overlap another's permute; a row is
+// not prefetched into a register array (at 8 or more 16-byte entries a
+// thread the compiler keeps such an array in scratch memory).  The
 // permutation is read once per workgroup into registers (16-bit entries, two
 // to a word), not once per row.  n and ldx multiples of 8, X 16-byte aligned,
 // n <= NCAP.  Out-of-range perm entries read as zero.
 template <int NCAP>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(512) void gather_rows_kernel(const uint16_t* __restrict__ X,
                                                           int64_t ldx,
                                                           const int32_t* __restrict__ perm,
                                                           int64_t tokens, int64_t n, int64_t ldxp,
                                                           int64_t rows_per_wg,
                                                           uint16_t* __restrict__ Xp) {
-  constexpr int CH = NCAP / 8 / 256;  // 16-byte chunks of a row per thread
-  constexpr int SEG = NCAP / 8 / 256; // output segments per thread (ldxp <= NCAP)
+  constexpr int CH = NCAP / 8 / 512;  // 16-byte chunks of a row per thread
+  constexpr int SEG = NCAP / 8 / 512; // output segments per thread (ldxp <= NCAP)
   static_assert(NCAP <= 65535 + 1, "16-bit permutation entries");
-  __shared__ __align__(16) uint16_t buf[2][NCAP];
+  __shared__ __align__(16) uint16_t buf[NCAP];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * rows_per_wg;
   const int64_t t1 = min(tokens, t0 + rows_per_wg);
   if (t0 >= t1) return;
   const int nch = (int)(n / 8);
   const int nseg = (int)(ldxp / 8);
-  // this thread's segments tid + 256 i: source positions, 0xFFFF = zero
+  // this thread's segments tid + 512 i: source positions, 0xFFFF = zero
   uint32_t pk[SEG][4];
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
-    const int sg = tid + 256 * i;
+    const int sg = tid + 512 * i;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t h[2];
@@ -1312,42 +1315,33 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
       pk[i][q] = h[0] | (h[1] << 16);
     }
   }
-  uint4 v[CH];
-  auto fetch = [&](int64_t t) {
-    const uint4* src = reinterpret_cast<const uint4*>(X + t * ldx);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      if (idx < nch) v[c] = src[idx];
-    }
-  };
-  fetch(t0);
   for (int64_t t = t0; t < t1; ++t) {
-    uint16_t* b = buf[(t - t0) & 1];
+    __syncthreads();  // every thread has permuted the previous row
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(X + t * ldx);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      if (idx < nch) reinterpret_cast<uint4*>(b)[idx] = v[c];
+      for (int c = 0; c < CH; ++c) {
+        const int idx = tid + 512 * c;
+        if (idx < nch) reinterpret_cast<uint4*>(buf)[idx] = src[idx];
+      }
     }
-    if (t + 1 < t1) fetch(t + 1);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
-      const int sg = tid + 256 * i;
+      const int sg = tid + 512 * i;
       if (sg < nseg) {
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t s0 = pk[i][q] & 0xFFFFu, s1 = pk[i][q] >> 16;
-          const uint32_t lo = s0 != 0xFFFFu ? (uint32_t)b[s0] : 0u;
-          const uint32_t hi = s1 != 0xFFFFu ? (uint32_t)b[s1] : 0u;
+          const uint32_t lo = s0 != 0xFFFFu ? (uint32_t)buf[s0] : 0u;
+          const uint32_t hi = s1 != 0xFFFFu ? (uint32_t)buf[s1] : 0u;
           w[q] = lo | (hi << 16);
         }
         *reinterpret_cast<uint4*>(Xp + t * ldxp + 8 * (int64_t)sg) =
             make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    // buffer (t - t0) & 1 is written again two rows on, after the next barrier
   }
 }
 
@@ -1437,10 +1431,10 @@ void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t 
     const int64_t rpw = hmax((int64_t)4, ceil_div(tokens, (int64_t)1024));
     const dim3 grid((unsigned)ceil_div(tokens, rpw));
     if (ldxp <= 16384)
-      hipLaunchKernelGGL(gather_rows_kernel<16384>, grid, dim3(256), 0, stream, X, ldx, perm,
+      hipLaunchKernelGGL(gather_rows_kernel<16384>, grid, dim3(512), 0, stream, X, ldx, perm,
                          tokens, n, ldxp, rpw, Xp);
     else
-      hipLaunchKernelGGL(gather_rows_kernel<32768>, grid, dim3(256), 0, stream, X, ldx, perm,
+      hipLaunchKernelGGL(gather_rows_kernel<32768>, grid, dim3(512), 0, stream, X, ldx, perm,
                          tokens, n, ldxp, rpw, Xp);
   } else {
     const int64_t total = tokens * (ldxp / 8);

@@ -30,7 +30,8 @@
 //    (the lookahead), the rest of the trailing matrix on a side stream, where
 //    it overlaps the next outer block.  Before its next lookahead the main
 //    stream waits for that side update (both write those columns).
-// 2. X = L^-1 by groups of GRP blocks (rows c .. c + 512), from L X = I:
+// 2. X = L^-1 by groups of GRP blocks (rows c .. c + 128 GRP; GRP = 8 for
+//    n >= 16384, else 4), from L X = I:
 //    X[g, 0:c] = -X_gg L[g, 0:c] X[0:c, 0:c].  Per group, on a third stream:
 //      X_gg, the inverse of the group's own diagonal block, joins the nodes'
 //      X_ii pairwise: for a split [[L11, 0], [L21, L22]] the inverse is
@@ -65,12 +66,25 @@ struct PrepWs {
   double* lam;             // [1]
   int32_t* perm;           // [n]
   int32_t* rank;           // [n] descending-order rank of each column (desc_act)
+  double* skey;            // [n rounded up to RANK_CHUNK] keys sorted within chunks (desc_act)
+  int32_t* sidx;           // [same] their columns
 };
 
-constexpr int GRP = 4;  // blocks per group of the inverse
+// Blocks per group of the inverse: a group's head product M_g reads the
+// whole inverse above it once for every 128 of its rows, so larger groups
+// read it fewer times; smaller ones leave less after the last node (the last
+// group's joins and product), which bounds small n.
+int64_t grp_blocks(int64_t n) { return n >= 16384 ? 8 : 4; }
 
-// Phase-2 product buffers: M_g ([GRP NODE, n]) and the joins' M ([2 NODE, 2 NODE]).
-int64_t m_elems(int64_t n) { return n > NODE ? GRP * NODE * n + 4 * NODE * NODE : 0; }
+// Phase-2 product buffers: M_g ([GRP NODE, n]) and the joins' M (at most
+// [GRP/2 NODE, GRP/2 NODE]).
+int64_t m_elems(int64_t n) {
+  const int64_t g = grp_blocks(n);
+  return n > NODE ? g * NODE * n + (g / 2) * (g / 2) * NODE * NODE : 0;
+}
+
+constexpr int RANK_CHUNK = 1024;  // keys per sorted chunk of the desc_act order
+int64_t rank_pad(int64_t n) { return ceil_div(n, (int64_t)RANK_CHUNK) * RANK_CHUNK; }
 
 PrepWs carve(void* ws, int64_t n) {
   char* p = reinterpret_cast<char*>(ws);
@@ -88,6 +102,10 @@ PrepWs carve(void* ws, int64_t n) {
   w.perm = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)n * sizeof(int32_t), 256);
   w.rank = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)n * sizeof(int32_t), 256);
+  w.skey = reinterpret_cast<double*>(p);
+  p += align_up((size_t)rank_pad(n) * sizeof(double), 256);
+  w.sidx = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -170,52 +188,96 @@ __global__ __launch_bounds__(1024) void diag_damp_kernel(const float* __restrict
 }
 
 // Stable descending order of diag.  The key of column i is its diagonal
-// entry, with a NaN taken as -inf, so that the keys are totally ordered and
-// rank_i = #{j : key_j > key_i or (key_j == key_i and j < i)} is a
-// permutation of 0 .. n-1 whatever the values (a non-finite diagonal is
-// reported through info by diag_damp_kernel; the order stays well formed).
-// The count is split over a 2-D grid: blockIdx.x takes RANK_I columns i (4 a
-// thread, so each key read from LDS serves four comparisons), blockIdx.y a
-// chunk of RANK_CHUNK columns j staged in LDS (every lane reads the same key:
-// an LDS broadcast); each partial count is added to rank[i] (zeroed by
-// diag_damp_kernel).  rank_scatter_kernel then writes perm.
-constexpr int RANK_CHUNK = 1024;
-constexpr int RANK_I = 1024;  // columns i per workgroup (4 per thread)
-
+// entry, with a NaN taken as -inf, so that the keys are totally ordered:
+// column j precedes column i when key_j > key_i, or key_j == key_i and j < i,
+// and rank_i, the number of columns preceding i, is a permutation of
+// 0 .. n-1 whatever the values (a non-finite diagonal is reported through
+// info by diag_damp_kernel; the order stays well formed).  The count goes
+// through sorted chunks: chunk_sort_kernel sorts each run of RANK_CHUNK
+// columns into that order in LDS (bitonic; padding entries (-inf, INT32_MAX)
+// sort last and precede nothing), then rank_search_kernel gives each column,
+// for each sorted chunk, the number of its entries that precede the column
+// (a binary search in LDS), added to rank[i] (zeroed by diag_damp_kernel).
+// n^2 / RANK_CHUNK log2(RANK_CHUNK) comparisons instead of n^2.
+// rank_scatter_kernel then writes perm.
 __device__ __forceinline__ double order_key(double d) { return d != d ? -INFINITY : d; }
 
-__global__ __launch_bounds__(256) void rank_count_kernel(const double* __restrict__ diag,
-                                                         int64_t n, int32_t* __restrict__ rank) {
-  __shared__ double key[RANK_CHUNK];
-  const int64_t base = (int64_t)blockIdx.y * RANK_CHUNK;
-  const int cnt = (int)min<int64_t>(RANK_CHUNK, n - base);
-  for (int t = threadIdx.x; t < cnt; t += blockDim.x) key[t] = order_key(diag[base + t]);
+__device__ __forceinline__ bool precedes(double ka, int32_t ia, double kb, int32_t ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__global__ __launch_bounds__(512) void chunk_sort_kernel(const double* __restrict__ diag,
+                                                         int64_t n, double* __restrict__ skey,
+                                                         int32_t* __restrict__ sidx) {
+  __shared__ double k[RANK_CHUNK];
+  __shared__ int32_t x[RANK_CHUNK];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * RANK_CHUNK;
+  for (int e = t; e < RANK_CHUNK; e += 512) {
+    const int64_t j = base + e;
+    k[e] = j < n ? order_key(diag[j]) : -INFINITY;
+    x[e] = j < n ? (int32_t)j : INT32_MAX;
+  }
   __syncthreads();
-  int64_t iv[4];
-  double ki[4];
-  int r[4], split[4];
+  // 512 pairs a step: pair t is (lo, lo + stride); blocks of `size` alternate
+  // direction until the last merge
+  for (int size = 2; size <= RANK_CHUNK; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int lo = 2 * t - (t & (stride - 1)), hi = lo + stride;
+      const double ka = k[lo], kb = k[hi];
+      const int32_t ia = x[lo], ib = x[hi];
+      const bool up = (lo & size) == 0;
+      if (up ? precedes(kb, ib, ka, ia) : precedes(ka, ia, kb, ib)) {
+        k[lo] = kb;
+        k[hi] = ka;
+        x[lo] = ib;
+        x[hi] = ia;
+      }
+      __syncthreads();
+    }
+  }
+  for (int e = t; e < RANK_CHUNK; e += 512) {
+    skey[base + e] = k[e];
+    sidx[base + e] = x[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void rank_search_kernel(const double* __restrict__ diag,
+                                                          int64_t n,
+                                                          const double* __restrict__ skey,
+                                                          const int32_t* __restrict__ sidx,
+                                                          int32_t* __restrict__ rank) {
+  __shared__ double k[RANK_CHUNK];
+  __shared__ int32_t x[RANK_CHUNK];
+  const int64_t base = (int64_t)blockIdx.y * RANK_CHUNK;
+  for (int e = threadIdx.x; e < RANK_CHUNK; e += 256) {
+    k[e] = skey[base + e];
+    x[e] = sidx[base + e];
+  }
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    iv[u] = (int64_t)blockIdx.x * RANK_I + threadIdx.x + 256 * u;
-    ki[u] = iv[u] < n ? order_key(diag[iv[u]]) : 0.0;
-    r[u] = 0;
-    // j < i inside the chunk: ties count; j >= i: only strictly greater keys
-    split[u] = (int)max<int64_t>(0, min<int64_t>(cnt, iv[u] - base));
+    const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x + 256 * u;
+    if (i >= n) continue;
+    const double ki = order_key(diag[i]);
+    // entries [0, lo) precede column i, entries [hi, RANK_CHUNK) do not
+    int lo = 0, hi = RANK_CHUNK;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (precedes(k[mid], x[mid], ki, (int32_t)i)) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo) atomicAdd(rank + i, lo);
   }
-  for (int t = 0; t < cnt; ++t) {
-    const double kj = key[t];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] += t < split[u] ? (kj >= ki[u]) : (kj > ki[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (iv[u] < n && r[u]) atomicAdd(rank + iv[u], r[u]);
 }
 
 __global__ __launch_bounds__(256) void rank_scatter_kernel(const int32_t* __restrict__ rank,
                                                            int64_t n, int32_t* __restrict__ perm) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) perm[rank[i]] = (int32_t)i;
+  if (i < n) {
+    const int32_t r = rank[i];
+    if (r >= 0 && r < n) perm[r] = (int32_t)i;
+  }
 }
 
 __global__ void iota_kernel(int32_t* __restrict__ perm, int64_t n) {
@@ -262,6 +324,82 @@ __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ 
     const int64_t a = a0 + r, b = b0 + tx;
     if (a < n && b <= a) A[a * n + b] = tile[tx][r];
   }
+}
+
+// With desc_act, entry (a, b) of a tile of A comes from a scattered row and
+// column of S, so build_a_kernel reads 4 useful bytes of every line it
+// fetches (~44 GB for a 28672-wide S).  Two coalesced passes instead, through
+// the X workspace (free until the factorization): sym_kernel writes the whole
+// symmetric S in fp32 (Sf[i][j] = S[max][min], 32 x 32 tiles and their
+// transposes through LDS), then gather_a_kernel builds each row a of A from
+// row perm[n-1-a] of Sf staged in LDS, the columns read in the order
+// perm[n-1-b] from there.
+__global__ __launch_bounds__(256) void sym_kernel(const float* __restrict__ S, int64_t n,
+                                                  int64_t lds, float* __restrict__ Sf) {
+  __shared__ float tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t i0 = (int64_t)blockIdx.y * 32, j0 = (int64_t)blockIdx.x * 32;
+  if (j0 > i0) return;
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t i = i0 + r, j = j0 + tx;
+    float v = 0.0f;
+    if (i < n && j <= i) v = S[i * lds + j];
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t i = i0 + r, j = j0 + tx;
+    // lower entries as they are; on a diagonal tile the upper ones mirrored
+    if (i < n && j < n) Sf[i * n + j] = j <= i ? tile[r][tx] : tile[tx][r];
+  }
+  if (i0 == j0) return;
+  for (int r = ty; r < 32; r += 8) {  // the transposed tile: Sf[j][i] = S[i][j]
+    const int64_t j = j0 + r, i = i0 + tx;
+    if (i < n && j < n) Sf[j * n + i] = tile[tx][r];
+  }
+}
+
+constexpr int GATHER_NCAP = 32768;  // columns of a row staged in LDS (128 KB)
+
+__global__ __launch_bounds__(512) void gather_a_kernel(const float* __restrict__ Sf, int64_t n,
+                                                       const int32_t* __restrict__ perm,
+                                                       const double* __restrict__ diag,
+                                                       const double* __restrict__ lam,
+                                                       int64_t rows_per_wg,
+                                                       double* __restrict__ A,
+                                                       int32_t* __restrict__ info) {
+  __shared__ __align__(16) float row[GATHER_NCAP];
+  const int tid = threadIdx.x;
+  const double l = *lam;
+  const int64_t a0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t a1 = min(n, a0 + rows_per_wg);
+  bool bad = false;
+  for (int64_t a = a0; a < a1; ++a) {
+    const int64_t p = min<int64_t>(max<int64_t>(perm[n - 1 - a], 0), n - 1);
+    const float* src = Sf + p * n;
+    __syncthreads();  // the previous row has been read by every thread
+    if (n % 4 == 0) {
+      for (int64_t c = tid; c < n / 4; c += 512)
+        reinterpret_cast<float4*>(row)[c] = reinterpret_cast<const float4*>(src)[c];
+    } else {
+      for (int64_t c = tid; c < n; c += 512) row[c] = src[c];
+    }
+    __syncthreads();
+    double* dst = A + a * n;
+    for (int64_t b = tid; b <= a; b += 512) {
+      double v;
+      if (b == a) {
+        v = diag[p] + l;
+      } else {
+        const int64_t q = min<int64_t>(max<int64_t>(perm[n - 1 - b], 0), n - 1);
+        const float sv = row[q];
+        bad |= !isfinite(sv);
+        v = 2.0 * (double)sv;
+      }
+      dst[b] = v;
+    }
+  }
+  if (bad) *info = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1346,7 +1484,7 @@ hipError_t join(const PrepWs& w, int64_t n, int64_t o, int64_t s1, int64_t s2, d
   return e;
 }
 
-// X_gg for the group of blocks [b0, b0 + cnt): pairs of blocks, then the two pairs.
+// X_gg for the group of blocks [b0, b0 + cnt): pairs of blocks, then pairs of those, ...
 hipError_t invert_group_diag(const PrepWs& w, int64_t n, int64_t b0, int64_t cnt, double* Mj,
                              hipStream_t st) {
   hipError_t e = hipSuccess;
@@ -1382,6 +1520,7 @@ hipError_t factor_invert(const PrepWs& w, int64_t n, int32_t* info, hipStream_t 
   // measured: 8192 x 8192 prepare 13.6 ms with 4, 15.2 ms with 1; 4096 x 4096 about the
   // same either way (the node chain bounds it)
   const int64_t ob = n >= 6144 ? 4 : 1;
+  const int64_t GRP = grp_blocks(n);
   double* Mg = w.M;
   double* Mj = w.M + GRP * NODE * n;
   auto node = [&](int64_t k) {
@@ -1519,6 +1658,8 @@ size_t prepare_ws_bytes(int64_t n) {
   b += align_up((size_t)n * sizeof(double), 256);
   b += 256;
   b += 2 * align_up((size_t)n * sizeof(int32_t), 256);  // perm, rank
+  b += align_up((size_t)rank_pad(n) * sizeof(double), 256);  // sorted chunk keys
+  b += align_up((size_t)rank_pad(n) * sizeof(int32_t), 256);  // and their columns
   return b;
 }
 
@@ -1530,15 +1671,26 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   hipLaunchKernelGGL(diag_damp_kernel, dim3(1), dim3(1024), 0, stream, S, n, lds, perc_damp,
                      w.diag, dead, w.lam, lambda_out, desc_act ? w.rank : nullptr, info);
   if (desc_act) {
-    hipLaunchKernelGGL(rank_count_kernel,
-                       dim3((unsigned)ceil_div(n, RANK_I), (unsigned)ceil_div(n, RANK_CHUNK)),
-                       dim3(256), 0, stream, w.diag, n, w.rank);
+    const unsigned nch = (unsigned)ceil_div(n, (int64_t)RANK_CHUNK);
+    hipLaunchKernelGGL(chunk_sort_kernel, dim3(nch), dim3(512), 0, stream, w.diag, n, w.skey,
+                       w.sidx);
+    hipLaunchKernelGGL(rank_search_kernel, dim3((unsigned)ceil_div(n, (int64_t)1024), nch),
+                       dim3(256), 0, stream, w.diag, n, w.skey, w.sidx, w.rank);
     hipLaunchKernelGGL(rank_scatter_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
                        w.rank, n, pm);
   } else {
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, pm, n);
   }
-  {
+  if (desc_act && n <= GATHER_NCAP && n >= 1024) {
+    // permuted: symmetric S into X's memory (fp32), then A row by row
+    float* Sf = reinterpret_cast<float*>(w.X);
+    const dim3 grid((unsigned)ceil_div(n, 32), (unsigned)ceil_div(n, 32));
+    hipLaunchKernelGGL(sym_kernel, grid, dim3(256), 0, stream, S, n, lds, Sf);
+    const int64_t wgs = hmin(n, (int64_t)256);
+    const int64_t rpw = ceil_div(n, wgs);
+    hipLaunchKernelGGL(gather_a_kernel, dim3((unsigned)ceil_div(n, rpw)), dim3(512), 0, stream, Sf,
+                       n, pm, w.diag, w.lam, rpw, w.A, info);
+  } else {
     const dim3 grid((unsigned)ceil_div(n, 32), (unsigned)ceil_div(n, 32));
     hipLaunchKernelGGL(build_a_kernel, grid, dim3(256), 0, stream, S, n, lds, pm, w.diag, w.lam,
                        w.A, info);

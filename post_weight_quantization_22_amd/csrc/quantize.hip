@@ -113,9 +113,10 @@ __global__ __launch_bounds__(256) void prep_weights_bf16_kernel(const uint16_t* 
 }
 
 // W' = W[:, perm] as fp32 for bf16 W with desc_act, a row at a time through
-// LDS: the row comes in by coalesced 16-byte loads (the next row's already in
-// flight), is staged in LDS, and leaves in processing order by 16-byte stores
-// of 8 fp32 values, the permuted reads served by the LDS.  Each thread keeps
+// LDS: the row comes in by coalesced 16-byte loads, is staged in LDS, and
+// leaves in processing order by 16-byte stores of 8 fp32 values, the permuted
+// reads served by the LDS.  One LDS row buffer (two barriers a row), so two
+// workgroups share a CU and one's loads overlap the other's gather.  Each thread keeps
 // the source columns of its output segments in registers for all its rows
 // (16-bit entries: the column in bits 0-14, the dead flag in bit 15), so the
 // permutation is read once per workgroup (512 threads).  Needs n % 8 == 0,
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(512) void prep_rows_bf16_kernel(const uint16_t* __r
                                                              int32_t* __restrict__ info) {
   constexpr int CH = NCAP / 8 / 512;  // 16-byte chunks (8 columns) of a row per thread
   static_assert(NCAP <= 32768, "15-bit column entries");
-  __shared__ __align__(16) uint16_t buf[2][NCAP];
+  __shared__ __align__(16) uint16_t buf[NCAP];
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
   const int64_t r1 = min(m, r0 + rows_per_wg);
@@ -159,25 +160,20 @@ __global__ __launch_bounds__(512) void prep_rows_bf16_kernel(const uint16_t* __r
       pk[i][q] = h[0] | (h[1] << 16);
     }
   }
-  uint4 v[CH];
-  auto fetch = [&](int64_t r) {
-    const uint4* src = reinterpret_cast<const uint4*>(W + r * ldw);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 512 * c;
-      if (idx < nseg) v[c] = src[idx];
-    }
-  };
   bool bad = false;
-  fetch(r0);
+  uint16_t* b = buf;
   for (int64_t r = r0; r < r1; ++r) {
-    uint16_t* b = buf[(r - r0) & 1];
+    __syncthreads();  // every thread has gathered the previous row
+    {
+      // the row straight into LDS (no prefetch array: at 8 x 16 bytes a thread
+      // the compiler keeps one in scratch memory)
+      const uint4* src = reinterpret_cast<const uint4*>(W + r * ldw);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 512 * c;
-      if (idx < nseg) reinterpret_cast<uint4*>(b)[idx] = v[c];
+      for (int c = 0; c < CH; ++c) {
+        const int idx = tid + 512 * c;
+        if (idx < nseg) reinterpret_cast<uint4*>(b)[idx] = src[idx];
+      }
     }
-    if (r + 1 < r1) fetch(r + 1);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -510,7 +506,9 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void update_gemm_kernel(UpdArgs g)
   constexpr int WC = TT / (NW / 2);      // columns per wave
   constexpr int SUBA = HW / 16, SUBB = WC / 16;  // MFMA tiles per wave edge
   constexpr int AQ = TT * TK / (4 * NT);  // float4 per thread per operand chunk
-  __shared__ float As[2][TT][TK + 1];
+  // A rows of TK + 4 floats: the operand reads (16 rows x 4 k a wave) fall on
+  // distinct banks and a thread's 4 k of a row go in one 16-byte store
+  __shared__ __align__(16) float As[2][TT][TK + 4];
   __shared__ __align__(16) float Bs[2][TK][TT + 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -543,7 +541,23 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void update_gemm_kernel(UpdArgs g)
   // staging: A chunk TT x 32 (thread: rows tid/8 + (NT/8) q, k 4 (tid%8) .. +3),
   //          B chunk 32 x TT (thread: k (tid / (TT/4)) + (4 NT/TT) q, cols 4 (tid % (TT/4)) .. +3)
   float4 ra[AQ], rb[AQ];
+  // whole chunks of a tile inside E and U take unchecked 16-byte loads
+  const bool full_tile = row0 + TT <= g.m && col0 + TT <= g.nc && g.vec_u;
   auto fetch = [&](int64_t kk0) {
+    if (full_tile && kk0 + TK <= g.kc) {  // uniform over the workgroup
+#pragma unroll
+      for (int q = 0; q < AQ; ++q) {
+        const int rr = (tid >> 3) + (NT / 8) * q, kk = 4 * (tid & 7);
+        ra[q] = *reinterpret_cast<const float4*>(g.E + (row0 + rr) * g.lde + g.k0 + kk0 + kk);
+      }
+#pragma unroll
+      for (int q = 0; q < AQ; ++q) {
+        const int kk = (tid / (TT / 4)) + (4 * NT / TT) * q, cc = 4 * (tid % (TT / 4));
+        rb[q] = *reinterpret_cast<const float4*>(g.U + (g.u0 + kk0 + kk) * g.ldu + g.c0 + col0 +
+                                                 cc);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
       const int rr = (tid >> 3) + (NT / 8) * q, kk = 4 * (tid & 7);
@@ -579,10 +593,8 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void update_gemm_kernel(UpdArgs g)
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
       const int rr = (tid >> 3) + (NT / 8) * q, kk = 4 * (tid & 7);
-      As[buf][rr][kk] = -ra[q].x;
-      As[buf][rr][kk + 1] = -ra[q].y;
-      As[buf][rr][kk + 2] = -ra[q].z;
-      As[buf][rr][kk + 3] = -ra[q].w;
+      *reinterpret_cast<float4*>(&As[buf][rr][kk]) =
+          make_float4(-ra[q].x, -ra[q].y, -ra[q].z, -ra[q].w);
     }
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
@@ -789,7 +801,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   } else if (a.wdt == GPTQ_BF16 && a.desc_act && n % 8 == 0 && a.ldw % 8 == 0 &&
              reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && n <= 32768) {
     // permuted rows through LDS: 32 KB per workgroup up to 8192 columns, else 128 KB
-    const int64_t wgs = hmin(m, n <= 8192 ? 512 : 256);
+    const int64_t wgs = hmin(m, (int64_t)512);  // two workgroups a CU
     const int64_t rpw = ceil_div(m, wgs);
     const dim3 grid((unsigned)ceil_div(m, rpw));
     if (n <= 8192)

@@ -122,6 +122,7 @@ PREP_CASES = [
     (130, 2048, False, 0.0),
     (4500, 9000, True, 0.01),    # trailing updates on the 128 x 128-tile product, ragged
     (8448, 9000, False, 0.01),   # the inverse's block-row products on it as well
+    (16512, 4096, True, 0.01),   # inverse groups of 8 blocks, the last one ragged (1 block)
 ]
 
 
@@ -192,17 +193,41 @@ def test_prepare_reports_not_positive_definite():
     assert 1 <= v <= n
 
 
-def test_prepare_reports_non_finite():
+@pytest.mark.parametrize("n,desc", [(64, False), (1280, True)])
+def test_prepare_reports_non_finite(n, desc):
+    """A NaN below the diagonal of S is reported (at n = 1280 with desc_act the
+    permuted matrix is built through the symmetric copy and the row gather)."""
     q = need_gpu()
-    n = 64
     S = _S_case(n, 256, seed=2)
     S[10, 3] = np.nan
     info = torch.zeros(1, dtype=torch.int32, device="cuda")
     U = torch.empty((n, n), dtype=torch.float32, device="cuda")
-    say("prepare non-finite")
-    q.gptq_prepare(dev(S.astype(np.float32), torch.float32), 256, 0.01, False, U, info=info)
+    say("prepare non-finite", n, desc)
+    q.gptq_prepare(dev(S.astype(np.float32), torch.float32), 256, 0.01, desc, U, info=info)
     torch.cuda.synchronize()
     assert int(host(info)[0]) == -1
+
+
+@pytest.mark.parametrize("n,desc", [(96, False), (1283, True)])
+def test_prepare_reads_only_the_lower_triangle(n, desc):
+    """NaN everywhere above S's diagonal changes nothing: info stays 0 and U is
+    the oracle's (from the lower triangle alone).  n = 1283 with desc_act stages
+    rows of the symmetric copy element by element (n not a multiple of 4)."""
+    q = need_gpu()
+    S = _S_case(n, 2048, seed=6)
+    P = oracle.prepare(S, float(np.float32(0.01)), desc)
+    S2 = S.astype(np.float32)
+    S2[np.triu_indices(n, 1)] = np.nan
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    U = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    say("prepare lower triangle only", n, desc)
+    q.gptq_prepare(dev(S2, torch.float32), 2048, 0.01, desc, U, perm=perm, info=info)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0
+    assert np.array_equal(host(perm), P.perm)
+    Ug = host(U).astype(np.float64)
+    assert np.all(np.abs(Ug - P.U) <= 2.0 ** -22 * np.abs(P.U) + 1e-12 * np.abs(P.U).max())
 
 
 def test_prepare_nan_on_diagonal_with_desc_act():
@@ -232,10 +257,10 @@ def test_prepare_nan_on_diagonal_with_desc_act():
 
 
 def test_prepare_desc_act_order_with_exact_ties_over_several_chunks():
-    """The order kernel counts over column chunks of 1024 and rows of 1024
-    columns per workgroup: at n = 4500 (five of each, the last ragged) with a
-    diagonal of exactly tied values the device order equals the stable
-    descending argsort bit for bit."""
+    """The order kernels sort chunks of 1024 columns and count by binary
+    search in each: at n = 4500 (five chunks, the last ragged) with a diagonal
+    of exactly tied values the device order equals the stable descending
+    argsort bit for bit."""
     q = need_gpu()
     n = 4500
     rng = np.random.default_rng(9)
