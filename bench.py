@@ -521,26 +521,33 @@ def cpu_baseline(wl, rows: int, chunks: int, prep_n: int):
     }
 
 
-def dequant_gemm_measure(gq, buf, X, m, n, q, stream):
+def dequant_gemm_measure(gq, buf, X, m, n, q, stream, desc_act=False):
     """The quantized layer used: Y = X W_q^T from its packed codes (gptq_dequant_gemm).
 
     prefill: one 2048-token calibration sequence, bound by bf16 MFMA (2 tokens m n
     flop); decode: 16 tokens, bound by HBM (codes b/8 B, scale and zero 8 B per
     group, X and Y once per weight).  The decode launches are replayed from a
-    HIP graph so that the host's launch cost is not timed."""
+    HIP graph so that the host's launch cost is not timed.  With desc_act the
+    codes are packed in processing order (gptq_pack_ordered) and the product
+    gathers the activations into that order (timed with it)."""
     import torch
 
     out = {}
     ng = buf.scales.shape[1]
+    packed, perm = buf.packed, None
+    if desc_act:
+        packed = torch.empty_like(buf.packed)
+        gq.gptq_pack_ordered(buf.codes, q.bits, buf.perm, packed, stream=stream)
+        perm = buf.perm
     for name, tokens, reps in (("prefill_2048", 2048, 20), ("decode_16", 16, 200)):
         Xt = X[:tokens]
         Y = torch.empty((tokens, m), dtype=torch.float32, device=X.device)
-        nws = gq.gptq_dequant_gemm_workspace_size(tokens, m, n, False)
+        nws = gq.gptq_dequant_gemm_workspace_size(tokens, m, n, perm is not None)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=X.device)
 
         def call():
-            gq.gptq_dequant_gemm(Xt, buf.packed, q.bits, q.group_size, buf.scales, buf.zeros,
-                                 Y, ws=ws, stream=torch.cuda.current_stream())
+            gq.gptq_dequant_gemm(Xt, packed, q.bits, q.group_size, buf.scales, buf.zeros,
+                                 Y, perm=perm, ws=ws, stream=torch.cuda.current_stream())
 
         for _ in range(3):
             call()
@@ -791,8 +798,8 @@ def main():
         return
 
     print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
-    head, _ = run_workload(gq, wl, dev, args.steps, args.warmup,
-                           breakdown=not args.no_breakdown)
+    head, hstate = run_workload(gq, wl, dev, args.steps, args.warmup,
+                                breakdown=not args.no_breakdown, keep=not args.no_dequant)
     g0 = head["streams"][0]
     ls = wl.layer()
     xs = wl.xs[ls.x]
@@ -853,6 +860,14 @@ def main():
         "input_setup_s": head["input_setup_s"],
         "detail": g0,
     }
+    if hstate is not None:
+        # the headline layer's own product: its codes, its shape, its activation order
+        print("bench: dequantized-weight product of the headline layer", file=sys.stderr,
+              flush=True)
+        out.setdefault("dequant_gemm", {})[args.workload] = dequant_gemm_measure(
+            gq, hstate["buf"], hstate["X"], hstate["m"], hstate["n"], hstate["q"],
+            hstate["stream"], desc_act=bool(hstate["q"].desc_act))
+    del hstate
     torch.cuda.empty_cache()
     if not args.no_extra:
         configs = {}
@@ -867,9 +882,9 @@ def main():
             configs[name] = rec
             if state is not None:
                 if not args.no_dequant:
-                    out["dequant_gemm"] = dequant_gemm_measure(
+                    out.setdefault("dequant_gemm", {})[name] = dequant_gemm_measure(
                         gq, state["buf"], state["X"], state["m"], state["n"], state["q"],
-                        state["stream"])
+                        state["stream"], desc_act=bool(state["q"].desc_act))
                 if not args.no_awq:
                     out["awq"] = awq_measure(gq, state["W"], state["X"], state["buf"].S,
                                              state["m"], state["n"], state["q"], state["stream"])

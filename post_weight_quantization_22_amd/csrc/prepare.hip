@@ -360,43 +360,63 @@ __global__ __launch_bounds__(256) void sym_kernel(const float* __restrict__ S, i
 }
 
 constexpr int GATHER_NCAP = 32768;  // columns of a row staged in LDS (128 KB)
+constexpr int GATHER_T = 1024;      // threads of gather_a_kernel
+constexpr int GATHER_PER = GATHER_NCAP / GATHER_T / 2;  // packed position words a thread
 
-__global__ __launch_bounds__(512) void gather_a_kernel(const float* __restrict__ Sf, int64_t n,
-                                                       const int32_t* __restrict__ perm,
-                                                       const double* __restrict__ diag,
-                                                       const double* __restrict__ lam,
-                                                       int64_t rows_per_wg,
-                                                       double* __restrict__ A,
-                                                       int32_t* __restrict__ info) {
+// Thread t writes columns b = t + GATHER_T j of every row; their sources
+// perm[n-1-b] (16-bit, two to a word) stay in registers for all the
+// workgroup's rows, so perm is read once per workgroup.
+__global__ __launch_bounds__(GATHER_T) void gather_a_kernel(const float* __restrict__ Sf,
+                                                            int64_t n,
+                                                            const int32_t* __restrict__ perm,
+                                                            const double* __restrict__ diag,
+                                                            const double* __restrict__ lam,
+                                                            int64_t rows_per_wg,
+                                                            double* __restrict__ A,
+                                                            int32_t* __restrict__ info) {
   __shared__ __align__(16) float row[GATHER_NCAP];
   const int tid = threadIdx.x;
   const double l = *lam;
   const int64_t a0 = (int64_t)blockIdx.x * rows_per_wg;
   const int64_t a1 = min(n, a0 + rows_per_wg);
+  if (a0 >= a1) return;
+  uint32_t pq[GATHER_PER];
+#pragma unroll
+  for (int j = 0; j < GATHER_PER; ++j) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t b = tid + (int64_t)GATHER_T * (2 * j + e);
+      h[e] = b < n ? (uint32_t)min<int64_t>(max<int64_t>(perm[n - 1 - b], 0), n - 1) : 0u;
+    }
+    pq[j] = h[0] | (h[1] << 16);
+  }
   bool bad = false;
   for (int64_t a = a0; a < a1; ++a) {
     const int64_t p = min<int64_t>(max<int64_t>(perm[n - 1 - a], 0), n - 1);
     const float* src = Sf + p * n;
     __syncthreads();  // the previous row has been read by every thread
     if (n % 4 == 0) {
-      for (int64_t c = tid; c < n / 4; c += 512)
+      for (int64_t c = tid; c < n / 4; c += GATHER_T)
         reinterpret_cast<float4*>(row)[c] = reinterpret_cast<const float4*>(src)[c];
     } else {
-      for (int64_t c = tid; c < n; c += 512) row[c] = src[c];
+      for (int64_t c = tid; c < n; c += GATHER_T) row[c] = src[c];
     }
     __syncthreads();
     double* dst = A + a * n;
-    for (int64_t b = tid; b <= a; b += 512) {
-      double v;
-      if (b == a) {
-        v = diag[p] + l;
-      } else {
-        const int64_t q = min<int64_t>(max<int64_t>(perm[n - 1 - b], 0), n - 1);
-        const float sv = row[q];
-        bad |= !isfinite(sv);
-        v = 2.0 * (double)sv;
+#pragma unroll
+    for (int j = 0; j < GATHER_PER; ++j) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t b = tid + (int64_t)GATHER_T * (2 * j + e);
+        if (b < a) {
+          const float sv = row[(pq[j] >> (16 * e)) & 0xFFFFu];
+          bad |= !isfinite(sv);
+          dst[b] = 2.0 * (double)sv;
+        } else if (b == a) {
+          dst[b] = diag[p] + l;
+        }
       }
-      dst[b] = v;
     }
   }
   if (bad) *info = -1;
@@ -1688,8 +1708,8 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
     hipLaunchKernelGGL(sym_kernel, grid, dim3(256), 0, stream, S, n, lds, Sf);
     const int64_t wgs = hmin(n, (int64_t)256);
     const int64_t rpw = ceil_div(n, wgs);
-    hipLaunchKernelGGL(gather_a_kernel, dim3((unsigned)ceil_div(n, rpw)), dim3(512), 0, stream, Sf,
-                       n, pm, w.diag, w.lam, rpw, w.A, info);
+    hipLaunchKernelGGL(gather_a_kernel, dim3((unsigned)ceil_div(n, rpw)), dim3(GATHER_T), 0,
+                       stream, Sf, n, pm, w.diag, w.lam, rpw, w.A, info);
   } else {
     const dim3 grid((unsigned)ceil_div(n, 32), (unsigned)ceil_div(n, 32));
     hipLaunchKernelGGL(build_a_kernel, grid, dim3(256), 0, stream, S, n, lds, pm, w.diag, w.lam,

@@ -671,63 +671,65 @@ __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
 }
 
 // codes[r, c] = codes_proc[r, inv[c]] a row at a time through LDS: the
-// processing-order row comes in by coalesced 16-byte loads (the next row's in
-// flight), is staged in LDS, and leaves in original order by 16-byte stores
-// (16 codes), the permuted reads served by the LDS.  The source positions
-// (16-bit) sit in LDS too, read once per workgroup.  Needs n % 16 == 0, n <=
-// NCAP <= 32768.  g_idx is written by unpermute_kernel's g_idx-only form.
-template <int NCAP>
-__global__ __launch_bounds__(512) void unpermute_rows_kernel(const uint8_t* __restrict__ cproc,
-                                                             const int32_t* __restrict__ inv,
-                                                             int64_t m, int64_t n,
-                                                             int64_t rows_per_wg,
-                                                             uint8_t* __restrict__ codes) {
-  constexpr int CH = NCAP / 16 / 512;  // 16-byte chunks (16 codes) of a row per thread
+// processing-order row comes in by coalesced 16-byte loads straight into one
+// LDS row buffer (two barriers a row; up to four workgroups share a CU and
+// overlap each other's loads), and leaves in original order by 16-byte stores
+// (16 codes), the permuted reads served by the LDS.  The source positions of
+// a thread's two output segments (16-bit, two to a word) stay in registers,
+// read once per workgroup (NCAP / 32 threads).  Needs n % 16 == 0, n <= NCAP <= 32768.  g_idx is
+// written by unpermute_kernel's g_idx-only form.
+template <int NCAP, int NT = NCAP / 32>
+__global__ __launch_bounds__(NT) void unpermute_rows_kernel(const uint8_t* __restrict__ cproc,
+                                                            const int32_t* __restrict__ inv,
+                                                            int64_t m, int64_t n,
+                                                            int64_t rows_per_wg,
+                                                            uint8_t* __restrict__ codes) {
+  constexpr int CH = NCAP / 16 / NT;  // 16-byte chunks (16 codes) of a row per thread (2)
   static_assert(NCAP <= 32768, "16-bit position entries");
-  __shared__ __align__(16) uint8_t buf[2][NCAP];
-  __shared__ __align__(16) uint16_t pos[NCAP];
+  __shared__ __align__(16) uint8_t buf[NCAP];
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
   const int64_t r1 = min(m, r0 + rows_per_wg);
   if (r0 >= r1) return;
   const int nseg = (int)(n / 16);
-  for (int64_t c = tid; c < n; c += 512) {
-    int64_t k = inv[c];
-    if (k < 0 || k >= n) k = c;  // a malformed permutation must not address out of range
-    pos[c] = (uint16_t)k;
+  uint32_t pk[CH][8];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int sg = tid + NT * i;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t h[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t c = 16 * (int64_t)sg + 2 * q + e;
+        int64_t k = sg < nseg ? inv[c] : 0;
+        if (k < 0 || k >= n) k = c < n ? c : 0;  // a malformed permutation must not address out of range
+        h[e] = (uint32_t)k;
+      }
+      pk[i][q] = h[0] | (h[1] << 16);
+    }
   }
-  uint4 v[CH];
-  auto fetch = [&](int64_t r) {
-    const uint4* src = reinterpret_cast<const uint4*>(cproc + r * n);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 512 * c;
-      if (idx < nseg) v[c] = src[idx];
-    }
-  };
-  fetch(r0);
   for (int64_t r = r0; r < r1; ++r) {
-    uint8_t* b = buf[(r - r0) & 1];
+    __syncthreads();  // every thread has read the previous row
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(cproc + r * n);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 512 * c;
-      if (idx < nseg) reinterpret_cast<uint4*>(b)[idx] = v[c];
+      for (int c = 0; c < CH; ++c) {
+        const int idx = tid + NT * c;
+        if (idx < nseg) reinterpret_cast<uint4*>(buf)[idx] = src[idx];
+      }
     }
-    if (r + 1 < r1) fetch(r + 1);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int sg = tid + 512 * i;
+      const int sg = tid + NT * i;
       if (sg < nseg) {
-        const uint4 p0 = reinterpret_cast<const uint4*>(pos)[2 * sg];
-        const uint4 p1 = reinterpret_cast<const uint4*>(pos)[2 * sg + 1];
-        const uint32_t pk[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t a = pk[2 * q], c2 = pk[2 * q + 1];
-          w[q] = (uint32_t)b[a & 0xFFFFu] | ((uint32_t)b[a >> 16] << 8) |
-                 ((uint32_t)b[c2 & 0xFFFFu] << 16) | ((uint32_t)b[c2 >> 16] << 24);
+          const uint32_t a = pk[i][2 * q], c2 = pk[i][2 * q + 1];
+          w[q] = (uint32_t)buf[a & 0xFFFFu] | ((uint32_t)buf[a >> 16] << 8) |
+                 ((uint32_t)buf[c2 & 0xFFFFu] << 16) | ((uint32_t)buf[c2 >> 16] << 24);
         }
         *reinterpret_cast<uint4*>(codes + r * n + 16 * (int64_t)sg) =
             make_uint4(w[0], w[1], w[2], w[3]);
@@ -870,14 +872,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
                        a.perm, n, inv);
     if (n % 16 == 0 && n <= 32768) {
       // codes through LDS rows; g_idx by the per-column kernel alone
-      const int64_t wgs = hmin(m, n <= 16384 ? 512 : 256);
+      const int64_t wgs = hmin(m, (int64_t)1024);
       const int64_t rpw = ceil_div(m, wgs);
       const dim3 grid((unsigned)ceil_div(m, rpw));
       if (n <= 16384)
         hipLaunchKernelGGL(unpermute_rows_kernel<16384>, grid, dim3(512), 0, stream, cproc, inv,
                            m, n, rpw, a.codes);
       else
-        hipLaunchKernelGGL(unpermute_rows_kernel<32768>, grid, dim3(512), 0, stream, cproc, inv,
+        hipLaunchKernelGGL(unpermute_rows_kernel<32768>, grid, dim3(1024), 0, stream, cproc, inv,
                            m, n, rpw, a.codes);
       if (a.g_idx)
         hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)ceil_div(n, 256), 1), dim3(256), 0,
