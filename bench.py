@@ -595,6 +595,46 @@ def dequant_gemm_measure(gq, buf, X, m, n, q, stream, desc_act=False):
     return out
 
 
+def layer_error_measure(gq, W, buf, m, n, q, stream):
+    """The layer objective ||W X - W_q X||^2 over the calibration tokens, from S, on the
+    device (gptq_layer_error), for the step's GPTQ codes and for RTN's on the same
+    layer; timed with HIP events (one call, after a warm-up), against the fp32 MFMA
+    peak (m n^2 flop: the product of the differences with S)."""
+    import torch
+
+    err = torch.empty(m, dtype=torch.float64, device=W.device)
+    ws = torch.empty(gq.gptq_layer_error_workspace_size(m, n), dtype=torch.uint8,
+                     device=W.device)
+
+    def call(codes, scales, zeros, g_idx):
+        gq.gptq_layer_error(W, codes, scales, zeros, g_idx, buf.S, err, ws=ws, stream=stream)
+
+    call(buf.codes, buf.scales, buf.zeros, buf.g_idx)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    call(buf.codes, buf.scales, buf.zeros, buf.g_idx)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    gptq = float(err.sum().item())
+    rc, rs, rz = torch.empty_like(buf.codes), torch.empty_like(buf.scales), torch.empty_like(
+        buf.zeros)
+    gq.rtn_minmax(W, q.bits, q.group_size, rc, rs, rz, sym=bool(q.sym), stream=stream)
+    G = q.group_size if q.group_size > 0 else n
+    rg = (torch.arange(n, device=W.device, dtype=torch.int32) // G).contiguous()
+    call(rc, rs, rz, rg)
+    torch.cuda.synchronize()
+    rtn = float(err.sum().item())
+    tf = m * n * n / (ms * 1e-3) / 1e12
+    return {"gptq": gptq, "rtn": rtn, "gptq_over_rtn": round(gptq / rtn, 4),
+            "ms": round(ms, 3), "tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4)},
+            "what": "sum over rows of delta_r S delta_r^T (gptq_layer_error), the step's GPTQ "
+                    "codes and RTN (group min-max) on the same layer"}
+
+
 def awq_measure(gq, W, X, S, m, n, q, stream):
     """AWQ-lite then awq_clip on the same layer and calibration set (S = X^T X from
     the Hessian step): the activation statistic (one pass over X, bound by HBM),
@@ -860,6 +900,9 @@ def main():
         "input_setup_s": head["input_setup_s"],
         "detail": g0,
     }
+    if hstate is not None:
+        out["layer_error"] = layer_error_measure(gq, hstate["W"], hstate["buf"], hstate["m"],
+                                                 hstate["n"], hstate["q"], hstate["stream"])
     if hstate is not None:
         # the headline layer's own product: its codes, its shape, its activation order
         print("bench: dequantized-weight product of the headline layer", file=sys.stderr,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 0x00020004u /* major 2, minor 4 */
+#define GPTQ_ABI_VERSION 0x00020005u /* major 2, minor 5 */
 
 typedef enum gptq_status {
   GPTQ_OK = 0,
@@ -350,6 +350,32 @@ gptq_status awq_clip_quantize(const void* W, gptq_dtype wdt, int64_t m, int64_t 
 gptq_status rtn_minmax(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
                        int32_t bits, int32_t group_size, int32_t sym, uint8_t* codes,
                        float* scales, float* zeros, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Layer reconstruction error -- "LLM quantization principles: GPTQ, AWQ,
+ * GGUF" (0539edu.com news 6111416), section 3.1: the quantity GPTQ minimizes
+ * layer by layer is the output error ||W X - W_q X||^2 over the calibration
+ * inputs.  Through the raw second moments S = X^T X of gptq_hessian_accumulate
+ * (lower triangle read, lds >= n):
+ *   err[r] = delta_r S delta_r^T = sum over calibration tokens of (delta_r . x_t)^2,
+ *   delta_r = W[r] - W_q[r],  W_q[r][c] = scales[r][g] * (codes[r][c] - zeros[r][g]),
+ *   g = g_idx[c]
+ * for W [m, n] (row stride ldw, fp32 or bf16) and the ORIGINAL-order outputs
+ * of gptq_quantize_layer or rtn_minmax: codes [m, n] (row stride n),
+ * scales/zeros [m, ngroups], g_idx [n] (for rtn_minmax, g_idx[c] =
+ * c / group_size).  The sum over rows is the layer objective (half of
+ * delta^T H delta with H = 2S, undamped).  err: double [m] on the device.
+ * fp32 differences and products (the fp32 MFMA update product), each row
+ * summed in fp64 in a fixed order: deterministic.  g_idx entries outside
+ * [0, ngroups) are clamped.  m == 0 is a no-op.  Workspace:
+ * gptq_layer_error_workspace_size(m, n) bytes (S made symmetric, the
+ * differences and their product with S, in fp32).
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_layer_error_workspace_size(int64_t m, int64_t n, size_t* bytes);
+gptq_status gptq_layer_error(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                             const uint8_t* codes, const float* scales, const float* zeros,
+                             int64_t ngroups, const int32_t* g_idx, const float* S, int64_t lds,
+                             double* err, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,8 @@ from ._lib import (  # noqa: F401
     gptq_gemm_bf16,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_size,
+    gptq_layer_error,
+    gptq_layer_error_workspace_size,
     gptq_pack,
     gptq_pack_ordered,
     gptq_prepare,

@@ -51,6 +51,8 @@ EXPORTED = (
     "awq_lite",
     "awq_clip_quantize",
     "rtn_minmax",
+    "gptq_layer_error_workspace_size",
+    "gptq_layer_error",
 )
 
 
@@ -147,6 +149,11 @@ def load() -> ctypes.CDLL:
                                       _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.rtn_minmax.restype = _i32
     lib.rtn_minmax.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.gptq_layer_error_workspace_size.restype = _i32
+    lib.gptq_layer_error_workspace_size.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.gptq_layer_error.restype = _i32
+    lib.gptq_layer_error.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
+                                     _i64, _vp, _vp, _sz, _vp]
     _lib = lib
     return lib
 
@@ -556,3 +563,30 @@ def rtn_minmax(W, bits: int, group_size: int, codes, scales, zeros, sym: bool = 
     _check(load().rtn_minmax(_ptr(W), _dtype_code(W), m, n, _ld(W), int(bits), int(group_size),
                              int(sym), _ptr(codes), _ptr(scales), _ptr(zeros), _stream(stream)),
            "rtn_minmax")
+
+
+def gptq_layer_error_workspace_size(m: int, n: int) -> int:
+    out = _sz()
+    _check(load().gptq_layer_error_workspace_size(int(m), int(n), ctypes.byref(out)),
+           "gptq_layer_error_workspace_size")
+    return int(out.value)
+
+
+def gptq_layer_error(W, codes, scales, zeros, g_idx, S, err, ws=None, stream=None) -> None:
+    """err[m] (float64) = per-row output error delta_r S delta_r^T of the quantized layer."""
+    m, n = W.shape
+    d = W.device
+    ng = scales.shape[1] if scales.dim() == 2 else 0
+    _buf(codes, "codes", (m, n), ("uint8",), d, optional=False)
+    _buf(scales, "scales", (m, ng), ("float32",), d, optional=False)
+    _buf(zeros, "zeros", (m, ng), ("float32",), d, optional=False)
+    _buf(g_idx, "g_idx", (n,), _INT32_LIKE, d, optional=False)
+    _mat(S, "S", n, n, ("float32",), d)
+    _buf(err, "err", (m,), ("float64",), d, optional=False)
+    if ws is None:
+        ws = _workspace(gptq_layer_error_workspace_size(m, n), d, stream)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().gptq_layer_error(_ptr(W), _dtype_code(W), m, n, _ld(W), _ptr(codes),
+                                   _ptr(scales), _ptr(zeros), int(ng), _ptr(g_idx), _ptr(S),
+                                   _ld(S), _ptr(err), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_layer_error")

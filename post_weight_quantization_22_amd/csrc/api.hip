@@ -271,6 +271,26 @@ gptq_status awq_lite(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_
                                     sym, n_alpha, s_out, alpha_out, losses, ws, stream));
 }
 
+gptq_status gptq_layer_error_workspace_size(int64_t m, int64_t n, size_t* bytes) {
+  if (!bytes || bad_dim(m) || n <= 0 || bad_dim(n)) return GPTQ_ERR_INVALID_ARG;
+  *bytes = layer_error_ws_bytes(m, n);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_layer_error(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
+                             const uint8_t* codes, const float* scales, const float* zeros,
+                             int64_t ngroups, const int32_t* g_idx, const float* S, int64_t lds,
+                             double* err, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!W || !codes || !scales || !zeros || !g_idx || !S || !err || bad_dim(m) || n <= 0 ||
+      bad_dim(n) || ldw < n || lds < n || ngroups < 1 || ngroups > n || !valid_dtype(wdt))
+    return GPTQ_ERR_INVALID_ARG;
+  if (m == 0) return GPTQ_OK;
+  const gptq_status w = check_ws(ws, ws_bytes, layer_error_ws_bytes(m, n));
+  if (w != GPTQ_OK) return w;
+  return hip_status(launch_layer_error(W, wdt, m, n, ldw, codes, scales, zeros, ngroups, g_idx, S,
+                                       lds, err, ws, stream));
+}
+
 gptq_status awq_clip_quantize(const void* W, gptq_dtype wdt, int64_t m, int64_t n, int64_t ldw,
                               const float* S, int64_t lds, const float* s, int32_t bits,
                               int32_t group_size, int32_t sym, int32_t n_steps, uint8_t* codes,

@@ -26,7 +26,8 @@
 // (shorter units keep an XCD's workgroups on the same token rows, so they
 // share them through its L2).
 //
-// fp32 path (fp32 activations; small layers): a SIMT fp32 SYRK, lower tiles.
+// fp32 path (fp32 activations; small layers): 64 x 64 lower tiles on the fp32
+// MFMA (v_mfma_f32_16x16x4_f32).
 #include "kernels.hpp"
 
 namespace gptq {
@@ -525,47 +526,78 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
 }
 
 // fp32 activations: SIMT SYRK, 64x64 lower tiles, 256 threads x 4x4 outputs.
-constexpr int FT = 64, FK = 16;
+// fp32 activations: S += X^T X on v_mfma_f32_16x16x4_f32.  64 x 64 lower
+// tiles, one per workgroup of 4 waves (each 32 x 32: 2 x 2 MFMA tiles), 64
+// tokens a stage staged in LDS in X's own token-major layout (row stride 80
+// floats: the 4 k rows of an operand read fall on distinct banks), the next
+// stage's loads in registers while this one is multiplied.  Any n, tokens,
+// ldx (bounds-checked loads; zeros past the ends).  fp32 products and sums:
+// each entry within (tokens + 8) 2^-24 sum_t |x_ti x_tj| of the exact sum.
+constexpr int FT = 64, FK = 64, FLD = FT + 16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ X, int64_t ldx,
                                                        int64_t tokens, int64_t n,
                                                        float* __restrict__ S, int64_t lds) {
-  __shared__ float As[FK][FT + 1];
-  __shared__ float Bs[FK][FT + 1];
+  __shared__ float As[FK][FLD];
+  __shared__ float Bs[FK][FLD];
   int64_t ti, tj;
   tile_coords(blockIdx.x, ti, tj);
   const int64_t i0 = ti * FT, j0 = tj * FT;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int64_t t0 = 0; t0 < tokens; t0 += FK) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < FK * FT; idx += 256) {
-      const int kk = idx / FT, cc = idx % FT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wi = wv >> 1, wj = wv & 1;
+  constexpr int PER = FK * FT / 256;  // elements a thread stages per operand (16)
+  float ra[PER], rb[PER];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + 256 * e, kk = idx / FT, cc = idx % FT;
       const int64_t t = t0 + kk;
-      As[kk][cc] = (t < tokens && i0 + cc < n) ? X[t * ldx + i0 + cc] : 0.0f;
-      Bs[kk][cc] = (t < tokens && j0 + cc < n) ? X[t * ldx + j0 + cc] : 0.0f;
+      ra[e] = (t < tokens && i0 + cc < n) ? X[t * ldx + i0 + cc] : 0.0f;
+      rb[e] = (t < tokens && j0 + cc < n) ? X[t * ldx + j0 + cc] : 0.0f;
+    }
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  fetch(0);
+  for (int64_t t0 = 0; t0 < tokens; t0 += FK) {
+    __syncthreads();  // every wave has read the previous stage
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + 256 * e, kk = idx / FT, cc = idx % FT;
+      As[kk][cc] = ra[e];
+      Bs[kk][cc] = rb[e];
     }
     __syncthreads();
+    if (t0 + FK < tokens) fetch(t0 + FK);
 #pragma unroll
-    for (int kk = 0; kk < FK; ++kk) {
-      float a[4], b[4];
+    for (int ks = 0; ks < FK; ks += 4) {
+      float af[2], bf[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = As[kk][ty + 16 * u];
-        b[u] = Bs[kk][tx + 16 * u];
-      }
+      for (int a = 0; a < 2; ++a) af[a] = As[ks + (lane >> 4)][32 * wi + 16 * a + (lane & 15)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int b = 0; b < 2; ++b) bf[b] = Bs[ks + (lane >> 4)][32 * wj + 16 * b + (lane & 15)];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
   }
+  // D layout: lane l, element q -> row 4 (l / 16) + q, column l % 16
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t gi = i0 + ty + 16 * u, gj = j0 + tx + 16 * v;
-      if (gi < n && gj <= gi) S[gi * lds + gj] += acc[u][v];
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t gi = i0 + 32 * wi + 16 * a + 4 * (lane >> 4) + q;
+        const int64_t gj = j0 + 32 * wj + 16 * b + (lane & 15);
+        if (gi < n && gj <= gi) S[gi * lds + gj] += acc[a][b][q];
+      }
 }
 
 struct HessPlan {

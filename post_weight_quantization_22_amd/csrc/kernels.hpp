@@ -102,6 +102,13 @@ void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t 
                    int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream);
 hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream);
 
+// ---- error.hip ------------------------------------------------------------
+size_t layer_error_ws_bytes(int64_t m, int64_t n);
+hipError_t launch_layer_error(const void* W, int wdt, int64_t m, int64_t n, int64_t ldw,
+                              const uint8_t* codes, const float* scales, const float* zeros,
+                              int64_t ngroups, const int32_t* g_idx, const float* S, int64_t lds,
+                              double* err, void* ws, hipStream_t stream);
+
 // ---- forward.hip ----------------------------------------------------------
 hipError_t launch_swiglu(const float* G, int64_t ldg, const float* U, int64_t ldu, int64_t rows,
                          int64_t n, void* H, int64_t ldh, hipStream_t stream);

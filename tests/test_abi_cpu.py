@@ -293,3 +293,25 @@ def test_noalloc_quantize_validation(lib):
     need = lib.gptq_quantize_workspace_size(4096, 2048, cfg)
     assert need <= lib.GPTQ_NOALLOC_SCRATCH_BYTES < lib.gptq_quantize_workspace_size(4096, 4096,
                                                                                        cfg)
+
+
+def test_layer_error_validation(lib):
+    so = lib.load()
+    n = ctypes.c_size_t(0)
+    assert so.gptq_layer_error_workspace_size(64, 256, ctypes.byref(n)) == lib.GPTQ_OK
+    # symmetric S [n, 4-padded n] and the differences and their product [m, 4-padded n], fp32
+    assert n.value >= 4 * (256 * 256 + 2 * 64 * 256)
+    assert so.gptq_layer_error_workspace_size(64, 0, ctypes.byref(n)) == lib.GPTQ_ERR_INVALID_ARG
+
+    def call(m=64, nn=256, ldw=256, ng=2, lds=256, dt=1, ws=1 << 40, gidx=FAKE):
+        return so.gptq_layer_error(FAKE, dt, m, nn, ldw, FAKE, FAKE, FAKE, ng, gidx, FAKE, lds,
+                                   FAKE, FAKE, ws, None)
+
+    assert call(m=0) == lib.GPTQ_OK  # nothing to do, nothing enqueued
+    assert call(ldw=100) == lib.GPTQ_ERR_INVALID_ARG
+    assert call(lds=100) == lib.GPTQ_ERR_INVALID_ARG
+    assert call(ng=0) == lib.GPTQ_ERR_INVALID_ARG
+    assert call(ng=257) == lib.GPTQ_ERR_INVALID_ARG  # more groups than columns
+    assert call(dt=7) == lib.GPTQ_ERR_INVALID_ARG
+    assert call(gidx=None) == lib.GPTQ_ERR_INVALID_ARG
+    assert call(ws=16) == lib.GPTQ_ERR_WORKSPACE

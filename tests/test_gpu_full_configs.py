@@ -15,7 +15,8 @@ and on properties that hold at any size:
     rate with its root and cascade counts, and the replay check for rounding
     ties on every row;
   - the packed words on a sample of rows, and the reconstruction error on all
-    rows (a sample of 1024 rows for the 28672-wide layer).
+    rows (a sample of 1024 rows for the 28672-wide layer), also on the device
+    (gptq_layer_error), where GPTQ's must come out below RTN's.
 """
 import time
 
@@ -105,7 +106,7 @@ def _check_order_and_U(buf, S_dev, perc_damp, desc_act):
     return U32, perm, dead
 
 
-def _check_rows(wl, lname, buf, pool, perm, dead, S_dev):
+def _check_rows(wl, lname, buf, pool, perm, dead, S_dev, Wd):
     """The column loop on every row, given the device's U (in ``pool``)."""
     q = wl.quant
     ls = wl.layer(lname)
@@ -155,6 +156,28 @@ def _check_rows(wl, lname, buf, pool, perm, dead, S_dev):
     print(f"{lname}: reconstruction error on {len(er)} rows: device {e_dev:.6e} oracle "
           f"{e_ref:.6e} rel {rel:.2e}", flush=True)
     assert rel <= 1e-3
+    # the same objective on the device (gptq_layer_error), every row; and RTN's
+    q_ = need_gpu()
+    err = torch.empty(ls.m, dtype=torch.float64, device="cuda")
+    q_.gptq_layer_error(Wd, buf.codes, buf.scales, buf.zeros, buf.g_idx, buf.S, err)
+    ng = buf.scales.shape[1]
+    rc = torch.empty_like(buf.codes)
+    rs = torch.empty_like(buf.scales)
+    rz = torch.empty_like(buf.zeros)
+    q_.rtn_minmax(Wd, q.bits, q.group_size, rc, rs, rz)
+    G = q.group_size if q.group_size > 0 else ls.n
+    rg = (torch.arange(ls.n, device="cuda", dtype=torch.int32) // G).contiguous()
+    err_rtn = torch.empty(ls.m, dtype=torch.float64, device="cuda")
+    q_.gptq_layer_error(Wd, rc, rs, rz, rg, buf.S, err_rtn)
+    torch.cuda.synchronize()
+    e_k9 = host(err)
+    e_k9_er = float(e_k9[er].sum())
+    gp, rt = float(e_k9.sum()), float(host(err_rtn).sum())
+    print(f"{lname}: gptq_layer_error on those rows {e_k9_er:.6e} (host through the device's S "
+          f"{e_dev:.6e}, rel {abs(e_k9_er - e_dev) / e_dev:.2e}); whole layer GPTQ {gp:.6e} "
+          f"RTN {rt:.6e} ratio {gp / rt:.4f} ({ng} groups a row)", flush=True)
+    assert abs(e_k9_er - e_dev) <= 1e-4 * e_dev
+    assert gp < rt
 
 
 def _run(wl_name, xname, layer_names):
@@ -198,7 +221,7 @@ def _run(wl_name, xname, layer_names):
             pipeline.pack(buf)
             torch.cuda.synchronize()
             pipeline.check_info(buf)
-            _check_rows(wl, lname, buf, pool, perm, dead, S_dev)
+            _check_rows(wl, lname, buf, pool, perm, dead, S_dev, Wd)
             del Wd
 
 
