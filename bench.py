@@ -599,7 +599,7 @@ def layer_error_measure(gq, W, buf, m, n, q, stream):
     """The layer objective ||W X - W_q X||^2 over the calibration tokens, from S, on the
     device (gptq_layer_error), for the step's GPTQ codes and for RTN's on the same
     layer; timed with HIP events (one call, after a warm-up), against the fp32 MFMA
-    peak (m n^2 flop: the product of the differences with S)."""
+    peak (2 m n^2 flop: the product of the differences with S)."""
     import torch
 
     err = torch.empty(m, dtype=torch.float64, device=W.device)
@@ -626,7 +626,7 @@ def layer_error_measure(gq, W, buf, m, n, q, stream):
     call(rc, rs, rz, rg)
     torch.cuda.synchronize()
     rtn = float(err.sum().item())
-    tf = m * n * n / (ms * 1e-3) / 1e12
+    tf = 2.0 * m * n * n / (ms * 1e-3) / 1e12
     return {"gptq": gptq, "rtn": rtn, "gptq_over_rtn": round(gptq / rtn, 4),
             "ms": round(ms, 3), "tflops": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS,

@@ -1423,9 +1423,13 @@ hipError_t launch_bits(const DqArgs& a, int bm, hipStream_t stream) {
 void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t tokens,
                    int64_t n, int64_t ldxp, uint16_t* Xp, hipStream_t stream) {
   if (tokens <= 0) return;
-  // (ldxp bounds the output segments a thread holds positions for)
-  const bool rows = n % 8 == 0 && ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
-                    ldxp <= 32768;
+  // (ldxp bounds the output segments a thread holds positions for).  Rows
+  // staged in LDS pay for reading the permutation once per workgroup over its
+  // rows; below 64 tokens (decode batches) the per-element gather spreads the
+  // few rows over many workgroups instead (16 x 28672: 35 us staged in 4
+  // workgroups)
+  const bool rows = tokens >= 64 && n % 8 == 0 && ldx % 8 == 0 &&
+                    (reinterpret_cast<uintptr_t>(X) & 15) == 0 && ldxp <= 32768;
   if (rows) {
     // about 1024 workgroups, at least 4 rows each
     const int64_t rpw = hmax((int64_t)4, ceil_div(tokens, (int64_t)1024));
@@ -1498,8 +1502,11 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
                    (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 && a.ldx < (int64_t(1) << 23) &&
                    d.ldp < (int64_t(1) << 23);
   hipError_t e;
-  // up to 16 tokens: the single-kernel path (whole K per workgroup)
-  const bool gv16 = dma && d.tokens <= 16 && d.n % 128 == 0 &&
+  // up to 16 tokens and n <= 8192: the single-kernel path (whole K per
+  // workgroup).  Each workgroup of 16 rows reads all of X from the L2, which
+  // at large n costs more than the split path's partial sums (at 8192 x
+  // 28672, 16 tokens: the split path reads X once per 128-row block)
+  const bool gv16 = dma && d.tokens <= 16 && d.n % 128 == 0 && d.n <= 8192 &&
                     (d.group_size <= 0 || d.group_size % 32 == 0);
   if (gv16) {
     const dim3 grid((unsigned)ceil_div(d.m, 16));

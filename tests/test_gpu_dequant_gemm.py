@@ -268,10 +268,11 @@ def test_dequant_gemm_full_size(name, m, n, bits, G, perm_on, tokens):
 
 
 @pytest.mark.parametrize("tokens,n,ldx,ldxp", [
-    (37, 4096, 4096, 4096),      # rows staged in LDS (n <= 16384)
-    (9, 11008, 11016, 11008),    # row stride past n
-    (5, 20000, 20000, 20008),    # the 32768-position LDS variant, zeroed tail of Xp
+    (67, 4096, 4096, 4096),      # rows staged in LDS (n <= 16384, >= 64 tokens)
+    (64, 11008, 11016, 11008),   # row stride past n
+    (70, 20000, 20000, 20008),   # the 32768-position LDS variant, zeroed tail of Xp
     (3, 77, 77, 80),             # n not a multiple of 8: the per-element gather
+    (16, 28672, 28672, 28672),   # a decode batch: the per-element gather
     (1000, 256, 256, 256),       # many rows per workgroup
 ])
 def test_gather_columns_exact(tokens, n, ldx, ldxp):
