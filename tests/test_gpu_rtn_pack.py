@@ -68,7 +68,7 @@ def test_rtn_strided_input():
     assert np.array_equal(host(scales).astype(np.float64), scales_o)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n", [1, 7, 33, 100, 4096])
 def test_pack_bit_exact(bits, n):
     q = need_gpu()
@@ -84,3 +84,22 @@ def test_pack_bit_exact(bits, n):
     got = host(packed).view(np.uint32)
     assert np.array_equal(got, ref)
     assert np.array_equal(oracle.unpack_ref(got, n, bits), codes.astype(np.int64))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("n", [1, 31, 100, 4096])
+def test_pack_ordered_bit_exact(bits, n):
+    """gptq_pack_ordered: row r's stream holds codes[r, perm[0]], codes[r, perm[1]], ...
+    in the gptq_pack layout, bit for bit against the oracle's packing of the
+    permuted codes."""
+    q = need_gpu()
+    m = 5
+    rng = np.random.default_rng(bits * 31 + n)
+    codes = rng.integers(0, 2 ** bits, (m, n)).astype(np.uint8)
+    perm = rng.permutation(n).astype(np.int32)
+    ref = oracle.pack_ref(codes[:, perm], bits)
+    packed = torch.full((m, ref.shape[1]), -1, dtype=torch.int32, device="cuda")
+    say("pack ordered", bits, n)
+    q.gptq_pack_ordered(dev(codes, torch.uint8), bits, dev(perm, torch.int32), packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(packed).view(np.uint32), ref)
