@@ -279,30 +279,51 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 
 // Interior kernel: every tile full (n % 256 == 0), every split a whole number
 // of 64-token stages, rows 16-byte aligned; no bounds checks.  256 x 256 lower
-// tiles, 512 threads = 8 waves (2 per SIMD), each a 128 x 64 block (4 x 2
-// MFMA accumulators), so one wave's waits are covered by its SIMD partner's
-// MFMAs.  Each 64-token stage of the two 256-channel operands
-// goes from global memory straight into LDS with global_load_lds_dwordx4 (16
-// bytes per lane, lane l landing at base + 16 l), in X's own token-major
-// layout: token row t takes 512 bytes and 16-byte chunk k of the row sits at
-// position k ^ 4 (t % 4).  MFMA operands come back with ds_read_b64_tr_b16,
-// which hands each 16-lane group a 4-token x 16-channel block transposed
-// (lane i: channel i, 4 consecutive tokens), i.e. the bf16 operand layout, so
-// there is no register staging and no permute.  With the swizzle the 16 lanes
-// x 4 tokens of a half-wave read 16 distinct chunk positions: all 64 banks.
-// Two LDS buffers: the DMA of stage s + 2 is issued as soon as stage s is in
-// registers.  The one barrier per stage (publishing stage s + 1) sits before
-// the MFMAs of the last 16 tokens of stage s, so the first operands of stage
-// s + 1 are read while those MFMAs run.  Diagonal tiles do the same work as
-// the others (both operands loaded, every wave busy): tiles that finish early
-// would start their next unit early and pull the workgroups of an XCD out of
-// step, so that they no longer share the same token rows in its L2 (measured:
-// 8 % faster than skipping the waves above the diagonal).
+// tiles, 1024 threads = 16 waves (4 per SIMD), each a 64 x 64 block of 4 x 4
+// v_mfma_f32_16x16x32_bf16 accumulators (k-step 32 tokens), so one wave's
+// waits are covered by the MFMAs of the three others on its SIMD.  Each
+// output element is accumulated by one wave in token order.  The kernel is
+// power-bound (the shader clock, not the MFMA pipes' busy fraction, sets the
+// rate): at 28672 channels, 16 x 16 x 32 MFMAs run 6-8 % faster than
+// 32 x 32 x 16 ones over the same tile (half the accumulator traffic per
+// flop), and 16 waves faster than 8 waves of 128 x 64, which read a third
+// less from LDS but leave each SIMD one partner wave.
+//
+// Each 64-token stage of the two 256-channel operands goes from global memory
+// straight into LDS with global_load_lds_dwordx4 (16 bytes per lane, lane l
+// landing at base + 16 l), in X's own token-major layout: token row t takes
+// 512 bytes and 16-byte chunk k of the row sits at position
+// k ^ (4 (t % 4) + 2 ((t / 8) % 2)).  MFMA operands come back with
+// ds_read_b64_tr_b16, which hands each 16-lane group a 4-token x 16-channel
+// block transposed (lane i: channel i, 4 consecutive tokens), i.e. the bf16
+// operand layout, so there is no register staging and no permute.  With the
+// swizzle the two 16-lane groups of a half-wave (tokens t .. t + 3 and
+// t + 8 .. t + 11, the same two chunks of each row) read 16 distinct chunk
+// positions: all 64 banks.  Two LDS buffers: the DMA of stage s + 2 is issued
+// as soon as stage s is in registers.  The one barrier per stage (publishing
+// stage s + 1) sits before the MFMAs of the last 32 tokens of stage s, whose
+// operands are already in registers; each operand register is refilled for
+// the next k-step right after its last MFMA, so LDS reads run under the
+// MFMAs.  Diagonal tiles do the same work as the others (both operands
+// loaded, every wave busy): tiles that finish early would start their next
+// unit early and pull the workgroups of an XCD out of step, so that they no
+// longer share the same token rows in its L2 (measured: 8 % faster than
+// skipping the waves above the diagonal).
 constexpr int FT_I = 256, FT_J = 256;   // tile
-constexpr int WI = 128, WJ = 64;        // per wave
+constexpr int WI = 64, WJ = 64;         // per wave
+constexpr int MA = WI / 16, MB = WJ / 16;  // 16 x 16 accumulators per wave
+constexpr int HWAVES = (FT_I / WI) * (FT_J / WJ);
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int DROW = FT_I * 2;    // bytes per token row of one operand stage
 constexpr int DSTAGE = HK * DROW;  // 32 KB per operand per stage
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
   // two transposing reads: tokens +0..3 and +4..7 of this lane's channel
@@ -315,7 +336,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* p0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(64 * HWAVES) void syrk_bf16_dma_kernel(const uint16_t* __restrict__ X,
                                                             int64_t ldx, int64_t tokens,
                                                             int64_t P, int64_t T2,
                                                             float* __restrict__ S, int64_t lds,
@@ -324,8 +345,10 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
   __shared__ __align__(16) uint8_t smem[4 * DSTAGE];  // [buffer][operand]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  constexpr int RPW = HK / 8;  // token rows loaded per wave per operand
-  const int wr = wv >> 2, wc = wv & 3;
+  constexpr int RPW = HK / HWAVES;  // token rows loaded per wave per operand
+  static_assert(RPW % 4 == 0 && 8 % RPW == 0,
+                "a wave's rows: whole groups of 4, inside one group of 8");
+  const int wr = wv / (FT_J / WJ), wc = wv % (FT_J / WJ);
   int64_t p, ti, tj, slot;
   bool half;
   hess_unit(blockIdx.x, P, ntiles_edge, T2, p, ti, tj, half, slot);
@@ -334,19 +357,23 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
   const int nstage = (int)(tok_per_split / HK);
 
   // DMA: instruction q of wave wv fills token rows RPW wv + 2 q and + 1 (lane
-  // / 32); the swizzle depends on the row only through (2 q + lane / 32) % 4,
-  // so two per-lane offsets (q even / odd) serve all q, with the rest of the
-  // address wave-uniform.
+  // / 32); the swizzle depends on the row only through (2 q + lane / 32) % 4
+  // and bit 3 of RPW wv, so two per-lane offsets (q even / odd) serve all q,
+  // with the rest of the address wave-uniform.
+  const int b3 = ((RPW * wv) >> 3) & 1;
   uint32_t voff[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int t = 2 * q + (lane >> 5);
-    const int k = (lane & 31) ^ (4 * (t & 3));
+    const int k = (lane & 31) ^ (4 * (t & 3) + 2 * b3);
     voff[q] = (uint32_t)(2 * (t * ldx + 8 * k));
   }
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  const char* xa = reinterpret_cast<const char*>(X + (p * tok_per_split + RPW * wvu) * ldx + i0);
-  const int64_t jmi2 = 2 * (j0 - i0);
+  // the tile offsets come out of the unit's float arithmetic, where the
+  // compiler cannot see that they are wave-uniform; the DMA wants them in SGPRs
+  const char* xa = reinterpret_cast<const char*>(
+      X + uniform64((p * tok_per_split + RPW * wvu) * ldx + i0));
+  const int64_t jmi2 = uniform64(2 * (j0 - i0));
   const int64_t step2 = 2 * HK * ldx;
   const uint32_t lbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(
       __attribute__((address_space(3))) void*)(smem + RPW * wv * DROW));
@@ -362,43 +389,42 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
   };
 
   // transposing reads: lane (g = lane / 16, i = lane % 16) points at token
-  // 8 (g / 2) + i / 4 (+ 16 kk, + 4 for the second read), channel quad
-  // 16 (g % 2) + 4 (i % 4) of a 32-channel block
+  // 8 g + i / 4 (+ 32 kk, + 4 for the second read), channels 4 (i % 4) .. + 3
+  // of a 16-channel block; the swizzle term of those rows is 4 (i / 4) +
+  // 2 (g % 2)
   const int g = lane >> 4, i = lane & 15, qq = i >> 2, pch = i & 3;
-  const int lane_off = (8 * (g >> 1) + qq) * DROW + 8 * (pch & 1);
-  const int lane_chk = 2 * (g & 1) + (pch >> 1);
-  int offA[WI / 32], offB[WJ / 32];
+  const int lane_off = (8 * g + qq) * DROW + 8 * (pch & 1);
+  const int swz = 4 * qq + 2 * (g & 1);
+  int offA[MA], offB[MB];
 #pragma unroll
-  for (int a = 0; a < WI / 32; ++a)
-    offA[a] = lane_off + 16 * ((((WI * wr + 32 * a) >> 3) ^ (4 * qq)) + lane_chk);
+  for (int a = 0; a < MA; ++a)
+    offA[a] = lane_off + 16 * ((((WI * wr + 16 * a) >> 3) + (pch >> 1)) ^ swz);
 #pragma unroll
-  for (int b = 0; b < WJ / 32; ++b)
-    offB[b] = lane_off + 16 * ((((WJ * wc + 32 * b) >> 3) ^ (4 * qq)) + lane_chk);
+  for (int b = 0; b < MB; ++b)
+    offB[b] = DSTAGE + lane_off + 16 * ((((WJ * wc + 16 * b) >> 3) + (pch >> 1)) ^ swz);
 
-  f32x16 acc[WI / 32][WJ / 32];
+  f32x4 acc[MA][MB];
 #pragma unroll
-  for (int a = 0; a < WI / 32; ++a)
+  for (int a = 0; a < MA; ++a)
 #pragma unroll
-    for (int b = 0; b < WJ / 32; ++b)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+    for (int b = 0; b < MB; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   struct Ops {
-    bf16x8 a[WI / 32], b[WJ / 32];
+    bf16x8 a[MA], b[MB];
   };
-  auto read_ops = [&](int s, int kk, Ops& o) {
-    const uint8_t* At = smem + (s & 1) * 2 * DSTAGE;
-    const uint8_t* Bt = At + DSTAGE;
-#pragma unroll
-    for (int a = 0; a < WI / 32; ++a) o.a[a] = tr_operand(At + offA[a] + 16 * kk * DROW);
-#pragma unroll
-    for (int b = 0; b < WJ / 32; ++b) o.b[b] = tr_operand(Bt + offB[b] + 16 * kk * DROW);
+  auto rd = [&](int s, int kk, int off) {
+    return tr_operand(smem + (s & 1) * 2 * DSTAGE + off + 32 * kk * DROW);
   };
-  auto mfma = [&](const Ops& o) {
+  // the MFMAs of one k-step; each operand register is refilled with k-step
+  // kn of stage sn right after its last use
+  auto step = [&](Ops& o, int sn, int kn) {
 #pragma unroll
-    for (int a = 0; a < WI / 32; ++a)
+    for (int a = 0; a < MA; ++a)
 #pragma unroll
-      for (int b = 0; b < WJ / 32; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[a], o.b[b], acc[a][b], 0, 0, 0);
+      for (int b = 0; b < MB; ++b) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[a], o.b[b], acc[a][b], 0, 0, 0);
+        if (b == MB - 1) o.a[a] = rd(sn, kn, offA[a]);
+        if (a == MA - 1) o.b[b] = rd(sn, kn, offB[b]);
+      }
   };
 
   // stages 0 and 1 in flight; wait for stage 0 (vmcnt counts this wave's
@@ -411,35 +437,36 @@ __global__ __launch_bounds__(512) void syrk_bf16_dma_kernel(const uint16_t* __re
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
   __syncthreads();
-  static_assert(HK == 64, "the k-step schedule below covers 4 x 16 tokens");
-  Ops r0, r1;
-  read_ops(0, 0, r0);
+  static_assert(HK == 64, "the k-step schedule below covers 2 x 32 tokens");
+  Ops o;
+#pragma unroll
+  for (int a = 0; a < MA; ++a) o.a[a] = rd(0, 0, offA[a]);
+#pragma unroll
+  for (int b = 0; b < MB; ++b) o.b[b] = rd(0, 0, offB[b]);
   for (int s = 0; s < nstage; ++s) {
-    read_ops(s, 1, r1);
-    mfma(r0);
-    read_ops(s, 2, r0);
-    mfma(r1);
-    read_ops(s, 3, r1);
-    mfma(r0);
-    // stage s is in registers once r1 has landed (the barrier waits for this
-    // wave's LDS reads); stage s + 1 is published once every wave's DMA has
+    step(o, s, 1);
+    // stage s is in registers once the refills above have landed (the
+    // barrier waits for this wave's LDS reads); stage s + 1 is published once
+    // every wave's DMA has
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     if (s + 2 < nstage) issue(s + 2);
-    if (s + 1 < nstage) read_ops(s + 1, 0, r0);
-    mfma(r1);
+    // after the last stage these refills read the other buffer's stale (in
+    // bounds) contents, which nothing uses
+    step(o, s + 1, 0);
   }
 
+  // accumulator (a, b): lane l holds rows 4 (l / 16) + q, column l % 16
 #pragma unroll
-  for (int a = 0; a < WI / 32; ++a)
+  for (int a = 0; a < MA; ++a)
 #pragma unroll
-    for (int b = 0; b < WJ / 32; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int ii = WI * wr + 32 * a + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int jj = WJ * wc + 32 * b + (lane & 31);
+      for (int q = 0; q < 4; ++q) {
+        const int ii = WI * wr + 16 * a + 4 * (lane >> 4) + q;
+        const int jj = WJ * wc + 16 * b + (lane & 15);
         if (part) {
           part[(slot * FT_I + ii) * FT_J + jj] = acc[a][b][q];
         } else if (jj + j0 <= ii + i0) {
@@ -707,7 +734,7 @@ hipError_t launch_hessian(float* S, int64_t n, int64_t lds, const void* X, int d
     // The tokens are whole stages (P == 1 plans need tokens % HK == 0).
     const int64_t chunk = fp.P == 1 ? HCHUNK : tokens;
     for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
-      hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)units), dim3(512), 0, stream,
+      hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3((unsigned)units), dim3(64 * HWAVES), 0, stream,
                          reinterpret_cast<const uint16_t*>(X) + t0 * ldx, ldx,
                          hmin(chunk, tokens - t0), fp.P, fp.T2, S, lds, part, n / FT_I);
     }
