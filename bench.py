@@ -71,6 +71,12 @@ def parse():
                     help="skip the layer-sequential MLP-stack measurement")
     ap.add_argument("--no-dequant", action="store_true",
                     help="skip the dequantized-weight product measurement")
+    ap.add_argument("--no-library-gemm", action="store_true",
+                    help="skip the library bf16 product on the headline's tokens (context for "
+                         "the Hessian's rate)")
+    ap.add_argument("--library-gemm-probe", action="store_true",
+                    help="run only the library bf16 product X^T X on the workload's first "
+                         "65536 tokens, 1 + 8 times, for rocprofv3 counter runs, then exit")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--cpu-sample-chunks", type=int, default=2)
     ap.add_argument("--cpu-prepare-n", type=int, default=8192)
@@ -836,6 +842,12 @@ def main():
     if args.traffic_probe:
         traffic_probe(gq, wl, dev)
         return
+    if args.library_gemm_probe:
+        ls = wl.layer()
+        X = upload_x(wl, ls.x, dev)
+        rec = library_gemm_measure(X)
+        print(f"library gemm probe ({wl.name}): {json.dumps(rec)}", flush=True)
+        return
 
     print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
     head, hstate = run_workload(gq, wl, dev, args.steps, args.warmup,
@@ -900,6 +912,12 @@ def main():
         "input_setup_s": head["input_setup_s"],
         "detail": g0,
     }
+    if hstate is not None and not args.no_library_gemm:
+        print("bench: library bf16 product on the headline's tokens", file=sys.stderr, flush=True)
+        lib = library_gemm_measure(hstate["X"])
+        if lib is not None:
+            lib["hessian_launch_over_library"] = round(hess_tf / lib["tflops"], 4)
+        out["library_gemm"] = lib
     if hstate is not None:
         out["layer_error"] = layer_error_measure(gq, hstate["W"], hstate["buf"], hstate["m"],
                                                  hstate["n"], hstate["q"], hstate["stream"])
@@ -954,6 +972,42 @@ WORKLOAD_LABEL = {
     "llama7b_attn": "Llama-7B-shaped attention projection 4096x4096, 128x2048 calibration "
                     "tokens, 4-bit asymmetric, group 128, block 128, damp 0.01, desc_act off",
 }
+
+
+def library_gemm_measure(X, tokens: int = HESS_LAUNCH_TOKENS, calls: int = 8):
+    """Context for the Hessian's rate, not a step of the path: the ROCm library's
+    bf16 product (torch.mm, hipBLASLt) C = X^T X over the first ``tokens``
+    calibration tokens, the whole n x n square (2 n^2 tokens flop), bf16 out,
+    ``calls`` back to back after one warm-up, on the same values the Hessian
+    reads.  Its sustained rate is what the chip delivers on these values under
+    its power limit."""
+    import torch
+
+    if X.dtype != torch.bfloat16 or X.shape[0] < tokens:
+        return None
+    Xs = X[:tokens].contiguous()
+    XT = Xs.t().contiguous()  # a plain row-major left operand
+    n = Xs.shape[1]
+    C = torch.mm(XT, Xs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        torch.mm(XT, Xs, out=C)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    flop = 2.0 * n * n * tokens
+    del C, XT, Xs
+    torch.cuda.empty_cache()
+    return {
+        "what": f"torch.mm bf16 X^T X over {tokens} of the same tokens, full {n} x {n} square, "
+                f"bf16 out, {calls} calls after one warm-up (the library's sustained MFMA rate "
+                "on these values; context, not a step of the path)",
+        "ms_per_call": round(ms, 4),
+        "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
 
 
 def traffic_probe(gq, wl, dev):
