@@ -1199,6 +1199,147 @@ __global__ __launch_bounds__(256) void dequant_gemv_kernel(DqArgs a) {
   }
 }
 
+// Decode batches of at most 16 tokens over a long K (n a multiple of 256,
+// groups a multiple of 64 positions): a workgroup of 8 waves owns 128 weight
+// rows (16 per wave) and a K range walked in steps of 256 positions.  The
+// v_mfma_f32_16x16x32_bf16 k index is permuted inside a step so that lane
+// (q = lane / 16, r = lane % 16) owns positions 64 q .. 64 q + 63 of row r:
+// k-block j of the step takes positions 64 q + 8 j .. + 7 on both sides, so a
+// lane's codes are 2 BITS contiguous words (16-byte loads at even widths) and
+// its 64 positions lie in one group (one scale and zero a step).  Codes,
+// group parameters and the lane's share of the step's X tile are loaded two
+// steps ahead into registers; the 16 x 256 X tile goes through LDS with its
+// 16-byte segments XOR-swizzled by token.  The codes take 16 of the 64 lanes'
+// worth of each MFMA's k slots per row block, so the dequantization (decode,
+// fma, round to bf16: ~21 VALU instructions per 8 codes) is the other bound
+// beside the HBM stream; K splits go through dequant_reduce_kernel.
+constexpr int GW_STEP = 256;  // positions per step
+constexpr int GW_WAVES = 8;
+
+template <int BITS, bool VEC16>
+__global__ __launch_bounds__(GW_WAVES * 64) void dequant_gemv16w_kernel(DqArgs a) {
+  constexpr int QP = GW_STEP / 4;          // positions a lane owns in a step
+  constexpr int NKB = QP / 8;              // k-blocks of a step
+  constexpr int WPR = QP * BITS / 32;      // code words a lane loads a step
+  constexpr int ROWB = GW_STEP * 2;        // bytes of one X row of a step
+  constexpr int NSEG = ROWB / 16;          // 16-byte segments of such a row
+  constexpr int XU = NSEG * 16 / (64 * GW_WAVES);  // segments a thread stages
+  static_assert(XU == 1 && NSEG == 32, "one X segment per thread");
+  __shared__ __align__(16) uint8_t xs[2][16 * ROWB];
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, idx = b / kXcds;
+  const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return;
+  const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int64_t rb = L % a.nrb;
+  const int64_t kspl = L / a.nrb;
+  const int s_begin = (int)(kspl * a.chunks_per_split);
+  const int s_end = (int)min(a.nchunks, (int64_t)s_begin + a.chunks_per_split);
+  const int nst = s_end - s_begin;  // >= 1: the host leaves no split empty
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t row = rb * (16 * GW_WAVES) + 16 * wv + r16;
+  const int64_t rc = min(row, a.m - 1);
+  const uint32_t* crow = a.P + rc * a.ldp + q * WPR;
+  const float* srow = a.scales + rc * a.ngroups;
+  const float* zrow = a.zeros + rc * a.ngroups;
+  // X staging: thread -> token row tid / 32 (rows past the last token repeat
+  // it; their sums are never written), segment tid % 32
+  const int xt_row = tid >> 5, xt_seg = tid & 31;
+  const uint16_t* xsrc = a.X + (xt_row < a.tokens ? xt_row : a.tokens - 1) * a.ldx + 8 * xt_seg;
+  auto xoff = [](int t, int sg) { return t * ROWB + ((sg ^ t) << 4); };
+  struct Ld {
+    uint32_t w[WPR];
+    uint4 x;
+    float sc, z;
+  };
+  auto load = [&](int i, Ld& d) {
+    const int st = s_begin + min(i, nst - 1);  // past the end: a valid step again
+    const uint32_t* src = crow + (int64_t)st * (GW_STEP * BITS / 32);
+    if constexpr (VEC16) {
+#pragma unroll
+      for (int u = 0; u < WPR / 4; ++u) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * u);
+        d.w[4 * u] = v.x; d.w[4 * u + 1] = v.y; d.w[4 * u + 2] = v.z; d.w[4 * u + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < WPR / 2; ++u) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src + 2 * u);
+        d.w[2 * u] = v.x; d.w[2 * u + 1] = v.y;
+      }
+    }
+    const int64_t k0 = (int64_t)st * GW_STEP;
+    d.x = *reinterpret_cast<const uint4*>(xsrc + k0);
+    const int64_t gi = a.G > 0 ? (k0 + QP * q) / a.G : 0;
+    d.sc = srow[gi];
+    d.z = zrow[gi];
+  };
+  auto stage_x = [&](const Ld& d, int buf) {
+    *reinterpret_cast<uint4*>(&xs[buf][xoff(xt_row, xt_seg)]) = d.x;
+  };
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto step = [&](const Ld& d, int buf) {
+    const float sc = d.sc, nzs = -(d.z * d.sc);
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&xs[buf][xoff(r16, (QP * q + 8 * j) / 8)]);
+      float f[8];
+      uint32_t w4[BITS];
+#pragma unroll
+      for (int u = 0; u < BITS; ++u) w4[u] = d.w[(j >> 2) * BITS + u];
+      decode8<BITS>(w4, j & 3, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fmaf(f[e], sc, nzs);
+      uint4 o;
+      o.x = bf16x2_bits(f[0], f[1]);
+      o.y = bf16x2_bits(f[2], f[3]);
+      o.z = bf16x2_bits(f[4], f[5]);
+      o.w = bf16x2_bits(f[6], f[7]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, o), acc, 0, 0,
+                                                    0);
+    }
+  };
+  // step i multiplies from X buffer i % 2; then step i + 2 is loaded into the
+  // registers step i has consumed and the X of step i + 1 is staged into the
+  // other buffer (scheduling barriers keep the next step's work, and a wait
+  // on the loads just issued, below the barrier)
+  Ld d0, d1;
+  load(0, d0);
+  load(1, d1);
+  stage_x(d0, 0);
+  __syncthreads();
+  auto body = [&](Ld& cur, Ld& nxt, int i, int buf) {
+    if (i < nst) step(cur, buf);
+    __builtin_amdgcn_sched_barrier(0);
+    load(i + 2, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < nst) stage_x(nxt, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int i = 0; i < nst; i += 2) {
+    body(d0, d1, i, 0);
+    body(d1, d0, i + 1, 1);
+  }
+  // element e of lane l: token 4 (l / 16) + e, weight row r
+  if (row < a.m) {
+    float* outf = a.ks > 1 ? a.part + kspl * a.tokens * a.m : reinterpret_cast<float*>(a.Y);
+    const int64_t ld = a.ks > 1 ? a.m : a.ldy;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tt = 4 * q + e;
+      if (tt >= a.tokens) continue;
+      if (a.ks == 1 && a.ybf16) {
+        reinterpret_cast<__bf16*>(a.Y)[tt * ld + row] = (__bf16)acc[e];
+      } else {
+        outf[tt * ld + row] = acc[e];
+      }
+    }
+  }
+}
+
 // Y[t, r] = sum over splits s = 0, 1, ... of part[s, t, r], in that order.
 // One thread per 4 consecutive outputs of a row; the loads of 8 splits are in
 // flight before their in-order adds.
@@ -1508,6 +1649,41 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
   // 28672, 16 tokens: the split path reads X once per 128-row block)
   const bool gv16 = dma && d.tokens <= 16 && d.n % 128 == 0 && d.n <= 8192 &&
                     (d.group_size <= 0 || d.group_size % 32 == 0);
+  // up to 16 tokens over a longer K: 128-row workgroups, K split over ~256
+  // workgroups (at 8192 x 28672, 16 tokens, 4 bits: 38 us against 66 us for
+  // the 32 x 32 split kernel below; more splits, more waves per SIMD, were not
+  // faster, the dequantization's VALU work being the other bound)
+  const bool even = d.bits % 2 == 0;
+  const bool w16 = dma && d.tokens <= 16 && d.n > 8192 && d.n % GW_STEP == 0 &&
+                   (d.group_size <= 0 || d.group_size % 64 == 0) &&
+                   (reinterpret_cast<uintptr_t>(d.packed) & (even ? 15 : 7)) == 0 &&
+                   d.ldp % (even ? 4 : 2) == 0;
+  if (w16) {
+    const int64_t steps = d.n / GW_STEP;
+    a.nrb = ceil_div(d.m, (int64_t)(16 * GW_WAVES));
+    int64_t ks = hmin(hmax((int64_t)1, ceil_div((int64_t)256, a.nrb)), hmin(s.ks, steps));
+    a.chunks_per_split = ceil_div(steps, ks);
+    ks = ceil_div(steps, a.chunks_per_split);  // no empty split
+    a.ks = ks;
+    a.nchunks = steps;
+    a.ntiles = a.nrb * ks;
+    a.part = ks > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+    const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
+    const dim3 g3((unsigned)grid), b3(GW_WAVES * 64);
+    switch (d.bits) {
+      case 2: hipLaunchKernelGGL((dequant_gemv16w_kernel<2, true>), g3, b3, 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((dequant_gemv16w_kernel<3, false>), g3, b3, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((dequant_gemv16w_kernel<4, true>), g3, b3, 0, stream, a); break;
+      case 5: hipLaunchKernelGGL((dequant_gemv16w_kernel<5, false>), g3, b3, 0, stream, a); break;
+      default: hipLaunchKernelGGL((dequant_gemv16w_kernel<6, true>), g3, b3, 0, stream, a);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || ks == 1) return e;
+    const int64_t total = d.tokens * ceil_div(d.m, 4);
+    hipLaunchKernelGGL(dequant_reduce_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                       stream, a.part, ks, d.tokens, d.m, d.Y, d.ldy, a.ybf16);
+    return hipGetLastError();
+  }
   if (gv16) {
     const dim3 grid((unsigned)ceil_div(d.m, 16));
     switch (d.bits) {

@@ -124,6 +124,11 @@ CASES = [
     (200, 64, 136, 2, -1, True, None),      # whole-row group, permuted, partial chunk
     (513, 300, 1000, 5, 64, True, None),    # 3 token tiles, 40-column last chunk
     (384, 256, 2048, 6, 128, False, None),  # K split across workgroups
+    # up to 16 tokens over a K past 8192 (the wide-K decode kernel)
+    (16, 200, 8448, 3, 64, False, None),    # 3-bit (8-byte code loads), ragged rows
+    (5, 130, 9216, 5, 128, True, None),     # 5-bit, permuted, 5 tokens
+    (16, 64, 8704, 2, -1, False, None),     # 2-bit, one group per row, many K splits
+    (1, 96, 16384, 6, 192, False, None),    # 6-bit, group 192, one token
 ]
 
 
@@ -148,6 +153,25 @@ def test_dequant_gemm_bf16_output(tokens):
     say("dequant_gemm bf16 out", tokens, m, n)
     Y, _ = _run(q, X, codes, scales, zeros, perm, bits, G, False, ydt=torch.bfloat16)
     _check(Y, X, codes, scales, zeros, perm, bits, G, ybf16=True)
+
+
+def test_dequant_gemm_wide_k_unsplit_bf16():
+    """16 tokens over a K past 8192 with 32768 weight rows: the wide-K decode
+    kernel runs without a K split (256 row blocks fill the GPU) and rounds its
+    sums to bf16 itself; checked on sampled rows, every token."""
+    q = need_gpu()
+    rng = np.random.default_rng(77)
+    m, n, bits, G, tokens = 32768, 8448, 4, 64, 16
+    ng = n // G
+    codes = rng.integers(0, 2 ** bits, (m, n), dtype=np.uint8)
+    scales = (rng.uniform(0.5, 2.0, (m, ng)) * 0.02 / (2 ** bits)).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, (m, ng)).astype(np.float32)
+    X = synth.round_to_bf16(rng.standard_normal((tokens, n)).astype(np.float32))
+    perm = np.arange(n)
+    say("dequant_gemm wide K unsplit", tokens, m, n)
+    Y, _ = _run(q, X, codes, scales, zeros, perm, bits, G, False, ydt=torch.bfloat16)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 30, replace=False)]))
+    _check(Y, X, codes.astype(np.int64), scales, zeros, perm, bits, G, rows=rows, ybf16=True)
 
 
 def test_dequant_gemm_deterministic():
