@@ -665,16 +665,22 @@ __global__ __launch_bounds__(256) void dequant_gemm_dma_kernel(DqArgs a) {
 
 // ---------------------------------------------------------------------------
 // Dense bf16 product Y = X W^T (X [tokens, n], W [m, n], both bf16 with n
-// contiguous) on the tile machinery of the DMA product above, without the
-// dequantization: X and W tiles both arrive by LDS DMA in the swizzled
-// 128-byte rows, one explicit vmcnt and one barrier per chunk.  The tile is
-// 256 tokens x TN rows, 4 waves of 128 x TN/2.  Used with TN = 256 and two
-// stages (the next chunk in flight while one multiplies): 128 x 128 wave tiles
-// read half the LDS bytes per MFMA that 128 x 64 ones do, and the LDS, not the
-// matrix cores, is what bounds the 128-row tile (measured: the layer-
-// sequential forward 195 -> 175 ms).  For the calibration forward of a quantized layer over many tokens
-// the weights are dequantized once (gptq_dequantize) and multiplied here, so
-// no tile re-dequantizes them.
+// contiguous).  256 x 256 tiles, 1024 threads = 16 waves (4 per SIMD), each a
+// 64 x 64 block of 4 x 4 v_mfma_f32_16x16x32_bf16 accumulators.  Chunks of 64
+// positions of both tiles arrive by LDS DMA (global_load_lds_dwordx4, each wave
+// 16 rows of each) in 128-byte rows whose 16-byte segments are XOR-swizzled by
+// the row (seg_off), two buffers, one explicit vmcnt and one barrier per chunk,
+// the DMA of chunk c + 2 issued as soon as chunk c is in registers.  A lane
+// (q = lane / 16, r = lane % 16) reads positions 8 q .. + 7 (k-step kk:
+// segment 4 kk + q) of row r of a 16-row block, the operand layout of the
+// 16 x 16 x 32 MFMA, conflict-free under the swizzle; each operand register is
+// refilled for the next k-step right after its last MFMA, so the LDS reads run
+// under the MFMAs.  The 16 x 16 x 32 instruction and 4 waves per SIMD against
+// 4 waves of 128 x 128 on 32 x 32 x 16 (measured on the calibration-forward
+// and prefill shapes: 0.95-1.06 -> 1.21-1.32 PFLOP/s, the same sums).  For the
+// calibration forward of a quantized layer over many tokens the weights are
+// dequantized once (gptq_dequantize) and multiplied here, so no tile
+// re-dequantizes them.
 struct DenseArgs {
   const uint16_t* X;
   int64_t ldx, tokens, n;
@@ -686,30 +692,13 @@ struct DenseArgs {
   int64_t nrb, ntiles, nchunks;
 };
 
-constexpr int DD_TM = 256;
+constexpr int DD_TM = 256, DD_TN = 256;
 
-template <int TN, int NST>
-struct DenseLayout {
-  static constexpr int X_BYTES = DD_TM * ROWB;  // 32 KB
-  static constexpr int W_BYTES = TN * ROWB;
-  static constexpr int X_OFF = 0;
-  static constexpr int W_OFF = NST * X_BYTES;
-  static constexpr int TOTAL = W_OFF + NST * W_BYTES;
-  static constexpr int WM = DD_TM / 2, WN = TN / 2;
-  static constexpr int X_PER_WAVE = X_BYTES / 1024 / 4;  // 8
-  static constexpr int W_PER_WAVE = W_BYTES / 1024 / 4;
-  static constexpr int ISSUE = X_PER_WAVE + W_PER_WAVE;  // DMAs per wave and chunk
-};
-
-template <int TN, int NST>
-__global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
-  using Lay = DenseLayout<TN, NST>;
-  constexpr int DD_STAGES = NST;
-  static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
-  constexpr int DWM = Lay::WM, DWN = Lay::WN;
-  constexpr int XPW = Lay::X_PER_WAVE, WPW = Lay::W_PER_WAVE;
-  __shared__ __align__(16) uint8_t smem[Lay::TOTAL];
-
+__global__ __launch_bounds__(1024) void dense_gemm16_kernel(DenseArgs a) {
+  constexpr int X_BYTES = DD_TM * ROWB, W_BYTES = DD_TN * ROWB;  // 32 KB each
+  constexpr int STAGE = X_BYTES + W_BYTES;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
   const int64_t b = blockIdx.x;
   const int64_t xcd = b % kXcds, idx = b / kXcds;
   const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
@@ -717,176 +706,155 @@ __global__ __launch_bounds__(256) void dense_gemm_dma_kernel(DenseArgs a) {
   const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int64_t rb = L % a.nrb;
   const int64_t tb = L / a.nrb;
-  const int64_t tok0 = tb * DD_TM, row0 = rb * TN;
-  const int c_end = (int)a.nchunks;
-
+  const int64_t tok0 = tb * DD_TM, row0 = rb * DD_TN;
+  const int nst = (int)a.nchunks;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 2, wn = wv & 3;
   const int n32 = (int)a.n;
   const int tmax = (int)(a.tokens - 1 - tok0);
   const int rmax = (int)(a.m - 1 - row0);
 
-  // DMA sources: instruction j of wave wv fills rows 8 (wv PER + j) .. + 8;
-  // lane l lands on row + l / 8, physical segment l % 8, so it loads the
-  // logical segment (l % 8) ^ swz(row); rows past the end re-read the last one.
-  // The offsets are formed at each issue (registers go to the accumulators).
+  // DMA: wave wv fills rows 16 wv .. 16 wv + 15 of both tiles, two
+  // instructions each; lane l lands on row + l / 8, physical segment l % 8, so
+  // it loads the logical segment (l % 8) ^ swz(row); rows past the end re-read
+  // the last one, and in the last chunk segments past n re-read the last valid
+  // one (finite values, multiplied by X's zeroed columns there)
   const char* xbase = reinterpret_cast<const char*>(a.X + tok0 * a.ldx);
   const char* wbase = reinterpret_cast<const char*>(a.W + row0 * a.ldw);
   const uint32_t lds0 = lds_addr(smem);
-  auto src_off = [&](int row, int rmaxv, int64_t ld, int k0, int& seg) -> uint32_t {
-    seg = (lane & 7) ^ swz(row);
+  auto src_off = [&](int row, int rmaxv, int64_t ld, int k0) -> uint32_t {
+    const int seg = (lane & 7) ^ swz(row);
     int s8 = 8 * seg;
-    if (k0 + BK > n32) s8 = min(s8, n32 - 8 - k0);  // last chunk: past n re-read the last valid segment
+    if (k0 + BK > n32) s8 = min(s8, n32 - 8 - k0);
     return (uint32_t)(2 * ((int64_t)min(row, rmaxv) * ld + s8));
   };
-
   auto issue = [&](int c) {
     const int k0 = c * BK;
-    const int st = c % DD_STAGES;
-    const uint32_t xdst = lds0 + Lay::X_OFF + st * Lay::X_BYTES + wv * XPW * 1024;
-    const uint32_t wdst = lds0 + Lay::W_OFF + st * Lay::W_BYTES + wv * WPW * 1024;
+    const uint32_t xdst = lds0 + (c & 1) * STAGE + wv * 2048;
+    const uint32_t wdst = xdst + X_BYTES;
     const char* xs = xbase + 2 * (int64_t)k0;
     const char* ws = wbase + 2 * (int64_t)k0;
-    int seg;
 #pragma unroll
-    for (int j = 0; j < XPW; ++j)
-      lds_dma16(xs, src_off(8 * (wv * XPW + j) + (lane >> 3), tmax, a.ldx, k0, seg),
-                xdst + 1024 * j);
+    for (int j = 0; j < 2; ++j)
+      lds_dma16(xs, src_off(16 * wv + 8 * j + (lane >> 3), tmax, a.ldx, k0), xdst + 1024 * j);
 #pragma unroll
-    for (int j = 0; j < WPW; ++j)
-      lds_dma16(ws, src_off(8 * (wv * WPW + j) + (lane >> 3), rmax, a.ldw, k0, seg),
-                wdst + 1024 * j);
+    for (int j = 0; j < 2; ++j)
+      lds_dma16(ws, src_off(16 * wv + 8 * j + (lane >> 3), rmax, a.ldw, k0), wdst + 1024 * j);
   };
-
-  f32x16 acc[DWM / 32][DWN / 32];
-#pragma unroll
-  for (int i = 0; i < DWM / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < DWN / 32; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  struct Ops {
-    bf16x8 a[DWM / 32], b[DWN / 32];
-  };
-  auto read_ops = [&](const uint8_t* xt, const uint8_t* wt, int kk, Ops& o) {
-    const int sg = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < DWM / 32; ++i)
-      o.a[i] = *reinterpret_cast<const bf16x8*>(xt + seg_off(DWM * wm + 32 * i + (lane & 31), sg));
-#pragma unroll
-    for (int j = 0; j < DWN / 32; ++j)
-      o.b[j] = *reinterpret_cast<const bf16x8*>(wt + seg_off(DWN * wn + 32 * j + (lane & 31), sg));
-  };
-  auto compute = [&](int c) {
-    const int st = c % DD_STAGES;
-    const uint8_t* xt = smem + Lay::X_OFF + st * Lay::X_BYTES;
-    const uint8_t* wt = smem + Lay::W_OFF + st * Lay::W_BYTES;
-    if constexpr (TN <= 128) {  // operands of step kk + 1 read while step kk multiplies
-      Ops o[2];
-      read_ops(xt, wt, 0, o[0]);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) read_ops(xt, wt, kk + 1, o[(kk + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < DWM / 32; ++i)
-#pragma unroll
-          for (int j = 0; j < DWN / 32; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[kk & 1].a[i], o[kk & 1].b[j],
-                                                                acc[i][j], 0, 0, 0);
-      }
-    } else {  // 16 MFMAs a step cover the next step's reads; one operand set fits
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        Ops o;
-        read_ops(xt, wt, kk, o);
-#pragma unroll
-        for (int i = 0; i < DWM / 32; ++i)
-#pragma unroll
-          for (int j = 0; j < DWN / 32; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0,
-                                                                0);
-      }
-    }
-  };
-  // columns past n of the last chunk are set to 0 in X's tile, so whatever
-  // the weights there, the products are 0
+  // columns past n of the last chunk are set to 0 in X's tile
   auto zero_x_tail = [&](int c) {
-    uint8_t* xt = smem + Lay::X_OFF + (c % DD_STAGES) * Lay::X_BYTES;
+    uint8_t* xt = smem + (c & 1) * STAGE;
     const int k0 = c * BK;
-    for (int i = tid; i < DD_TM * 8; i += 256) {
+    for (int i = tid; i < DD_TM * 8; i += 1024) {
       const int row = i >> 3, sg = i & 7;
       if (k0 + 8 * sg >= n32) *reinterpret_cast<uint4*>(xt + seg_off(row, sg)) = make_uint4(0, 0, 0, 0);
     }
   };
-  constexpr int VM = 0x0070 | (Lay::ISSUE & 15) | ((Lay::ISSUE >> 4) << 14);  // vmcnt(ISSUE), lgkmcnt(0)
 
-  if (c_end > 0 && NST == 3) {
-    issue(0);
-    if (1 < c_end) {
-      issue(1);
-      __builtin_amdgcn_s_waitcnt(VM);  // chunk 0 landed, chunk 1 may be in flight
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0070);
-    }
-    __syncthreads();
-    int c = 0;
-    for (; c + 1 < c_end; ++c) {
-      if (c + 2 < c_end) issue(c + 2);  // into the stage chunk c - 1 used
-      compute(c);
-      if (c + 2 < c_end) {
-        __builtin_amdgcn_s_waitcnt(VM);  // chunk c + 1 landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0070);
-      }
-      __syncthreads();
-    }
-    if (c_end * BK > n32) {
-      zero_x_tail(c);
-      __syncthreads();
-    }
-    compute(c);
-  } else if (c_end > 0) {  // two stages: the next chunk in flight while this one multiplies
-    issue(0);
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __syncthreads();
-    int c = 0;
-    for (; c + 1 < c_end; ++c) {
-      issue(c + 1);  // into the stage chunk c - 1 used
-      compute(c);
-      __builtin_amdgcn_s_waitcnt(0x0070);
-      __syncthreads();
-    }
-    if (c_end * BK > n32) {
-      zero_x_tail(c);
-      __syncthreads();
-    }
-    compute(c);
+  // a lane reads rows r + 16 i (+ 64 wm or 64 wn), whose swizzle is swz(r)
+  const int q = lane >> 4, r16 = lane & 15;
+  const int segoff0 = (q ^ swz(r16)) << 4, segoff1 = ((4 + q) ^ swz(r16)) << 4;
+  int offA[4], offB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    offA[i] = (64 * wm + 16 * i + r16) * ROWB;
+    offB[i] = X_BYTES + (64 * wn + 16 * i + r16) * ROWB;
   }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  struct Ops {
+    bf16x8 a[4], b[4];
+  };
+  auto rd = [&](int c, int kk, int off) {
+    return *reinterpret_cast<const bf16x8*>(smem + (c & 1) * STAGE + off + (kk ? segoff1 : segoff0));
+  };
+  // the MFMAs of one k-step; each operand register is refilled with k-step kn
+  // of chunk cn right after its last use
+  auto step = [&](Ops& o, int cn, int kn) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+        if (j == 3) o.a[i] = rd(cn, kn, offA[i]);
+        if (i == 3) o.b[j] = rd(cn, kn, offB[j]);
+      }
+  };
 
-  const int64_t tw = tok0 + DWM * wm + 4 * (lane >> 5);
-  const int64_t rw = row0 + DWN * wn + (lane & 31);
-  const bool fulltile = tok0 + DWM * (wm + 1) <= a.tokens && row0 + DWN * (wn + 1) <= a.m;
+  // chunks 0 and 1 in flight; wait for chunk 0 (vmcnt counts this wave's
+  // outstanding DMA instructions: 4 per chunk)
+  issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  __syncthreads();
+  if (nst == 1 && BK > n32) {
+    zero_x_tail(0);
+    __syncthreads();
+  }
+  Ops o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.a[i] = rd(0, 0, offA[i]);
+    o.b[i] = rd(0, 0, offB[i]);
+  }
+  // steady chunks (the tail chunk, if any, is not among the next ones); the
+  // barrier publishes chunk c + 1 after chunk c is in registers
+  int c = 0;
+  for (; c + 2 < nst; ++c) {
+    step(o, c, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c + 2);
+    step(o, c + 1, 0);
+  }
+  if (c + 1 < nst) {  // the last chunk arrives: its X past n to 0 before its reads
+    step(o, c, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (nst * BK > n32) {
+      zero_x_tail(c + 1);
+      __syncthreads();
+    }
+    step(o, c + 1, 0);
+    ++c;
+  }
+  // the last chunk's two k-steps; the refills past it read the other
+  // buffer's stale (in bounds) contents, which nothing uses
+  step(o, c, 1);
+  step(o, c + 1, 0);
+
+  // accumulator (i, j): lane l holds tokens 4 (l / 16) + e, weight row l % 16
+  const bool fulltile = tok0 + 64 * (wm + 1) <= a.tokens && row0 + 64 * (wn + 1) <= a.m;
   float* outf = reinterpret_cast<float*>(a.Y);
   __bf16* outh = reinterpret_cast<__bf16*>(a.Y);
 #pragma unroll
-  for (int i = 0; i < DWM / 32; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < DWN / 32; ++j) {
-      const int64_t base = (tw + 32 * i) * a.ldy + rw + 32 * j;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int dt = 8 * (q >> 2) + (q & 3);
-        if (!fulltile && (tw + 32 * i + dt >= a.tokens || rw + 32 * j >= a.m)) continue;
-        const int64_t o = base + (int64_t)dt * a.ldy;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = tok0 + 64 * wm + 16 * i + 4 * q + e;
+        const int64_t r = row0 + 64 * wn + 16 * j + r16;
+        if (!fulltile && (t >= a.tokens || r >= a.m)) continue;
+        const int64_t o2 = t * a.ldy + r;
         if (a.ybf16) {
-          outh[o] = (__bf16)acc[i][j][q];
+          outh[o2] = (__bf16)acc[i][j][e];
         } else {
-          outf[o] = acc[i][j][q];
+          outf[o2] = acc[i][j][e];
         }
       }
-    }
 }
 
 // W[r, p] = bf16(fma(q[r, p], s, -(z s))) from codes packed in processing order:
@@ -1755,13 +1723,11 @@ hipError_t launch_dense_gemm(const uint16_t* X, int64_t ldx, int64_t tokens, int
   a.X = X; a.ldx = ldx; a.tokens = tokens; a.n = n;
   a.W = W; a.ldw = ldw; a.m = m;
   a.Y = Y; a.ldy = ldy; a.ybf16 = ybf16;
-  constexpr int TN = 256, NST = 2;
-  a.nrb = ceil_div(m, TN);
+  a.nrb = ceil_div(m, DD_TN);
   a.ntiles = ceil_div(tokens, DD_TM) * a.nrb;
   a.nchunks = ceil_div(n, BK);
   const int64_t grid = ceil_div(a.ntiles, kXcds) * kXcds;
-  hipLaunchKernelGGL((dense_gemm_dma_kernel<TN, NST>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL(dense_gemm16_kernel, dim3((unsigned)grid), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
