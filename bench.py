@@ -87,6 +87,9 @@ def parse():
                     help="run the quantized layer's product 10 times at 2048 and at 16 tokens "
                          "(4096 x 4096, random 4-bit codes, group 128), for rocprofv3 counter "
                          "runs, then exit")
+    ap.add_argument("--dequant-probe-layer", action="store_true",
+                    help="as --dequant-probe, on the weight shape, width and group size of "
+                         "--workload's layer (random codes, identity order), then exit")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter files of two --traffic-probe runs of --workload into "
                          "profiles/traffic_hessian_<workload>.json, then exit")
@@ -711,20 +714,20 @@ def awq_measure(gq, W, X, S, m, n, q, stream):
     }
 
 
-def dequant_probe(gq, dev):
-    """Ten products at 2048 tokens, then ten at 16, on a 4096 x 4096 4-bit g128
-    layer of random codes packed in processing order (identity order)."""
+def dequant_probe(gq, dev, m=4096, n=4096, bits=4, G=128):
+    """Ten products at 2048 tokens, then ten at 16, on an m x n layer (default
+    4096 x 4096, 4-bit g128) of random codes packed in processing order
+    (identity order)."""
     import numpy as np
     import torch
 
-    m = n = 4096
-    bits, G = 4, 128
     rng = np.random.default_rng(0)
-    codes = torch.from_numpy(rng.integers(0, 16, size=(m, n), dtype=np.uint8)).to(dev)
-    packed = torch.empty((m, n * bits // 32), dtype=torch.int32, device=dev)
+    codes = torch.from_numpy(rng.integers(0, 2 ** bits, size=(m, n), dtype=np.uint8)).to(dev)
+    packed = torch.empty((m, -(-n * bits // 32)), dtype=torch.int32, device=dev)
     gq.gptq_pack_ordered(codes, bits, None, packed)
-    scales = torch.from_numpy(rng.uniform(1e-3, 1e-2, size=(m, n // G)).astype(np.float32)).to(dev)
-    zeros = torch.from_numpy(rng.integers(0, 16, size=(m, n // G)).astype(np.float32)).to(dev)
+    ng = -(-n // G) if G > 0 else 1
+    scales = torch.from_numpy(rng.uniform(1e-3, 1e-2, size=(m, ng)).astype(np.float32)).to(dev)
+    zeros = torch.from_numpy(rng.integers(0, 2 ** bits, size=(m, ng)).astype(np.float32)).to(dev)
     X = torch.from_numpy(rng.standard_normal((2048, n)).astype(np.float32)).to(dev).to(torch.bfloat16)
     for tokens in (2048, 16):
         Y = torch.empty((tokens, m), dtype=torch.float32, device=dev)
@@ -733,7 +736,8 @@ def dequant_probe(gq, dev):
         for _ in range(10):
             gq.gptq_dequant_gemm(X[:tokens], packed, bits, G, scales, zeros, Y, ws=ws)
         torch.cuda.synchronize()
-    print("dequant probe: 10 products at 2048 and 10 at 16 tokens done", flush=True)
+    print(f"dequant probe ({m} x {n}, {bits}-bit, group {G}): 10 products at 2048 and 10 at 16 "
+          "tokens done", flush=True)
 
 
 def stack_measure(gq, dev):
@@ -836,6 +840,11 @@ def main():
     torch.cuda.set_device(dev)
     if args.dequant_probe:
         dequant_probe(gq, dev)
+        return
+    if args.dequant_probe_layer:
+        ls = synth.get_workload(args.workload).layer()
+        q = synth.get_workload(args.workload).quant
+        dequant_probe(gq, dev, ls.m, ls.n, q.bits, q.group_size)
         return
 
     wl = synth.get_workload(args.workload)
