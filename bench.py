@@ -808,13 +808,13 @@ def main():
                            f"{COPY_BYTES})",
             "commands": [
                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format "
-                f"csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py "
+                f"csv -d $OUT/pmc_fetch -o run -- python3 $REPO/bench.py "
                 f"--traffic-probe --workload {args.workload}",
                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format "
-                f"csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py "
+                f"csv -d $OUT/pmc_write -o run -- python3 $REPO/bench.py "
                 f"--traffic-probe --workload {args.workload}",
-                "python3 bench.py --traffic-record gpurun_out/pmc_fetch/run_counter_collection.csv "
-                f"gpurun_out/pmc_write/run_counter_collection.csv --workload {args.workload}",
+                "python3 bench.py --traffic-record $OUT/pmc_fetch/run_counter_collection.csv "
+                f"$OUT/pmc_write/run_counter_collection.csv --workload {args.workload}",
             ],
             "kernel_source_sha256": source_hash(HESSIAN_SRC),
         }

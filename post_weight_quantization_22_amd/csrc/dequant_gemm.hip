@@ -1336,12 +1336,20 @@ __global__ __launch_bounds__(256) void dequant_reduce_kernel(const float* __rest
         s[3] += v[u].w;
       }
     }
-    for (; k < ks; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(src + k * plane);
-      s[0] += v.x;
-      s[1] += v.y;
-      s[2] += v.z;
-      s[3] += v.w;
+    if (k < ks) {  // the last < 8 splits: every load issued before the in-order adds
+      float4 v[7];
+#pragma unroll
+      for (int u = 0; u < 7; ++u)
+        if (k + u < ks) v[u] = *reinterpret_cast<const float4*>(src + (k + u) * plane);
+#pragma unroll
+      for (int u = 0; u < 7; ++u) {
+        if (k + u < ks) {
+          s[0] += v[u].x;
+          s[1] += v[u].y;
+          s[2] += v[u].z;
+          s[3] += v[u].w;
+        }
+      }
     }
   } else {
     for (int64_t k = 0; k < ks; ++k)
