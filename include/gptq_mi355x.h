@@ -230,7 +230,10 @@ gptq_status gptq_pack_ordered(const uint8_t* codes, int64_t m, int64_t n, int32_
  * rounded to bf16 (nearest even), multiplied exactly by the bf16 activation,
  * and the products are summed in fp32 (in a fixed order: deterministic).
  * Workspace: gptq_dequant_gemm_workspace_size(tokens, m, n, perm != NULL)
- * bytes (may be 0).  tokens == 0 or m == 0 is a no-op.
+ * bytes (may be 0; from 1024 tokens up, with n a multiple of 8, it holds the
+ * dequantized bf16 weights, m * n * 2 bytes, which the call forms once and
+ * multiplies as gptq_gemm_bf16 does -- the same weights, the same result
+ * contract).  tokens == 0 or m == 0 is a no-op.
  * ---------------------------------------------------------------------- */
 /* gptq_dequantize: W[m, n] bf16 (row stride ldw, a multiple of 8, 16-byte
  * aligned) = the weights gptq_dequant_gemm forms, bf16(fma(q, s, -(z s))) with

@@ -858,46 +858,54 @@ __global__ __launch_bounds__(1024) void dense_gemm16_kernel(DenseArgs a) {
 }
 
 // W[r, p] = bf16(fma(q[r, p], s, -(z s))) from codes packed in processing order:
-// the weights the products above form, written once (one thread per 8
-// positions, one 16-byte store; n a multiple of 8).
+// the weights the products above form, written once.  A wave covers 256
+// 8-position segments of a row: lane j, store s writes segment 256 x + 64 s + j
+// (16 bytes), so every store instruction writes 1 KB of whole lines; the lane
+// reads the BITS words of that segment's 32-code run (four lanes share a run:
+// one coalesced load) and its group's scale and zero (a group holds whole
+// segments; n a multiple of 8).  The row is blockIdx.y (strided past the
+// grid), so no 64-bit division is needed.
 template <int BITS>
-__global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t* __restrict__ P,
-                                                         int64_t ldp, int64_t m, int64_t n,
-                                                         const float* __restrict__ scales,
-                                                         const float* __restrict__ zeros,
-                                                         int64_t G, int64_t ngroups,
-                                                         uint16_t* __restrict__ W, int64_t ldw) {
-  const int64_t segs = n / 8;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= m * segs) return;
-  const int64_t r = i / segs, p0 = 8 * (i - r * segs);
-  // the 32-code run holding positions p0 .. p0 + 7 (BITS words; the last run of
-  // a row may end past n, its words past the row's are not read)
-  const int64_t run = p0 >> 5;
-  const int s8 = (int)((p0 >> 3) & 3);
-  const int64_t nwr = (n * BITS + 31) / 32;
-  uint32_t w[BITS];
+__global__ __launch_bounds__(64) void dequantize_kernel(const uint32_t* __restrict__ P,
+                                                        int64_t ldp, int64_t m, int64_t n,
+                                                        const float* __restrict__ scales,
+                                                        const float* __restrict__ zeros,
+                                                        int64_t G, int64_t ngroups,
+                                                        uint16_t* __restrict__ W, int64_t ldw) {
+  const int nseg = (int)(n / 8);
+  const int nwr = (int)((n * BITS + 31) / 32);
+  const int g32 = (int)G;
+  const int k0 = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
+    const uint32_t* prow = P + r * ldp;
+    const float* srow = scales + r * ngroups;
+    const float* zrow = zeros + r * ngroups;
+    uint16_t* wrow = W + r * ldw;
 #pragma unroll
-  for (int q = 0; q < BITS; ++q) {
-    const int64_t wi = run * BITS + q;
-    w[q] = wi < nwr ? P[r * ldp + wi] : 0u;
-  }
-  float f[8];
-  decode8<BITS>(w, s8, f);
-  uint32_t o[4];
+    for (int s = 0; s < 4; ++s) {
+      const int k = k0 + 64 * s;  // segment: positions 8 k .. 8 k + 7
+      if (k < nseg) {
+        const int run = k >> 2;
+        uint32_t w[BITS];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t p = p0 + 2 * e + h;
-      const int64_t g = G > 0 ? p / G : 0;
-      const float sc = scales[r * ngroups + g];
-      v[h] = fmaf(f[2 * e + h], sc, -(zeros[r * ngroups + g] * sc));
+        for (int q = 0; q < BITS; ++q) {
+          const int wi = run * BITS + q;
+          w[q] = wi < nwr ? prow[wi] : 0u;  // the last run's words past the row are not read
+        }
+        const int g = g32 > 0 ? (8 * k) / g32 : 0;
+        const float sc = srow[g];
+        const float nzs = -(zrow[g] * sc);
+        float f[8];
+        decode8<BITS>(w, k & 3, f);
+        uint4 o;
+        o.x = bf16x2_bits(fmaf(f[0], sc, nzs), fmaf(f[1], sc, nzs));
+        o.y = bf16x2_bits(fmaf(f[2], sc, nzs), fmaf(f[3], sc, nzs));
+        o.z = bf16x2_bits(fmaf(f[4], sc, nzs), fmaf(f[5], sc, nzs));
+        o.w = bf16x2_bits(fmaf(f[6], sc, nzs), fmaf(f[7], sc, nzs));
+        *reinterpret_cast<uint4*>(wrow + 8 * k) = o;
+      }
     }
-    o[e] = bf16x2_bits(v[0], v[1]);
   }
-  *reinterpret_cast<uint4*>(W + r * ldw + p0) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1564,10 +1572,24 @@ void launch_gather(const uint16_t* X, int64_t ldx, const int32_t* perm, int64_t 
   }
 }
 
+// Batches of at least this many tokens, whose 256 x 256 output tiles fill the
+// GPU, dequantize the weights once into the workspace (bf16, the same weights
+// the fused kernels form) and multiply them with the dense kernel: at 2048
+// tokens on 8192 x 28672 the dense product runs at ~1.25 PFLOP/s against ~0.75
+// for the fused one, which pays back the weights' extra 2 bytes written and
+// read.  Fewer tiles leave CUs idle (the fused kernel splits K instead).
+constexpr int64_t DENSE_PATH_TOKENS = 1024;
+
+static bool dense_path(int64_t tokens, int64_t m, int64_t n) {
+  return tokens >= DENSE_PATH_TOKENS && n % 8 == 0 &&
+         ceil_div(tokens, (int64_t)256) * ceil_div(m, (int64_t)256) >= 256;
+}
+
 size_t dequant_gemm_ws_bytes(int64_t tokens, int64_t m, int64_t n, int has_perm) {
   const Shape s = choose_shape(tokens, m, n);
   size_t bytes = 0;
   if (has_perm) bytes += align_up((size_t)tokens * (size_t)align_up((size_t)n, 8) * 2, 256);
+  if (dense_path(tokens, m, n)) return bytes + align_up((size_t)m * (size_t)n * 2, 256);
   if (s.ks > 1) bytes += (size_t)s.ks * (size_t)tokens * (size_t)m * 4;
   return bytes;
 }
@@ -1585,6 +1607,14 @@ hipError_t launch_dequant_gemm(const DequantArgs& d, hipStream_t stream) {
     launch_gather(a.X, d.ldx, d.perm, d.tokens, d.n, ldxp, Xp, stream);
     a.X = Xp;
     a.ldx = ldxp;
+  }
+  if (dense_path(d.tokens, d.m, d.n) && a.ldx < (int64_t(1) << 23) && d.n < (int64_t(1) << 23)) {
+    uint16_t* Wd = reinterpret_cast<uint16_t*>(ws);  // [m, n] bf16, row stride n
+    hipError_t e = launch_dequantize(d.packed, d.ldp, d.bits, d.m, d.n, d.scales, d.zeros,
+                                     d.group_size, Wd, d.n, stream);
+    if (e != hipSuccess) return e;
+    return launch_dense_gemm(a.X, a.ldx, d.tokens, d.n, Wd, d.n, d.m, d.Y, d.ldy,
+                             d.ydt == GPTQ_BF16 ? 1 : 0, stream);
   }
   a.tokens = d.tokens;
   a.n = d.n;
@@ -1744,9 +1774,9 @@ hipError_t launch_dequantize(const uint32_t* P, int64_t ldp, int bits, int64_t m
                              uint16_t* W, int64_t ldw, hipStream_t stream) {
   const int64_t G = group_size > 0 ? group_size : 0;
   const int64_t ngroups = G > 0 ? ceil_div(n, G) : 1;
-  const dim3 grid((unsigned)ceil_div(m * (n / 8), 256));
+  const dim3 grid((unsigned)ceil_div(n / 8, (int64_t)256), (unsigned)hmin(m, (int64_t)65535));
 #define GPTQ_DQ(B)                                                                            \
-  hipLaunchKernelGGL(dequantize_kernel<B>, grid, dim3(256), 0, stream, P, ldp, m, n, scales, \
+  hipLaunchKernelGGL(dequantize_kernel<B>, grid, dim3(64), 0, stream, P, ldp, m, n, scales,  \
                      zeros, G, ngroups, W, ldw)
   switch (bits) {
     case 2: GPTQ_DQ(2); break;

@@ -129,6 +129,8 @@ CASES = [
     (5, 130, 9216, 5, 128, True, None),     # 5-bit, permuted, 5 tokens
     (16, 64, 8704, 2, -1, False, None),     # 2-bit, one group per row, many K splits
     (1, 96, 16384, 6, 192, False, None),    # 6-bit, group 192, one token
+    # >= 1024 tokens over >= 256 output tiles: weights dequantized once, dense product
+    (1100, 13100, 264, 3, 8, True, None),   # ragged tokens, rows and last chunk; permuted
 ]
 
 
