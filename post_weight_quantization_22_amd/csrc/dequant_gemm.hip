@@ -693,6 +693,7 @@ struct DenseArgs {
 };
 
 constexpr int DD_TM = 256, DD_TN = 256;
+constexpr int64_t DD_GT = 4;  // token blocks per group of the tile order
 
 __global__ __launch_bounds__(1024) void dense_gemm16_kernel(DenseArgs a) {
   constexpr int X_BYTES = DD_TM * ROWB, W_BYTES = DD_TN * ROWB;  // 32 KB each
@@ -704,8 +705,15 @@ __global__ __launch_bounds__(1024) void dense_gemm16_kernel(DenseArgs a) {
   const int64_t per = a.ntiles / kXcds, rem = a.ntiles % kXcds;
   if (idx >= per + (xcd < rem ? 1 : 0)) return;
   const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  const int64_t rb = L % a.nrb;
-  const int64_t tb = L / a.nrb;
+  // tiles in groups of DD_GT token blocks: consecutive L walk down a group's
+  // token blocks, then its next row block, so the ~32 workgroups an XCD runs at
+  // once cover ~4 token x 8 row blocks and share both operands in its L2
+  // (rather than one token block and 32 row blocks: every weight tile fetched
+  // again for each token block)
+  const int64_t ntb = (a.tokens + DD_TM - 1) / DD_TM;
+  const int64_t grp = L / (DD_GT * a.nrb), in = L - grp * DD_GT * a.nrb;
+  const int64_t tb0 = grp * DD_GT, gsz = min((int64_t)DD_GT, ntb - tb0);
+  const int64_t tb = tb0 + in % gsz, rb = in / gsz;
   const int64_t tok0 = tb * DD_TM, row0 = rb * DD_TN;
   const int nst = (int)a.nchunks;
   const int tid = threadIdx.x, lane = tid & 63;
