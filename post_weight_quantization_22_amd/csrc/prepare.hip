@@ -330,32 +330,81 @@ __global__ __launch_bounds__(256) void build_a_kernel(const float* __restrict__ 
 // column of S, so build_a_kernel reads 4 useful bytes of every line it
 // fetches (~44 GB for a 28672-wide S).  Two coalesced passes instead, through
 // the X workspace (free until the factorization): sym_kernel writes the whole
-// symmetric S in fp32 (Sf[i][j] = S[max][min], 32 x 32 tiles and their
-// transposes through LDS), then gather_a_kernel builds each row a of A from
-// row perm[n-1-a] of Sf staged in LDS, the columns read in the order
-// perm[n-1-b] from there.
+// symmetric S in fp32 (Sf[i][j] = S[max][min]), then gather_a_kernel builds
+// each row a of A from row perm[n-1-a] of Sf staged in LDS, the columns read
+// in the order perm[n-1-b] from there.
+//
+// sym_kernel: one workgroup per lower 64 x 64 tile (the grid enumerates the
+// lower triangle of tiles only).  The tile comes in by 16-byte loads (VEC:
+// lds and n multiples of 4, S 16-byte aligned; else element by element) and
+// is staged in LDS; it leaves as itself in its own place and, off the
+// diagonal, transposed in the mirrored place, both by 16-byte stores.  On a
+// diagonal tile the entries above the diagonal are mirrored from below (S's
+// upper triangle is never read).
+constexpr int SYM_T = 64;
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void sym_kernel(const float* __restrict__ S, int64_t n,
                                                   int64_t lds, float* __restrict__ Sf) {
-  __shared__ float tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t i0 = (int64_t)blockIdx.y * 32, j0 = (int64_t)blockIdx.x * 32;
-  if (j0 > i0) return;
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t i = i0 + r, j = j0 + tx;
-    float v = 0.0f;
-    if (i < n && j <= i) v = S[i * lds + j];
-    tile[r][tx] = v;
+  __shared__ float tile[SYM_T][SYM_T + 1];
+  const int64_t L = blockIdx.x;
+  int64_t ti = (int64_t)((sqrt(8.0 * (double)L + 1.0) - 1.0) * 0.5);
+  while (ti * (ti + 1) / 2 > L) --ti;
+  while ((ti + 1) * (ti + 2) / 2 <= L) ++ti;
+  const int64_t tj = L - ti * (ti + 1) / 2;
+  const int64_t i0 = ti * SYM_T, j0 = tj * SYM_T;
+  const int c4 = threadIdx.x & 15, rr = threadIdx.x >> 4;  // float4 column, row in 16
+  float4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = i0 + rr + 16 * k, j = j0 + 4 * c4;
+    const float* src = S + i * lds + j;
+    if (VEC && i < n && j + 3 <= i && j + 4 <= n) {
+      v[k] = *reinterpret_cast<const float4*>(src);
+    } else {
+      float t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (i < n && j + e <= i) ? src[e] : 0.0f;
+      v[k] = make_float4(t[0], t[1], t[2], t[3]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float* d = &tile[rr + 16 * k][4 * c4];
+    d[0] = v[k].x; d[1] = v[k].y; d[2] = v[k].z; d[3] = v[k].w;
   }
   __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t i = i0 + r, j = j0 + tx;
-    // lower entries as they are; on a diagonal tile the upper ones mirrored
-    if (i < n && j < n) Sf[i * n + j] = j <= i ? tile[r][tx] : tile[tx][r];
+  auto put4 = [&](int64_t row, int64_t col, const float (&t)[4]) {
+    if (row >= n) return;
+    float* dst = Sf + row * n + col;
+    if (VEC && col + 4 <= n) {
+      *reinterpret_cast<float4*>(dst) = make_float4(t[0], t[1], t[2], t[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < n) dst[e] = t[e];
+    }
+  };
+  const bool diag = ti == tj;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // the tile itself (mirrored above a diagonal)
+    const int r = rr + 16 * k;
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 4 * c4 + e;
+      t[e] = (diag && c > r) ? tile[c][r] : tile[r][c];
+    }
+    put4(i0 + r, j0 + 4 * c4, t);
   }
-  if (i0 == j0) return;
-  for (int r = ty; r < 32; r += 8) {  // the transposed tile: Sf[j][i] = S[i][j]
-    const int64_t j = j0 + r, i = i0 + tx;
-    if (i < n && j < n) Sf[j * n + i] = tile[tx][r];
+  if (diag) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // its transpose: Sf[j][i] = S[i][j]
+    const int r = rr + 16 * k;    // row j0 + r of Sf, columns i0 + 4 c4 ..
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = tile[4 * c4 + e][r];
+    put4(j0 + r, i0 + 4 * c4, t);
   }
 }
 
@@ -1704,8 +1753,13 @@ hipError_t launch_prepare(const float* S, int64_t n, int64_t lds, float perc_dam
   if (desc_act && n <= GATHER_NCAP && n >= 1024) {
     // permuted: symmetric S into X's memory (fp32), then A row by row
     float* Sf = reinterpret_cast<float*>(w.X);
-    const dim3 grid((unsigned)ceil_div(n, 32), (unsigned)ceil_div(n, 32));
-    hipLaunchKernelGGL(sym_kernel, grid, dim3(256), 0, stream, S, n, lds, Sf);
+    const int64_t T = ceil_div(n, (int64_t)SYM_T);
+    const dim3 grid((unsigned)(T * (T + 1) / 2));
+    const bool vec = lds % 4 == 0 && n % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+    if (vec)
+      hipLaunchKernelGGL(sym_kernel<true>, grid, dim3(256), 0, stream, S, n, lds, Sf);
+    else
+      hipLaunchKernelGGL(sym_kernel<false>, grid, dim3(256), 0, stream, S, n, lds, Sf);
     const int64_t wgs = hmin(n, (int64_t)256);
     const int64_t rpw = ceil_div(n, wgs);
     hipLaunchKernelGGL(gather_a_kernel, dim3((unsigned)ceil_div(n, rpw)), dim3(GATHER_T), 0,

@@ -434,6 +434,10 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
       e_own[s] = e;
       q_own[s] = q;
     }
+    // take the owner's select here: left to the compiler, the 16 selects of
+    // a slot (one per owner) sink to the end of the block, keeping every
+    // column's code and error live (~330 registers, one wave per SIMD)
+    asm volatile("" : "+v"(e_own[s]), "+v"(q_own[s]));
     w[0] = fmaf(-e, uc0.x, w[0]);
     w[1] = fmaf(-e, uc0.y, w[1]);
     w[2] = fmaf(-e, uc0.z, w[2]);
@@ -683,9 +687,9 @@ __global__ void invert_perm_kernel(const int32_t* __restrict__ perm, int64_t n,
 }
 
 // codes[r, c] = codes_proc[r, inv[c]] a row at a time through LDS: the
-// processing-order row comes in by coalesced 16-byte loads straight into one
-// LDS row buffer (two barriers a row; up to four workgroups share a CU and
-// overlap each other's loads), and leaves in original order by 16-byte stores
+// processing-order row comes in by coalesced 16-byte loads (issued while the
+// previous row is gathered) into one LDS row buffer (two barriers a row), and
+// leaves in original order by 16-byte stores
 // (16 codes), the permuted reads served by the LDS.  The source positions of
 // a thread's two output segments (16-bit, two to a word) stay in registers,
 // read once per workgroup (NCAP / 32 threads).  Needs n % 16 == 0, n <= NCAP <= 32768.  g_idx is
@@ -708,30 +712,51 @@ __global__ __launch_bounds__(NT) void unpermute_rows_kernel(const uint8_t* __res
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int sg = tid + NT * i;
+    int32_t kk[16];
+    if ((reinterpret_cast<uintptr_t>(inv) & 15) == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {  // a segment's 16 positions by four 16-byte loads
+        const int4 t =
+            sg < nseg ? reinterpret_cast<const int4*>(inv)[4 * sg + v] : int4{0, 0, 0, 0};
+        kk[4 * v] = t.x; kk[4 * v + 1] = t.y; kk[4 * v + 2] = t.z; kk[4 * v + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) kk[v] = sg < nseg ? inv[16 * (int64_t)sg + v] : 0;
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       uint32_t h[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int64_t c = 16 * (int64_t)sg + 2 * q + e;
-        int64_t k = sg < nseg ? inv[c] : 0;
+        int64_t k = kk[2 * q + e];
         if (k < 0 || k >= n) k = c < n ? c : 0;  // a malformed permutation must not address out of range
         h[e] = (uint32_t)k;
       }
       pk[i][q] = h[0] | (h[1] << 16);
     }
   }
+  // the next row's chunks are loaded into registers while this row is gathered
+  uint4 nxt[CH];
+  auto load_row = [&](int64_t r) {
+    const uint4* src = reinterpret_cast<const uint4*>(cproc + r * n);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + NT * c;
+      if (idx < nseg) nxt[c] = src[idx];
+    }
+  };
+  load_row(r0);
   for (int64_t r = r0; r < r1; ++r) {
     __syncthreads();  // every thread has read the previous row
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(cproc + r * n);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int idx = tid + NT * c;
-        if (idx < nseg) reinterpret_cast<uint4*>(buf)[idx] = src[idx];
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + NT * c;
+      if (idx < nseg) reinterpret_cast<uint4*>(buf)[idx] = nxt[c];
     }
     __syncthreads();
+    if (r + 1 < r1) load_row(r + 1);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int sg = tid + NT * i;
@@ -884,7 +909,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
                        a.perm, n, inv);
     if (n % 16 == 0 && n <= 32768) {
       // codes through LDS rows; g_idx by the per-column kernel alone
-      const int64_t wgs = hmin(m, (int64_t)1024);
+      // as many workgroups as fit on the GPU at once (2048 threads a CU), so
+      // each reads its positions once and they run in one round
+      const int64_t wgs = hmin(m, (int64_t)(n <= 16384 ? 1024 : 512));
       const int64_t rpw = ceil_div(m, wgs);
       const dim3 grid((unsigned)ceil_div(m, rpw));
       if (n <= 16384)
