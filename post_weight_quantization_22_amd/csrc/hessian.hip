@@ -88,15 +88,42 @@ __device__ __forceinline__ int64_t order_of_tile(int64_t ti, int64_t tj, int64_t
   return bj < bi ? base + 16 * bj + 4 * li + lj : base + 16 * bi + li * (li + 1) / 2 + lj;
 }
 
+// Order of the unsplit kernel's tiles for T % 16 == 0: first the regions of
+// 16 x 16 tiles below the diagonal (rows of regions), each as 8 runs of 32
+// tiles that are 4 x 8 blocks (12 channel blocks a run, 32 a region); then
+// the diagonal regions, each in the 4 x 4 super-tile order.  With the units
+// dealt as below, the 32 workgroups of an XCD run one such block and the 8
+// XCDs one region at a time: a round's units read ~33 channel blocks of the
+// stage instead of ~81 (the other XCDs' requests for them can be served
+// beyond the L2 without HBM), and an XCD's ~12 instead of ~15.
+__device__ __forceinline__ void region_tile(int64_t Lb, int64_t T, int64_t& ti, int64_t& tj) {
+  const int64_t Ts = T / 16, noff = Ts * (Ts - 1) / 2 * 256;
+  if (Lb < noff) {
+    int64_t a, b;
+    tile_coords(Lb / 256, a, b);  // region (a + 1, b), b <= a
+    const int64_t k = Lb % 256, c = k / 32, e = k % 32;
+    ti = 16 * (a + 1) + 4 * (c / 2) + e / 8;
+    tj = 16 * b + 8 * (c % 2) + e % 8;
+  } else {
+    const int64_t d = Lb - noff, R = d / 136;
+    int64_t li, lj;
+    tile_of_order(d % 136, 16, li, lj);
+    ti = 16 * R + li;
+    tj = 16 * R + lj;
+  }
+}
+
 // Work units of the interior kernel.  The first ntiles - T2 tiles (in the
 // order above) are split P ways over the tokens, the last T2 tiles 2P ways
 // into half-length units, which run last: T2 is chosen so that the full
 // units fill whole rounds of 256 workgroups and the half units the rest, so
 // no CU idles through a last, partly filled round of full units.  Workgroup
-// b runs on XCD b % 8; each kind of unit is dealt so that XCD x takes a
-// contiguous range of it: whole token splits per XCD when the split count is
-// a multiple of 8, and so the ~32 workgroups in flight on one XCD read the
-// same token rows of a few channel blocks and share them through its L2.
+// b runs on XCD b % 8.  Split plans (P > 1): each kind of unit is dealt so
+// that XCD x takes a contiguous range of it: whole token splits per XCD when
+// the split count is a multiple of 8, and so the ~32 workgroups in flight on
+// one XCD read the same token rows of a few channel blocks and share them
+// through its L2.  Unsplit (P == 1): round by round, XCD x takes the x-th run
+// of 32 of the round's 256 consecutive units (the region order above).
 // half: the unit is a half-length one; slot: its partial tile.
 __device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64_t T2,
                                           int64_t& p, int64_t& ti, int64_t& tj, bool& half,
@@ -107,12 +134,21 @@ __device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64
   half = b >= U1;
   const int64_t bb = half ? b - U1 : b;
   const int64_t U = half ? T2 * 2 * P : U1;
-  const int64_t U8 = (U / 8) * 8;
-  const int64_t u = bb < U8 ? (bb % 8) * (U8 / 8) + bb / 8 : bb;
+  int64_t u;
+  if (P == 1) {
+    // unsplit: round g's 256 units (one a CU) are consecutive in the order,
+    // XCD x takes the x-th run of 32 of them
+    const int64_t U256 = (U / 256) * 256;
+    u = bb < U256 ? (bb / 256) * 256 + (bb % 8) * 32 + (bb % 256) / 8 : bb;
+  } else {
+    const int64_t U8 = (U / 8) * 8;
+    u = bb < U8 ? (bb % 8) * (U8 / 8) + bb / 8 : bb;
+  }
   const int64_t nt = half ? T2 : n1;
   p = u / nt;
   const int64_t Lb = (half ? n1 : 0) + u % nt;
-  tile_of_order(Lb, T, ti, tj);
+  if (P == 1 && T % 16 == 0) region_tile(Lb, T, ti, tj);
+  else tile_of_order(Lb, T, ti, tj);
   slot = half ? P * ntiles + p * T2 + (Lb - n1) : p * ntiles + ti * (ti + 1) / 2 + tj;
 }
 
