@@ -52,6 +52,21 @@ __device__ __forceinline__ float quant_code(float w, float scale, float zero, fl
   return fminf(fmaxf(q, 0.0f), maxq);
 }
 
+// q = clamp(rne(w / scale) + zero, 0, maxq) with the IEEE quotient w / scale,
+// computed as w * (1 / scale): that product is within 1.5 * 2^-23 |w / scale|
+// of the quotient, so the two round to different integers only if a
+// half-integer lies that close; then (rarely) the division itself decides.
+// A non-finite t (w not finite, or 1 / scale overflowing for a subnormal
+// scale) also takes the division: the test below is false only for a number.
+__device__ __forceinline__ float quant_code_fast(float w, float scale, float rscale, float zero,
+                                                 float maxq) {
+  const float t = w * rscale;
+  float q = rintf(t);
+  const float tol = fmaxf(fabsf(t), 1.0f) * 3.6e-7f;
+  if (!(fabsf(fabsf(t - floorf(t)) - 0.5f) > tol)) q = rintf(__fdiv_rn(w, scale));
+  return fminf(fmaxf(q + zero, 0.0f), maxq);
+}
+
 __device__ __forceinline__ bool is_finite(float x) { return isfinite(x); }
 
 // LDS DMA of 16 (4) bytes per lane: lane l's bytes land at lds + 16 l (4 l),

@@ -268,19 +268,6 @@ __global__ __launch_bounds__(256) void static_params_kernel(const void* __restri
   zeros[i] = zero;
 }
 
-// q = clamp(rne(w / scale) + zero, 0, maxq) with the IEEE quotient w / scale,
-// computed as w * (1 / scale): that product is within 1.5 * 2^-23 |w / scale|
-// of the quotient, so the two round to different integers only if a
-// half-integer lies that close; then (rarely) the division itself decides.
-__device__ __forceinline__ float quant_code_fast(float w, float scale, float rscale, float zero,
-                                                 float maxq) {
-  const float t = w * rscale;
-  float q = rintf(t);
-  const float tol = fmaxf(fabsf(t), 1.0f) * 3.6e-7f;
-  if (fabsf(fabsf(t - floorf(t)) - 0.5f) <= tol) q = rintf(__fdiv_rn(w, scale));
-  return fminf(fmaxf(q + zero, 0.0f), maxq);
-}
-
 // One 128-column block.  G > 0: group size (8..128, divides 128), parameters
 // computed here at each group's first column.  G < 0: parameters given in
 // scales/zeros before the block; processing column k takes group

@@ -6,8 +6,8 @@
 // zero-point, per group of consecutive weights.
 //
 // HBM-bound: each lane owns 8 consecutive weights of a row (16 B bf16 or
-// 32 B fp32 loaded at once), a group spans G/8 lanes of one wave and its
-// min/max is a butterfly over those lanes.  Whole-row groups (G == -1, or any
+// 32 B fp32 loaded at once) in each of two rows, a group spans G/8 lanes of
+// one wave and its min/max is a butterfly over those lanes.  Whole-row groups (G == -1, or any
 // G the wave path does not cover) take a workgroup-per-group path.
 #include "kernels.hpp"
 
@@ -70,25 +70,13 @@ __device__ __forceinline__ void store8_codes(uint8_t* codes, int64_t off, int64_
 }
 
 // Wave path: G is a power of two in [8, 512]; LPG = G / 8 lanes per group.
+// A lane takes the same 8 columns of two rows, r and r + hm (hm = ceil(m / 2)),
+// both loads in flight before either is quantized.
 template <int LPG>
-__global__ __launch_bounds__(256) void rtn_wave_kernel(const void* __restrict__ W, int dt,
-                                                       int64_t m, int64_t n, int64_t ldw,
-                                                       int64_t ngroups, float maxq, int sym,
-                                                       uint8_t* __restrict__ codes,
-                                                       float* __restrict__ scales,
-                                                       float* __restrict__ zeros) {
-  const int64_t slots_per_row = ngroups * LPG;
-  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool live = slot < m * slots_per_row;
-  const int64_t r = live ? slot / slots_per_row : 0;
-  const int64_t k = slot - r * slots_per_row;
-  const int64_t g = k / LPG;
-  const int64_t c0 = g * (LPG * 8) + (k % LPG) * 8;
-  Chunk8 ch;
-  if (live) ch = load8(W, dt, r * ldw, c0, n);
-  else
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ch.v[e] = 0.0f;
+__device__ __forceinline__ void rtn_chunk(const Chunk8& ch, bool live, int64_t r, int64_t n,
+                                          int64_t ngroups, int64_t g, int64_t k, int64_t c0,
+                                          float maxq, int sym, uint8_t* __restrict__ codes,
+                                          float* __restrict__ scales, float* __restrict__ zeros) {
   float vmin = ch.v[0], vmax = ch.v[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) {
@@ -105,14 +93,46 @@ __global__ __launch_bounds__(256) void rtn_wave_kernel(const void* __restrict__ 
   if (sym) sym_params(fmaxf(fabsf(vmin), fabsf(vmax)), maxq, scale, zero);
   else minmax_params(vmin, vmax, maxq, scale, zero);
   if (!live) return;
+  // codes by the reciprocal, the IEEE quotient where a half-integer is near
+  const float rscale = 1.0f / scale;
   float q[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) q[e] = quant_code(ch.v[e], scale, zero, maxq);
+  for (int e = 0; e < 8; ++e) q[e] = quant_code_fast(ch.v[e], scale, rscale, zero, maxq);
   store8_codes(codes, r * n, c0, n, q);
   if ((k % LPG) == 0) {
     scales[r * ngroups + g] = scale;
     zeros[r * ngroups + g] = zero;
   }
+}
+
+template <int LPG>
+__global__ __launch_bounds__(256) void rtn_wave_kernel(const void* __restrict__ W, int dt,
+                                                       int64_t m, int64_t n, int64_t ldw,
+                                                       int64_t ngroups, float maxq, int sym,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       float* __restrict__ zeros) {
+  const int64_t slots_per_row = ngroups * LPG;
+  const int64_t hm = (m + 1) / 2;
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live0 = slot < hm * slots_per_row;
+  int64_t r;
+  if (hm * slots_per_row <= INT32_MAX) {  // 32-bit division (a 64-bit one is a long sequence)
+    r = live0 ? (int64_t)((uint32_t)slot / (uint32_t)slots_per_row) : 0;
+  } else {
+    r = live0 ? slot / slots_per_row : 0;
+  }
+  const int64_t k = live0 ? slot - r * slots_per_row : 0;
+  const bool live1 = live0 && r + hm < m;
+  const int64_t g = k / LPG;
+  const int64_t c0 = g * (LPG * 8) + (k % LPG) * 8;
+  Chunk8 ch0, ch1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ch0.v[e] = ch1.v[e] = 0.0f;
+  if (live0) ch0 = load8(W, dt, r * ldw, c0, n);
+  if (live1) ch1 = load8(W, dt, (r + hm) * ldw, c0, n);
+  rtn_chunk<LPG>(ch0, live0, r, n, ngroups, g, k, c0, maxq, sym, codes, scales, zeros);
+  rtn_chunk<LPG>(ch1, live1, r + hm, n, ngroups, g, k, c0, maxq, sym, codes, scales, zeros);
 }
 
 // Workgroup path: one workgroup per (row, group) of any length.
@@ -172,7 +192,7 @@ hipError_t launch_rtn(const void* W, int dt, int64_t m, int64_t n, int64_t ldw, 
   const int64_t lpg = Ge / 8;
   const bool wave_path = G > 0 && (G & (G - 1)) == 0 && G >= 8 && G <= 512;
   if (wave_path) {
-    const int64_t slots = m * ngroups * lpg;
+    const int64_t slots = (m + 1) / 2 * ngroups * lpg;  // a lane takes two rows
     const dim3 grid((unsigned)ceil_div(slots, 256));
 #define GPTQ_RTN_CASE(L)                                                                     \
   case L:                                                                                  \

@@ -103,3 +103,33 @@ def test_pack_ordered_bit_exact(bits, n):
     q.gptq_pack_ordered(dev(codes, torch.uint8), bits, dev(perm, torch.int32), packed)
     torch.cuda.synchronize()
     assert np.array_equal(host(packed).view(np.uint32), ref)
+
+
+def test_rtn_subnormal_groups_and_exact_half_steps():
+    """Groups whose scale is subnormal (1 / scale overflows to inf in fp32) and
+    groups whose values sit exactly on half steps of the grid (rounding ties):
+    the codes still equal the oracle's rint(w / scale) decisions bit for bit."""
+    q = need_gpu()
+    rng = np.random.default_rng(11)
+    m, n, G = 8, 256, 64
+    W = f32(rng.standard_normal((m, n)) * 0.02)
+    W[0, :] = f32(rng.standard_normal(n) * 1e-41)      # subnormal range: scale ~1e-43
+    W[1, :64] = f32(rng.standard_normal(64) * 1e-44)   # a few subnormal steps only
+    steps = np.arange(64) % 15 + 0.5                   # k + 1/2 on a unit grid
+    W[2, 64:128] = steps
+    W[2, 64] = 0.0
+    W[2, 65] = 15.0                                    # range [0, 15]: scale 1, zero 0
+    W[3, :64] = -steps * 0.25                          # scale 0.25, values on half steps
+    W[3, 0] = -3.75
+    W = W.astype(np.float32).astype(np.float64)
+    for bits in (4, 3):
+        codes_o, scales_o, zeros_o = oracle.rtn_minmax(W, bits, G)
+        codes = torch.empty((m, n), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((m, n // G), dtype=torch.float32, device="cuda")
+        zeros = torch.empty((m, n // G), dtype=torch.float32, device="cuda")
+        say("rtn subnormal / half steps", bits)
+        q.rtn_minmax(dev(W.astype(np.float32), torch.float32), bits, G, codes, scales, zeros)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(scales).astype(np.float64), scales_o)
+        assert np.array_equal(host(zeros).astype(np.float64), zeros_o)
+        assert np.array_equal(host(codes).astype(np.int64), codes_o.astype(np.int64))
