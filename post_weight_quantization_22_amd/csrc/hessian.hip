@@ -88,14 +88,15 @@ __device__ __forceinline__ int64_t order_of_tile(int64_t ti, int64_t tj, int64_t
   return bj < bi ? base + 16 * bj + 4 * li + lj : base + 16 * bi + li * (li + 1) / 2 + lj;
 }
 
-// Order of the unsplit kernel's tiles for T % 16 == 0: first the regions of
+// Order of the tiles for T % 16 == 0: first the regions of
 // 16 x 16 tiles below the diagonal (rows of regions), each as 8 runs of 32
 // tiles that are 4 x 8 blocks (12 channel blocks a run, 32 a region); then
 // the diagonal regions, each in the 4 x 4 super-tile order.  With the units
-// dealt as below, the 32 workgroups of an XCD run one such block and the 8
-// XCDs one region at a time: a round's units read ~33 channel blocks of the
-// stage instead of ~81 (the other XCDs' requests for them can be served
-// beyond the L2 without HBM), and an XCD's ~12 instead of ~15.
+// dealt as below, the 32 workgroups of an XCD run one such block (~12
+// channel blocks of the stage instead of ~15 in the super-tile order) and,
+// unsplit, the 8 XCDs one region at a time: a round's units read ~33 channel
+// blocks instead of ~81 (the other XCDs' requests for them can be served
+// beyond the L2 without HBM).
 __device__ __forceinline__ void region_tile(int64_t Lb, int64_t T, int64_t& ti, int64_t& tj) {
   const int64_t Ts = T / 16, noff = Ts * (Ts - 1) / 2 * 256;
   if (Lb < noff) {
@@ -113,8 +114,19 @@ __device__ __forceinline__ void region_tile(int64_t Lb, int64_t T, int64_t& ti, 
   }
 }
 
+// Position of tile (ti, tj) in the region order (T % 16 == 0).
+__device__ __forceinline__ int64_t order_of_region_tile(int64_t ti, int64_t tj, int64_t T) {
+  const int64_t Ts = T / 16, noff = Ts * (Ts - 1) / 2 * 256;
+  const int64_t SI = ti / 16, SJ = tj / 16, li = ti % 16, lj = tj % 16;
+  if (SI > SJ) {
+    const int64_t R = (SI - 1) * SI / 2 + SJ;  // region (a + 1, b) at a (a + 1) / 2 + b
+    return 256 * R + 32 * ((li / 4) * 2 + lj / 8) + 8 * (li % 4) + lj % 8;
+  }
+  return noff + 136 * SI + order_of_tile(li, lj, 16);
+}
+
 // Work units of the interior kernel.  The first ntiles - T2 tiles (in the
-// order above) are split P ways over the tokens, the last T2 tiles 2P ways
+// region order for T % 16 == 0, else the super-tile order) are split P ways over the tokens, the last T2 tiles 2P ways
 // into half-length units, which run last: T2 is chosen so that the full
 // units fill whole rounds of 256 workgroups and the half units the rest, so
 // no CU idles through a last, partly filled round of full units.  Workgroup
@@ -147,7 +159,7 @@ __device__ __forceinline__ void hess_unit(int64_t b, int64_t P, int64_t T, int64
   const int64_t nt = half ? T2 : n1;
   p = u / nt;
   const int64_t Lb = (half ? n1 : 0) + u % nt;
-  if (P == 1 && T % 16 == 0) region_tile(Lb, T, ti, tj);
+  if (T % 16 == 0) region_tile(Lb, T, ti, tj);
   else tile_of_order(Lb, T, ti, tj);
   slot = half ? P * ntiles + p * T2 + (Lb - n1) : p * ntiles + ti * (ti + 1) / 2 + tj;
 }
@@ -530,7 +542,8 @@ __global__ __launch_bounds__(256) void reduce_full_partials_kernel(const float* 
   const int64_t gi = ti * FT_I + ii, gj = tj * FT_J + jj;
   if (gj > gi) return;  // the whole quad lies above the diagonal
   // this tile's partials: P full splits, or 2P half splits for the last T2 tiles
-  const int64_t Lb = order_of_tile(ti, tj, T), n1 = ntiles - T2;
+  const int64_t Lb = T % 16 == 0 ? order_of_region_tile(ti, tj, T) : order_of_tile(ti, tj, T);
+  const int64_t n1 = ntiles - T2;
   const bool halves = Lb >= n1;
   const int64_t first = halves ? P * ntiles + (Lb - n1) : L;
   const int64_t nq = halves ? 2 * P : P;

@@ -19,6 +19,7 @@ HESS_CASES = [
     (1024, 4096, 2048, "bf16"),
     (1280, 8192, 2048, "bf16"),   # 5x5 tiles (row-major tile order), some tiles in half-length splits
     (2048, 16384, 2048, "bf16"),  # 8x8 tiles (super-tile order), some tiles in half-length splits
+    (8192, 4096, 2048, "bf16"),   # 32x32 tiles: the region order in a split plan
 ]
 
 
