@@ -102,6 +102,12 @@ def test_llama7b_attn_full_size():
           f"{sc_rel.max():.2e}", flush=True)
     assert sc_rel.max() <= 1e-4
     assert np.array_equal(zeros[clean], ref.zeros[clean])
+    # the free-running rate over every group of every row (a group after a tie in its row
+    # is a point on another valid trajectory, so this rate is reported, not bounded)
+    all_rel = np.abs(scales - ref.scales) / ref.scales
+    print(f"free-running scales within 1e-4: {float(np.mean(all_rel <= 1e-4)):.6f} of "
+          f"{all_rel.size} groups; zeros equal: {float(np.mean(zeros == ref.zeros)):.6f}",
+          flush=True)
     H = 2.0 * S_ref
     Wq = oracle.dequant_layer(codes.astype(np.float64), scales.astype(np.float64),
                               zeros.astype(np.float64), host(buf.g_idx))

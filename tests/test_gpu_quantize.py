@@ -91,17 +91,27 @@ def test_quantize_given_oracle_U(m, n, tokens, G, bits, desc, wdt, xdist):
     assert abs(e_dev - e_ref) <= 1e-3 * e_ref
 
 
-def test_quantize_symmetric_and_dead_columns():
+@pytest.mark.parametrize("bits,desc", [(4, False), (3, True)])
+def test_quantize_symmetric_and_dead_columns(bits, desc):
     q = need_gpu()
     W, X, S, P, U32, ref, codes, scales, zeros, g_idx, row_err, info = run_case(
-        q, 32, 256, 1024, 64, 4, False, "bf16", "normal", sym=True, dead_cols=(3, 200))
+        q, 32, 256, 1024, 64, bits, desc, "bf16", "normal", sym=True, dead_cols=(3, 200))
     assert info == 0
     assert P.dead[3] and P.dead[200]
     assert match_rate(codes, ref.codes) >= 0.999
     Wq = oracle.dequant_layer(codes.astype(np.float64), scales.astype(np.float64),
                               zeros.astype(np.float64), g_idx)
     assert np.all(Wq[:, [3, 200]] == 0.0)
-    assert np.all(zeros == 8.0)
+    assert np.all(zeros == float(2 ** (bits - 1)))
+    # the symmetric loop replayed on the oracle's arithmetic, following the device's choices
+    codes_proc = codes.astype(np.float64)[:, P.perm]
+    rep = oracle.replay_check(W, U32, bits, 64, 128, P.perm, P.dead, codes_proc, scales, zeros,
+                              sym=True)
+    print(f"replay (sym): mism {rep.mismatches} ties {rep.ties} hard {rep.hard} "
+          f"zero-hard {rep.zero_hard} scale rel {rep.scale_max_rel:.2e}")
+    assert rep.hard == 0 and rep.zero_hard == 0
+    assert rep.scale_max_rel <= 1e-4
+    assert np.allclose(row_err, rep.row_err, rtol=1e-3, atol=1e-12 * rep.row_err.max())
 
 
 def test_quantize_reports_non_finite_weights():
