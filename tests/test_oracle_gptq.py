@@ -63,6 +63,48 @@ def test_error_identity_W_minus_Q_equals_E_U():
     assert np.allclose(lhs, rhs, rtol=1e-9, atol=0)
 
 
+def test_inverse_free_route_gives_the_same_codes():
+    """A third route to the loop's decisions, needing no inverse of H_d: with R the upper
+    factor of H_d = R R^T (a Cholesky factorization taken from the last index backwards),
+    U = R^-1, so W - Q = E U gives E = (W - Q) R and the pre-rounding value of column j is
+    w_j + sum_{k<j} d_k R_kj / R_jj with d_k = w_k - dequant(q_k) of the ORIGINAL weights.
+    A group's parameters come from its columns' values when its first column j0 is reached
+    (every column before j0 applied, none after); with T = D[:, :j0] R[:j0, group] and
+    R U = I those values are W[:, group] + T inv(R[group, group]), so only the groups'
+    diagonal blocks are inverted.  Written here column by column from R (no E, no lazy
+    blocks, no U), it must give the oracle's codes, scales and zero-points (plain fp64
+    decisions on both sides)."""
+    from oracle.quantizer import group_params, quantize_codes
+    W, X = _layer(32, 192, 800, seed=7)
+    S = oracle.hessian_S([X])
+    m, n = W.shape
+    G = 64
+    for desc in (False, True):
+        P = oracle.prepare(S, 0.01, desc)
+        assert not P.dead.any()
+        r = oracle.gptq_quantize(W, P.U, 4, G, 64, P.perm, P.dead, exact=True)
+        rev = np.arange(n)[::-1]
+        R = np.linalg.cholesky(P.Hd[np.ix_(rev, rev)])[np.ix_(rev, rev)]
+        assert np.allclose(R, np.triu(R), rtol=0, atol=0)
+        Wp = W[:, P.perm].astype(np.float64)
+        D = np.zeros_like(Wp)
+        codes = np.zeros_like(Wp)
+        scales, zeros = [], []
+        for j in range(n):
+            if j % G == 0:
+                T = D[:, :j] @ R[:j, j:j + G]
+                pre = Wp[:, j:j + G] + T @ np.linalg.inv(R[j:j + G, j:j + G])
+                sc, zp = group_params(pre, 4, False, True)
+                scales.append(sc)
+                zeros.append(zp)
+            w = Wp[:, j] + (D[:, :j] @ R[:j, j]) / R[j, j]
+            codes[:, j] = quantize_codes(w, sc, zp, 4, True)
+            D[:, j] = Wp[:, j] - sc * (codes[:, j] - zp)
+        assert np.array_equal(codes, r.codes[:, P.perm])
+        assert np.allclose(np.stack(scales, 1), r.scales, rtol=1e-12, atol=0)
+        assert np.array_equal(np.stack(zeros, 1), r.zeros)
+
+
 def test_diagonal_hessian_reduces_to_rtn():
     rng = np.random.default_rng(4)
     W = f32(rng.standard_normal((32, 128)) * 0.02)
